@@ -1,0 +1,177 @@
+/*
+ * dsa.h -- C ABI of libdsa: the DeepSeek Sparse Attention (DSA) forward on one
+ * context-parallel (CP) rank's share, for AMD Instinct MI355X (gfx950).
+ *
+ * The share is a slice of local query rows scored by the Lightning Indexer, reduced to each
+ * row's causal top-k keys, and attended with multi-query attention over the selected rows of
+ * the FULL, already all-gathered key / latent-KV sequence.  Sources:
+ *   - page "CANNTorchTitan: DeepSeek-V3.2 32k长序列预训练昇腾优化实践", section
+ *     "SparseLightningIndexerGradKLLoss" (Lightning Indexer and Sparse Flash Attention
+ *     formulas), section "SparseFlashAttentionGrad" (backward), section "自定义CP策略"
+ *     (CP = local queries against all-gathered keys/values);
+ *   - page "context_parallel.md" (HyperParallel CP guide), section "DSA CP" (the indexer,
+ *     sparse-attention and indexer-loss boundaries and their query/key placements, BSND/TND
+ *     layouts), and the load_balance note (head-tail shares, masks from K's global length);
+ *   - page "CANN/torchtitan-npu融合算子适配", section "DSA" (indexer selects the indices the
+ *     sparse multi-query attention consumes).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE memory owned by the caller; the library never allocates or
+ *     frees device memory.  Scratch space for dsa_forward comes from the caller's workspace,
+ *     sized by dsa_workspace_bytes.  The dsa_shape struct and its segment array are HOST
+ *     memory, read before the call returns.
+ *   - Tensors are dense row-major.  bf16 values are raw IEEE bfloat16 bit patterns.
+ *   - Key indices are absolute rows of k_idx / kv; -1 marks an empty top-k slot.
+ *   - Arguments are validated synchronously: DSA_ERR_INVALID_ARG / DSA_ERR_UNSUPPORTED /
+ *     DSA_ERR_WORKSPACE return without launching anything.  Otherwise the work is enqueued on
+ *     `stream` (a hipStream_t; NULL means the default stream) and DSA_OK is returned with no
+ *     host synchronisation.  A failed launch returns DSA_ERR_HIP.  Device-side faults surface
+ *     at the caller's next synchronisation.  dsa_last_error() describes the last non-OK status
+ *     of the calling thread.  No C++ exception crosses this interface.
+ *   - Supported dimensions (anything else is DSA_ERR_UNSUPPORTED):
+ *       indexer (h_idx, d_idx) in {(4, 32), (64, 128)};
+ *       attention (h, d_qk, d_v) in {(8, 80, 64), (128, 576, 512)};
+ *       1 <= topk <= 4096; every window length <= 65536 keys.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad segment table        */
+  DSA_ERR_UNSUPPORTED = 2, /* dimensions or options this build has no kernel for    */
+  DSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dsa_workspace_bytes  */
+  DSA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed             */
+} dsa_status;
+
+/* Element type of the index query / index key tensors. */
+typedef enum {
+  DSA_IDX_BF16 = 0,    /* q_idx, k_idx are bf16; q_scale, k_scale must be NULL          */
+  DSA_IDX_FP8_E4M3 = 1 /* q_idx, k_idx are OCP e4m3fn codes (uint8) with one fp32 scale
+                          per token row: represented value = code value * row scale    */
+} dsa_idx_dtype;
+
+/*
+ * One run of local query rows sharing a key sequence (the CP guide's DSA CP placements:
+ * query side sharded along the sequence, key side replicated).  Local rows
+ * [q_start, q_start + q_len) sit at global positions pos0 .. pos0 + q_len - 1 of a sequence
+ * whose keys are rows [k_start, k_start + k_len) of k_idx / kv.  Row q_start + r attends
+ * keys k_start .. k_start + pos0 + r inclusive (causal, diagonal included), so its window
+ * holds pos0 + r + 1 keys; pos0 + q_len <= k_len is required.
+ *   - an unsharded causal sequence is one segment with pos0 = 0;
+ *   - a CP rank's contiguous share of a gathered sequence sets pos0 to its offset;
+ *   - a head-tail balanced share is two segments (two chunks, each with its own pos0);
+ *   - BSND with B sequences / packed TND documents are one segment per sequence.
+ * Segments must not overlap in query rows.  Rows covered by no segment are left untouched
+ * by the indexer, top-k and fused forward.
+ */
+typedef struct {
+  int32_t q_start, q_len, k_start, k_len, pos0;
+} dsa_segment;
+
+typedef struct {
+  int32_t n_q, n_k;       /* local query rows, gathered key rows                          */
+  int32_t h_idx, d_idx;   /* index heads, index head width                                */
+  int32_t h, d_qk, d_v;   /* query heads, latent row width (value + rope), value width    */
+  int32_t topk;           /* selected keys per row; a row keeps min(topk, window) of them */
+  float softmax_scale;    /* multiplies q.k before the softmax (1/sqrt(d_qk) usually)     */
+  int32_t idx_dtype;      /* dsa_idx_dtype                                                 */
+  const dsa_segment *segs; /* host array of n_segs segments                                */
+  int32_t n_segs;
+} dsa_shape;
+
+/* DSA_ABI_VERSION of the built library. */
+int dsa_abi_version(void);
+
+/* Message for the calling thread's last non-OK status ("" if none).  Valid until the next
+ * call on the same thread. */
+const char *dsa_last_error(void);
+
+/*
+ * Workspace bytes dsa_forward needs for `shape` (the per-row indexer scores of each row's
+ * window, and the top-k indices when the caller does not keep them).  Host-only.
+ */
+dsa_status dsa_workspace_bytes(const dsa_shape *shape, size_t *bytes);
+
+/*
+ * Lightning Indexer scores (page "CANNTorchTitan: ...", section
+ * "SparseLightningIndexerGradKLLoss", indexer top-k value formula; the CP guide's indexer
+ * boundary (query, key, weights)):
+ *     scores[i, s] = sum_j w_idx[i, j] * ReLU( q_idx[i, j, :] . k_idx[s, :] )
+ * for s in row i's window, -inf for every other column of a covered row.
+ *   q_idx   [n_q, h_idx, d_idx]  bf16 (or e4m3fn codes with q_scale [n_q] fp32)
+ *   k_idx   [n_k, d_idx]         bf16 (or e4m3fn codes with k_scale [n_k] fp32)
+ *   w_idx   [n_q, h_idx]         fp32 per-token head weights (any sign)
+ *   scores  [n_q, n_k]           fp32 output
+ * bf16 products are accumulated in fp32 (MFMA); ReLU, weights and the head sum are fp32.
+ */
+dsa_status dsa_indexer_scores(const dsa_shape *shape, const void *q_idx, const float *q_scale,
+                              const void *k_idx, const float *k_scale, const float *w_idx,
+                              float *scores, void *stream);
+
+/*
+ * Per-row causal top-k over indexer scores laid out as dsa_indexer_scores writes them
+ * ([n_q, n_k] fp32; only each row's window is read).  Row i keeps n_i = min(topk, window)
+ * keys with the largest scores; equal scores go to the lower key index and -0.0 equals +0.0.
+ * topk_idx [n_q, topk] int32 receives the kept absolute key rows in ascending order followed
+ * by -1.  Scores inside a window must be finite (NaN ordering is unspecified).
+ */
+dsa_status dsa_topk_select(const dsa_shape *shape, const float *scores, int32_t *topk_idx,
+                           void *stream);
+
+/*
+ * Sparse multi-query attention over gathered latent rows (page "CANNTorchTitan: ...",
+ * Sparse Flash Attention formula; the CP guide's sparse-attention boundary with key = value
+ * = the shared latent row under weight absorption, rope = its last d_qk - d_v columns):
+ *     z[h, t]       = softmax_scale * q[i, h, :] . kv[topk_idx[i, t], :]
+ *     out[i, h, :]  = sum_t softmax_t(z[h, :]) * kv[topk_idx[i, t], :d_v]
+ *     softmax_max[i, h] = max_t z[h, t];  softmax_sum[i, h] = sum_t exp(z[h, t] - max)
+ *   q [n_q, h, d_qk] bf16, kv [n_k, d_qk] bf16, topk_idx [n_q, topk] int32,
+ *   out [n_q, h, d_v] bf16; softmax_max / softmax_sum [n_q, h] fp32 (either may be NULL).
+ * Every row 0..n_q-1 is computed (segments are not used).  Slots holding a negative index or
+ * an index >= n_k are skipped; a row with no valid slot gets out = 0, max = -inf, sum = 0.
+ * bf16 MFMA with fp32 accumulation and an fp32 online softmax.
+ */
+dsa_status dsa_sparse_attn(const dsa_shape *shape, const void *q, const void *kv,
+                           const int32_t *topk_idx, void *out, float *softmax_max,
+                           float *softmax_sum, void *stream);
+
+/*
+ * The fused DSA forward on one CP rank's share: indexer -> top-k -> sparse attention,
+ * enqueued back to back on `stream` (the page "CANNTorchTitan: ..." section "自定义CP策略":
+ * the CP forward is the plain forward over all-gathered keys).  Arguments as above; scores
+ * live only in `workspace` (each row's window, never the full [n_q, n_k]).  topk_idx may be
+ * NULL (then the indices stay in the workspace), softmax_max / softmax_sum may be NULL.
+ * Rows covered by no segment are left untouched.
+ */
+dsa_status dsa_forward(const dsa_shape *shape, const void *q_idx, const float *q_scale,
+                       const void *k_idx, const float *k_scale, const float *w_idx,
+                       const void *q, const void *kv, void *out, int32_t *topk_idx,
+                       float *softmax_max, float *softmax_sum, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
+ * Per-row (per-token) fp8 quantization for the fp8 indexer: for each of `rows` rows of
+ * `cols` bf16 values, scale = amax(|row|) / 448 (1.0 for an all-zero row) and
+ * code = e4m3fn(round-to-nearest-even(x / scale)), saturating at +-448; scale and x / scale
+ * are computed in fp32 with correctly rounded division.
+ *   x_bf16 [rows, cols] bf16 -> x_fp8 [rows, cols] uint8 codes, scale [rows] fp32.
+ * For the index query use rows = n_q, cols = h_idx * d_idx (one scale per token).
+ */
+dsa_status dsa_quantize_fp8_rows(const void *x_bf16, int64_t rows, int32_t cols, void *x_fp8,
+                                 float *scale, void *stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,354 @@
+// C ABI of libdsa (declared in include/dsa.h): argument validation, per-launch segment
+// tables, workspace layout and kernel launches on the caller's stream.  Nothing here
+// allocates device memory or synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "dsa.h"
+#include "dsa_device.h"
+
+namespace dsa {
+hipError_t launch_indexer(const IndexerArgs& a, int h_idx, int d_idx, bool fp8, hipStream_t s);
+hipError_t launch_fill_outside(const FillArgs& a, hipStream_t s);
+int indexer_rows_per_block();
+hipError_t launch_topk(const TopkArgs& a, int max_window, hipStream_t s);
+hipError_t launch_sparse_attn(const AttnArgs& a, int h, int d_qk, int d_v, int nblocks,
+                              hipStream_t s);
+hipError_t launch_quant_fp8_rows(const QuantArgs& a, hipStream_t s);
+}  // namespace dsa
+
+namespace {
+
+thread_local std::string g_err;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+dsa_status ok() {
+  g_err.clear();
+  return DSA_OK;
+}
+
+dsa_status hip_fail(hipError_t e, const char* what) {
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxTopk = 4096;
+constexpr int64_t kMaxWindow = 65536;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool indexer_dims_ok(int h_idx, int d_idx) {
+  return (h_idx == 64 && d_idx == 128) || (h_idx == 4 && d_idx == 32);
+}
+bool attn_dims_ok(int h, int d_qk, int d_v) {
+  return (h == 128 && d_qk == 576 && d_v == 512) || (h == 8 && d_qk == 80 && d_v == 64);
+}
+
+struct Plan {
+  std::vector<dsa_segment> segs;  // non-empty segments, longest windows first
+  int64_t max_window = 0;         // longest window over all rows
+  int64_t covered_rows = 0;
+};
+
+enum Need { kNeedIndexer = 1, kNeedTopk = 2, kNeedAttn = 4, kNeedSegs = 8 };
+
+dsa_status check_shape(const dsa_shape* s, int need, Plan& p) {
+  if (!s) return fail(DSA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->n_q < 0 || s->n_k < 0) return fail(DSA_ERR_INVALID_ARG, "negative n_q or n_k");
+  if ((need & (kNeedTopk | kNeedAttn)) && (s->topk < 1))
+    return fail(DSA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", s->topk);
+  if ((need & (kNeedTopk | kNeedAttn)) && s->topk > kMaxTopk)
+    return fail(DSA_ERR_UNSUPPORTED, "topk %d > %d", s->topk, kMaxTopk);
+  if (need & kNeedIndexer) {
+    if (s->idx_dtype != DSA_IDX_BF16 && s->idx_dtype != DSA_IDX_FP8_E4M3)
+      return fail(DSA_ERR_INVALID_ARG, "unknown idx_dtype %d", s->idx_dtype);
+    if (!indexer_dims_ok(s->h_idx, s->d_idx))
+      return fail(DSA_ERR_UNSUPPORTED, "indexer dims (h_idx=%d, d_idx=%d) not built",
+                  s->h_idx, s->d_idx);
+  }
+  if (need & kNeedAttn) {
+    if (!attn_dims_ok(s->h, s->d_qk, s->d_v))
+      return fail(DSA_ERR_UNSUPPORTED, "attention dims (h=%d, d_qk=%d, d_v=%d) not built",
+                  s->h, s->d_qk, s->d_v);
+    if (!std::isfinite(s->softmax_scale))
+      return fail(DSA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  }
+  p = Plan();
+  if (!(need & kNeedSegs)) return DSA_OK;
+  if (s->n_segs < 0) return fail(DSA_ERR_INVALID_ARG, "negative n_segs");
+  if (s->n_segs > 0 && !s->segs) return fail(DSA_ERR_INVALID_ARG, "segs is NULL");
+  std::vector<std::pair<int64_t, int64_t>> spans;
+  for (int i = 0; i < s->n_segs; ++i) {
+    const dsa_segment& g = s->segs[i];
+    if (g.q_start < 0 || g.q_len < 0 || g.k_start < 0 || g.k_len < 0 || g.pos0 < 0)
+      return fail(DSA_ERR_INVALID_ARG, "segment %d has a negative field", i);
+    if ((int64_t)g.q_start + g.q_len > s->n_q)
+      return fail(DSA_ERR_INVALID_ARG, "segment %d: query rows past n_q", i);
+    if ((int64_t)g.k_start + g.k_len > s->n_k)
+      return fail(DSA_ERR_INVALID_ARG, "segment %d: key rows past n_k", i);
+    if (g.q_len == 0) continue;
+    if ((int64_t)g.pos0 + g.q_len > g.k_len)
+      return fail(DSA_ERR_INVALID_ARG,
+                  "segment %d: last position %lld is beyond its %d keys", i,
+                  (long long)g.pos0 + g.q_len - 1, g.k_len);
+    const int64_t w = (int64_t)g.pos0 + g.q_len;
+    if (w > kMaxWindow)
+      return fail(DSA_ERR_UNSUPPORTED, "segment %d: window of %lld keys > %lld", i,
+                  (long long)w, (long long)kMaxWindow);
+    p.max_window = std::max(p.max_window, w);
+    p.covered_rows += g.q_len;
+    spans.push_back({g.q_start, (int64_t)g.q_start + g.q_len});
+    p.segs.push_back(g);
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].first < spans[i - 1].second)
+      return fail(DSA_ERR_INVALID_ARG, "segments overlap in query rows");
+  std::stable_sort(p.segs.begin(), p.segs.end(), [](const dsa_segment& a, const dsa_segment& b) {
+    return (int64_t)a.pos0 + a.q_len > (int64_t)b.pos0 + b.q_len;
+  });
+  return DSA_OK;
+}
+
+// Split the plan into launch-sized tables; rows_per_block rows of a segment share a block.
+std::vector<dsa::SegTable> make_tables(const Plan& p, int rows_per_block) {
+  std::vector<dsa::SegTable> out;
+  for (size_t i = 0; i < p.segs.size(); i += dsa::kMaxSegs) {
+    dsa::SegTable t = {};
+    const size_t n = std::min(p.segs.size() - i, (size_t)dsa::kMaxSegs);
+    t.n = (int)n;
+    int blk = 0;
+    for (size_t j = 0; j < n; ++j) {
+      const dsa_segment& g = p.segs[i + j];
+      t.q_start[j] = g.q_start;
+      t.q_len[j] = g.q_len;
+      t.k_start[j] = g.k_start;
+      t.pos0[j] = g.pos0;
+      t.blk_off[j] = blk;
+      blk += (g.q_len + rows_per_block - 1) / rows_per_block;
+    }
+    t.blk_off[n] = blk;
+    out.push_back(t);
+  }
+  return out;
+}
+
+// Row stride (floats) of the compact per-window score rows in the forward workspace.
+int64_t ws_score_ld(const Plan& p) { return (p.max_window + 63) / 64 * 64; }
+
+struct WsLayout {
+  size_t scores_off = 0, idx_off = 0, total = 0;
+};
+
+WsLayout ws_layout(const dsa_shape* s, const Plan& p) {
+  WsLayout w;
+  w.scores_off = 0;
+  w.idx_off = align_up((size_t)s->n_q * (size_t)ws_score_ld(p) * sizeof(float));
+  w.total = w.idx_off + align_up((size_t)s->n_q * (size_t)s->topk * sizeof(int32_t));
+  return w;
+}
+
+dsa_status run_indexer(const dsa_shape* s, const Plan& p, const void* q_idx,
+                       const float* q_scale, const void* k_idx, const float* k_scale,
+                       const float* w_idx, float* scores, long long ld, int dense,
+                       hipStream_t st) {
+  const bool fp8 = s->idx_dtype == DSA_IDX_FP8_E4M3;
+  for (const dsa::SegTable& t : make_tables(p, dsa::indexer_rows_per_block())) {
+    dsa::IndexerArgs a = {};
+    a.segs = t;
+    a.q_idx = q_idx;
+    a.k_idx = k_idx;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.w_idx = w_idx;
+    a.scores = scores;
+    a.ld = ld;
+    a.dense = dense;
+    hipError_t e = dsa::launch_indexer(a, s->h_idx, s->d_idx, fp8, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  }
+  return DSA_OK;
+}
+
+dsa_status run_topk(const dsa_shape* s, const Plan& p, const float* scores, long long ld,
+                    int dense, int32_t* idx, hipStream_t st) {
+  for (const dsa::SegTable& t : make_tables(p, 1)) {
+    dsa::TopkArgs a = {};
+    a.segs = t;
+    a.scores = scores;
+    a.ld = ld;
+    a.dense = dense;
+    a.topk = s->topk;
+    a.idx = idx;
+    hipError_t e = dsa::launch_topk(a, (int)p.max_window, st);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  }
+  return DSA_OK;
+}
+
+dsa_status run_attn(const dsa_shape* s, const Plan* p, const void* q, const void* kv,
+                    const int32_t* idx, void* out, float* smax, float* ssum, hipStream_t st) {
+  dsa::AttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.idx = idx;
+  a.out = static_cast<uint16_t*>(out);
+  a.smax = smax;
+  a.ssum = ssum;
+  a.n_q = s->n_q;
+  a.n_k = s->n_k;
+  a.topk = s->topk;
+  a.scale_log2 = s->softmax_scale * 1.4426950408889634f;
+  if (!p) {
+    a.use_segs = 0;
+    a.xcd_remap = (s->n_q % 8) == 0;
+    hipError_t e = dsa::launch_sparse_attn(a, s->h, s->d_qk, s->d_v, s->n_q, st);
+    if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+    return DSA_OK;
+  }
+  for (const dsa::SegTable& t : make_tables(*p, 1)) {
+    a.segs = t;
+    a.use_segs = 1;
+    const int nb = t.blk_off[t.n];
+    a.xcd_remap = (nb % 8) == 0;
+    hipError_t e = dsa::launch_sparse_attn(a, s->h, s->d_qk, s->d_v, nb, st);
+    if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+  }
+  return DSA_OK;
+}
+
+dsa_status check_idx_ptrs(const dsa_shape* s, const void* q_idx, const float* q_scale,
+                          const void* k_idx, const float* k_scale, const float* w_idx) {
+  if (!q_idx || !k_idx || !w_idx) return fail(DSA_ERR_INVALID_ARG, "indexer input is NULL");
+  if (s->idx_dtype == DSA_IDX_FP8_E4M3) {
+    if (!q_scale || !k_scale) return fail(DSA_ERR_INVALID_ARG, "fp8 indexer needs q_scale and k_scale");
+  } else if (q_scale || k_scale) {
+    return fail(DSA_ERR_INVALID_ARG, "q_scale / k_scale must be NULL for bf16 indexer inputs");
+  }
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_last_error(void) { return g_err.c_str(); }
+
+dsa_status dsa_workspace_bytes(const dsa_shape* shape, size_t* bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedSegs | kNeedTopk, p);
+  if (st != DSA_OK) return st;
+  *bytes = ws_layout(shape, p).total;
+  return ok();
+}
+
+dsa_status dsa_indexer_scores(const dsa_shape* shape, const void* q_idx, const float* q_scale,
+                              const void* k_idx, const float* k_scale, const float* w_idx,
+                              float* scores, void* stream) {
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedSegs | kNeedIndexer, p);
+  if (st != DSA_OK) return st;
+  if (p.covered_rows == 0) return ok();
+  if ((st = check_idx_ptrs(shape, q_idx, q_scale, k_idx, k_scale, w_idx)) != DSA_OK) return st;
+  if (!scores) return fail(DSA_ERR_INVALID_ARG, "scores is NULL");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (const dsa::SegTable& t : make_tables(p, 1)) {
+    dsa::FillArgs f = {};
+    f.segs = t;
+    f.scores = scores;
+    f.ld = shape->n_k;
+    f.n_k = shape->n_k;
+    hipError_t e = dsa::launch_fill_outside(f, hs);
+    if (e != hipSuccess) return hip_fail(e, "fill launch");
+  }
+  st = run_indexer(shape, p, q_idx, q_scale, k_idx, k_scale, w_idx, scores, shape->n_k, 1, hs);
+  return st == DSA_OK ? ok() : st;
+}
+
+dsa_status dsa_topk_select(const dsa_shape* shape, const float* scores, int32_t* topk_idx,
+                           void* stream) {
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedSegs | kNeedTopk, p);
+  if (st != DSA_OK) return st;
+  if (p.covered_rows == 0) return ok();
+  if (!scores || !topk_idx) return fail(DSA_ERR_INVALID_ARG, "scores or topk_idx is NULL");
+  st = run_topk(shape, p, scores, shape->n_k, 1, topk_idx, static_cast<hipStream_t>(stream));
+  return st == DSA_OK ? ok() : st;
+}
+
+dsa_status dsa_sparse_attn(const dsa_shape* shape, const void* q, const void* kv,
+                           const int32_t* topk_idx, void* out, float* softmax_max,
+                           float* softmax_sum, void* stream) {
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedAttn, p);
+  if (st != DSA_OK) return st;
+  if (shape->n_q == 0) return ok();
+  if (!q || !kv || !topk_idx || !out) return fail(DSA_ERR_INVALID_ARG, "attention tensor is NULL");
+  st = run_attn(shape, nullptr, q, kv, topk_idx, out, softmax_max, softmax_sum,
+                static_cast<hipStream_t>(stream));
+  return st == DSA_OK ? ok() : st;
+}
+
+dsa_status dsa_forward(const dsa_shape* shape, const void* q_idx, const float* q_scale,
+                       const void* k_idx, const float* k_scale, const float* w_idx,
+                       const void* q, const void* kv, void* out, int32_t* topk_idx,
+                       float* softmax_max, float* softmax_sum, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedSegs | kNeedIndexer | kNeedTopk | kNeedAttn, p);
+  if (st != DSA_OK) return st;
+  if (p.covered_rows == 0) return ok();   // nothing to do: no pointer is read
+  if ((st = check_idx_ptrs(shape, q_idx, q_scale, k_idx, k_scale, w_idx)) != DSA_OK) return st;
+  if (!q || !kv || !out) return fail(DSA_ERR_INVALID_ARG, "attention tensor is NULL");
+  const WsLayout w = ws_layout(shape, p);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                workspace ? workspace_bytes : (size_t)0);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + w.scores_off);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + w.idx_off);
+  const long long ld = ws_score_ld(p);
+  if ((st = run_indexer(shape, p, q_idx, q_scale, k_idx, k_scale, w_idx, scores, ld, 0, hs)) != DSA_OK)
+    return st;
+  if ((st = run_topk(shape, p, scores, ld, 0, idx, hs)) != DSA_OK) return st;
+  if ((st = run_attn(shape, &p, q, kv, idx, out, softmax_max, softmax_sum, hs)) != DSA_OK) return st;
+  return ok();
+}
+
+dsa_status dsa_quantize_fp8_rows(const void* x_bf16, int64_t rows, int32_t cols, void* x_fp8,
+                                 float* scale, void* stream) {
+  if (rows < 0 || cols < 0) return fail(DSA_ERR_INVALID_ARG, "negative rows or cols");
+  if (rows > 0x7fffffff) return fail(DSA_ERR_UNSUPPORTED, "more than 2^31-1 rows");
+  if (rows == 0) return ok();
+  if (!x_bf16 || !x_fp8 || !scale) return fail(DSA_ERR_INVALID_ARG, "quantize tensor is NULL");
+  dsa::QuantArgs a = {};
+  a.x = static_cast<const uint16_t*>(x_bf16);
+  a.y = static_cast<uint8_t*>(x_fp8);
+  a.scale = scale;
+  a.rows = rows;
+  a.cols = cols;
+  hipError_t e = dsa::launch_quant_fp8_rows(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,390 @@
+// Sparse multi-query attention over gathered latent rows on gfx950 MFMA.
+//
+// Page "CANNTorchTitan: DeepSeek-V3.2 32k长序列预训练昇腾优化实践", section
+// "SparseLightningIndexerGradKLLoss" (Sparse Flash Attention formula): per query token and
+// head, softmax(q K_topk^T / sqrt(d)) over the token's selected keys, applied to the same
+// selected rows; under weight absorption key and value are one shared latent row whose first
+// d_v columns are the value and whose tail is the rope part.  softmax_max / softmax_sum are
+// exported for the indexer-loss boundary (page "context_parallel.md", section "DSA CP").
+//
+// Mapping: one workgroup per query row, one wave per 32 query heads (4 waves for 128 heads,
+// one per SIMD), 32 selected keys per tile.
+//   * Gather: the tile's 32 latent rows are copied HBM -> LDS with global_load_lds (16 B per
+//     lane, no VGPR staging), double-buffered so the next tile's gather overlaps this tile's
+//     math.  Each wave copies whole rows, so the row base is a scalar.  Rows are padded by
+//     16 B in LDS (conflict-free 16-byte reads).  Empty slots gather row 0 and are masked.
+//   * Logits: S^T[key, head] = K_tile (A, from LDS) x Q^T (B) on v_mfma_f32_32x32x16_bf16.
+//     The first 320 Q dims stay in VGPRs for the whole row, the other 256 are staged once in
+//     LDS (Q and the 512-wide accumulator do not both fit in registers otherwise).  A rows
+//     are fed in a fixed key permutation so that each lane's 16 accumulators come out as two
+//     runs of 8 consecutive keys of one head -- the B-operand layout of the next product.
+//   * Softmax per lane (a lane pair holds one head), exp2 with the scale folded in.  The
+//     scaling max is the first valid tile's max; p = exp2(z - m) may exceed 1 (fp32 / bf16
+//     keep their relative precision), and only growth past 2^64 is treated as overflow: the
+//     row is then marked (a NaN-payload sentinel in its first output element) and a second,
+//     normally idle launch recomputes marked rows exactly (row max first).  The accumulator
+//     is never rescaled and never carried through a branch.
+//   * Output: O^T[col, head] += V^T (A: read straight from the row-major LDS tile with the
+//     transposing ds_read_b64_tr_b16) x P^T (B: the lane's bf16 probabilities, no shuffle).
+//     O^T is DV/32 M-tiles of 32 value columns; each lane owns one head's columns, so the
+//     final 1/l is lane-local.
+#include "dsa_device.h"
+
+namespace dsa {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr_t;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+
+// LDS row (within a 32-key tile) that feeds A-operand row m of the logits product
+__device__ __forceinline__ int key_perm(int m) {
+  const int q = m >> 3, gg = (m >> 2) & 1, rr = m & 3;
+  return (q >> 1) * 16 + gg * 8 + (q & 1) * 4 + rr;
+}
+
+// key within the tile held by accumulator register r of a lane in half g (0/1)
+__device__ __forceinline__ int acc_key(int r, int g) {
+  return r < 8 ? g * 8 + r : 16 + g * 8 + (r - 8);
+}
+
+constexpr float kOverflowLog2 = 64.0f;  // p may reach 2^64 before the row is recomputed
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegInf = -__builtin_huge_valf();
+// bf16 quiet NaN with a payload arithmetic does not produce: marks a row for the exact pass
+constexpr uint16_t kOverflowMark = 0x7FD5;
+
+template <int H, int DQK, int DV>
+struct AttnCfg {
+  static constexpr int NW = (H + 31) / 32;   // waves, 32 heads each
+  static constexpr int NT = NW * 64;
+  static constexpr int KS = DQK / 16;        // K steps of the logits product
+  static constexpr int DQR = DQK > 320 ? 320 : DQK;  // Q dims held in VGPRs
+  static constexpr int KSR = DQR / 16;
+  static constexpr int DQL = DQK - DQR;      // Q dims staged in LDS
+  static constexpr int QROWE = DQL + 8;      // LDS row stride (elements) of staged Q
+  static constexpr int MTV = DV / 32;        // 32-column M tiles of the output product
+  static constexpr int NK = 32;              // keys per tile
+  static constexpr int CPR = DQK / 8;        // 16-byte chunks per latent row
+  static constexpr int ROWE = (CPR + 1) * 8; // LDS row stride (elements): one pad chunk
+  static constexpr int TILE = NK * ROWE;     // elements per KV tile buffer
+  static constexpr int QLDS = DQL > 0 ? H * QROWE : 8;
+  static_assert(DQK % 16 == 0 && DV % 32 == 0 && DV <= DQK && DQR % 16 == 0, "head dims");
+};
+
+// Per-row state shared by the fast and exact paths.
+struct RowCtx {
+  int row, tid, lane, wave, wave_u, hl, g, head, ntiles;
+  const int32_t* idx_row;
+  uint16_t* lds;     // 2 KV tile buffers
+  uint16_t* qlds;    // staged Q dims
+  int* flags;        // [2][NW] per-tile overflow flags
+};
+
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void gather_tile(const AttnArgs& a, const RowCtx& c, int t, int b) {
+  using C = AttnCfg<H, DQK, DV>;
+#pragma unroll
+  for (int rr = 0; rr < C::NK / C::NW; ++rr) {
+    const int key = rr * C::NW + c.wave_u;
+    const int slot = t * C::NK + key;
+    int id = slot < a.topk ? c.idx_row[slot] : -1;
+    id = (id < 0 || id >= a.n_k) ? 0 : id;
+    id = __builtin_amdgcn_readfirstlane(id);
+    const uint16_t* src = a.kv + (size_t)id * DQK;
+#pragma unroll
+    for (int c0 = 0; c0 < C::CPR; c0 += 64) {
+      if (c0 + c.lane < C::CPR)
+        __builtin_amdgcn_global_load_lds(src + (c0 + c.lane) * 8,
+                                         (lds_ptr_t)(c.lds + b * C::TILE + key * C::ROWE + c0 * 8),
+                                         16, 0, 0);
+    }
+  }
+}
+
+// S^T for one tile (32 keys x the wave's 32 heads) scaled into log2 units, -inf at empty
+// slots; `mx` receives the lane pair's (= one head's) tile max.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ f32x16 tile_logits(const AttnArgs& a, const RowCtx& c,
+                                              const bf16x8* qf, const uint16_t* tile,
+                                              unsigned vmask, float& mx) {
+  using C = AttnCfg<H, DQK, DV>;
+  f32x16 s = (f32x16){};
+  const uint16_t* arow = tile + key_perm(c.hl) * C::ROWE + c.g * 8;
+  const uint16_t* qlrow = c.qlds + (C::DQL > 0 ? c.head % H : 0) * C::QROWE + c.g * 8;
+  // A fragments one group ahead of their MFMAs; sched_barrier bounds the live fragments
+  constexpr int QG = 4;
+  constexpr int NG = (C::KS + QG - 1) / QG;
+  bf16x8 af[2][QG];
+#pragma unroll
+  for (int u = 0; u < QG; ++u)
+    if (u < C::KS) af[0][u] = *reinterpret_cast<const bf16x8*>(arow + u * 16);
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int cur = gi & 1;
+    if (gi + 1 < NG) {
+#pragma unroll
+      for (int u = 0; u < QG; ++u) {
+        const int ks = (gi + 1) * QG + u;
+        if (ks < C::KS) af[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(arow + ks * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < QG; ++u) {
+      const int ks = gi * QG + u;
+      if (ks < C::KS) {
+        bf16x8 bq;
+        if (ks < C::KSR) bq = qf[ks < C::KSR ? ks : 0];
+        else bq = *reinterpret_cast<const bf16x8*>(qlrow + (ks - C::KSR) * 16);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][u], bq, s, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float m = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const bool ok = (vmask >> acc_key(r, c.g)) & 1u;
+    s[r] = ok ? s[r] * a.scale_log2 : kNegInf;
+    m = fmaxf(m, s[r]);
+  }
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(m), __float_as_int(m), false, false);
+  mx = fmaxf(__int_as_float(pr[0]), __int_as_float(pr[1]));
+  return s;
+}
+
+// O^T += V^T P^T for one tile
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void tile_pv(const RowCtx& c, const uint16_t* tile, const bf16x8* pf,
+                                        f32x16* o) {
+  using C = AttnCfg<H, DQK, DV>;
+  // transposing read: lane (G = lane/16, i = lane%16) supplies row kbase + i/4, columns
+  // cbase + (i%4)*4 .. +3 and receives column cbase + i of rows kbase .. kbase+3
+  const int G = c.lane >> 4, i = c.lane & 15;
+  const uint16_t* vbase = tile + ((G >> 1) * 8 + (i >> 2)) * C::ROWE + (G & 1) * 16 + (i & 3) * 4;
+  auto vfrag = [&](int kk, int mt) {
+    const uint16_t* p0 = vbase + kk * 16 * C::ROWE + mt * 32;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)p0);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p0 + 4 * C::ROWE));
+    return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  };
+  bf16x8 vf[2][2];
+  vf[0][0] = vfrag(0, 0);
+  vf[0][1] = vfrag(1, 0);
+#pragma unroll
+  for (int mt = 0; mt < C::MTV; ++mt) {
+    const int cur = mt & 1;
+    if (mt + 1 < C::MTV) {
+      vf[cur ^ 1][0] = vfrag(0, mt + 1);
+      vf[cur ^ 1][1] = vfrag(1, mt + 1);
+    }
+    o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][0], pf[0], o[mt], 0, 0, 0);
+    o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][1], pf[1], o[mt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int H, int DQK, int DV>
+__device__ __forceinline__ unsigned tile_vmask(const AttnArgs& a, const RowCtx& c, int t) {
+  const int slot = t * AttnCfg<H, DQK, DV>::NK + c.hl;
+  const int id = slot < a.topk ? c.idx_row[slot] : -1;
+  return (unsigned)__ballot(id >= 0 && id < a.n_k);
+}
+
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void load_q(const AttnArgs& a, const RowCtx& c, bf16x8* qf) {
+  using C = AttnCfg<H, DQK, DV>;
+  const bool hv = (H % 32 == 0) || c.head < H;
+  const uint16_t* qp = a.q + ((size_t)c.row * H + (hv ? c.head : 0)) * DQK + c.g * 8;
+#pragma unroll
+  for (int ks = 0; ks < C::KSR; ++ks) {
+    const uint4 v = *reinterpret_cast<const uint4*>(qp + ks * 16);
+    qf[ks] = hv ? __builtin_bit_cast(bf16x8, v) : (bf16x8){};
+  }
+}
+
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void write_row(const AttnArgs& a, const RowCtx& c, const f32x16* o,
+                                          float lsum, float m_used, float m_true) {
+  using C = AttnCfg<H, DQK, DV>;
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(lsum), __float_as_int(lsum),
+                                                   false, false);
+  lsum = __int_as_float(pr[0]) + __int_as_float(pr[1]);
+  if (c.head >= H) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  uint16_t* op = a.out + ((size_t)c.row * H + c.head) * DV;
+#pragma unroll
+  for (int mt = 0; mt < C::MTV; ++mt) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int col = mt * 32 + q4 * 8 + c.g * 4;
+      const uint32_t lo = (uint32_t)f32_to_bf16(o[mt][q4 * 4 + 0] * inv) |
+                          ((uint32_t)f32_to_bf16(o[mt][q4 * 4 + 1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(o[mt][q4 * 4 + 2] * inv) |
+                          ((uint32_t)f32_to_bf16(o[mt][q4 * 4 + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(op + col) = make_uint2(lo, hi);
+    }
+  }
+  if (c.g == 0) {
+    const size_t si = (size_t)c.row * H + c.head;
+    const bool any = m_true != kNegInf;
+    if (a.smax) a.smax[si] = any ? m_true * kLn2 : kNegInf;
+    if (a.ssum) a.ssum[si] = any ? lsum * exp2f(m_used - m_true) : 0.f;
+  }
+}
+
+// One pass over the row's tiles accumulating O with scaling max m_fix (or, when m_fix is
+// -inf, the first valid tile's max).  Returns false -- outputs not written -- when some
+// head's max grows past the scaling range (only possible when m_fix is -inf).
+template <int H, int DQK, int DV>
+__device__ __forceinline__ bool accumulate_row(const AttnArgs& a, const RowCtx& c,
+                                               const bf16x8* qf, float m_fix) {
+  using C = AttnCfg<H, DQK, DV>;
+  f32x16 o[C::MTV];
+#pragma unroll
+  for (int mt = 0; mt < C::MTV; ++mt) o[mt] = (f32x16){};
+  float m_used = m_fix, m_true = kNegInf, lsum = 0.f;
+  bool overflow = false;
+  if (c.ntiles > 0) gather_tile<H, DQK, DV>(a, c, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < c.ntiles; ++t) {
+    const int b = t & 1;
+    if (t + 1 < c.ntiles) gather_tile<H, DQK, DV>(a, c, t + 1, b ^ 1);
+    const unsigned vmask = tile_vmask<H, DQK, DV>(a, c, t);
+    const uint16_t* tile = c.lds + b * C::TILE;
+    float mx;
+    f32x16 s = tile_logits<H, DQK, DV>(a, c, qf, tile, vmask, mx);
+    m_true = fmaxf(m_true, mx);
+    if (m_used == kNegInf) m_used = mx;  // first tile with a valid key
+    const bool over = mx > m_used + kOverflowLog2;
+    bf16x8 pf[2];
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = s[r] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(s[r] - m_used);
+      ls += p;
+      pf[r >> 3][r & 7] = (__bf16)p;
+    }
+    lsum += ls;
+    tile_pv<H, DQK, DV>(c, tile, pf, o);
+    if (c.lane == 0) c.flags[b * C::NW + c.wave] = __ballot(over) != 0ull;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) overflow |= c.flags[b * C::NW + w] != 0;
+    if (overflow) break;
+  }
+  if (overflow) return false;
+  write_row<H, DQK, DV>(a, c, o, lsum, m_used, m_true);
+  return true;
+}
+
+}  // namespace
+
+// EXACT = false: the fast path over blocks = rows (a block per row).
+// EXACT = true: a grid-stride pass that recomputes only rows the fast path marked, with the
+// row max found first so nothing can overflow.
+template <int H, int DQK, int DV, bool EXACT>
+__global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a) {
+  using C = AttnCfg<H, DQK, DV>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[C::QLDS];
+  __shared__ int flags[2 * C::NW];
+  __shared__ int s_last[C::NW];
+
+  const int nblk = EXACT ? a.nrows : (int)gridDim.x;
+  for (int bi = EXACT ? (int)blockIdx.x : 0; bi < (EXACT ? nblk : 1); bi += (int)gridDim.x) {
+  // XCD-aware row order: consecutive blocks go to different XCDs; give each XCD a contiguous
+  // run of rows (neighbouring queries tend to select neighbouring keys).
+  int blk = EXACT ? bi : (int)blockIdx.x;
+  if (!EXACT && a.xcd_remap) blk = (blk & 7) * (nblk >> 3) + (blk >> 3);
+  RowCtx c;
+  if (a.use_segs) {
+    const int g0 = seg_of_block(a.segs, blk);
+    c.row = a.segs.q_start[g0] + (blk - a.segs.blk_off[g0]);
+  } else {
+    c.row = blk;
+  }
+  if (EXACT) {
+    __syncthreads();   // the previous row's LDS use is over
+    if (a.out[(size_t)c.row * H * DV] != kOverflowMark) continue;
+  }
+  c.tid = threadIdx.x;
+  c.lane = c.tid & 63;
+  c.wave = c.tid >> 6;
+  c.wave_u = __builtin_amdgcn_readfirstlane(c.wave);
+  c.hl = c.lane & 31;
+  c.g = c.lane >> 5;
+  c.head = c.wave * 32 + c.hl;
+  c.idx_row = a.idx + (size_t)c.row * a.topk;
+  c.lds = lds;
+  c.qlds = qlds;
+  c.flags = flags;
+
+  // tiles past the last valid slot are never gathered or computed
+  int last = -1;
+  for (int sl = c.tid; sl < a.topk; sl += C::NT) {
+    const int id = c.idx_row[sl];
+    if (id >= 0 && id < a.n_k) last = sl;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if (c.lane == 0) s_last[c.wave] = last;
+
+  // stage q[row, :, DQR:] in LDS
+  if constexpr (C::DQL > 0) {
+    constexpr int CH = C::DQL / 8;
+    const uint16_t* qrow = a.q + (size_t)c.row * H * DQK + C::DQR;
+    for (int i = c.tid; i < H * CH; i += C::NT) {
+      const int hh = i / CH, cc = i % CH;
+      *reinterpret_cast<uint4*>(&qlds[hh * C::QROWE + cc * 8]) =
+          *reinterpret_cast<const uint4*>(qrow + (size_t)hh * DQK + cc * 8);
+    }
+  }
+  __syncthreads();
+  last = -1;
+#pragma unroll
+  for (int w = 0; w < C::NW; ++w) last = max(last, s_last[w]);
+  c.ntiles = (last + C::NK) / C::NK;
+
+  bf16x8 qf[C::KSR];
+  load_q<H, DQK, DV>(a, c, qf);
+  float m_fix = kNegInf;
+  if (EXACT) {
+    // row max from the logits alone
+    for (int t = 0; t < c.ntiles; ++t) {
+      gather_tile<H, DQK, DV>(a, c, t, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      float mx;
+      (void)tile_logits<H, DQK, DV>(a, c, qf, c.lds, tile_vmask<H, DQK, DV>(a, c, t), mx);
+      m_fix = fmaxf(m_fix, mx);
+      __syncthreads();
+    }
+  }
+  if (!accumulate_row<H, DQK, DV>(a, c, qf, m_fix) && c.tid == 0)
+    a.out[(size_t)c.row * H * DV] = kOverflowMark;
+  }
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& a, int h, int d_qk, int d_v, int nblocks,
+                              hipStream_t s) {
+  if (nblocks == 0) return hipSuccess;
+  AttnArgs ax = a;
+  ax.nrows = nblocks;
+  const int exact_grid = nblocks < 1024 ? nblocks : 1024;
+  if (h == 128 && d_qk == 576 && d_v == 512) {
+    k_sparse_attn<128, 576, 512, false><<<nblocks, 256, 0, s>>>(ax);
+    k_sparse_attn<128, 576, 512, true><<<exact_grid, 256, 0, s>>>(ax);
+  } else if (h == 8 && d_qk == 80 && d_v == 64) {
+    k_sparse_attn<8, 80, 64, false><<<nblocks, 64, 0, s>>>(ax);
+    k_sparse_attn<8, 80, 64, true><<<exact_grid, 64, 0, s>>>(ax);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,135 @@
+// Device-side building blocks shared by the gfx950 kernels of libdsa: bf16 / MFMA vector
+// types, the launch-argument structs (segment tables are passed by value in kernel
+// arguments, so no device metadata buffer is needed) and small wave/block primitives.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+
+// Segments handed to one launch.  A launch covers at most kMaxSegs segments; the host splits
+// larger tables over several launches.
+constexpr int kMaxSegs = 64;
+
+struct SegTable {
+  int n;                       // segments in this launch
+  int q_start[kMaxSegs];
+  int q_len[kMaxSegs];
+  int k_start[kMaxSegs];
+  int pos0[kMaxSegs];
+  int blk_off[kMaxSegs + 1];   // first block of each segment; blk_off[n] = grid size
+};
+
+// Find the segment owning block `blk` (linear scan: at most kMaxSegs entries).
+__device__ __forceinline__ int seg_of_block(const SegTable& t, int blk) {
+  int g = 0;
+  while (g + 1 < t.n && blk >= t.blk_off[g + 1]) ++g;
+  return g;
+}
+
+struct IndexerArgs {
+  SegTable segs;
+  const void* q_idx;      // [n_q, h_idx, d_idx] bf16 or e4m3fn codes
+  const void* k_idx;      // [n_k, d_idx]
+  const float* q_scale;   // fp8 only
+  const float* k_scale;   // fp8 only
+  const float* w_idx;     // [n_q, h_idx]
+  float* scores;          // row i at scores + i * ld (+ k_start when dense)
+  long long ld;           // row stride of scores in elements
+  int dense;              // 1: column = absolute key row; 0: column = key - k_start
+};
+
+struct FillArgs {
+  SegTable segs;
+  float* scores;
+  long long ld;
+  int n_k;
+};
+
+struct TopkArgs {
+  SegTable segs;
+  const float* scores;
+  long long ld;
+  int dense;
+  int topk;
+  int32_t* idx;           // [n_q, topk]
+};
+
+struct AttnArgs {
+  SegTable segs;          // rows to compute when use_segs (else rows 0 .. grid-1)
+  int use_segs;
+  int xcd_remap;          // 1: give each XCD a contiguous run of rows (grid % 8 == 0)
+  const uint16_t* q;      // [n_q, H, DQK] bf16
+  const uint16_t* kv;     // [n_k, DQK] bf16
+  const int32_t* idx;     // [n_q, topk]
+  uint16_t* out;          // [n_q, H, DV] bf16
+  float* smax;            // [n_q, H] or null
+  float* ssum;            // [n_q, H] or null
+  int n_q, n_k, topk;
+  int nrows;              // rows (blocks) of this launch
+  float scale_log2;       // softmax_scale * log2(e)
+};
+
+struct QuantArgs {
+  const uint16_t* x;
+  uint8_t* y;
+  float* scale;
+  long long rows;
+  int cols;
+};
+
+// ----------------------------------------------------------------------------------------
+// small helpers
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// number of set bits of `mask` below the calling lane
+__device__ __forceinline__ unsigned lanes_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((unsigned)b) << 16);
+}
+
+// round-to-nearest-even float -> bf16 bits (inputs here are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Block-wide exclusive prefix sum of one value per thread; `scratch` holds NW words of LDS.
+// Returns the exclusive prefix; `total` receives the block sum.  Contains two barriers.
+template <int NW>
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* scratch,
+                                                    unsigned& total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  unsigned x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    unsigned t = __shfl_up(x, o, 64);
+    if (lane >= o) x += t;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  unsigned before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    unsigned s = scratch[w];
+    before += (w < wave) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return before + x - v;
+}
+
+}  // namespace dsa

@@ -1,0 +1,159 @@
+// Per-row causal top-k over indexer scores: LDS radix select with a deterministic tie-break.
+//
+// Page "CANNTorchTitan: DeepSeek-V3.2 32k长序列预训练昇腾优化实践", section
+// "SparseLightningIndexerGradKLLoss": K_topk holds the keys of each token's top-k indexer
+// scores; the selection here keeps n = min(topk, window) keys, gives equal scores to the
+// lower key index (-0.0 counts as +0.0) and emits the kept keys in ascending order.
+//
+// One workgroup per row.  The row's window (at most THREADS * ITEMS scores) is read once from
+// HBM, coalesced, into registers as order-preserving 32-bit keys.  Three radix passes over
+// digits of 12, 12 and 8 bits (LDS histograms, one LDS atomic per candidate, candidates
+// narrowing to those matching the prefix found so far) find the exact k-th largest key T and
+// how many keys equal to T are needed.  A single ballot / mbcnt compaction in key-index order
+// then writes every key > T and the first `need` keys == T straight to their output slot, so
+// the output comes out sorted by key index with no sort.  Rows whose window is not longer
+// than topk skip the selection and write the window plus -1 padding.
+#include "dsa_device.h"
+
+namespace dsa {
+
+namespace {
+
+// fp32 -> uint32 whose unsigned order is the float order; -0.0 is mapped like +0.0
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+}  // namespace
+
+template <int THREADS, int ITEMS>
+__global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
+  constexpr int NW = THREADS / 64;
+  constexpr int NE = ITEMS * NW;          // (item, wave) compaction groups
+  static_assert(NE <= THREADS, "compaction scan needs one group per thread");
+  __shared__ uint32_t hist[4096];
+  __shared__ uint32_t grp_gt[NE];
+  __shared__ uint32_t grp_eq[NE];
+  __shared__ uint32_t scan_tmp[NW];
+  __shared__ uint32_t found[2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int blk = blockIdx.x;
+  const int g = seg_of_block(a.segs, blk);
+  const int r = a.segs.q_len[g] - 1 - (blk - a.segs.blk_off[g]);  // longer windows first
+  const int row = a.segs.q_start[g] + r;
+  const int k_lo = a.segs.k_start[g];
+  const int L = a.segs.pos0[g] + r + 1;
+  const int topk = a.topk;
+  const float* src = a.scores + (size_t)row * a.ld + (a.dense ? k_lo : 0);
+  int32_t* dst = a.idx + (size_t)row * topk;
+
+  if (L <= topk) {
+    for (int t = tid; t < topk; t += THREADS) dst[t] = t < L ? k_lo + t : -1;
+    return;
+  }
+
+  uint32_t key[ITEMS];
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const int e = j * THREADS + tid;
+    key[j] = e < L ? order_key(src[e]) : 0u;
+  }
+
+  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)topk;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    const int nbins = pass == 2 ? 256 : 4096;
+    for (int b = tid; b < nbins; b += THREADS) hist[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int e = j * THREADS + tid;
+      if (e < L && (key[j] & pmask) == prefix)
+        atomicAdd(&hist[(key[j] >> shift) & (uint32_t)(nbins - 1)], 1u);
+    }
+    __syncthreads();
+    // thread t owns chunk (nchunks-1-t) of consecutive bins, so the exclusive scan in thread
+    // order counts the keys in all higher bins
+    const int cpt = nbins >= THREADS ? nbins / THREADS : 1;
+    const int nchunks = nbins / cpt;
+    const int chunk = nchunks - 1 - tid;
+    uint32_t csum = 0;
+    if (chunk >= 0)
+      for (int i = 0; i < cpt; ++i) csum += hist[chunk * cpt + i];
+    uint32_t tot;
+    uint32_t above = block_excl_scan<NW>(csum, scan_tmp, tot);
+    if (chunk >= 0 && above < krem && krem <= above + csum) {
+      for (int i = cpt - 1; i >= 0; --i) {
+        const uint32_t h = hist[chunk * cpt + i];
+        if (above + h >= krem) {
+          found[0] = (uint32_t)(chunk * cpt + i);
+          found[1] = above;
+          break;
+        }
+        above += h;
+      }
+    }
+    __syncthreads();
+    prefix |= found[0] << shift;
+    pmask |= (uint32_t)(nbins - 1) << shift;
+    krem -= found[1];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;   // the topk-th largest key
+  const uint32_t need = krem;  // how many keys equal to T are kept (lowest indices first)
+
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const int e = j * THREADS + tid;
+    const bool v = e < L;
+    const unsigned long long mg = __ballot(v && key[j] > T);
+    const unsigned long long me = __ballot(v && key[j] == T);
+    if (lane == 0) {
+      grp_gt[j * NW + wave] = (uint32_t)__popcll(mg);
+      grp_eq[j * NW + wave] = (uint32_t)__popcll(me);
+    }
+  }
+  __syncthreads();
+  {
+    const uint32_t vg = tid < NE ? grp_gt[tid] : 0u;
+    const uint32_t ve = tid < NE ? grp_eq[tid] : 0u;
+    uint32_t tg, te;
+    const uint32_t eg = block_excl_scan<NW>(vg, scan_tmp, tg);
+    const uint32_t ee = block_excl_scan<NW>(ve, scan_tmp, te);
+    if (tid < NE) {
+      grp_gt[tid] = eg;
+      grp_eq[tid] = ee;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const int e = j * THREADS + tid;
+    const bool v = e < L;
+    const bool gt = v && key[j] > T;
+    const bool eq = v && key[j] == T;
+    const unsigned long long mg = __ballot(gt);
+    const unsigned long long me = __ballot(eq);
+    const uint32_t n_gt = grp_gt[j * NW + wave] + lanes_below(mg);
+    const uint32_t n_eq = grp_eq[j * NW + wave] + lanes_below(me);
+    const uint32_t pos = n_gt + min(n_eq, need);
+    if ((gt || (eq && n_eq < need)) && pos < (uint32_t)topk) dst[pos] = k_lo + e;
+  }
+}
+
+hipError_t launch_topk(const TopkArgs& a, int max_window, hipStream_t s) {
+  const dim3 grid(a.segs.blk_off[a.segs.n]);
+  if (grid.x == 0) return hipSuccess;
+  if (max_window <= 2048) k_topk<256, 8><<<grid, 256, 0, s>>>(a);
+  else if (max_window <= 8192) k_topk<512, 16><<<grid, 512, 0, s>>>(a);
+  else if (max_window <= 32768) k_topk<1024, 32><<<grid, 1024, 0, s>>>(a);
+  else if (max_window <= 65536) k_topk<1024, 64><<<grid, 1024, 0, s>>>(a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace dsa
