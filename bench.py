@@ -1,0 +1,213 @@
+"""DSA forward benchmark on one MI355X: one CP rank's share of a 32K sequence.
+
+A step is one fused forward (indexer -> top-k -> sparse attention) over the whole local
+share, inputs resident in HBM.  Prints one JSON line: useful TFLOP/s of the step (indexer
+2*H_idx*d_idx per window key + attention 2*H*(d_qk+d_v) per selected key), queries/s, a
+roofline entry for the dominant kernel (sparse attention, MFMA-bound), per-stage timings and
+the CPU oracle's throughput on a bounded row sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_attention_11_amd import dsa, inputs as I  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "sparse_attention_11_amd", "csrc", "attention.hip")
+
+
+def work(wl):
+    """Algorithmic work of the forward for the workload's segments."""
+    L = []
+    for (qs, ql, ks, kl, p0) in wl.segments:
+        L.append(np.arange(p0 + 1, p0 + ql + 1, dtype=np.int64))
+    L = np.concatenate(L) if L else np.zeros(0, np.int64)
+    n = np.minimum(L, wl.topk)
+    f_idx = float(2 * wl.h_idx * wl.d_idx * L.sum())
+    f_attn = float(2 * wl.h * (wl.d_qk + wl.d_v) * n.sum())
+    return dict(rows=int(L.size), window_keys=int(L.sum()), selected=int(n.sum()),
+                f_idx=f_idx, f_attn=f_attn,
+                gather_bytes=float(n.sum() * wl.d_qk * 2),
+                topk_bytes=float(L.sum() * 4 + L.size * wl.topk * 4))
+
+
+def time_launches(fn, reps, stream):
+    """Average duration of fn() over reps launches, HIP events on the launch stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def cpu_baseline(wl, budget_s=15.0, max_rows=2048):
+    """The float64 oracle on a seeded sample of the workload's rows, on the host cores."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    x = I.generate(wl)                     # CPU generator: the oracle's own inputs
+    f64 = I.to_f64
+    qi, ki, wi, q, kv = (f64(x[k]) for k in ("q_idx", "k_idx", "w_idx", "q", "kv"))
+    rng = np.random.default_rng(0)
+    order = rng.permutation(wl.n_q)
+    segs = list(wl.segments)
+    done, flops, t0 = [], 0.0, time.perf_counter()
+    k_lo, L = oracle.row_windows(segs, wl.n_q, wl.n_k)
+    for r in order[:max_rows]:
+        if L[r] < 0:
+            continue
+        oracle.dsa_forward(qi, ki, wi, q, kv, segs, wl.topk, wl.softmax_scale, wl.d_v,
+                           rows=np.array([r]))
+        done.append(int(r))
+        n = min(wl.topk, int(L[r]))
+        flops += 2 * wl.h_idx * wl.d_idx * int(L[r]) + 2 * wl.h * (wl.d_qk + wl.d_v) * n
+        if time.perf_counter() - t0 > budget_s and len(done) >= 4:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "queries_per_s": len(done) / dt,
+            "sample": f"{len(done)} seeded random rows of {wl.name} (indexer over each row's "
+                      f"window, top-k, attention), float64 NumPy, {dt:.1f} s"}
+
+
+def traffic_entry():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was
+    taken on the current attention kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        h = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if t.get("attention_hip_sha256") == h:
+            return float(t["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share only (got --gpus {args.gpus}); the CP "
+              "all-gather and multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    wl = I.workload(args.workload).with_(with_dout=False)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    print(f"bench: {wl.name} n_q={wl.n_q} n_k={wl.n_k} topk={wl.topk}", file=sys.stderr, flush=True)
+    g = I.generate(wl, device=dev, gen_device="cuda")
+    W = work(wl)
+
+    out = torch.empty(wl.n_q, wl.h, wl.d_v, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(dsa.dsa_workspace_bytes(wl.n_q, wl.n_k, wl.topk, wl.segments),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        return dsa.dsa_forward(g["q_idx"], g["k_idx"], g["w_idx"], g["q"], g["kv"],
+                               wl.segments, wl.topk, wl.softmax_scale, wl.d_v, out=out,
+                               return_idx=True, stats=True, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        res = step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    print(f"bench: forward {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    idx = res[1]
+
+    stages = {}
+    if not args.no_stages:
+        reps = max(3, min(args.steps, 10))
+        scores = torch.empty(wl.n_q, wl.n_k, dtype=torch.float32, device=dev)
+        stages["indexer_ms"] = time_launches(
+            lambda: dsa.dsa_indexer_scores(g["q_idx"], g["k_idx"], g["w_idx"], wl.segments,
+                                           out=scores), reps, stream)
+        tk = torch.empty(wl.n_q, wl.topk, dtype=torch.int32, device=dev)
+        stages["topk_ms"] = time_launches(
+            lambda: dsa.dsa_topk_select(scores, wl.segments, wl.topk, out=tk), reps, stream)
+        del scores
+        stages["attention_ms"] = time_launches(
+            lambda: dsa.dsa_sparse_attn(g["q"], g["kv"], idx, wl.softmax_scale, wl.d_v, out=out),
+            reps, stream)
+    t_attn = stages.get("attention_ms")
+    attn_tf = W["f_attn"] / (t_attn * 1e-3) / 1e12 if t_attn else None
+
+    line = {
+        "metric": "DSA fwd useful TFLOP/s + queries/s at 32K CP shard; % MFMA peak, HBM GB/s",
+        "value": (W["f_idx"] + W["f_attn"]) / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian index/query/latent rows, uniform index weights)",
+        "config": {"workload": wl.name, "local_queries": wl.n_q, "keys": wl.n_k,
+                   "segments": [list(s) for s in wl.segments], "topk": wl.topk,
+                   "index_heads": wl.h_idx, "index_dim": wl.d_idx, "heads": wl.h,
+                   "d_qk": wl.d_qk, "d_v": wl.d_v, "parallelism": "one CP rank's share"},
+        "queries_per_s": wl.n_q / (ms * 1e-3),
+        "useful_tflop": (W["f_idx"] + W["f_attn"]) / 1e12,
+    }
+    if stages:
+        ti, tt = stages["indexer_ms"], stages["topk_ms"]
+        line["stages"] = {
+            "indexer_ms_incl_minus_inf_fill": ti,
+            "indexer_tflops": W["f_idx"] / (ti * 1e-3) / 1e12,
+            "indexer_mfma_frac": W["f_idx"] / (ti * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "topk_ms": tt,
+            "topk_gbs": W["topk_bytes"] / (tt * 1e-3) / 1e9,
+            "attention_ms": t_attn,
+            "attention_tflops": attn_tf,
+            "attention_mfma_frac": attn_tf / PEAK_BF16_TFLOPS,
+            "kv_gather_gbs": W["gather_bytes"] / (t_attn * 1e-3) / 1e9,
+        }
+        traffic = traffic_entry()
+        line["roofline"] = {"bound": "mfma", "kernel": "k_sparse_attn (sparse MQA attention)",
+                            "achieved": attn_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": attn_tf / PEAK_BF16_TFLOPS, "traffic": traffic,
+                            "per_launch_flop": W["f_attn"]}
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

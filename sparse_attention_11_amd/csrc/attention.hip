@@ -263,9 +263,12 @@ __device__ __forceinline__ bool accumulate_row(const AttnArgs& a, const RowCtx& 
     float ls = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      // the sum uses the same bf16-rounded probabilities that enter the value product, so
+      // the output is an exact convex combination of the rounded weights
       const float p = s[r] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(s[r] - m_used);
-      ls += p;
-      pf[r >> 3][r & 7] = (__bf16)p;
+      const __bf16 pb = (__bf16)p;
+      ls += (float)pb;
+      pf[r >> 3][r & 7] = pb;
     }
     lsum += ls;
     tile_pv<H, DQK, DV>(c, tile, pf, o);

@@ -58,9 +58,11 @@ def test_indexer_scores_bf16(n):
     rows = np.arange(wl.n_q) if n == 1 else sample_rows(wl.n_q, wl.segments, 24)
     ref = O.indexer_scores(f64(x["q_idx"]), f64(x["k_idx"]), f64(x["w_idx"]), list(wl.segments),
                            rows=rows)
+    mag = O.indexer_scores(np.abs(f64(x["q_idx"])), np.abs(f64(x["k_idx"])),
+                           np.abs(f64(x["w_idx"])), list(wl.segments), rows=rows)
     got = sc[torch.from_numpy(rows).cuda()].cpu().numpy()
     k_lo, L = _windows(wl, rows)
-    check_scores(got, ref, k_lo, L)
+    check_scores(got, ref, k_lo, L, mag)
 
 
 def test_quantize_fp8_bit_exact():
@@ -104,9 +106,11 @@ def test_indexer_scores_fp8(n):
     rows = np.arange(wl.n_q) if n == 1 else sample_rows(wl.n_q, wl.segments, 24)
     r = O.indexer_scores(ref["q"], ref["k"], f64(x["w_idx"]), list(wl.segments), rows=rows,
                          q_scale=ref["qs"], k_scale=ref["ks"])
+    mag = O.indexer_scores(np.abs(ref["q"]), np.abs(ref["k"]), np.abs(f64(x["w_idx"])),
+                           list(wl.segments), rows=rows, q_scale=ref["qs"], k_scale=ref["ks"])
     got = sc[torch.from_numpy(rows).cuda()].cpu().numpy()
     k_lo, L = _windows(wl, rows)
-    check_scores(got, r, k_lo, L)
+    check_scores(got, r, k_lo, L, mag)
 
 
 # ------------------------------------------------------------------------------- top-k ----
@@ -215,7 +219,10 @@ def test_sparse_attn_large_logit_growth_takes_exact_path():
     ro, rm, rs = O.sparse_attn(f64(q), f64(kv), idx.numpy().astype(np.int64), wl.softmax_scale,
                                wl.d_v)
     assert np.max(rm[0:4]) - np.median(rm[4:]) > 64 * math.log(2), "case does not overflow"
-    check_attention(out.float().cpu().numpy(), smax.cpu().numpy(), ssum.cpu().numpy(), ro, rm, rs)
+    # p is rounded to bf16 (2^-9 relative) before the value product: |dO| <= 2^-9 max|v|
+    atol = 2e-2 + 2.0 ** -9 * float(kv[:, :wl.d_v].float().abs().max())
+    check_attention(out.float().cpu().numpy(), smax.cpu().numpy(), ssum.cpu().numpy(), ro, rm, rs,
+                    atol=atol)
 
 
 # ------------------------------------------------------------------------- fused forward ----
