@@ -34,7 +34,7 @@ namespace dsa {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) uint16_t* lds_u16_ptr_t;
 typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr_t;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 
@@ -60,7 +60,7 @@ struct AttnCfg {
   static constexpr int NW = (H + 31) / 32;   // waves, 32 heads each
   static constexpr int NT = NW * 64;
   static constexpr int KS = DQK / 16;        // K steps of the logits product
-  static constexpr int DQR = DQK > 320 ? 320 : DQK;  // Q dims held in VGPRs
+  static constexpr int DQR = DQK > 416 ? 416 : DQK;  // Q dims held in VGPRs
   static constexpr int KSR = DQR / 16;
   static constexpr int DQL = DQK - DQR;      // Q dims staged in LDS
   static constexpr int QROWE = DQL + 8;      // LDS row stride (elements) of staged Q
@@ -70,6 +70,10 @@ struct AttnCfg {
   static constexpr int ROWE = (CPR + 1) * 8; // LDS row stride (elements): one pad chunk
   static constexpr int TILE = NK * ROWE;     // elements per KV tile buffer
   static constexpr int QLDS = DQL > 0 ? H * QROWE : 8;
+  static constexpr int NBUF = 3;             // gather ring depth (tiles t+1, t+2 in flight)
+  // vector-memory instructions one wave issues per tile gather (rows x 64-lane pieces)
+  static constexpr int GOPS = (NK / NW) * ((CPR + 63) / 64);
+  static_assert(GOPS < 64, "vmcnt range");
   static_assert(DQK % 16 == 0 && DV % 32 == 0 && DV <= DQK && DQR % 16 == 0, "head dims");
 };
 
@@ -77,30 +81,96 @@ struct AttnCfg {
 struct RowCtx {
   int row, tid, lane, wave, wave_u, hl, g, head, ntiles;
   const int32_t* idx_row;
-  uint16_t* lds;     // 2 KV tile buffers
+  uint16_t* buf[3];  // KV tile buffers (separate LDS objects)
   uint16_t* qlds;    // staged Q dims
   int* flags;        // [2][NW] per-tile overflow flags
+  unsigned* vm;      // [3][NW] per-tile validity bits of each wave's gathered rows
 };
 
+// Copy one latent row into LDS row `key` of `dst` (16 bytes per lane; lanes past the row idle)
 template <int H, int DQK, int DV>
-__device__ __forceinline__ void gather_tile(const AttnArgs& a, const RowCtx& c, int t, int b) {
+__device__ __forceinline__ void gather_row(const AttnArgs& a, const RowCtx& c, int id, int key,
+                                           uint16_t* dst) {
+  using C = AttnCfg<H, DQK, DV>;
+  id = (id < 0 || id >= a.n_k) ? 0 : id;   // empty slot: any in-bounds row, masked later
+  const uint16_t* src = a.kv + (size_t)id * DQK;
+#pragma unroll
+  for (int c0 = 0; c0 < C::CPR; c0 += 64) {
+    // LDS DMA issued from inline asm: the compiler neither sees the LDS write nor adds waits
+    // for it; completion is tracked by hand (vmcnt before each barrier).  M0 holds the
+    // wave's LDS destination, each lane writes 16 bytes at M0 + 16 * lane.
+    const unsigned lds_addr =
+        (unsigned)(size_t)(lds_u16_ptr_t)(dst + key * C::ROWE + c0 * 8);
+    if (c0 + c.lane < C::CPR)
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(lds_addr), "v"(src + (c0 + c.lane) * 8) : "memory", "m0");
+  }
+}
+
+// Gather of tile t with the indices read by scalar loads (exact path)
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void gather_tile(const AttnArgs& a, const RowCtx& c, int t,
+                                            uint16_t* dst) {
   using C = AttnCfg<H, DQK, DV>;
 #pragma unroll
   for (int rr = 0; rr < C::NK / C::NW; ++rr) {
     const int key = rr * C::NW + c.wave_u;
     const int slot = t * C::NK + key;
-    int id = slot < a.topk ? c.idx_row[slot] : -1;
-    id = (id < 0 || id >= a.n_k) ? 0 : id;
-    id = __builtin_amdgcn_readfirstlane(id);
-    const uint16_t* src = a.kv + (size_t)id * DQK;
-#pragma unroll
-    for (int c0 = 0; c0 < C::CPR; c0 += 64) {
-      if (c0 + c.lane < C::CPR)
-        __builtin_amdgcn_global_load_lds(src + (c0 + c.lane) * 8,
-                                         (lds_ptr_t)(c.lds + b * C::TILE + key * C::ROWE + c0 * 8),
-                                         16, 0, 0);
-    }
+    const int id = slot < a.topk ? c.idx_row[slot] : -1;
+    gather_row<H, DQK, DV>(a, c, __builtin_amdgcn_readfirstlane(id), key, dst);
   }
+}
+
+// The slot indices one wave gathers for tile t (rows wave*RPW .. +RPW-1 of the tile), read
+// with scalar loads: they count against lgkmcnt, so waiting for them never drains the
+// in-flight gathers (which count against vmcnt).  Slots past topk read as -1.
+template <int H, int DQK, int DV>
+struct TileIdx {
+  int v[AttnCfg<H, DQK, DV>::NK / AttnCfg<H, DQK, DV>::NW];
+};
+
+template <int H, int DQK, int DV>
+__device__ __forceinline__ TileIdx<H, DQK, DV> load_tile_idx_s(const AttnArgs& a,
+                                                               const RowCtx& c, int t) {
+  using C = AttnCfg<H, DQK, DV>;
+  constexpr int RPW = C::NK / C::NW;
+  // the index list is read-only while the kernel runs: reading it through the constant
+  // address space lets uniform loads go to the scalar unit
+  typedef __attribute__((address_space(4))) const int32_t* cidx_t;
+  const cidx_t ip = (cidx_t)c.idx_row;
+  TileIdx<H, DQK, DV> r;
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int slot = t * C::NK + c.wave_u * RPW + j;
+    const int v = ip[min(slot, a.topk - 1)];
+    r.v[j] = slot < a.topk ? v : -1;
+  }
+  return r;
+}
+
+// Validity bits of this wave's slots of a tile (bit j: row wave*RPW + j).
+template <int H, int DQK, int DV>
+__device__ __forceinline__ unsigned tile_bits(const AttnArgs& a, const TileIdx<H, DQK, DV>& ti) {
+  constexpr int RPW = AttnCfg<H, DQK, DV>::NK / AttnCfg<H, DQK, DV>::NW;
+  unsigned m = 0;
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) m |= (ti.v[j] >= 0 && ti.v[j] < a.n_k) ? (1u << j) : 0u;
+  return m;
+}
+
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void gather_tile_s(const AttnArgs& a, const RowCtx& c,
+                                              const TileIdx<H, DQK, DV>& ti, uint16_t* dst) {
+  constexpr int RPW = AttnCfg<H, DQK, DV>::NK / AttnCfg<H, DQK, DV>::NW;
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) gather_row<H, DQK, DV>(a, c, ti.v[j], c.wave_u * RPW + j, dst);
+}
+
+// Wait until at most N of this wave's vector-memory instructions are outstanding, then meet
+// the other waves at a barrier (one asm block, so no memory access moves across it).
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // S^T for one tile (32 keys x the wave's 32 heads) scaled into log2 units, -inf at empty
@@ -192,6 +262,8 @@ __device__ __forceinline__ unsigned tile_vmask(const AttnArgs& a, const RowCtx& 
   return (unsigned)__ballot(id >= 0 && id < a.n_k);
 }
 
+
+
 template <int H, int DQK, int DV>
 __device__ __forceinline__ void load_q(const AttnArgs& a, const RowCtx& c, bf16x8* qf) {
   using C = AttnCfg<H, DQK, DV>;
@@ -234,54 +306,111 @@ __device__ __forceinline__ void write_row(const AttnArgs& a, const RowCtx& c, co
   }
 }
 
-// One pass over the row's tiles accumulating O with scaling max m_fix (or, when m_fix is
-// -inf, the first valid tile's max).  Returns false -- outputs not written -- when some
-// head's max grows past the scaling range (only possible when m_fix is -inf).
+// Logits, probabilities and the output product of one tile.  Returns whether some head's
+// max exceeded the scaling max by more than the fast path's range.
 template <int H, int DQK, int DV>
-__device__ __forceinline__ bool accumulate_row(const AttnArgs& a, const RowCtx& c,
-                                               const bf16x8* qf, float m_fix) {
+__device__ __forceinline__ bool tile_step(const AttnArgs& a, const RowCtx& c, const bf16x8* qf,
+                                          const uint16_t* tile, unsigned vmask, float& m_used,
+                                          float& m_true, float& lsum, f32x16* o) {
+  float mx;
+  f32x16 s = tile_logits<H, DQK, DV>(a, c, qf, tile, vmask, mx);
+  m_true = fmaxf(m_true, mx);
+  if (m_used == kNegInf) m_used = mx;  // first tile with a valid key
+  const bool over = mx > m_used + kOverflowLog2;
+  bf16x8 pf[2];
+  float ls = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    // the sum uses the same bf16-rounded probabilities that enter the value product, so
+    // the output is an exact convex combination of the rounded weights
+    const float p = s[r] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(s[r] - m_used);
+    const __bf16 pb = (__bf16)p;
+    ls += (float)pb;
+    pf[r >> 3][r & 7] = pb;
+  }
+  lsum += ls;
+  tile_pv<H, DQK, DV>(c, tile, pf, o);
+  return over;
+}
+
+// Fast path: tiles in a 3-deep LDS ring (gathers of tiles t+1 and t+2 in flight while tile t
+// is computed).  The loop is unrolled by three so every buffer is a distinct LDS object with
+// a static role: the compiler then only waits for the gather of the buffer it reads, and
+// the explicit vmcnt before each barrier retires exactly this wave's gather of the next
+// tile.  The tile count is padded to a multiple of three with empty tiles (p = 0).
+// Returns false -- outputs not written -- when some head's max outgrows the scaling range
+// (the loop still runs to the end: a second loop exit would keep the accumulator from
+// staying in registers).
+template <int H, int DQK, int DV>
+__device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx& c,
+                                                const bf16x8* qf) {
+  using C = AttnCfg<H, DQK, DV>;
+  f32x16 o[C::MTV];
+#pragma unroll
+  for (int mt = 0; mt < C::MTV; ++mt) o[mt] = (f32x16){};
+  float m_used = kNegInf, m_true = kNegInf, lsum = 0.f;
+  bool overflow = false;
+  const int ntiles = (c.ntiles + 2) / 3 * 3;
+  constexpr int RPW = C::NK / C::NW;
+  using TI = TileIdx<H, DQK, DV>;
+  const TI i0 = load_tile_idx_s<H, DQK, DV>(a, c, 0);
+  const TI i1 = load_tile_idx_s<H, DQK, DV>(a, c, 1);
+  TI i2 = load_tile_idx_s<H, DQK, DV>(a, c, 2);
+  gather_tile_s<H, DQK, DV>(a, c, i0, c.buf[0]);
+  gather_tile_s<H, DQK, DV>(a, c, i1, c.buf[1]);
+  if (c.lane == 0) {
+    c.vm[0 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i0);
+    c.vm[1 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i1);
+  }
+  wait_vm_barrier<C::GOPS>();          // tile 0 landed; tile 1 may be in flight
+
+  // step t: fetch the indices of t+3, gather t+2, compute t, then retire this wave's gather
+  // of t+1 and meet at the barrier.  `nxt2` holds the indices of t+2 on entry, t+3 on exit.
+  auto step = [&](int t, int slot, uint16_t* cur, uint16_t* ahead2, TI& nxt2) {
+    const TI i3 = load_tile_idx_s<H, DQK, DV>(a, c, t + 3);
+    gather_tile_s<H, DQK, DV>(a, c, nxt2, ahead2);
+    if (c.lane == 0) c.vm[((slot + 2) % 3) * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, nxt2);
+    unsigned vmask = 0;
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) vmask |= c.vm[slot * C::NW + w] << (w * RPW);
+    const bool over = tile_step<H, DQK, DV>(a, c, qf, cur, vmask, m_used, m_true, lsum, o);
+    if (c.lane == 0) c.flags[(t & 1) * C::NW + c.wave] = __ballot(over) != 0ull;
+    wait_vm_barrier<C::GOPS>();        // tile t+1 landed for every wave; t+2 may be in flight
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) overflow |= c.flags[(t & 1) * C::NW + w] != 0;
+    nxt2 = i3;
+  };
+  for (int t = 0; t < ntiles; t += 3) {
+    step(t, 0, c.buf[0], c.buf[2], i2);
+    step(t + 1, 1, c.buf[1], c.buf[0], i2);
+    step(t + 2, 2, c.buf[2], c.buf[1], i2);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no gather may outlive the block
+  if (overflow) return false;
+  write_row<H, DQK, DV>(a, c, o, lsum, m_used, m_true);
+  return true;
+}
+
+// Exact path: scaling max fixed to the row max (computed beforehand), two buffers, full
+// waits; only runs for rows the fast path gave up on.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void accumulate_exact(const AttnArgs& a, const RowCtx& c,
+                                                 const bf16x8* qf, float m_fix) {
   using C = AttnCfg<H, DQK, DV>;
   f32x16 o[C::MTV];
 #pragma unroll
   for (int mt = 0; mt < C::MTV; ++mt) o[mt] = (f32x16){};
   float m_used = m_fix, m_true = kNegInf, lsum = 0.f;
-  bool overflow = false;
-  if (c.ntiles > 0) gather_tile<H, DQK, DV>(a, c, 0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < c.ntiles; ++t) {
-    const int b = t & 1;
-    if (t + 1 < c.ntiles) gather_tile<H, DQK, DV>(a, c, t + 1, b ^ 1);
-    const unsigned vmask = tile_vmask<H, DQK, DV>(a, c, t);
-    const uint16_t* tile = c.lds + b * C::TILE;
-    float mx;
-    f32x16 s = tile_logits<H, DQK, DV>(a, c, qf, tile, vmask, mx);
-    m_true = fmaxf(m_true, mx);
-    if (m_used == kNegInf) m_used = mx;  // first tile with a valid key
-    const bool over = mx > m_used + kOverflowLog2;
-    bf16x8 pf[2];
-    float ls = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // the sum uses the same bf16-rounded probabilities that enter the value product, so
-      // the output is an exact convex combination of the rounded weights
-      const float p = s[r] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(s[r] - m_used);
-      const __bf16 pb = (__bf16)p;
-      ls += (float)pb;
-      pf[r >> 3][r & 7] = pb;
-    }
-    lsum += ls;
-    tile_pv<H, DQK, DV>(c, tile, pf, o);
-    if (c.lane == 0) c.flags[b * C::NW + c.wave] = __ballot(over) != 0ull;
+    gather_tile<H, DQK, DV>(a, c, t, c.buf[0]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-#pragma unroll
-    for (int w = 0; w < C::NW; ++w) overflow |= c.flags[b * C::NW + w] != 0;
-    if (overflow) break;
+    (void)tile_step<H, DQK, DV>(a, c, qf, c.buf[0], tile_vmask<H, DQK, DV>(a, c, t), m_used,
+                                m_true, lsum, o);
+    __syncthreads();
   }
-  if (overflow) return false;
   write_row<H, DQK, DV>(a, c, o, lsum, m_used, m_true);
-  return true;
 }
 
 }  // namespace
@@ -292,9 +421,12 @@ __device__ __forceinline__ bool accumulate_row(const AttnArgs& a, const RowCtx& 
 template <int H, int DQK, int DV, bool EXACT>
 __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a) {
   using C = AttnCfg<H, DQK, DV>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv1[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv2[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t qlds[C::QLDS];
   __shared__ int flags[2 * C::NW];
+  __shared__ unsigned vmring[3 * C::NW];
   __shared__ int s_last[C::NW];
 
   const int nblk = EXACT ? a.nrows : (int)gridDim.x;
@@ -322,9 +454,12 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
   c.g = c.lane >> 5;
   c.head = c.wave * 32 + c.hl;
   c.idx_row = a.idx + (size_t)c.row * a.topk;
-  c.lds = lds;
+  c.buf[0] = kv0;
+  c.buf[1] = kv1;
+  c.buf[2] = kv2;
   c.qlds = qlds;
   c.flags = flags;
+  c.vm = vmring;
 
   // tiles past the last valid slot are never gathered or computed
   int last = -1;
@@ -354,21 +489,26 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
 
   bf16x8 qf[C::KSR];
   load_q<H, DQK, DV>(a, c, qf);
-  float m_fix = kNegInf;
+  // compiler-visible vmcnt(0) (exp/lgkm counters left alone): the Q loads are done before the
+  // gather ring starts, so the compiler adds no waits for them inside the loop
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   if (EXACT) {
-    // row max from the logits alone
+    // row max from the logits alone, then the exact accumulation
+    float m_fix = kNegInf;
+    __syncthreads();
     for (int t = 0; t < c.ntiles; ++t) {
-      gather_tile<H, DQK, DV>(a, c, t, 0);
+      gather_tile<H, DQK, DV>(a, c, t, c.buf[0]);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       float mx;
-      (void)tile_logits<H, DQK, DV>(a, c, qf, c.lds, tile_vmask<H, DQK, DV>(a, c, t), mx);
+      (void)tile_logits<H, DQK, DV>(a, c, qf, c.buf[0], tile_vmask<H, DQK, DV>(a, c, t), mx);
       m_fix = fmaxf(m_fix, mx);
       __syncthreads();
     }
-  }
-  if (!accumulate_row<H, DQK, DV>(a, c, qf, m_fix) && c.tid == 0)
+    accumulate_exact<H, DQK, DV>(a, c, qf, m_fix);
+  } else if (!accumulate_fast<H, DQK, DV>(a, c, qf) && c.tid == 0) {
     a.out[(size_t)c.row * H * DV] = kOverflowMark;
+  }
   }
 }
 
