@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only (got --gpus {args.gpus}); the CP "
@@ -124,6 +126,14 @@ def main():
     print(f"bench: {wl.name} n_q={wl.n_q} n_k={wl.n_k} topk={wl.topk}", file=sys.stderr, flush=True)
     g = I.generate(wl, device=dev, gen_device="cuda")
     W = work(wl)
+    if args.calibrate_copy:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE under rocprofv3 --pmc give
+        # the scale from counter units to bytes for the kernels measured in the same run
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = torch.empty(wl.n_q, wl.h, wl.d_v, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(dsa.dsa_workspace_bytes(wl.n_q, wl.n_k, wl.topk, wl.segments),

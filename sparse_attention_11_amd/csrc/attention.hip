@@ -10,12 +10,15 @@
 // Mapping: one workgroup per query row, one wave per 32 query heads (4 waves for 128 heads,
 // one per SIMD), 32 selected keys per tile.
 //   * Gather: the tile's 32 latent rows are copied HBM -> LDS with global_load_lds (16 B per
-//     lane, no VGPR staging), double-buffered so the next tile's gather overlaps this tile's
-//     math.  Each wave copies whole rows, so the row base is a scalar.  Rows are padded by
-//     16 B in LDS (conflict-free 16-byte reads).  Empty slots gather row 0 and are masked.
+//     lane, no VGPR staging) into a ring of three tile buffers, so the gathers of the next two
+//     tiles overlap this tile's math.  Each wave copies whole rows, so the row base is a
+//     scalar (its index is read ahead through the scalar cache).  Rows are stored unpadded
+//     with their 16-byte chunks XOR-swizzled by row, which keeps both the 16-row logits reads
+//     and the 4-row transposing value reads free of bank conflicts.  Empty slots gather row 0
+//     and are masked.
 //   * Logits: S^T[key, head] = K_tile (A, from LDS) x Q^T (B) on v_mfma_f32_32x32x16_bf16.
-//     The first 320 Q dims stay in VGPRs for the whole row, the other 256 are staged once in
-//     LDS (Q and the 512-wide accumulator do not both fit in registers otherwise).  A rows
+//     The first 416 Q dims stay in VGPRs for the whole row, the rest are staged once in LDS
+//     (Q and the 512-wide accumulator do not both fit in registers otherwise).  A rows
 //     are fed in a fixed key permutation so that each lane's 16 accumulators come out as two
 //     runs of 8 consecutive keys of one head -- the B-operand layout of the next product.
 //   * Softmax per lane (a lane pair holds one head), exp2 with the scale folded in.  The
@@ -35,6 +38,7 @@ namespace dsa {
 namespace {
 
 typedef __attribute__((address_space(3))) uint16_t* lds_u16_ptr_t;
+typedef __attribute__((address_space(3))) const uint16_t* lds_cptr_t;   // 32-bit LDS address
 typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr_t;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 
@@ -67,7 +71,12 @@ struct AttnCfg {
   static constexpr int MTV = DV / 32;        // 32-column M tiles of the output product
   static constexpr int NK = 32;              // keys per tile
   static constexpr int CPR = DQK / 8;        // 16-byte chunks per latent row
-  static constexpr int ROWE = (CPR + 1) * 8; // LDS row stride (elements): one pad chunk
+  // Rows are stored unpadded; when a row is a whole number of 8-chunk groups the 16-byte
+  // chunks of row r are XOR-swizzled by swz(r) (< 8, so a chunk never leaves its group).  With
+  // 64 four-byte banks this makes both LDS read patterns conflict-free: 16 rows x one chunk
+  // (logits operand) and 4 consecutive rows x 4 consecutive chunks (transposed value reads).
+  static constexpr bool SWZ = CPR % 8 == 0;
+  static constexpr int ROWE = CPR * 8;       // LDS row stride (elements)
   static constexpr int TILE = NK * ROWE;     // elements per KV tile buffer
   static constexpr int QLDS = DQL > 0 ? H * QROWE : 8;
   static constexpr int NBUF = 3;             // gather ring depth (tiles t+1, t+2 in flight)
@@ -76,6 +85,8 @@ struct AttnCfg {
   static_assert(GOPS < 64, "vmcnt range");
   static_assert(DQK % 16 == 0 && DV % 32 == 0 && DV <= DQK && DQR % 16 == 0, "head dims");
 };
+
+__device__ __forceinline__ int swz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 
 // Per-row state shared by the fast and exact paths.
 struct RowCtx {
@@ -87,23 +98,28 @@ struct RowCtx {
   unsigned* vm;      // [3][NW] per-tile validity bits of each wave's gathered rows
 };
 
-// Copy one latent row into LDS row `key` of `dst` (16 bytes per lane; lanes past the row idle)
+// Copy one latent row into LDS row `key` of `dst`: the LDS DMA, issued from inline asm so
+// the compiler neither sees the LDS write nor adds waits for it (completion is tracked by
+// hand with vmcnt before each barrier).  M0 holds the wave's LDS destination and lane L
+// writes 16 bytes at M0 + 16 L; the source is the row base (SGPRs) plus a 32-bit per-lane
+// offset that applies the chunk swizzle: physical chunk c0 + L holds logical chunk
+// c0 + (L ^ swz(key)) (c0 is a multiple of 64, swz < 8).
 template <int H, int DQK, int DV>
 __device__ __forceinline__ void gather_row(const AttnArgs& a, const RowCtx& c, int id, int key,
                                            uint16_t* dst) {
   using C = AttnCfg<H, DQK, DV>;
   id = (id < 0 || id >= a.n_k) ? 0 : id;   // empty slot: any in-bounds row, masked later
   const uint16_t* src = a.kv + (size_t)id * DQK;
+  const unsigned sw16 = C::SWZ ? (unsigned)swz(key) * 16u : 0u;
+  const unsigned voff = ((unsigned)c.lane * 16u) ^ sw16;
 #pragma unroll
   for (int c0 = 0; c0 < C::CPR; c0 += 64) {
-    // LDS DMA issued from inline asm: the compiler neither sees the LDS write nor adds waits
-    // for it; completion is tracked by hand (vmcnt before each barrier).  M0 holds the
-    // wave's LDS destination, each lane writes 16 bytes at M0 + 16 * lane.
-    const unsigned lds_addr =
-        (unsigned)(size_t)(lds_u16_ptr_t)(dst + key * C::ROWE + c0 * 8);
+    const unsigned lds_addr = (unsigned)(size_t)(lds_u16_ptr_t)(dst + key * C::ROWE + c0 * 8);
+    // the chunk-group offset goes into the scalar base: an immediate instruction offset would
+    // also move the LDS destination
     if (c0 + c.lane < C::CPR)
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                   :: "s"(lds_addr), "v"(src + (c0 + c.lane) * 8) : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(lds_addr), "v"(voff), "s"(src + c0 * 8) : "memory", "m0");
   }
 }
 
@@ -181,15 +197,25 @@ __device__ __forceinline__ f32x16 tile_logits(const AttnArgs& a, const RowCtx& c
                                               unsigned vmask, float& mx) {
   using C = AttnCfg<H, DQK, DV>;
   f32x16 s = (f32x16){};
-  const uint16_t* arow = tile + key_perm(c.hl) * C::ROWE + c.g * 8;
+  // row key_perm(hl), logical chunk 2*ks + g at physical chunk (2*ks + g) ^ swz(row): the
+  // XOR only touches the low 3 bits, so four per-lane bases (ks mod 4) plus the immediate
+  // offset 128 B * (ks / 4) address every step
+  const int arow_i = key_perm(c.hl);
+  const int asw = C::SWZ ? swz(arow_i) : 0;
+  const lds_cptr_t ltile = (lds_cptr_t)tile;
+  lds_cptr_t abase[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    abase[j] = ltile + arow_i * C::ROWE + (((2 * j + c.g) ^ asw) - 2 * j) * 8;
+  auto arow_at = [&](int ks) { return abase[ks & 3] + ks * 16; };
   const uint16_t* qlrow = c.qlds + (C::DQL > 0 ? c.head % H : 0) * C::QROWE + c.g * 8;
   // A fragments one group ahead of their MFMAs; sched_barrier bounds the live fragments
-  constexpr int QG = 4;
+  constexpr int QG = 3;                 // K steps per prefetch group (36 = 12 x 3)
   constexpr int NG = (C::KS + QG - 1) / QG;
   bf16x8 af[2][QG];
 #pragma unroll
   for (int u = 0; u < QG; ++u)
-    if (u < C::KS) af[0][u] = *reinterpret_cast<const bf16x8*>(arow + u * 16);
+    if (u < C::KS) af[0][u] = *(__attribute__((address_space(3))) const bf16x8*)(arow_at(u));
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     const int cur = gi & 1;
@@ -197,7 +223,7 @@ __device__ __forceinline__ f32x16 tile_logits(const AttnArgs& a, const RowCtx& c
 #pragma unroll
       for (int u = 0; u < QG; ++u) {
         const int ks = (gi + 1) * QG + u;
-        if (ks < C::KS) af[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(arow + ks * 16);
+        if (ks < C::KS) af[cur ^ 1][u] = *(__attribute__((address_space(3))) const bf16x8*)(arow_at(ks));
       }
     }
 #pragma unroll
@@ -232,11 +258,27 @@ __device__ __forceinline__ void tile_pv(const RowCtx& c, const uint16_t* tile, c
   // transposing read: lane (G = lane/16, i = lane%16) supplies row kbase + i/4, columns
   // cbase + (i%4)*4 .. +3 and receives column cbase + i of rows kbase .. kbase+3
   const int G = c.lane >> 4, i = c.lane & 15;
-  const uint16_t* vbase = tile + ((G >> 1) * 8 + (i >> 2)) * C::ROWE + (G & 1) * 16 + (i & 3) * 4;
+  // Lane reads row r = kk*16 + (G/2)*8 + i/4 (+4 for the second half), logical chunk
+  // 4*mt + low with low = 2*(G&1) + (i&3)/2, at physical chunk 4*(mt ^ s2) + (low ^ s01)
+  // where s2 = swz(r) >> 2, s01 = swz(r) & 3.  For even / odd mt that is
+  // 4*mt + 4*s2 / 4*mt - 4*s2: two per-lane bases per (kk, half) plus an immediate 64 B * mt.
+  // swz ignores row bit 4, so the kk = 1 rows (16 further) share the kk = 0 bases plus an
+  // immediate 16-row offset.
+  const int low = 2 * (G & 1) + ((i & 3) >> 1);
+  const lds_cptr_t ltile = (lds_cptr_t)tile;
+  lds_cptr_t vb[2][2];   // [half][mt parity]
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int r = (G >> 1) * 8 + (i >> 2) + hf * 4;
+    const int sw = C::SWZ ? swz(r) : 0;
+    const lds_cptr_t b = ltile + r * C::ROWE + ((low ^ (sw & 3)) * 8) + (i & 1) * 4;
+    vb[hf][0] = b + (sw >> 2) * 32;
+    vb[hf][1] = b - (sw >> 2) * 32;
+  }
   auto vfrag = [&](int kk, int mt) {
-    const uint16_t* p0 = vbase + kk * 16 * C::ROWE + mt * 32;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)p0);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p0 + 4 * C::ROWE));
+    const int off = kk * 16 * C::ROWE + mt * 32;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[0][mt & 1] + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[1][mt & 1] + off));
     return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
   };
   bf16x8 vf[2][2];

@@ -24,6 +24,18 @@ namespace {
 constexpr int kIdxWaves = 8;    // query rows (waves) per workgroup
 constexpr int kIdxKeys = 64;    // keys per LDS stage
 
+// ReLU(x) * w + s with ReLU as one integer max on the fp32 bits: a set sign bit (negative
+// values and -0.0) makes the integer negative, so the result is +0 exactly as max(x, 0).
+__device__ __forceinline__ float relu_fma(float x, float w, float s) {
+  return fmaf(__int_as_float(max(__float_as_int(x), 0)), w, s);
+}
+
+// sum of v over the lane pair (l, l ^ 32)
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(pr[0]) + __int_as_float(pr[1]);
+}
+
 struct RowInfo {
   int row, r, q_len, k_lo, pos, L_blk;
   bool ok;
@@ -122,30 +134,33 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
     const int buf = t & 1;
     if (t + 1 < ntiles) fetch(t + 1);
     if (ri.ok) {
+      // both 32-key sub-tiles are computed unconditionally (keys past the row's window are
+      // only masked at the store), so the second sub-tile's MFMAs overlap the first one's
+      // epilogue
+      f32x16 acc[kIdxKeys / 32][MT];
 #pragma unroll
       for (int nt = 0; nt < kIdxKeys / 32; ++nt) {
-        const int kbase = t * kIdxKeys + nt * 32;
-        if (kbase <= ri.pos) {
-          f32x16 acc[MT];
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x16){};
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = (f32x16){};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 b =
-                *reinterpret_cast<const bf16x8*>(&sk[buf][(nt * 32 + hl) * ROW + ks * 16 + g * 8]);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[mt][ks], b, acc[mt], 0, 0, 0);
-          }
-          float s = 0.f;
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 b =
+              *reinterpret_cast<const bf16x8*>(&sk[buf][(nt * 32 + hl) * ROW + ks * 16 + g * 8]);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s = fmaf(fmaxf(acc[mt][r], 0.f), wv[mt][r], s);
-          s += __shfl_xor(s, 32, 64);
-          const int key = kbase + hl;
-          if (g == 0 && key <= ri.pos) out[key] = s;
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[mt][ks], b, acc[nt][mt], 0, 0, 0);
         }
+      }
+#pragma unroll
+      for (int nt = 0; nt < kIdxKeys / 32; ++nt) {
+        float s = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s = relu_fma(acc[nt][mt][r], wv[mt][r], s);
+        s = pair_sum(s);
+        const int key = t * kIdxKeys + nt * 32 + hl;
+        if (g == 0 && key <= ri.pos) out[key] = s;
       }
     }
     if (t + 1 < ntiles) stash(buf ^ 1);
@@ -275,8 +290,8 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s = fmaf(fmaxf(acc[mt][r], 0.f), wv[mt][r], s);
-          s += __shfl_xor(s, 32, 64);
+            for (int r = 0; r < 16; ++r) s = relu_fma(acc[mt][r], wv[mt][r], s);
+          s = pair_sum(s);
           const int key = kbase + hl;
           if (g == 0 && key <= ri.pos) out[key] = s * sks[buf][nt * 32 + hl];
         }
