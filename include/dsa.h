@@ -31,7 +31,8 @@
  *   - Supported dimensions (anything else is DSA_ERR_UNSUPPORTED):
  *       indexer (h_idx, d_idx) in {(4, 32), (64, 128)};
  *       attention (h, d_qk, d_v) in {(8, 80, 64), (128, 576, 512)};
- *       1 <= topk <= 4096; every window length <= 65536 keys.
+ *       1 <= topk <= 4096; every window length <= 65536 keys; the latent KV (n_k * d_qk
+ *       bf16 values) at most 4 GiB.
  */
 #ifndef DSA_H
 #define DSA_H

@@ -87,6 +87,9 @@ dsa_status check_shape(const dsa_shape* s, int need, Plan& p) {
                   s->h, s->d_qk, s->d_v);
     if (!std::isfinite(s->softmax_scale))
       return fail(DSA_ERR_INVALID_ARG, "softmax_scale is not finite");
+    // the gather addresses latent rows with 32-bit byte offsets
+    if ((int64_t)s->n_k * s->d_qk * 2 > (int64_t)UINT32_MAX)
+      return fail(DSA_ERR_UNSUPPORTED, "latent KV of %d rows exceeds 4 GiB", s->n_k);
   }
   p = Plan();
   if (!(need & kNeedSegs)) return DSA_OK;

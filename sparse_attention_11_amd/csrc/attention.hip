@@ -31,6 +31,8 @@
 //     transposing ds_read_b64_tr_b16) x P^T (B: the lane's bf16 probabilities, no shuffle).
 //     O^T is DV/32 M-tiles of 32 value columns; each lane owns one head's columns, so the
 //     final 1/l is lane-local.
+#include <utility>
+
 #include "dsa_device.h"
 
 namespace dsa {
@@ -80,8 +82,13 @@ struct AttnCfg {
   static constexpr int TILE = NK * ROWE;     // elements per KV tile buffer
   static constexpr int QLDS = DQL > 0 ? H * QROWE : 8;
   static constexpr int NBUF = 3;             // gather ring depth (tiles t+1, t+2 in flight)
-  // vector-memory instructions one wave issues per tile gather (rows x 64-lane pieces)
-  static constexpr int GOPS = (NK / NW) * ((CPR + 63) / 64);
+  static constexpr int RPW = NK / NW;        // tile rows gathered by each wave
+  // Flat gather: a wave's RPW rows are RPW*CPR consecutive 16-byte chunks of the tile buffer,
+  // copied by NI full-wave instructions; each instruction then spans at most two rows.
+  static constexpr bool FLAT = CPR >= 64 && (RPW * CPR) % 64 == 0;
+  static constexpr int NI = FLAT ? RPW * CPR / 64 : 1;
+  // vector-memory instructions one wave issues per tile gather
+  static constexpr int GOPS = FLAT ? NI : RPW * ((CPR + 63) / 64);
   static_assert(GOPS < 64, "vmcnt range");
   static_assert(DQK % 16 == 0 && DV % 32 == 0 && DV <= DQK && DQR % 16 == 0, "head dims");
 };
@@ -145,7 +152,10 @@ struct TileIdx {
   int v[AttnCfg<H, DQK, DV>::NK / AttnCfg<H, DQK, DV>::NW];
 };
 
-template <int H, int DQK, int DV>
+// AL8: topk is a multiple of 8 and the index rows are 32-byte aligned, so a wave's 8 slots of
+// a tile are one aligned 8-dword block, read by one scalar load (the block of the last slots
+// stands in for blocks past topk, whose slots read as -1).
+template <int H, int DQK, int DV, bool AL8>
 __device__ __forceinline__ TileIdx<H, DQK, DV> load_tile_idx_s(const AttnArgs& a,
                                                                const RowCtx& c, int t) {
   using C = AttnCfg<H, DQK, DV>;
@@ -153,13 +163,21 @@ __device__ __forceinline__ TileIdx<H, DQK, DV> load_tile_idx_s(const AttnArgs& a
   // the index list is read-only while the kernel runs: reading it through the constant
   // address space lets uniform loads go to the scalar unit
   typedef __attribute__((address_space(4))) const int32_t* cidx_t;
+  typedef __attribute__((address_space(4))) const i32x8* cidx8_t;
   const cidx_t ip = (cidx_t)c.idx_row;
   TileIdx<H, DQK, DV> r;
+  if constexpr (AL8 && RPW == 8) {
+    const int s0 = t * C::NK + c.wave_u * RPW;
+    const i32x8 v = *(cidx8_t)(ip + min(s0, a.topk - RPW));
 #pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int slot = t * C::NK + c.wave_u * RPW + j;
-    const int v = ip[min(slot, a.topk - 1)];
-    r.v[j] = slot < a.topk ? v : -1;
+    for (int j = 0; j < RPW; ++j) r.v[j] = s0 < a.topk ? v[j] : -1;
+  } else {
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int slot = t * C::NK + c.wave_u * RPW + j;
+      const int v = ip[min(slot, a.topk - 1)];
+      r.v[j] = slot < a.topk ? v : -1;
+    }
   }
   return r;
 }
@@ -182,6 +200,54 @@ __device__ __forceinline__ void gather_tile_s(const AttnArgs& a, const RowCtx& c
   for (int j = 0; j < RPW; ++j) gather_row<H, DQK, DV>(a, c, ti.v[j], c.wave_u * RPW + j, dst);
 }
 
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Byte offset, within its latent row, of the chunk this lane copies in flat instruction i:
+// the lane fills physical chunk f = 64 i + lane of the wave's rows, i.e. chunk f mod CPR of
+// row f / CPR, which holds logical chunk (f mod CPR) ^ swz(row).
+template <int H, int DQK, int DV>
+__device__ __forceinline__ unsigned flat_lane_offset(const RowCtx& c, int i) {
+  using C = AttnCfg<H, DQK, DV>;
+  const int f = i * 64 + c.lane;
+  const int j = f / C::CPR, ch = f - j * C::CPR;
+  const int sw = C::SWZ ? swz(c.wave * C::RPW + j) : 0;
+  return (unsigned)(ch ^ sw) * 16u;
+}
+
+// Flat gather of this wave's rows of a tile.  wb: LDS byte address of the wave's first row.
+// The row offsets are scalars; each lane picks the one of the (at most two) rows its chunk
+// falls in.  Empty slots copy row 0 (masked later).
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void gather_tile_flat(const AttnArgs& a, const RowCtx& c,
+                                                 const TileIdx<H, DQK, DV>& ti,
+                                                 const unsigned* loff, unsigned wb) {
+  using C = AttnCfg<H, DQK, DV>;
+  unsigned so[C::RPW];
+#pragma unroll
+  for (int j = 0; j < C::RPW; ++j)
+    so[j] = (unsigned)ti.v[j] < (unsigned)a.n_k ? (unsigned)ti.v[j] * (C::CPR * 16u) : 0u;
+  static_for<C::NI>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    constexpr int j0 = i * 64 / C::CPR;              // row of lane 0
+    constexpr int b = (j0 + 1) * C::CPR - 64 * i;    // first lane in row j0 + 1
+    unsigned ro = so[j0];
+    if constexpr (b < 64) ro = c.lane >= b ? so[j0 + 1] : ro;
+    const unsigned voff = loff[i] + ro;
+    const unsigned m0v = wb;       // (named locals: asm operands alone do not capture)
+    const uint16_t* base = a.kv;
+    // M0 = LDS destination of lane 0; one wait state between writing M0 and the DMA
+    asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3"
+                 :: "s"(m0v), "n"(i * 1024), "v"(voff), "s"(base) : "memory", "m0", "scc");
+  });
+}
+
 // Wait until at most N of this wave's vector-memory instructions are outstanding, then meet
 // the other waves at a barrier (one asm block, so no memory access moves across it).
 template <int N>
@@ -189,8 +255,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// S^T for one tile (32 keys x the wave's 32 heads) scaled into log2 units, -inf at empty
-// slots; `mx` receives the lane pair's (= one head's) tile max.
+// S^T for one tile (32 keys x the wave's 32 heads), unscaled, -inf at empty slots; `mx`
+// receives the lane pair's (= one head's) tile max in scaled log2 units.
 template <int H, int DQK, int DV>
 __device__ __forceinline__ f32x16 tile_logits(const AttnArgs& a, const RowCtx& c,
                                               const bf16x8* qf, const uint16_t* tile,
@@ -238,15 +304,17 @@ __device__ __forceinline__ f32x16 tile_logits(const AttnArgs& a, const RowCtx& c
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (vmask != 0xFFFFFFFFu) {   // uniform: only tiles with empty slots pay for the mask
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (!((vmask >> acc_key(r, c.g)) & 1u)) s[r] = kNegInf;
+  }
   float m = kNegInf;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const bool ok = (vmask >> acc_key(r, c.g)) & 1u;
-    s[r] = ok ? s[r] * a.scale_log2 : kNegInf;
-    m = fmaxf(m, s[r]);
-  }
+  for (int r = 0; r < 16; ++r) m = fmaxf(m, s[r]);
   const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(m), __float_as_int(m), false, false);
-  mx = fmaxf(__int_as_float(pr[0]), __int_as_float(pr[1]));
+  // the scale is positive, so scaling after the max keeps the order
+  mx = fmaxf(__int_as_float(pr[0]), __int_as_float(pr[1])) * a.scale_log2;
   return s;
 }
 
@@ -359,16 +427,22 @@ __device__ __forceinline__ bool tile_step(const AttnArgs& a, const RowCtx& c, co
   m_true = fmaxf(m_true, mx);
   if (m_used == kNegInf) m_used = mx;  // first tile with a valid key
   const bool over = mx > m_used + kOverflowLog2;
+  // m_used is still -inf only while every key so far is empty; all logits are then -inf
+  const float msub = m_used == kNegInf ? 0.f : m_used;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   bf16x8 pf[2];
   float ls = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    // the sum uses the same bf16-rounded probabilities that enter the value product, so
-    // the output is an exact convex combination of the rounded weights
-    const float p = s[r] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(s[r] - m_used);
-    const __bf16 pb = (__bf16)p;
-    ls += (float)pb;
-    pf[r >> 3][r & 7] = pb;
+  for (int r = 0; r < 16; r += 2) {
+    // p = 2^(z * scale - m) (0 at -inf); the sum uses the same bf16-rounded probabilities
+    // that enter the value product, so the output is an exact convex combination of them
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -msub));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], a.scale_log2, -msub));
+    const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
+    ls = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, ls, false);
+    pf[r >> 3][r & 7] = pk[0];
+    pf[r >> 3][(r & 7) + 1] = pk[1];
   }
   lsum += ls;
   tile_pv<H, DQK, DV>(c, tile, pf, o);
@@ -383,7 +457,7 @@ __device__ __forceinline__ bool tile_step(const AttnArgs& a, const RowCtx& c, co
 // Returns false -- outputs not written -- when some head's max outgrows the scaling range
 // (the loop still runs to the end: a second loop exit would keep the accumulator from
 // staying in registers).
-template <int H, int DQK, int DV>
+template <int H, int DQK, int DV, bool AL8>
 __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx& c,
                                                 const bf16x8* qf) {
   using C = AttnCfg<H, DQK, DV>;
@@ -395,11 +469,24 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
   const int ntiles = (c.ntiles + 2) / 3 * 3;
   constexpr int RPW = C::NK / C::NW;
   using TI = TileIdx<H, DQK, DV>;
-  const TI i0 = load_tile_idx_s<H, DQK, DV>(a, c, 0);
-  const TI i1 = load_tile_idx_s<H, DQK, DV>(a, c, 1);
-  TI i2 = load_tile_idx_s<H, DQK, DV>(a, c, 2);
-  gather_tile_s<H, DQK, DV>(a, c, i0, c.buf[0]);
-  gather_tile_s<H, DQK, DV>(a, c, i1, c.buf[1]);
+  unsigned loff[C::NI];
+  unsigned wb[3];
+  if constexpr (C::FLAT) {
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) loff[i] = flat_lane_offset<H, DQK, DV>(c, i);
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      wb[k] = (unsigned)(size_t)(lds_u16_ptr_t)(c.buf[k]) + c.wave_u * (RPW * C::ROWE * 2);
+  }
+  auto gather = [&](const TI& ti, int k) {
+    if constexpr (C::FLAT) gather_tile_flat<H, DQK, DV>(a, c, ti, loff, wb[k]);
+    else gather_tile_s<H, DQK, DV>(a, c, ti, c.buf[k]);
+  };
+  const TI i0 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 0);
+  const TI i1 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 1);
+  TI i2 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 2);
+  gather(i0, 0);
+  gather(i1, 1);
   if (c.lane == 0) {
     c.vm[0 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i0);
     c.vm[1 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i1);
@@ -408,9 +495,9 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
 
   // step t: fetch the indices of t+3, gather t+2, compute t, then retire this wave's gather
   // of t+1 and meet at the barrier.  `nxt2` holds the indices of t+2 on entry, t+3 on exit.
-  auto step = [&](int t, int slot, uint16_t* cur, uint16_t* ahead2, TI& nxt2) {
-    const TI i3 = load_tile_idx_s<H, DQK, DV>(a, c, t + 3);
-    gather_tile_s<H, DQK, DV>(a, c, nxt2, ahead2);
+  auto step = [&](int t, int slot, uint16_t* cur, int ahead2, TI& nxt2) {
+    const TI i3 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, t + 3);
+    gather(nxt2, ahead2);
     if (c.lane == 0) c.vm[((slot + 2) % 3) * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, nxt2);
     unsigned vmask = 0;
 #pragma unroll
@@ -423,9 +510,9 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
     nxt2 = i3;
   };
   for (int t = 0; t < ntiles; t += 3) {
-    step(t, 0, c.buf[0], c.buf[2], i2);
-    step(t + 1, 1, c.buf[1], c.buf[0], i2);
-    step(t + 2, 2, c.buf[2], c.buf[1], i2);
+    step(t, 0, c.buf[0], 2, i2);
+    step(t + 1, 1, c.buf[1], 0, i2);
+    step(t + 2, 2, c.buf[2], 1, i2);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no gather may outlive the block
   if (overflow) return false;
@@ -460,7 +547,7 @@ __device__ __forceinline__ void accumulate_exact(const AttnArgs& a, const RowCtx
 // EXACT = false: the fast path over blocks = rows (a block per row).
 // EXACT = true: a grid-stride pass that recomputes only rows the fast path marked, with the
 // row max found first so nothing can overflow.
-template <int H, int DQK, int DV, bool EXACT>
+template <int H, int DQK, int DV, bool EXACT, bool AL8>
 __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a) {
   using C = AttnCfg<H, DQK, DV>;
   __shared__ __attribute__((aligned(16))) uint16_t kv0[C::TILE];
@@ -548,7 +635,7 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
       __syncthreads();
     }
     accumulate_exact<H, DQK, DV>(a, c, qf, m_fix);
-  } else if (!accumulate_fast<H, DQK, DV>(a, c, qf) && c.tid == 0) {
+  } else if (!accumulate_fast<H, DQK, DV, AL8>(a, c, qf) && c.tid == 0) {
     a.out[(size_t)c.row * H * DV] = kOverflowMark;
   }
   }
@@ -560,12 +647,15 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int h, int d_qk, int d_v, int n
   AttnArgs ax = a;
   ax.nrows = nblocks;
   const int exact_grid = nblocks < 1024 ? nblocks : 1024;
+  // 8-slot index blocks: topk a multiple of 8 and 32-byte aligned index rows
+  const bool al8 = a.topk >= 8 && a.topk % 8 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 31) == 0;
   if (h == 128 && d_qk == 576 && d_v == 512) {
-    k_sparse_attn<128, 576, 512, false><<<nblocks, 256, 0, s>>>(ax);
-    k_sparse_attn<128, 576, 512, true><<<exact_grid, 256, 0, s>>>(ax);
+    if (al8) k_sparse_attn<128, 576, 512, false, true><<<nblocks, 256, 0, s>>>(ax);
+    else k_sparse_attn<128, 576, 512, false, false><<<nblocks, 256, 0, s>>>(ax);
+    k_sparse_attn<128, 576, 512, true, false><<<exact_grid, 256, 0, s>>>(ax);
   } else if (h == 8 && d_qk == 80 && d_v == 64) {
-    k_sparse_attn<8, 80, 64, false><<<nblocks, 64, 0, s>>>(ax);
-    k_sparse_attn<8, 80, 64, true><<<exact_grid, 64, 0, s>>>(ax);
+    k_sparse_attn<8, 80, 64, false, false><<<nblocks, 64, 0, s>>>(ax);
+    k_sparse_attn<8, 80, 64, true, false><<<exact_grid, 64, 0, s>>>(ax);
   } else {
     return hipErrorInvalidValue;
   }
