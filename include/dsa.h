@@ -161,6 +161,32 @@ dsa_status dsa_forward(const dsa_shape *shape, const void *q_idx, const float *q
                        size_t workspace_bytes, void *stream);
 
 /*
+ * Sparse-attention backward (page "CANNTorchTitan: ...", section "SparseFlashAttentionGrad"):
+ * for each row i, head h and selected slot s (valid index k = topk_idx[i][s]):
+ *   z = softmax_scale * q[i,h,:] . kv[k,:];  P = exp(z - softmax_max[i,h]) / softmax_sum[i,h];
+ *   D = sum_c dout[i,h,c] * out[i,h,c];  dP = dout[i,h,:] . kv[k,:d_v];  dS = P * (dP - D);
+ *   dq[i,h,:]   = softmax_scale * sum_s dS * kv[k,:]
+ *   dkv[k,:]   += softmax_scale * sum_h dS * q[i,h,:]
+ *   dkv[k,:d_v] += sum_h P * dout[i,h,:]
+ * q [n_q, h, d_qk], kv [n_k, d_qk], out / dout [n_q, h, d_v] bf16 (out and the statistics as
+ * written by the forward); topk_idx [n_q, topk] as for dsa_sparse_attn (empty slots skipped);
+ * dq [n_q, h, d_qk] bf16 (written); dkv [n_k, d_qk] fp32 is ADDED to with atomics, so the
+ * caller zeroes it (or accumulates into it) and the order of the additions is not fixed.
+ * Built for (h, d_qk, d_v) = (128, 576, 512) only (else DSA_ERR_UNSUPPORTED).  The workspace
+ * (16-byte aligned) holds bf16 P and dS for a chunk of rows; rows are processed in chunks of
+ * as many rows as it fits (DSA_ERR_WORKSPACE if not even one).
+ */
+dsa_status dsa_sparse_attn_bwd(const dsa_shape *shape, const void *q, const void *kv,
+                               const int32_t *topk_idx, const void *out, const void *dout,
+                               const float *softmax_max, const float *softmax_sum, void *dq,
+                               float *dkv, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Workspace size for dsa_sparse_attn_bwd that processes up to 4096 rows per pass:
+ * 4 * topk_p * h bytes per row, topk_p = topk rounded up to a multiple of 96. */
+dsa_status dsa_sparse_attn_bwd_workspace_bytes(const dsa_shape *shape, size_t *bytes);
+
+/*
  * Per-row (per-token) fp8 quantization for the fp8 indexer: for each of `rows` rows of
  * `cols` bf16 values, scale = amax(|row|) / 448 (1.0 for an all-zero row) and
  * code = e4m3fn(round-to-nearest-even(x / scale)), saturating at +-448; scale and x / scale

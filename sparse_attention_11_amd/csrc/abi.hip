@@ -20,6 +20,7 @@ int indexer_rows_per_block();
 hipError_t launch_topk(const TopkArgs& a, int max_window, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnArgs& a, int h, int d_qk, int d_v, int nblocks,
                               hipStream_t s);
+hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v, hipStream_t s);
 hipError_t launch_quant_fp8_rows(const QuantArgs& a, hipStream_t s);
 }  // namespace dsa
 
@@ -246,6 +247,20 @@ dsa_status check_idx_ptrs(const dsa_shape* s, const void* q_idx, const float* q_
   return DSA_OK;
 }
 
+// Backward workspace: bf16 P and softmax_scale * dS for every (row, slot, head), with the
+// slots of a row padded to a multiple of 96 (three 32-slot tiles: the gather ring processes
+// tiles in threes).
+size_t bwd_topkp(const dsa_shape* s) { return ((size_t)s->topk + 95) / 96 * 96; }
+size_t bwd_row_bytes(const dsa_shape* s) { return 2 * bwd_topkp(s) * (size_t)s->h * 2; }
+constexpr int kBwdChunkRows = 4096;
+
+dsa_status check_bwd_dims(const dsa_shape* s) {
+  if (!(s->h == 128 && s->d_qk == 576 && s->d_v == 512))
+    return fail(DSA_ERR_UNSUPPORTED, "attention backward built for (h, d_qk, d_v) = "
+                "(128, 576, 512) only (got %d, %d, %d)", s->h, s->d_qk, s->d_v);
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -351,6 +366,65 @@ dsa_status dsa_quantize_fp8_rows(const void* x_bf16, int64_t rows, int32_t cols,
   a.cols = cols;
   hipError_t e = dsa::launch_quant_fp8_rows(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return ok();
+}
+
+dsa_status dsa_sparse_attn_bwd_workspace_bytes(const dsa_shape* shape, size_t* bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedAttn, p);
+  if (st != DSA_OK) return st;
+  if ((st = check_bwd_dims(shape)) != DSA_OK) return st;
+  *bytes = bwd_row_bytes(shape) * (size_t)std::min(shape->n_q, kBwdChunkRows);
+  return ok();
+}
+
+dsa_status dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void* kv,
+                               const int32_t* topk_idx, const void* out, const void* dout,
+                               const float* softmax_max, const float* softmax_sum, void* dq,
+                               float* dkv, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedAttn, p);
+  if (st != DSA_OK) return st;
+  if ((st = check_bwd_dims(shape)) != DSA_OK) return st;
+  if (shape->n_q == 0) return ok();
+  if (!q || !kv || !topk_idx || !out || !dout || !softmax_max || !softmax_sum || !dq || !dkv)
+    return fail(DSA_ERR_INVALID_ARG, "attention backward tensor is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const size_t per_row = bwd_row_bytes(shape);
+  const size_t fit = workspace ? workspace_bytes / per_row : 0;
+  if (fit == 0)
+    return fail(DSA_ERR_WORKSPACE, "workspace of at least %zu bytes (one row) needed, %zu given",
+                per_row, workspace ? workspace_bytes : (size_t)0);
+  const int chunk = (int)std::min<size_t>(fit, (size_t)shape->n_q);
+  const int h = shape->h, dqk = shape->d_qk, dv = shape->d_v, topk = shape->topk;
+  const size_t topkp = bwd_topkp(shape);
+  dsa::AttnBwdArgs a = {};
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.dkv = dkv;
+  a.n_k = shape->n_k;
+  a.topk = topk;
+  a.topkp = (int)topkp;
+  a.scale = shape->softmax_scale;
+  a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
+  a.ws_p = static_cast<uint16_t*>(workspace);
+  a.ws_ds = a.ws_p + (size_t)chunk * topkp * h;
+  for (int r0 = 0; r0 < shape->n_q; r0 += chunk) {
+    const int rows = std::min(chunk, shape->n_q - r0);
+    a.rows = rows;
+    a.q = static_cast<const uint16_t*>(q) + (size_t)r0 * h * dqk;
+    a.idx = topk_idx + (size_t)r0 * topk;
+    a.out = static_cast<const uint16_t*>(out) + (size_t)r0 * h * dv;
+    a.dout = static_cast<const uint16_t*>(dout) + (size_t)r0 * h * dv;
+    a.smax = softmax_max + (size_t)r0 * h;
+    a.ssum = softmax_sum + (size_t)r0 * h;
+    a.dq = static_cast<uint16_t*>(dq) + (size_t)r0 * h * dqk;
+    a.xcd_remap = rows % 8 == 0;
+    hipError_t e = dsa::launch_sparse_attn_bwd(a, h, dqk, dv, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  }
   return ok();
 }
 

@@ -31,229 +31,11 @@
 //     transposing ds_read_b64_tr_b16) x P^T (B: the lane's bf16 probabilities, no shuffle).
 //     O^T is DV/32 M-tiles of 32 value columns; each lane owns one head's columns, so the
 //     final 1/l is lane-local.
-#include <utility>
-
-#include "dsa_device.h"
+#include "attn_common.h"
 
 namespace dsa {
 
 namespace {
-
-typedef __attribute__((address_space(3))) uint16_t* lds_u16_ptr_t;
-typedef __attribute__((address_space(3))) const uint16_t* lds_cptr_t;   // 32-bit LDS address
-typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr_t;
-typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
-
-// LDS row (within a 32-key tile) that feeds A-operand row m of the logits product
-__device__ __forceinline__ int key_perm(int m) {
-  const int q = m >> 3, gg = (m >> 2) & 1, rr = m & 3;
-  return (q >> 1) * 16 + gg * 8 + (q & 1) * 4 + rr;
-}
-
-// key within the tile held by accumulator register r of a lane in half g (0/1)
-__device__ __forceinline__ int acc_key(int r, int g) {
-  return r < 8 ? g * 8 + r : 16 + g * 8 + (r - 8);
-}
-
-constexpr float kOverflowLog2 = 64.0f;  // p may reach 2^64 before the row is recomputed
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kNegInf = -__builtin_huge_valf();
-// bf16 quiet NaN with a payload arithmetic does not produce: marks a row for the exact pass
-constexpr uint16_t kOverflowMark = 0x7FD5;
-
-template <int H, int DQK, int DV>
-struct AttnCfg {
-  static constexpr int NW = (H + 31) / 32;   // waves, 32 heads each
-  static constexpr int NT = NW * 64;
-  static constexpr int KS = DQK / 16;        // K steps of the logits product
-  static constexpr int DQR = DQK > 416 ? 416 : DQK;  // Q dims held in VGPRs
-  static constexpr int KSR = DQR / 16;
-  static constexpr int DQL = DQK - DQR;      // Q dims staged in LDS
-  static constexpr int QROWE = DQL + 8;      // LDS row stride (elements) of staged Q
-  static constexpr int MTV = DV / 32;        // 32-column M tiles of the output product
-  static constexpr int NK = 32;              // keys per tile
-  static constexpr int CPR = DQK / 8;        // 16-byte chunks per latent row
-  // Rows are stored unpadded; when a row is a whole number of 8-chunk groups the 16-byte
-  // chunks of row r are XOR-swizzled by swz(r) (< 8, so a chunk never leaves its group).  With
-  // 64 four-byte banks this makes both LDS read patterns conflict-free: 16 rows x one chunk
-  // (logits operand) and 4 consecutive rows x 4 consecutive chunks (transposed value reads).
-  static constexpr bool SWZ = CPR % 8 == 0;
-  static constexpr int ROWE = CPR * 8;       // LDS row stride (elements)
-  static constexpr int TILE = NK * ROWE;     // elements per KV tile buffer
-  static constexpr int QLDS = DQL > 0 ? H * QROWE : 8;
-  static constexpr int NBUF = 3;             // gather ring depth (tiles t+1, t+2 in flight)
-  static constexpr int RPW = NK / NW;        // tile rows gathered by each wave
-  // Flat gather: a wave's RPW rows are RPW*CPR consecutive 16-byte chunks of the tile buffer,
-  // copied by NI full-wave instructions; each instruction then spans at most two rows.
-  static constexpr bool FLAT = CPR >= 64 && (RPW * CPR) % 64 == 0;
-  static constexpr int NI = FLAT ? RPW * CPR / 64 : 1;
-  // vector-memory instructions one wave issues per tile gather
-  static constexpr int GOPS = FLAT ? NI : RPW * ((CPR + 63) / 64);
-  static_assert(GOPS < 64, "vmcnt range");
-  static_assert(DQK % 16 == 0 && DV % 32 == 0 && DV <= DQK && DQR % 16 == 0, "head dims");
-};
-
-__device__ __forceinline__ int swz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
-
-// Per-row state shared by the fast and exact paths.
-struct RowCtx {
-  int row, tid, lane, wave, wave_u, hl, g, head, ntiles;
-  const int32_t* idx_row;
-  uint16_t* buf[3];  // KV tile buffers (separate LDS objects)
-  uint16_t* qlds;    // staged Q dims
-  int* flags;        // [2][NW] per-tile overflow flags
-  unsigned* vm;      // [3][NW] per-tile validity bits of each wave's gathered rows
-};
-
-// Copy one latent row into LDS row `key` of `dst`: the LDS DMA, issued from inline asm so
-// the compiler neither sees the LDS write nor adds waits for it (completion is tracked by
-// hand with vmcnt before each barrier).  M0 holds the wave's LDS destination and lane L
-// writes 16 bytes at M0 + 16 L; the source is the row base (SGPRs) plus a 32-bit per-lane
-// offset that applies the chunk swizzle: physical chunk c0 + L holds logical chunk
-// c0 + (L ^ swz(key)) (c0 is a multiple of 64, swz < 8).
-template <int H, int DQK, int DV>
-__device__ __forceinline__ void gather_row(const AttnArgs& a, const RowCtx& c, int id, int key,
-                                           uint16_t* dst) {
-  using C = AttnCfg<H, DQK, DV>;
-  id = (id < 0 || id >= a.n_k) ? 0 : id;   // empty slot: any in-bounds row, masked later
-  const uint16_t* src = a.kv + (size_t)id * DQK;
-  const unsigned sw16 = C::SWZ ? (unsigned)swz(key) * 16u : 0u;
-  const unsigned voff = ((unsigned)c.lane * 16u) ^ sw16;
-#pragma unroll
-  for (int c0 = 0; c0 < C::CPR; c0 += 64) {
-    const unsigned lds_addr = (unsigned)(size_t)(lds_u16_ptr_t)(dst + key * C::ROWE + c0 * 8);
-    // the chunk-group offset goes into the scalar base: an immediate instruction offset would
-    // also move the LDS destination
-    if (c0 + c.lane < C::CPR)
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :: "s"(lds_addr), "v"(voff), "s"(src + c0 * 8) : "memory", "m0");
-  }
-}
-
-// Gather of tile t with the indices read by scalar loads (exact path)
-template <int H, int DQK, int DV>
-__device__ __forceinline__ void gather_tile(const AttnArgs& a, const RowCtx& c, int t,
-                                            uint16_t* dst) {
-  using C = AttnCfg<H, DQK, DV>;
-#pragma unroll
-  for (int rr = 0; rr < C::NK / C::NW; ++rr) {
-    const int key = rr * C::NW + c.wave_u;
-    const int slot = t * C::NK + key;
-    const int id = slot < a.topk ? c.idx_row[slot] : -1;
-    gather_row<H, DQK, DV>(a, c, __builtin_amdgcn_readfirstlane(id), key, dst);
-  }
-}
-
-// The slot indices one wave gathers for tile t (rows wave*RPW .. +RPW-1 of the tile), read
-// with scalar loads: they count against lgkmcnt, so waiting for them never drains the
-// in-flight gathers (which count against vmcnt).  Slots past topk read as -1.
-template <int H, int DQK, int DV>
-struct TileIdx {
-  int v[AttnCfg<H, DQK, DV>::NK / AttnCfg<H, DQK, DV>::NW];
-};
-
-// AL8: topk is a multiple of 8 and the index rows are 32-byte aligned, so a wave's 8 slots of
-// a tile are one aligned 8-dword block, read by one scalar load (the block of the last slots
-// stands in for blocks past topk, whose slots read as -1).
-template <int H, int DQK, int DV, bool AL8>
-__device__ __forceinline__ TileIdx<H, DQK, DV> load_tile_idx_s(const AttnArgs& a,
-                                                               const RowCtx& c, int t) {
-  using C = AttnCfg<H, DQK, DV>;
-  constexpr int RPW = C::NK / C::NW;
-  // the index list is read-only while the kernel runs: reading it through the constant
-  // address space lets uniform loads go to the scalar unit
-  typedef __attribute__((address_space(4))) const int32_t* cidx_t;
-  typedef __attribute__((address_space(4))) const i32x8* cidx8_t;
-  const cidx_t ip = (cidx_t)c.idx_row;
-  TileIdx<H, DQK, DV> r;
-  if constexpr (AL8 && RPW == 8) {
-    const int s0 = t * C::NK + c.wave_u * RPW;
-    const i32x8 v = *(cidx8_t)(ip + min(s0, a.topk - RPW));
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) r.v[j] = s0 < a.topk ? v[j] : -1;
-  } else {
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int slot = t * C::NK + c.wave_u * RPW + j;
-      const int v = ip[min(slot, a.topk - 1)];
-      r.v[j] = slot < a.topk ? v : -1;
-    }
-  }
-  return r;
-}
-
-// Validity bits of this wave's slots of a tile (bit j: row wave*RPW + j).
-template <int H, int DQK, int DV>
-__device__ __forceinline__ unsigned tile_bits(const AttnArgs& a, const TileIdx<H, DQK, DV>& ti) {
-  constexpr int RPW = AttnCfg<H, DQK, DV>::NK / AttnCfg<H, DQK, DV>::NW;
-  unsigned m = 0;
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) m |= (ti.v[j] >= 0 && ti.v[j] < a.n_k) ? (1u << j) : 0u;
-  return m;
-}
-
-template <int H, int DQK, int DV>
-__device__ __forceinline__ void gather_tile_s(const AttnArgs& a, const RowCtx& c,
-                                              const TileIdx<H, DQK, DV>& ti, uint16_t* dst) {
-  constexpr int RPW = AttnCfg<H, DQK, DV>::NK / AttnCfg<H, DQK, DV>::NW;
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) gather_row<H, DQK, DV>(a, c, ti.v[j], c.wave_u * RPW + j, dst);
-}
-
-template <typename F, int... Is>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Byte offset, within its latent row, of the chunk this lane copies in flat instruction i:
-// the lane fills physical chunk f = 64 i + lane of the wave's rows, i.e. chunk f mod CPR of
-// row f / CPR, which holds logical chunk (f mod CPR) ^ swz(row).
-template <int H, int DQK, int DV>
-__device__ __forceinline__ unsigned flat_lane_offset(const RowCtx& c, int i) {
-  using C = AttnCfg<H, DQK, DV>;
-  const int f = i * 64 + c.lane;
-  const int j = f / C::CPR, ch = f - j * C::CPR;
-  const int sw = C::SWZ ? swz(c.wave * C::RPW + j) : 0;
-  return (unsigned)(ch ^ sw) * 16u;
-}
-
-// Flat gather of this wave's rows of a tile.  wb: LDS byte address of the wave's first row.
-// The row offsets are scalars; each lane picks the one of the (at most two) rows its chunk
-// falls in.  Empty slots copy row 0 (masked later).
-template <int H, int DQK, int DV>
-__device__ __forceinline__ void gather_tile_flat(const AttnArgs& a, const RowCtx& c,
-                                                 const TileIdx<H, DQK, DV>& ti,
-                                                 const unsigned* loff, unsigned wb) {
-  using C = AttnCfg<H, DQK, DV>;
-  unsigned so[C::RPW];
-#pragma unroll
-  for (int j = 0; j < C::RPW; ++j)
-    so[j] = (unsigned)ti.v[j] < (unsigned)a.n_k ? (unsigned)ti.v[j] * (C::CPR * 16u) : 0u;
-  static_for<C::NI>([&](auto I) {
-    constexpr int i = decltype(I)::value;
-    constexpr int j0 = i * 64 / C::CPR;              // row of lane 0
-    constexpr int b = (j0 + 1) * C::CPR - 64 * i;    // first lane in row j0 + 1
-    unsigned ro = so[j0];
-    if constexpr (b < 64) ro = c.lane >= b ? so[j0 + 1] : ro;
-    const unsigned voff = loff[i] + ro;
-    const unsigned m0v = wb;       // (named locals: asm operands alone do not capture)
-    const uint16_t* base = a.kv;
-    // M0 = LDS destination of lane 0; one wait state between writing M0 and the DMA
-    asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3"
-                 :: "s"(m0v), "n"(i * 1024), "v"(voff), "s"(base) : "memory", "m0", "scc");
-  });
-}
-
-// Wait until at most N of this wave's vector-memory instructions are outstanding, then meet
-// the other waves at a barrier (one asm block, so no memory access moves across it).
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
 
 // S^T for one tile (32 keys x the wave's 32 heads), unscaled, -inf at empty slots; `mx`
 // receives the lane pair's (= one head's) tile max in scaled log2 units.
@@ -365,26 +147,9 @@ __device__ __forceinline__ void tile_pv(const RowCtx& c, const uint16_t* tile, c
   }
 }
 
-template <int H, int DQK, int DV>
-__device__ __forceinline__ unsigned tile_vmask(const AttnArgs& a, const RowCtx& c, int t) {
-  const int slot = t * AttnCfg<H, DQK, DV>::NK + c.hl;
-  const int id = slot < a.topk ? c.idx_row[slot] : -1;
-  return (unsigned)__ballot(id >= 0 && id < a.n_k);
-}
 
 
 
-template <int H, int DQK, int DV>
-__device__ __forceinline__ void load_q(const AttnArgs& a, const RowCtx& c, bf16x8* qf) {
-  using C = AttnCfg<H, DQK, DV>;
-  const bool hv = (H % 32 == 0) || c.head < H;
-  const uint16_t* qp = a.q + ((size_t)c.row * H + (hv ? c.head : 0)) * DQK + c.g * 8;
-#pragma unroll
-  for (int ks = 0; ks < C::KSR; ++ks) {
-    const uint4 v = *reinterpret_cast<const uint4*>(qp + ks * 16);
-    qf[ks] = hv ? __builtin_bit_cast(bf16x8, v) : (bf16x8){};
-  }
-}
 
 template <int H, int DQK, int DV>
 __device__ __forceinline__ void write_row(const AttnArgs& a, const RowCtx& c, const f32x16* o,

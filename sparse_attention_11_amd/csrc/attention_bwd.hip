@@ -1,0 +1,549 @@
+// Sparse multi-query attention backward on gfx950 MFMA.
+//
+// Page "CANNTorchTitan: DeepSeek-V3.2 32k长序列预训练昇腾优化实践", section
+// "SparseFlashAttentionGrad": the selected latent rows are gathered again, the probabilities
+// P are recomputed from the forward's softmax statistics, dP = dY V_sel^T,
+// dS = P * (dP - D) with D = rowsum(dY * out) (the FlashSoftmaxGrad step),
+// dQ = dS K_sel / sqrt(d), and the key / value gradients dS^T Q / sqrt(d) and P^T dY are
+// scatter-added into the selected rows.  Under weight absorption key and value share one
+// latent row, so both land in one fp32 dKV row (the value part in its first d_v columns).
+//
+// Three kernels over a chunk of query rows, one workgroup per row and four waves:
+//   * k_attn_bwd_p: the forward's gather ring and logits product; every 16-dim A fragment
+//     of the key tile feeds both S^T = K Q^T and (first d_v dims) dP^T = V dY^T, so the
+//     tile is read from LDS once for both.  Each wave owns 32 heads.  It writes P and
+//     softmax_scale * dS as bf16 to a [row][slot][head] workspace (zero at empty slots).
+//   * k_attn_bwd_dq: gathers the key tiles again together with the wave's dS tile (both by
+//     LDS DMA) and accumulates dQ^T[dim, head] += K^T dS^T over the 18 dim tiles of the row
+//     (K^T read with the transposing LDS read), one wave per 32 heads.
+//   * k_attn_bwd_dkv: no gather.  Each wave owns 144 of the 576 latent dims and holds
+//     Q[:, dims] and dY[:, dims] for all 128 heads as B fragments (staged through LDS once
+//     per row); per tile it forms dKV[slot, dim] = dS^T Q + P^T dY on 16x16x32 MFMA with
+//     A fragments loaded straight from the workspace, then adds the tile into the fp32 dKV
+//     rows with global atomics (64-byte runs of consecutive dims per slot).
+#include "attn_common.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Number of 32-slot tiles up to the row's last valid index (block-wide; one barrier).
+template <int H, int DQK, int DV>
+__device__ __forceinline__ int row_tiles(const AttnBwdArgs& a, const RowCtx& c, int* s_last) {
+  using C = AttnCfg<H, DQK, DV>;
+  int last = -1;
+  for (int sl = c.tid; sl < a.topk; sl += C::NT) {
+    const int id = c.idx_row[sl];
+    if (id >= 0 && id < a.n_k) last = sl;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if (c.lane == 0) s_last[c.wave] = last;
+  __syncthreads();
+  last = -1;
+#pragma unroll
+  for (int w = 0; w < C::NW; ++w) last = max(last, s_last[w]);
+  return (last + C::NK) / C::NK;
+}
+
+__device__ __forceinline__ RowCtx make_ctx(const AttnBwdArgs& a, int row) {
+  RowCtx c;
+  c.row = row;
+  c.tid = threadIdx.x;
+  c.lane = c.tid & 63;
+  c.wave = c.tid >> 6;
+  c.wave_u = __builtin_amdgcn_readfirstlane(c.wave);
+  c.hl = c.lane & 31;
+  c.g = c.lane >> 5;
+  c.head = c.wave * 32 + c.hl;
+  c.idx_row = a.idx + (size_t)row * a.topk;
+  c.flags = nullptr;
+  c.vm = nullptr;
+  c.qlds = nullptr;
+  return c;
+}
+
+__device__ __forceinline__ int block_row(const AttnBwdArgs& a) {
+  int blk = blockIdx.x;
+  if (a.xcd_remap) blk = (blk & 7) * ((int)gridDim.x >> 3) + (blk >> 3);
+  return blk;
+}
+
+// Transposed fragment of a row-major LDS matrix with `cols` columns: within each 16-lane
+// group, lane i supplies row r0 + i/4 (r0 + 4 + i/4 for the second half), columns
+// c0 + 4 (i % 4) .. +3, and receives column c0 + i of rows r0 .. r0 + 7.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* m, int cols, int r0, int c0, int i) {
+  const lds_cptr_t b = (lds_cptr_t)m + (r0 + (i >> 2)) * cols + c0 + (i & 3) * 4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)b);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(b + 4 * cols));
+  return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
+// ---------------------------------------------------------------------------------------
+// k_attn_bwd_p: P and softmax_scale * dS per (row, slot, head)
+// ---------------------------------------------------------------------------------------
+
+// S^T (all DQK dims) and dP^T (first DV dims) of one tile; A fragments shared.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void tile_s_dp(const RowCtx& c, const bf16x8* qf, const bf16x8* dof,
+                                          const uint16_t* tile, f32x16& s, f32x16& dp) {
+  using C = AttnCfg<H, DQK, DV>;
+  constexpr int KSV = DV / 16;
+  s = (f32x16){};
+  dp = (f32x16){};
+  const int arow_i = key_perm(c.hl);
+  const int asw = C::SWZ ? swz(arow_i) : 0;
+  const lds_cptr_t ltile = (lds_cptr_t)tile;
+  lds_cptr_t abase[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    abase[j] = ltile + arow_i * C::ROWE + (((2 * j + c.g) ^ asw) - 2 * j) * 8;
+  auto arow_at = [&](int ks) { return abase[ks & 3] + ks * 16; };
+  const uint16_t* qlrow = c.qlds + (C::DQL > 0 ? c.head % H : 0) * C::QROWE + c.g * 8;
+  constexpr int QG = 3;
+  constexpr int NG = (C::KS + QG - 1) / QG;
+  bf16x8 af[2][QG];
+#pragma unroll
+  for (int u = 0; u < QG; ++u)
+    if (u < C::KS) af[0][u] = *(__attribute__((address_space(3))) const bf16x8*)(arow_at(u));
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int cur = gi & 1;
+    if (gi + 1 < NG) {
+#pragma unroll
+      for (int u = 0; u < QG; ++u) {
+        const int ks = (gi + 1) * QG + u;
+        if (ks < C::KS) af[cur ^ 1][u] = *(__attribute__((address_space(3))) const bf16x8*)(arow_at(ks));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < QG; ++u) {
+      const int ks = gi * QG + u;
+      if (ks < C::KS) {
+        bf16x8 bq;
+        if (ks < C::KSR) bq = qf[ks < C::KSR ? ks : 0];
+        else bq = *reinterpret_cast<const bf16x8*>(qlrow + (ks - C::KSR) * 16);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][u], bq, s, 0, 0, 0);
+        if (ks < KSV) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][u], dof[ks < KSV ? ks : 0], dp, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int H, int DQK, int DV, bool AL8>
+__global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p(AttnBwdArgs a) {
+  using C = AttnCfg<H, DQK, DV>;
+  static_assert(H % 32 == 0, "32 heads per wave");
+  constexpr int RPW = C::RPW;
+  constexpr int KSV = DV / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t kv0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv1[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv2[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[C::QLDS];
+  __shared__ unsigned vmring[3 * C::NW];
+  __shared__ int s_last[C::NW];
+
+  RowCtx c = make_ctx(a, block_row(a));
+  c.buf[0] = kv0;
+  c.buf[1] = kv1;
+  c.buf[2] = kv2;
+  c.qlds = qlds;
+  c.vm = vmring;
+  c.ntiles = row_tiles<H, DQK, DV>(a, c, s_last);
+  if (c.ntiles == 0) return;   // nothing selected: the row has no P / dS and no dKV share
+
+  if constexpr (C::DQL > 0) {
+    constexpr int CH = C::DQL / 8;
+    const uint16_t* qrow = a.q + (size_t)c.row * H * DQK + C::DQR;
+    for (int i = c.tid; i < H * CH; i += C::NT) {
+      const int hh = i / CH, cc = i % CH;
+      *reinterpret_cast<uint4*>(&qlds[hh * C::QROWE + cc * 8]) =
+          *reinterpret_cast<const uint4*>(qrow + (size_t)hh * DQK + cc * 8);
+    }
+  }
+  bf16x8 qf[C::KSR];
+  load_q<H, DQK, DV>(a, c, qf);
+  // dY fragments (B operand of dP^T, same lane layout as Q) and D = rowsum(dY * out)
+  bf16x8 dof[KSV];
+  const size_t hrow = (size_t)c.row * H + c.head;
+  const uint16_t* dop = a.dout + hrow * DV + c.g * 8;
+  const uint16_t* op = a.out + hrow * DV + c.g * 8;
+  float dpart = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KSV; ++ks) {
+    dof[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dop + ks * 16));
+    const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(op + ks * 16));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 x = {dof[ks][e], dof[ks][e + 1]};
+      const bf16x2 y = {ov[e], ov[e + 1]};
+      dpart = __builtin_amdgcn_fdot2_f32_bf16(x, y, dpart, false);
+    }
+  }
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(dpart), __float_as_int(dpart), false, false);
+  const float D = __int_as_float(pr[0]) + __int_as_float(pr[1]);
+  const float mrow = a.smax[hrow];
+  const float msub = mrow == kNegInf ? 0.f : mrow * kLog2e;   // scaled log2 units
+  const float lrow = a.ssum[hrow];
+  const float invl = lrow > 0.f ? 1.f / lrow : 0.f;
+  __syncthreads();                        // staged Q visible
+  __builtin_amdgcn_s_waitcnt(0x0F70);     // row loads done before the gather ring starts
+
+  using TI = TileIdx<H, DQK, DV>;
+  unsigned loff[C::NI];
+  unsigned wb[3];
+  if constexpr (C::FLAT) {
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) loff[i] = flat_lane_offset<H, DQK, DV>(c, i);
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      wb[k] = (unsigned)(size_t)(lds_u16_ptr_t)(c.buf[k]) + c.wave_u * (RPW * C::ROWE * 2);
+  }
+  auto gather = [&](const TI& ti, int k) {
+    if constexpr (C::FLAT) gather_tile_flat<H, DQK, DV>(a, c, ti, loff, wb[k]);
+    else gather_tile_s<H, DQK, DV>(a, c, ti, c.buf[k]);
+  };
+  uint16_t* prow = a.ws_p + (size_t)c.row * a.topkp * H + c.head;
+  uint16_t* drow = a.ws_ds + (size_t)c.row * a.topkp * H + c.head;
+  // results of the previous tile, stored at the start of the next step -- before that
+  // step's gather, so the vmcnt wait at its end still only has to spare the gather
+  uint16_t pend_p[16], pend_d[16];
+  int pend_t = -1;
+  auto flush = [&]() {
+    if (pend_t >= 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const size_t o = (size_t)(pend_t * C::NK + acc_key(r, c.g)) * H;
+        prow[o] = pend_p[r];
+        drow[o] = pend_d[r];
+      }
+    }
+  };
+
+  const int ntiles = (c.ntiles + 2) / 3 * 3;
+  const TI i0 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 0);
+  const TI i1 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 1);
+  TI i2 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 2);
+  gather(i0, 0);
+  gather(i1, 1);
+  if (c.lane == 0) {
+    c.vm[0 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i0);
+    c.vm[1 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i1);
+  }
+  wait_vm_barrier<C::GOPS>();
+
+  auto step = [&](int t, int slot, const uint16_t* cur, int ahead2, TI& nxt2) {
+    const TI i3 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, t + 3);
+    flush();
+    gather(nxt2, ahead2);
+    if (c.lane == 0) c.vm[((slot + 2) % 3) * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, nxt2);
+    unsigned vmask = 0;
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) vmask |= c.vm[slot * C::NW + w] << (w * RPW);
+    f32x16 s, dp;
+    tile_s_dp<H, DQK, DV>(c, qf, dof, cur, s, dp);
+    if (vmask != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (!((vmask >> acc_key(r, c.g)) & 1u)) s[r] = kNegInf;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -msub)) * invl;
+      pend_p[r] = f32_to_bf16(p);
+      pend_d[r] = f32_to_bf16(a.scale * p * (dp[r] - D));
+    }
+    pend_t = t;
+    wait_vm_barrier<C::GOPS>();   // tile t+1 landed for every wave
+    nxt2 = i3;
+  };
+  for (int t = 0; t < ntiles; t += 3) {
+    step(t, 0, c.buf[0], 2, i2);
+    step(t + 1, 1, c.buf[1], 0, i2);
+    step(t + 2, 2, c.buf[2], 1, i2);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no gather may outlive the block
+  flush();
+}
+
+// ---------------------------------------------------------------------------------------
+// k_attn_bwd_dq: dQ = (softmax_scale * dS) K_sel
+// ---------------------------------------------------------------------------------------
+
+template <int H, int DQK, int DV, bool AL8>
+__global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_dq(AttnBwdArgs a) {
+  using C = AttnCfg<H, DQK, DV>;
+  static_assert(H % 32 == 0, "32 heads per wave");
+  constexpr int RPW = C::RPW;
+  constexpr int MTQ = DQK / 32;          // 32-dim M tiles of dQ^T
+  constexpr int DSW = C::NK * 32;        // dS elements per wave and tile: [32 slots][32 heads]
+  constexpr int GOPS2 = C::GOPS + 2;     // + two 1 KB DMA pieces of the wave's dS tile
+  __shared__ __attribute__((aligned(16))) uint16_t kv0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv1[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv2[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t ds0[C::NW * DSW];
+  __shared__ __attribute__((aligned(16))) uint16_t ds1[C::NW * DSW];
+  __shared__ __attribute__((aligned(16))) uint16_t ds2[C::NW * DSW];
+  __shared__ unsigned vmring[3 * C::NW];
+  __shared__ int s_last[C::NW];
+
+  RowCtx c = make_ctx(a, block_row(a));
+  c.buf[0] = kv0;
+  c.buf[1] = kv1;
+  c.buf[2] = kv2;
+  c.vm = vmring;
+  c.ntiles = row_tiles<H, DQK, DV>(a, c, s_last);
+
+  f32x16 acc[MTQ];
+#pragma unroll
+  for (int mt = 0; mt < MTQ; ++mt) acc[mt] = (f32x16){};
+
+  if (c.ntiles > 0) {
+    using TI = TileIdx<H, DQK, DV>;
+    unsigned loff[C::NI];
+    unsigned wb[3], wd[3];
+    const uint16_t* dsb[3] = {ds0, ds1, ds2};
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) loff[i] = flat_lane_offset<H, DQK, DV>(c, i);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      wb[k] = (unsigned)(size_t)(lds_u16_ptr_t)(c.buf[k]) + c.wave_u * (RPW * C::ROWE * 2);
+      wd[k] = (unsigned)(size_t)(lds_cptr_t)(dsb[k]) + c.wave_u * (DSW * 2);
+    }
+    // dS DMA piece i: lane L copies 16 bytes (8 heads) of slot 16 i + L/4: heads
+    // 32 wave + 8 (L % 4) .. +7
+    unsigned dsoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dsoff[i] = (unsigned)(((16 * i + (c.lane >> 2)) * H + 32 * c.wave + 8 * (c.lane & 3)) * 2);
+    const int tiles_row = a.topkp / C::NK;
+    const uint16_t* dsrow = a.ws_ds + (size_t)c.row * a.topkp * H;
+    auto gather = [&](const TI& ti, int t, int k) {
+      static_assert(C::FLAT, "flat gather");
+      gather_tile_flat<H, DQK, DV>(a, c, ti, loff, wb[k]);
+      const uint16_t* src = dsrow + (size_t)min(t, tiles_row - 1) * C::NK * H;
+      const unsigned m0v = wd[k];
+      static_for<2>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const unsigned voff = dsoff[i];
+        const unsigned m0 = m0v;
+        const uint16_t* base = src;
+        asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3"
+                     :: "s"(m0), "n"(i * 1024), "v"(voff), "s"(base) : "memory", "m0", "scc");
+      });
+    };
+
+    // K^T fragment addressing (as the forward's value reads, over all DQK dims)
+    const int G = c.lane >> 4, i16 = c.lane & 15;
+    const int low = 2 * (G & 1) + ((i16 & 3) >> 1);
+    lds_cptr_t vb[3][2][2];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r = (G >> 1) * 8 + (i16 >> 2) + hf * 4;
+        const int sw = C::SWZ ? swz(r) : 0;
+        const lds_cptr_t b = (lds_cptr_t)c.buf[k] + r * C::ROWE + ((low ^ (sw & 3)) * 8) + (i16 & 1) * 4;
+        vb[k][hf][0] = b + (sw >> 2) * 32;
+        vb[k][hf][1] = b - (sw >> 2) * 32;
+      }
+    }
+
+    const int ntiles = (c.ntiles + 2) / 3 * 3;
+    const TI i0 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 0);
+    const TI i1 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 1);
+    TI i2 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 2);
+    gather(i0, 0, 0);
+    gather(i1, 1, 1);
+    wait_vm_barrier<GOPS2>();
+
+    auto step = [&](int t, int k, int ahead2, TI& nxt2) {
+      const TI i3 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, t + 3);
+      gather(nxt2, t + 2, ahead2);
+      // B = (scale dS)^T[slot, head]: lane (head hl, g) takes slots 16 kk + 8 g .. +7
+      const uint16_t* dsw = dsb[k] + c.wave * DSW;
+      bf16x8 bq[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) bq[kk] = tr_frag(dsw, 32, 16 * kk + 8 * (G >> 1), 16 * (G & 1), i16);
+      if (t >= c.ntiles) {   // padding tile: no contribution
+        bq[0] = (bf16x8){};
+        bq[1] = (bf16x8){};
+      }
+      auto kfrag = [&](int kk, int mt) {
+        const int off = kk * 16 * C::ROWE + mt * 32;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[k][0][mt & 1] + off));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[k][1][mt & 1] + off));
+        return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      };
+      bf16x8 kf[2][2];
+      kf[0][0] = kfrag(0, 0);
+      kf[0][1] = kfrag(1, 0);
+#pragma unroll
+      for (int mt = 0; mt < MTQ; ++mt) {
+        const int cur = mt & 1;
+        if (mt + 1 < MTQ) {
+          kf[cur ^ 1][0] = kfrag(0, mt + 1);
+          kf[cur ^ 1][1] = kfrag(1, mt + 1);
+        }
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][0], bq[0], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][1], bq[1], acc[mt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_vm_barrier<GOPS2>();
+      nxt2 = i3;
+    };
+    for (int t = 0; t < ntiles; t += 3) {
+      step(t, 0, 2, i2);
+      step(t + 1, 1, 0, i2);
+      step(t + 2, 2, 1, i2);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  // dQ^T C layout: lane (head hl, half g) holds dims mt*32 + q4*8 + g*4 + e
+  uint16_t* qp = a.dq + ((size_t)c.row * H + c.head) * DQK;
+#pragma unroll
+  for (int mt = 0; mt < MTQ; ++mt) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int col = mt * 32 + q4 * 8 + c.g * 4;
+      const uint32_t lo = (uint32_t)f32_to_bf16(acc[mt][q4 * 4 + 0]) |
+                          ((uint32_t)f32_to_bf16(acc[mt][q4 * 4 + 1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(acc[mt][q4 * 4 + 2]) |
+                          ((uint32_t)f32_to_bf16(acc[mt][q4 * 4 + 3]) << 16);
+      *reinterpret_cast<uint2*>(qp + col) = make_uint2(lo, hi);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// k_attn_bwd_dkv: dKV[idx] += (softmax_scale * dS)^T Q + P^T dY
+// ---------------------------------------------------------------------------------------
+
+template <int H, int DQK, int DV>
+__global__ __launch_bounds__(256) void k_attn_bwd_dkv(AttnBwdArgs a) {
+  constexpr int NW = 4;
+  constexpr int DW = DQK / NW;         // latent dims per wave (144)
+  constexpr int NT = DW / 16;          // 16-dim N tiles per wave
+  constexpr int KH = H / 32;           // 32-head K steps
+  constexpr int NK = 32;               // slots per tile
+  static_assert(DQK % (16 * NW) == 0 && H % 32 == 0, "tiling");
+  __shared__ __attribute__((aligned(16))) uint16_t stage[H * DQK];
+  __shared__ int s_last[NW];
+
+  const int row = block_row(a);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, G = lane >> 4;
+  const int32_t* idx_row = a.idx + (size_t)row * a.topk;
+  // tiles up to the last valid slot
+  int last = -1;
+  for (int sl = tid; sl < a.topk; sl += 256) {
+    const int id = idx_row[sl];
+    if (id >= 0 && id < a.n_k) last = sl;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if (lane == 0) s_last[wave] = last;
+  __syncthreads();
+  last = max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3]));
+  const int ntiles = (last + NK) / NK;
+  if (ntiles == 0) return;
+
+  const int d0 = wave * DW;
+  // B fragments: Q[heads 32 kk + 8 G .. +7, dim d0 + 16 nt + n] and the same of dY
+  bf16x8 qb[NT][KH], db[NT][KH];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.q + (size_t)row * H * DQK);
+    for (int i = tid; i < H * DQK / 8; i += 256) reinterpret_cast<uint4*>(stage)[i] = src[i];
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int kk = 0; kk < KH; ++kk)
+        qb[nt][kk] = tr_frag(stage, DQK, 32 * kk + 8 * G, d0 + 16 * nt, n);
+    __syncthreads();
+    const uint4* dsrc = reinterpret_cast<const uint4*>(a.dout + (size_t)row * H * DV);
+    for (int i = tid; i < H * DV / 8; i += 256) reinterpret_cast<uint4*>(stage)[i] = dsrc[i];
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int kk = 0; kk < KH; ++kk)
+        db[nt][kk] = (d0 + 16 * nt < DV) ? tr_frag(stage, DV, 32 * kk + 8 * G, d0 + 16 * nt, n)
+                                         : (bf16x8){};
+  }
+
+  const uint16_t* prow = a.ws_p + (size_t)row * a.topkp * H;
+  const uint16_t* drow = a.ws_ds + (size_t)row * a.topkp * H;
+  for (int t = 0; t < ntiles; ++t) {
+    f32x4 acc[2][NT];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f32x4){};
+    // slot indices of the A rows (lane n: slot 16 mt + n of the tile)
+    int myid[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int sl = t * NK + 16 * mt + n;
+      myid[mt] = sl < a.topk ? idx_row[sl] : -1;
+    }
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk) {
+      bf16x8 ad[2], ap[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const size_t o = (size_t)(t * NK + 16 * mt + n) * H + 32 * kk + 8 * G;
+        ad[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(drow + o));
+        ap[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(prow + o));
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          // (dims past DV have zero dY fragments: the product is issued anyway -- the wave
+          // owning them would otherwise finish early, which buys nothing)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad[mt], qb[nt][kk], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[mt], db[nt][kk], acc[mt][nt], 0, 0, 0);
+        }
+      }
+    }
+    // C layout: lane (dim n, group G) register r holds slot 16 mt + 4 G + r
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int id = __shfl(myid[mt], 4 * G + r, 64);
+        if ((unsigned)id < (unsigned)a.n_k) {
+          float* dst = a.dkv + (size_t)id * DQK + d0 + n;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) unsafeAtomicAdd(dst + 16 * nt, acc[mt][nt][r]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  if (!(h == 128 && d_qk == 576 && d_v == 512)) return hipErrorInvalidValue;
+  const bool al8 = a.topk >= 8 && a.topk % 8 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 31) == 0;
+  if (al8) {
+    k_attn_bwd_p<128, 576, 512, true><<<a.rows, 256, 0, s>>>(a);
+    k_attn_bwd_dq<128, 576, 512, true><<<a.rows, 256, 0, s>>>(a);
+  } else {
+    k_attn_bwd_p<128, 576, 512, false><<<a.rows, 256, 0, s>>>(a);
+    k_attn_bwd_dq<128, 576, 512, false><<<a.rows, 256, 0, s>>>(a);
+  }
+  k_attn_bwd_dkv<128, 576, 512><<<a.rows, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -77,6 +77,25 @@ struct AttnArgs {
   float scale_log2;       // softmax_scale * log2(e)
 };
 
+// Sparse-attention backward over one chunk of query rows (pointers offset to the chunk).
+struct AttnBwdArgs {
+  const uint16_t* q;      // [rows, H, DQK] bf16
+  const uint16_t* kv;     // [n_k, DQK] bf16
+  const int32_t* idx;     // [rows, topk]
+  const uint16_t* out;    // [rows, H, DV] bf16 forward output
+  const uint16_t* dout;   // [rows, H, DV] bf16
+  const float* smax;      // [rows, H] forward softmax_max
+  const float* ssum;      // [rows, H] forward softmax_sum
+  uint16_t* ws_p;         // [rows, topkp, H] bf16 probabilities
+  uint16_t* ws_ds;        // [rows, topkp, H] bf16 softmax_scale * dS
+  uint16_t* dq;           // [rows, H, DQK] bf16
+  float* dkv;             // [n_k, DQK] fp32, accumulated
+  int rows, n_k, topk;
+  int topkp;              // workspace slots per row: topk rounded up to 96
+  int xcd_remap;
+  float scale, scale_log2;
+};
+
 struct QuantArgs {
   const uint16_t* x;
   uint8_t* y;

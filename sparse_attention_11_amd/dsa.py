@@ -54,6 +54,10 @@ _SIGS = {
     "dsa_forward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, ctypes.c_size_t, _P]),
     "dsa_quantize_fp8_rows": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
+    "dsa_sparse_attn_bwd": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, ctypes.c_size_t, _P]),
+    "dsa_sparse_attn_bwd_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(Shape),
+                                                           ctypes.POINTER(ctypes.c_size_t)]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -222,6 +226,52 @@ def dsa_sparse_attn(q, kv, topk_idx, softmax_scale: float, d_v: int, out=None, s
                                           _ptr(out), _ptr(smax), _ptr(ssum),
                                           _stream(q.device, stream)))
     return out, smax, ssum
+
+
+def dsa_sparse_attn_bwd_workspace_bytes(n_q: int, n_k: int, topk: int, h: int = 128,
+                                        d_qk: int = 576, d_v: int = 512) -> int:
+    sh = _shape(n_q=n_q, n_k=n_k, h=h, d_qk=d_qk, d_v=d_v, topk=topk, softmax_scale=1.0)
+    n = ctypes.c_size_t(0)
+    _check(load_library().dsa_sparse_attn_bwd_workspace_bytes(ctypes.byref(sh), ctypes.byref(n)))
+    return int(n.value)
+
+
+def dsa_sparse_attn_bwd(q, kv, topk_idx, out, dout, softmax_max, softmax_sum,
+                        softmax_scale: float, dq=None, dkv=None, workspace=None, stream=None):
+    """Gradients of the sparse attention.  Returns (dq bf16 [n_q,h,d_qk], dkv fp32 [n_k,d_qk]);
+    a given ``dkv`` is accumulated into, a new one starts at zero."""
+    _dev(q, "q", (torch.bfloat16,), 3)
+    _dev(kv, "kv", (torch.bfloat16,), 2)
+    _dev(topk_idx, "topk_idx", (torch.int32,), 2)
+    _dev(out, "out", (torch.bfloat16,), 3)
+    _dev(dout, "dout", (torch.bfloat16,), 3)
+    _dev(softmax_max, "softmax_max", (torch.float32,), 2)
+    _dev(softmax_sum, "softmax_sum", (torch.float32,), 2)
+    n_q, h, d_qk = q.shape
+    n_k = kv.shape[0]
+    d_v = out.shape[2]
+    topk = topk_idx.shape[1]
+    if (kv.shape[1] != d_qk or topk_idx.shape[0] != n_q or out.shape[:2] != (n_q, h)
+            or dout.shape != out.shape or softmax_max.shape != (n_q, h)
+            or softmax_sum.shape != (n_q, h)):
+        raise ValueError("backward tensor shapes do not match q [n_q,h,d_qk] / kv [n_k,d_qk]")
+    dev = q.device
+    if dq is None:
+        dq = torch.empty(n_q, h, d_qk, dtype=torch.bfloat16, device=dev)
+    if dkv is None:
+        dkv = torch.zeros(n_k, d_qk, dtype=torch.float32, device=dev)
+    _dev(dq, "dq", (torch.bfloat16,), 3)
+    _dev(dkv, "dkv", (torch.float32,), 2)
+    sh = _shape(n_q=n_q, n_k=n_k, h=h, d_qk=d_qk, d_v=d_v, topk=topk,
+                softmax_scale=softmax_scale)
+    if workspace is None:
+        nb = dsa_sparse_attn_bwd_workspace_bytes(n_q, n_k, topk, h, d_qk, d_v)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    _check(load_library().dsa_sparse_attn_bwd(
+        ctypes.byref(sh), _ptr(q), _ptr(kv), _ptr(topk_idx), _ptr(out), _ptr(dout),
+        _ptr(softmax_max), _ptr(softmax_sum), _ptr(dq), _ptr(dkv), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev, stream)))
+    return dq, dkv
 
 
 def dsa_forward(q_idx, k_idx, w_idx, q, kv, segments, topk: int, softmax_scale: float,

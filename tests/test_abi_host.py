@@ -129,6 +129,33 @@ def test_forward_workspace_checks(lib):
     assert _fwd(lib, _ws(4, 4, 2, [(0, 0, 0, 4, 0)])[1], segs=((0, 0, 0, 4, 0),)) == dsa.DSA_OK
 
 
+def _bwd(lib, sh, ws_bytes, workspace=FAKE, null_dkv=False):
+    return lib.dsa_sparse_attn_bwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, None if null_dkv else FAKE, workspace,
+                                   ctypes.c_size_t(ws_bytes), None)
+
+
+def test_backward_argument_checks(lib):
+    # workspace formula: two bf16 [rows, topk rounded up to 96, h] arrays, up to 4096 rows
+    sh = dsa._shape(n_q=5000, n_k=8192, h=128, d_qk=576, d_v=512, topk=2048, softmax_scale=0.1)
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_sparse_attn_bwd_workspace_bytes(ctypes.byref(sh), ctypes.byref(n)) == dsa.DSA_OK
+    assert n.value == 4096 * 2 * 2112 * 128 * 2
+    assert dsa.dsa_sparse_attn_bwd_workspace_bytes(10, 100, 100) == 10 * 2 * 192 * 128 * 2
+    per_row = 2 * 2112 * 128 * 2
+    assert _bwd(lib, sh, per_row - 1) == dsa.DSA_ERR_WORKSPACE
+    assert _bwd(lib, sh, per_row, workspace=None) == dsa.DSA_ERR_WORKSPACE
+    assert _bwd(lib, sh, per_row, workspace=ctypes.c_void_p(0x1008)) == dsa.DSA_ERR_INVALID_ARG
+    assert _bwd(lib, sh, per_row, null_dkv=True) == dsa.DSA_ERR_INVALID_ARG
+    # only the DeepSeek-V3.2 attention dims are built for the backward
+    small = dsa._shape(n_q=4, n_k=4, h=8, d_qk=80, d_v=64, topk=4, softmax_scale=0.1)
+    assert _bwd(lib, small, 1 << 20) == dsa.DSA_ERR_UNSUPPORTED
+    assert "backward" in dsa.dsa_last_error()
+    # nothing to do for zero rows
+    empty = dsa._shape(n_q=0, n_k=4, h=128, d_qk=576, d_v=512, topk=4, softmax_scale=0.1)
+    assert _bwd(lib, empty, 0) == dsa.DSA_OK
+
+
 def test_quantize_argument_checks(lib):
     assert lib.dsa_quantize_fp8_rows(FAKE, -1, 8, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
     assert lib.dsa_quantize_fp8_rows(FAKE, 0, 8, FAKE, FAKE, None) == dsa.DSA_OK

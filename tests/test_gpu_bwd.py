@@ -1,0 +1,173 @@
+"""GPU parity of the sparse-attention backward (through the C ABI) against the float64 oracle.
+
+The forward that feeds the backward runs on the GPU (its indices, output and softmax
+statistics are the backward's inputs, as in training); the oracle recomputes everything from
+the same seeded q / kv / dout on those indices.  Acceptance: dq and dkv within 2e-2 of the
+oracle after normalising by the largest reference magnitude of each tensor.  At the full
+packed-varlen size dq is checked on sampled rows, dkv on keys whose every contribution comes
+from sampled rows (the tail keys of each document), and dkv's value part through an identity
+that holds at any size (summed over keys it equals dout summed over rows and heads).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_11_amd import dsa, inputs as I
+
+pytestmark = pytest.mark.gpu
+
+BWD_NORM_TOL = 2e-2
+f64 = I.to_f64
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a GPU")
+
+
+def _varlen_case(docs, topk, seed, pos0=None, n_k=None):
+    """Workload-5 recipe at a reduced size: packed documents with per-document causal
+    windows (or one segment at offset pos0 against n_k keys)."""
+    if pos0 is None:
+        cu = np.concatenate([[0], np.cumsum(docs)]).astype(int)
+        segs = tuple((int(cu[i]), int(docs[i]), int(cu[i]), int(docs[i]), 0)
+                     for i in range(len(docs)))
+        n_q = n_k = int(cu[-1])
+    else:
+        n_q = int(docs[0])
+        segs = ((0, n_q, 0, n_k, pos0),)
+    wl = I.workload(5).with_(n_q=n_q, n_k=n_k, topk=topk, segments=segs, seed=seed)
+    x = I.generate(wl)
+    return wl, x, {k: v.cuda() for k, v in x.items()}
+
+
+def _forward(wl, g):
+    out, idx, smax, ssum = dsa.dsa_forward(g["q_idx"], g["k_idx"], g["w_idx"], g["q"], g["kv"],
+                                           wl.segments, wl.topk, wl.softmax_scale, wl.d_v)
+    return out, idx, smax, ssum
+
+
+def _norm_err(got, ref):
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def _check_full(wl, x, idx, dq, dkv):
+    ref_idx = idx.cpu().numpy().astype(np.int64)
+    ref_idx[ref_idx >= wl.n_k] = -1
+    rdq, rdkv = O.sparse_attn_bwd(f64(x["q"]), f64(x["kv"]), ref_idx, f64(x["dout"]),
+                                  wl.softmax_scale, wl.d_v)
+    e_q = _norm_err(dq.float().cpu().numpy(), rdq)
+    e_kv = _norm_err(dkv.cpu().numpy().astype(np.float64), rdkv)
+    print(f"  dq err {e_q:.3e}  dkv err {e_kv:.3e} (normalised)", flush=True)
+    assert e_q <= BWD_NORM_TOL and e_kv <= BWD_NORM_TOL
+    return e_q, e_kv
+
+
+def test_bwd_varlen_small():
+    """Three packed documents, windows longer and shorter than topk, every row and key."""
+    _need_gpu()
+    wl, x, g = _varlen_case([100, 150, 262], 64, seed=2101)
+    print(f"bwd varlen small n_q={wl.n_q} topk={wl.topk}", flush=True)
+    out, idx, smax, ssum = _forward(wl, g)
+    dq, dkv = dsa.dsa_sparse_attn_bwd(g["q"], g["kv"], idx, out, g["dout"], smax, ssum,
+                                      wl.softmax_scale)
+    torch.cuda.synchronize()
+    _check_full(wl, x, idx, dq, dkv)
+
+
+def test_bwd_long_windows_topk2048():
+    """Rows at positions 2500.. of one sequence: 2048 selected keys (64 tiles) per row."""
+    _need_gpu()
+    wl, x, g = _varlen_case([40], 2048, seed=2102, pos0=2500, n_k=2540)
+    print(f"bwd long rows n_q={wl.n_q} n_k={wl.n_k} topk={wl.topk}", flush=True)
+    out, idx, smax, ssum = _forward(wl, g)
+    dq, dkv = dsa.dsa_sparse_attn_bwd(g["q"], g["kv"], idx, out, g["dout"], smax, ssum,
+                                      wl.softmax_scale)
+    torch.cuda.synchronize()
+    _check_full(wl, x, idx, dq, dkv)
+
+
+def test_bwd_edge_cases_and_chunking():
+    """topk not a multiple of 8, -1 holes anywhere, an empty row, an out-of-range index, a
+    repeated key; a workspace of 3 rows (many passes) gives the same dq bit for bit."""
+    _need_gpu()
+    wl, x, g = _varlen_case([90, 110], 100, seed=2103)
+    print(f"bwd edge cases n_q={wl.n_q} topk={wl.topk}", flush=True)
+    gen = torch.Generator().manual_seed(7)
+    idx = torch.randint(0, wl.n_k, (wl.n_q, wl.topk), generator=gen, dtype=torch.int32)
+    idx[torch.rand(wl.n_q, wl.topk, generator=gen) < 0.3] = -1
+    idx[5] = -1                      # empty row
+    idx[6, :70] = -1                 # leading holes
+    idx[7, 3] = wl.n_k + 9           # out of range: skipped
+    idx[9] = 4                       # one key repeated
+    idx = idx.cuda()
+    out, smax, ssum = dsa.dsa_sparse_attn(g["q"], g["kv"], idx, wl.softmax_scale, wl.d_v)
+    dq, dkv = dsa.dsa_sparse_attn_bwd(g["q"], g["kv"], idx, out, g["dout"], smax, ssum,
+                                      wl.softmax_scale)
+    per_row = dsa.dsa_sparse_attn_bwd_workspace_bytes(1, wl.n_k, wl.topk)
+    ws = torch.empty(3 * per_row + 5, dtype=torch.uint8, device="cuda")
+    dq3, dkv3 = dsa.dsa_sparse_attn_bwd(g["q"], g["kv"], idx, out, g["dout"], smax, ssum,
+                                        wl.softmax_scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq3)
+    assert torch.allclose(dkv, dkv3, rtol=1e-5, atol=1e-5 * float(dkv.abs().max()))
+    assert torch.all(dq[5] == 0)
+    _check_full(wl, x, idx, dq, dkv)
+
+
+def test_bwd_deterministic_dq():
+    _need_gpu()
+    wl, x, g = _varlen_case([64, 64], 32, seed=2104)
+    out, idx, smax, ssum = _forward(wl, g)
+    r1 = dsa.dsa_sparse_attn_bwd(g["q"], g["kv"], idx, out, g["dout"], smax, ssum, wl.softmax_scale)
+    r2 = dsa.dsa_sparse_attn_bwd(g["q"], g["kv"], idx, out, g["dout"], smax, ssum, wl.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(r1[0], r2[0])
+
+
+def test_bwd_full_varlen_workload():
+    """The packed 32768-token, 8-document workload at full size, launched as the bench does.
+    dq: sampled rows against the oracle.  dkv: the last 4 keys of every document lie only in
+    the windows of that document's last 4 rows, so the oracle over those rows gives their
+    complete gradient; plus the value-part identity sum_k dkv[k, :d_v] = sum_{i,h} dout[i,h]
+    (each row's probabilities sum to one) over all keys."""
+    _need_gpu()
+    wl = I.workload(5)
+    print(f"bwd full {wl.name}: generating on the device", flush=True)
+    g = I.generate(wl, device="cuda", gen_device="cuda")
+    out, idx, smax, ssum = _forward(wl, g)
+    dq, dkv = dsa.dsa_sparse_attn_bwd(g["q"], g["kv"], idx, out, g["dout"], smax, ssum,
+                                      wl.softmax_scale)
+    torch.cuda.synchronize()
+    print("  backward done; checking", flush=True)
+    assert torch.isfinite(dq.float()).all() and torch.isfinite(dkv).all()
+    rng = np.random.default_rng(5)
+    rows = set(rng.choice(wl.n_q, 8, replace=False).tolist())
+    keys = []
+    for (qs, ql, _, _, _) in wl.segments:
+        rows.update(range(qs + ql - 4, qs + ql))
+        rows.add(qs)
+        keys.extend(range(qs + ql - 4, qs + ql))
+    rows = np.array(sorted(rows))
+    keys = np.array(keys)
+    kv = f64(g["kv"])
+    ref_dq = []
+    ref_dkv = np.zeros((wl.n_k, wl.d_qk))
+    for r in rows:
+        d, sel, rws = O.attention_bwd_row(f64(g["q"][r]), kv, idx[r].cpu().numpy().astype(np.int64),
+                                          f64(g["dout"][r]), wl.softmax_scale, wl.d_v)
+        ref_dq.append(d)
+        np.add.at(ref_dkv, sel, rws)
+    e_q = _norm_err(dq[torch.as_tensor(rows, device="cuda")].float().cpu().numpy(), np.stack(ref_dq))
+    e_kv = _norm_err(dkv[torch.as_tensor(keys, device="cuda")].cpu().numpy().astype(np.float64),
+                     ref_dkv[keys])
+    print(f"  sampled dq err {e_q:.3e}, tail-key dkv err {e_kv:.3e}", flush=True)
+    assert e_q <= BWD_NORM_TOL and e_kv <= BWD_NORM_TOL
+    col = dkv[:, :wl.d_v].double().sum(0)
+    want = g["dout"].double().sum((0, 1))
+    err = float((col - want).abs().max())
+    print(f"  value-part column sums off by {err:.3e} (scale {float(want.abs().max()):.3e})",
+          flush=True)
+    assert err <= 1e-3 * float(want.abs().max())
