@@ -89,6 +89,34 @@ def cpu_baseline(wl, budget_s=15.0, max_rows=2048):
                       f"window, top-k, attention), float64 NumPy, {dt:.1f} s"}
 
 
+def backward_stage(args, n=5):
+    """Sparse-attention backward on the packed varlen workload (8 documents, 32768 tokens):
+    the GPU forward supplies indices, output and softmax statistics; the backward (P / dS,
+    dQ, dKV kernels) is timed on its own with HIP events."""
+    wl = I.workload(n)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    g = I.generate(wl, device=dev, gen_device="cuda")
+    out, idx, smax, ssum = dsa.dsa_forward(g["q_idx"], g["k_idx"], g["w_idx"], g["q"], g["kv"],
+                                           wl.segments, wl.topk, wl.softmax_scale, wl.d_v)
+    dq = torch.empty_like(g["q"])
+    dkv = torch.zeros(wl.n_k, wl.d_qk, dtype=torch.float32, device=dev)
+    nb = dsa.dsa_sparse_attn_bwd_workspace_bytes(wl.n_q, wl.n_k, wl.topk)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+    def bwd():
+        dsa.dsa_sparse_attn_bwd(g["q"], g["kv"], idx, out, g["dout"], smax, ssum,
+                                wl.softmax_scale, dq=dq, dkv=dkv, workspace=ws)
+    reps = max(3, min(args.steps, 10))
+    ms = time_launches(bwd, reps, stream)
+    n_sel = int((idx >= 0).sum())
+    flop = 2.0 * wl.h * (3 * wl.d_qk + 2 * wl.d_v) * n_sel
+    print(f"bench: backward {wl.name} {ms:.3f} ms", file=sys.stderr, flush=True)
+    return {"workload": wl.name, "ms": ms, "selected_keys": n_sel, "flop": flop,
+            "tflops": flop / (ms * 1e-3) / 1e12,
+            "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def traffic_entry():
     """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was
     taken on the current attention kernel source."""
@@ -111,6 +139,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the packed-varlen forward + backward timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -213,6 +243,8 @@ def main():
                             "achieved": attn_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": attn_tf / PEAK_BF16_TFLOPS, "traffic": traffic,
                             "per_launch_flop": W["f_attn"]}
+    if not args.no_backward:
+        line["backward"] = backward_stage(args)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl)

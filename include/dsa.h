@@ -170,11 +170,15 @@ dsa_status dsa_forward(const dsa_shape *shape, const void *q_idx, const float *q
  *   dkv[k,:d_v] += sum_h P * dout[i,h,:]
  * q [n_q, h, d_qk], kv [n_k, d_qk], out / dout [n_q, h, d_v] bf16 (out and the statistics as
  * written by the forward); topk_idx [n_q, topk] as for dsa_sparse_attn (empty slots skipped);
- * dq [n_q, h, d_qk] bf16 (written); dkv [n_k, d_qk] fp32 is ADDED to with atomics, so the
- * caller zeroes it (or accumulates into it) and the order of the additions is not fixed.
+ * dq [n_q, h, d_qk] bf16 (written); dkv [n_k, d_qk] fp32 (16-byte aligned) is ADDED to, so
+ * the caller zeroes it (or accumulates into it); the order in which a key's contributions
+ * are summed is not fixed.
  * Built for (h, d_qk, d_v) = (128, 576, 512) only (else DSA_ERR_UNSUPPORTED).  The workspace
- * (16-byte aligned) holds bf16 P and dS for a chunk of rows; rows are processed in chunks of
- * as many rows as it fits (DSA_ERR_WORKSPACE if not even one).
+ * (16-byte aligned) holds per-key counters and, for a chunk of rows, bf16 P and dS, the bf16
+ * dKV contribution of every selected slot and the per-key entry lists; rows are processed in
+ * chunks of as many rows as it fits (DSA_ERR_WORKSPACE if not even one).  dkv is updated
+ * with plain read-modify-writes (each key's sum is formed by one wave), so calls that
+ * update the same dkv must not overlap.
  */
 dsa_status dsa_sparse_attn_bwd(const dsa_shape *shape, const void *q, const void *kv,
                                const int32_t *topk_idx, const void *out, const void *dout,
@@ -182,8 +186,10 @@ dsa_status dsa_sparse_attn_bwd(const dsa_shape *shape, const void *q, const void
                                float *dkv, void *workspace, size_t workspace_bytes,
                                void *stream);
 
-/* Workspace size for dsa_sparse_attn_bwd that processes up to 4096 rows per pass:
- * 4 * topk_p * h bytes per row, topk_p = topk rounded up to a multiple of 96. */
+/* Workspace size for dsa_sparse_attn_bwd that processes up to 2048 rows per pass:
+ * (4 * topk_p * h + 2 * topk_p * d_qk + 4 * topk) bytes per row, topk_p = topk rounded up to a
+ * multiple of 96, plus 4 * (3 * n_k + 1) bytes rounded up to 256 and 2 KiB of alignment
+ * slack. */
 dsa_status dsa_sparse_attn_bwd_workspace_bytes(const dsa_shape *shape, size_t *bytes);
 
 /*

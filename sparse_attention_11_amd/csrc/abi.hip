@@ -247,12 +247,18 @@ dsa_status check_idx_ptrs(const dsa_shape* s, const void* q_idx, const float* q_
   return DSA_OK;
 }
 
-// Backward workspace: bf16 P and softmax_scale * dS for every (row, slot, head), with the
-// slots of a row padded to a multiple of 96 (three 32-slot tiles: the gather ring processes
-// tiles in threes).
+// Backward workspace.  Per call: per-key counters, offsets and cursors (3 n_k + 1 ints).  Per
+// row of a chunk: bf16 P and softmax_scale * dS for every (slot, head) and the bf16 dKV
+// contribution of every slot, with the slots padded to a multiple of 96 (the tile rings
+// process tiles in threes), and one list entry per slot.
 size_t bwd_topkp(const dsa_shape* s) { return ((size_t)s->topk + 95) / 96 * 96; }
-size_t bwd_row_bytes(const dsa_shape* s) { return 2 * bwd_topkp(s) * (size_t)s->h * 2; }
-constexpr int kBwdChunkRows = 4096;
+size_t bwd_row_bytes(const dsa_shape* s) {
+  return 2 * bwd_topkp(s) * (size_t)s->h * 2 + bwd_topkp(s) * s->d_qk * 2 + (size_t)s->topk * 4;
+}
+size_t bwd_fixed_bytes(const dsa_shape* s) {
+  return align_up(((size_t)3 * s->n_k + 1) * 4) + 8 * kAlign;   // + slack for region alignment
+}
+constexpr int kBwdChunkRows = 2048;
 
 dsa_status check_bwd_dims(const dsa_shape* s) {
   if (!(s->h == 128 && s->d_qk == 576 && s->d_v == 512))
@@ -375,7 +381,7 @@ dsa_status dsa_sparse_attn_bwd_workspace_bytes(const dsa_shape* shape, size_t* b
   dsa_status st = check_shape(shape, kNeedAttn, p);
   if (st != DSA_OK) return st;
   if ((st = check_bwd_dims(shape)) != DSA_OK) return st;
-  *bytes = bwd_row_bytes(shape) * (size_t)std::min(shape->n_q, kBwdChunkRows);
+  *bytes = bwd_fixed_bytes(shape) + bwd_row_bytes(shape) * (size_t)std::min(shape->n_q, kBwdChunkRows);
   return ok();
 }
 
@@ -391,17 +397,36 @@ dsa_status dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void
   if (shape->n_q == 0) return ok();
   if (!q || !kv || !topk_idx || !out || !dout || !softmax_max || !softmax_sum || !dq || !dkv)
     return fail(DSA_ERR_INVALID_ARG, "attention backward tensor is NULL");
-  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-    return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(dkv) % 16 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "workspace and dkv must be 16-byte aligned");
   const size_t per_row = bwd_row_bytes(shape);
-  const size_t fit = workspace ? workspace_bytes / per_row : 0;
+  const size_t fixed = bwd_fixed_bytes(shape);
+  const size_t fit = workspace && workspace_bytes > fixed ? (workspace_bytes - fixed) / per_row : 0;
   if (fit == 0)
     return fail(DSA_ERR_WORKSPACE, "workspace of at least %zu bytes (one row) needed, %zu given",
-                per_row, workspace ? workspace_bytes : (size_t)0);
-  const int chunk = (int)std::min<size_t>(fit, (size_t)shape->n_q);
+                fixed + per_row, workspace ? workspace_bytes : (size_t)0);
+  // list entries are row * topk + slot within a chunk: keep them below 2^31
+  const size_t max_rows = (size_t)INT32_MAX / (size_t)shape->topk;
+  const int chunk = (int)std::min({fit, (size_t)shape->n_q, max_rows});
   const int h = shape->h, dqk = shape->d_qk, dv = shape->d_v, topk = shape->topk;
   const size_t topkp = bwd_topkp(shape);
+  char* w = static_cast<char*>(workspace);
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    char* p = w + at;
+    at = align_up(at + bytes);
+    return p;
+  };
   dsa::AttnBwdArgs a = {};
+  a.cnt = reinterpret_cast<int*>(take((size_t)shape->n_k * 4));
+  a.off = reinterpret_cast<int*>(take(((size_t)shape->n_k + 1) * 4));
+  a.cur = reinterpret_cast<int*>(take((size_t)shape->n_k * 4));
+  a.ws_p = reinterpret_cast<uint16_t*>(take((size_t)chunk * topkp * h * 2));
+  a.ws_ds = reinterpret_cast<uint16_t*>(take((size_t)chunk * topkp * h * 2));
+  a.ws_c = reinterpret_cast<uint16_t*>(take((size_t)chunk * topkp * dqk * 2));
+  a.list = reinterpret_cast<int*>(take((size_t)chunk * topk * 4));
+  if (at > workspace_bytes)
+    return fail(DSA_ERR_WORKSPACE, "internal workspace layout exceeds %zu bytes", workspace_bytes);
   a.kv = static_cast<const uint16_t*>(kv);
   a.dkv = dkv;
   a.n_k = shape->n_k;
@@ -409,8 +434,6 @@ dsa_status dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void
   a.topkp = (int)topkp;
   a.scale = shape->softmax_scale;
   a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
-  a.ws_p = static_cast<uint16_t*>(workspace);
-  a.ws_ds = a.ws_p + (size_t)chunk * topkp * h;
   for (int r0 = 0; r0 < shape->n_q; r0 += chunk) {
     const int rows = std::min(chunk, shape->n_q - r0);
     a.rows = rows;

@@ -16,11 +16,18 @@
 //   * k_attn_bwd_dq: gathers the key tiles again together with the wave's dS tile (both by
 //     LDS DMA) and accumulates dQ^T[dim, head] += K^T dS^T over the 18 dim tiles of the row
 //     (K^T read with the transposing LDS read), one wave per 32 heads.
-//   * k_attn_bwd_dkv: no gather.  Each wave owns 144 of the 576 latent dims and holds
-//     Q[:, dims] and dY[:, dims] for all 128 heads as B fragments (staged through LDS once
-//     per row); per tile it forms dKV[slot, dim] = dS^T Q + P^T dY on 16x16x32 MFMA with
-//     A fragments loaded straight from the workspace, then adds the tile into the fp32 dKV
-//     rows with global atomics (64-byte runs of consecutive dims per slot).
+//   * k_attn_bwd_dkv_part: no gather.  Each wave owns 144 of the 576 latent dims and holds
+//     Q[:, dims] and dY[:, dims] for all 128 heads as MFMA fragments (staged through LDS once
+//     per row); per tile it forms C[slot, dims] = dS^T Q + P^T dY on 16x16x32 MFMA with the
+//     P / dS tile streamed through an LDS ring by LDS DMA, and writes every slot's 576-wide
+//     contribution as bf16 with plain stores.
+//   * The contributions are then summed per key: the chunk's (row, slot) entries are counted
+//     per key, prefix-summed and scattered into per-key lists (integer atomics on counters
+//     only), and k_bwd_reduce gives each key one wave that sums its list in fp32 and adds the
+//     result to dKV.  Float atomics on dKV would cost one atomic per element (576 per
+//     selected key), and the L2 retires those about five times slower than plain stores.
+#include <algorithm>
+
 #include "attn_common.h"
 
 namespace dsa {
@@ -422,14 +429,20 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_dq(AttnBwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// k_attn_bwd_dkv: dKV[idx] += (softmax_scale * dS)^T Q + P^T dY
+// dKV: per-(row, slot) contributions, then a per-key reduction (no float atomics)
 // ---------------------------------------------------------------------------------------
 
+// k_attn_bwd_dkv_part: C[row, slot, :] = (scale dS)^T Q + P^T dY for every slot of the
+// row's tiles (empty slots have P = dS = 0), bf16, [row][slot padded to topkp][DQK].
+// Each wave owns DQK / 4 latent dims and holds Q[:, dims] and dY[:, dims] for all heads as
+// A fragments (staged through LDS once per row).  Per tile C^T[dim, slot] comes out of
+// 16x16x32 MFMA with lane (slot n, group G) holding dims 4G .. 4G+3 of each 16-dim tile,
+// stored as one 8-byte write.
 template <int H, int DQK, int DV>
-__global__ __launch_bounds__(256) void k_attn_bwd_dkv(AttnBwdArgs a) {
+__global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
   constexpr int NW = 4;
   constexpr int DW = DQK / NW;         // latent dims per wave (144)
-  constexpr int NT = DW / 16;          // 16-dim N tiles per wave
+  constexpr int NT = DW / 16;          // 16-dim tiles per wave
   constexpr int KH = H / 32;           // 32-head K steps
   constexpr int NK = 32;               // slots per tile
   static_assert(DQK % (16 * NW) == 0 && H % 32 == 0, "tiling");
@@ -440,7 +453,6 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv(AttnBwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
   const int32_t* idx_row = a.idx + (size_t)row * a.topk;
-  // tiles up to the last valid slot
   int last = -1;
   for (int sl = tid; sl < a.topk; sl += 256) {
     const int id = idx_row[sl];
@@ -455,8 +467,8 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv(AttnBwdArgs a) {
   if (ntiles == 0) return;
 
   const int d0 = wave * DW;
-  // B fragments: Q[heads 32 kk + 8 G .. +7, dim d0 + 16 nt + n] and the same of dY
-  bf16x8 qb[NT][KH], db[NT][KH];
+  // fragments of Q^T[dim d0 + 16 nt + n, heads 32 kk + 8 G .. +7] and the same of dY
+  bf16x8 qa[NT][KH], da[NT][KH];
   {
     const uint4* src = reinterpret_cast<const uint4*>(a.q + (size_t)row * H * DQK);
     for (int i = tid; i < H * DQK / 8; i += 256) reinterpret_cast<uint4*>(stage)[i] = src[i];
@@ -465,7 +477,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv(AttnBwdArgs a) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int kk = 0; kk < KH; ++kk)
-        qb[nt][kk] = tr_frag(stage, DQK, 32 * kk + 8 * G, d0 + 16 * nt, n);
+        qa[nt][kk] = tr_frag(stage, DQK, 32 * kk + 8 * G, d0 + 16 * nt, n);
     __syncthreads();
     const uint4* dsrc = reinterpret_cast<const uint4*>(a.dout + (size_t)row * H * DV);
     for (int i = tid; i < H * DV / 8; i += 256) reinterpret_cast<uint4*>(stage)[i] = dsrc[i];
@@ -474,58 +486,203 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv(AttnBwdArgs a) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int kk = 0; kk < KH; ++kk)
-        db[nt][kk] = (d0 + 16 * nt < DV) ? tr_frag(stage, DV, 32 * kk + 8 * G, d0 + 16 * nt, n)
+        da[nt][kk] = (d0 + 16 * nt < DV) ? tr_frag(stage, DV, 32 * kk + 8 * G, d0 + 16 * nt, n)
                                          : (bf16x8){};
   }
 
-  const uint16_t* prow = a.ws_p + (size_t)row * a.topkp * H;
-  const uint16_t* drow = a.ws_ds + (size_t)row * a.topkp * H;
-  for (int t = 0; t < ntiles; ++t) {
-    f32x4 acc[2][NT];
+  __syncthreads();   // the staging area becomes the tile ring
+
+  // Ring of three tiles in the staging area: tile = [P | dS] x [32 slots][16 chunks of 8
+  // heads], chunk c of slot s stored at physical chunk c ^ (s & 15) (conflict-free reads of
+  // 16 slots x one chunk).  Each wave copies a quarter of a tile (4 x 1 KB LDS DMA pieces:
+  // tensor wave / 2, slots 16 (wave % 2) .. +15), so every tile needs the barrier.
+  constexpr int TILE_E = 2 * NK * H;   // bf16 elements per ring tile
+  static_assert(3 * TILE_E <= H * DQK && H == 128, "ring fits the staging area");
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // uniform: DMA bases are scalars
+  const uint16_t* tsrc0 = (wave_u >> 1) ? a.ws_ds : a.ws_p;
+  const uint16_t* tsrc = tsrc0 + (size_t)row * a.topkp * H;
+  unsigned doff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = 16 * (wave & 1) + 4 * i + (lane >> 4);
+    const int c = (lane & 15) ^ (slot & 15);
+    doff[i] = (unsigned)(slot * H * 2 + c * 16);
+  }
+  const unsigned ring_lds = (unsigned)(size_t)(lds_u16_ptr_t)stage;
+  const unsigned wdst = (unsigned)((wave_u >> 1) * NK * H * 2 + (wave_u & 1) * 16 * H * 2);
+  auto dma_tile = [&](int t, int k) {
+    const uint16_t* src = tsrc + (size_t)min(t, ntiles - 1) * NK * H;
+    const unsigned m0v = ring_lds + (unsigned)(k * TILE_E * 2) + wdst;
+    static_for<4>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const unsigned voff = doff[i];
+      const unsigned m0 = m0v;
+      const uint16_t* base = src;
+      asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3"
+                   :: "s"(m0), "n"(i * 1024), "v"(voff), "s"(base) : "memory", "m0", "scc");
+    });
+  };
+
+  f32x4 acc[2][NT];
+  uint16_t* crow = a.ws_c + (size_t)row * a.topkp * DQK + d0 + 4 * G;
+  int pend_t = -1;
+  // store the previous tile's contributions (at the start of the next step, ahead of that
+  // step's DMA, so the vmcnt wait before each barrier only spares the DMA)
+  auto flush = [&]() {
+    if (pend_t >= 0 && pend_t < ntiles) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        uint16_t* dst = crow + (size_t)(pend_t * NK + 16 * mt + n) * DQK;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint32_t lo = (uint32_t)f32_to_bf16(acc[mt][nt][0]) |
+                              ((uint32_t)f32_to_bf16(acc[mt][nt][1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16(acc[mt][nt][2]) |
+                              ((uint32_t)f32_to_bf16(acc[mt][nt][3]) << 16);
+          *reinterpret_cast<uint2*>(dst + 16 * nt) = make_uint2(lo, hi);
+        }
+      }
+    }
+  };
+  auto step = [&](int t, int k) {
+    flush();
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f32x4){};
-    // slot indices of the A rows (lane n: slot 16 mt + n of the tile)
-    int myid[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int sl = t * NK + 16 * mt + n;
-      myid[mt] = sl < a.topk ? idx_row[sl] : -1;
-    }
+    dma_tile(t + 2, (k + 2) % 3);
+    const lds_cptr_t tb = (lds_cptr_t)stage + k * TILE_E;
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk) {
-      bf16x8 ad[2], ap[2];
+      // B fragments: slot 16 mt + n, heads 32 kk + 8 G .. +7 (logical chunk 4 kk + G)
+      bf16x8 bp[2], bd[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const size_t o = (size_t)(t * NK + 16 * mt + n) * H + 32 * kk + 8 * G;
-        ad[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(drow + o));
-        ap[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(prow + o));
+        const int e = (16 * mt + n) * H + (((4 * kk + G) ^ n) * 8);
+        bp[mt] = *(__attribute__((address_space(3))) const bf16x8*)(tb + e);
+        bd[mt] = *(__attribute__((address_space(3))) const bf16x8*)(tb + NK * H + e);
       }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           // (dims past DV have zero dY fragments: the product is issued anyway -- the wave
-          // owning them would otherwise finish early, which buys nothing)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad[mt], qb[nt][kk], acc[mt][nt], 0, 0, 0);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[mt], db[nt][kk], acc[mt][nt], 0, 0, 0);
+          // owning them would otherwise only finish early, which buys nothing)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[nt][kk], bd[mt], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[nt][kk], bp[mt], acc[mt][nt], 0, 0, 0);
         }
       }
     }
-    // C layout: lane (dim n, group G) register r holds slot 16 mt + 4 G + r
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int id = __shfl(myid[mt], 4 * G + r, 64);
-        if ((unsigned)id < (unsigned)a.n_k) {
-          float* dst = a.dkv + (size_t)id * DQK + d0 + n;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) unsafeAtomicAdd(dst + 16 * nt, acc[mt][nt][r]);
-        }
-      }
+    pend_t = t;
+    wait_vm_barrier<4>();   // tile t+1 landed for every wave
+  };
+  dma_tile(0, 0);
+  dma_tile(1, 1);
+  wait_vm_barrier<4>();
+  const int npad = (ntiles + 2) / 3 * 3;
+  for (int t = 0; t < npad; t += 3) {
+    step(t, 0);
+    step(t + 1, 1);
+    step(t + 2, 2);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA may outlive the block
+  flush();
+}
+
+// Zero the per-key counters.
+__global__ __launch_bounds__(256) void k_bwd_zero(AttnBwdArgs a) {
+  for (int k = blockIdx.x * 256 + threadIdx.x; k < a.n_k; k += gridDim.x * 256) a.cnt[k] = 0;
+}
+
+// Count the valid (row, slot) entries of the chunk per key.
+__global__ __launch_bounds__(256) void k_bwd_count(AttnBwdArgs a) {
+  const long long total = (long long)a.rows * a.topk;
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (long long)gridDim.x * 256) {
+    const int k = a.idx[e];
+    if ((unsigned)k < (unsigned)a.n_k) atomicAdd(&a.cnt[k], 1);
+  }
+}
+
+// off = exclusive prefix sum of cnt (off[n_k] = total), cur = off.  One workgroup.
+__global__ __launch_bounds__(1024) void k_bwd_scan(AttnBwdArgs a) {
+  __shared__ unsigned scratch[16];
+  unsigned base = 0;
+  for (int k0 = 0; k0 < a.n_k; k0 += 1024) {
+    const int k = k0 + threadIdx.x;
+    const unsigned v = k < a.n_k ? (unsigned)a.cnt[k] : 0u;
+    unsigned tot;
+    const unsigned ex = block_excl_scan<16>(v, scratch, tot);
+    if (k < a.n_k) {
+      a.off[k] = (int)(base + ex);
+      a.cur[k] = (int)(base + ex);
     }
+    base += tot;
+  }
+  if (threadIdx.x == 0) a.off[a.n_k] = (int)base;
+}
+
+// list[cur[k]++] = row * topk + slot for every valid entry.
+__global__ __launch_bounds__(256) void k_bwd_scatter(AttnBwdArgs a) {
+  const long long total = (long long)a.rows * a.topk;
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (long long)gridDim.x * 256) {
+    const int k = a.idx[e];
+    if ((unsigned)k < (unsigned)a.n_k) a.list[atomicAdd(&a.cur[k], 1)] = (int)e;
+  }
+}
+
+// dkv[k] += sum of the key's contributions; one wave per key, so the row is owned and the
+// update is a plain read-modify-write.  Lane l sums dims 8 l .. 8 l + 7 (and, for l < 8,
+// the 64 dims past 512), four entries in flight.
+template <int DQK>
+__global__ __launch_bounds__(256) void k_bwd_reduce(AttnBwdArgs a) {
+  static_assert(DQK == 576, "lane split of the latent row");
+  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (k >= a.n_k) return;
+  const int beg = a.off[k], end = a.off[k + 1];
+  if (beg == end) return;
+  float s0[8] = {}, s1[8] = {};
+  const bool tail = lane < 8;
+  auto add = [&](int e) {
+    const int r = e / a.topk, sl = e - r * a.topk;
+    const uint16_t* src = a.ws_c + ((size_t)r * a.topkp + sl) * DQK;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * lane);
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (tail) w = *reinterpret_cast<const uint4*>(src + 512 + 8 * lane);
+    const uint32_t vv[4] = {v.x, v.y, v.z, v.w}, ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s0[2 * j] += __uint_as_float(vv[j] << 16);
+      s0[2 * j + 1] += __uint_as_float(vv[j] & 0xFFFF0000u);
+      s1[2 * j] += __uint_as_float(ww[j] << 16);
+      s1[2 * j + 1] += __uint_as_float(ww[j] & 0xFFFF0000u);
+    }
+  };
+  int p = beg;
+  for (; p + 4 <= end; p += 4) {
+    const int e0 = a.list[p], e1 = a.list[p + 1], e2 = a.list[p + 2], e3 = a.list[p + 3];
+    add(e0);
+    add(e1);
+    add(e2);
+    add(e3);
+  }
+  for (; p < end; ++p) add(a.list[p]);
+  float* dst = a.dkv + (size_t)k * DQK;
+  float4* d0 = reinterpret_cast<float4*>(dst + 8 * lane);
+  float4 x0 = d0[0], x1 = d0[1];
+  x0.x += s0[0]; x0.y += s0[1]; x0.z += s0[2]; x0.w += s0[3];
+  x1.x += s0[4]; x1.y += s0[5]; x1.z += s0[6]; x1.w += s0[7];
+  d0[0] = x0;
+  d0[1] = x1;
+  if (tail) {
+    float4* d1 = reinterpret_cast<float4*>(dst + 512 + 8 * lane);
+    float4 y0 = d1[0], y1 = d1[1];
+    y0.x += s1[0]; y0.y += s1[1]; y0.z += s1[2]; y0.w += s1[3];
+    y1.x += s1[4]; y1.y += s1[5]; y1.z += s1[6]; y1.w += s1[7];
+    d1[0] = y0;
+    d1[1] = y1;
   }
 }
 
@@ -535,6 +692,13 @@ hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v
   if (a.rows == 0) return hipSuccess;
   if (!(h == 128 && d_qk == 576 && d_v == 512)) return hipErrorInvalidValue;
   const bool al8 = a.topk >= 8 && a.topk % 8 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 31) == 0;
+  const long long entries = (long long)a.rows * a.topk;
+  const int eg = (int)std::min<long long>((entries + 255) / 256, 8192);
+  // key lists of the chunk (only the indices are needed)
+  k_bwd_zero<<<std::min((a.n_k + 255) / 256, 1024), 256, 0, s>>>(a);
+  k_bwd_count<<<eg, 256, 0, s>>>(a);
+  k_bwd_scan<<<1, 1024, 0, s>>>(a);
+  k_bwd_scatter<<<eg, 256, 0, s>>>(a);
   if (al8) {
     k_attn_bwd_p<128, 576, 512, true><<<a.rows, 256, 0, s>>>(a);
     k_attn_bwd_dq<128, 576, 512, true><<<a.rows, 256, 0, s>>>(a);
@@ -542,7 +706,8 @@ hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v
     k_attn_bwd_p<128, 576, 512, false><<<a.rows, 256, 0, s>>>(a);
     k_attn_bwd_dq<128, 576, 512, false><<<a.rows, 256, 0, s>>>(a);
   }
-  k_attn_bwd_dkv<128, 576, 512><<<a.rows, 256, 0, s>>>(a);
+  k_attn_bwd_dkv_part<128, 576, 512><<<a.rows, 256, 0, s>>>(a);
+  k_bwd_reduce<576><<<(a.n_k + 3) / 4, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -90,6 +90,11 @@ struct AttnBwdArgs {
   uint16_t* ws_ds;        // [rows, topkp, H] bf16 softmax_scale * dS
   uint16_t* dq;           // [rows, H, DQK] bf16
   float* dkv;             // [n_k, DQK] fp32, accumulated
+  uint16_t* ws_c;         // [rows, topkp, DQK] bf16 per-(row, slot) dKV contributions
+  int* list;              // [rows * topk] (row * topk + slot) entries grouped by key
+  int* cnt;               // [n_k] entries per key
+  int* off;               // [n_k + 1] first entry of each key in `list`
+  int* cur;               // [n_k] fill cursor
   int rows, n_k, topk;
   int topkp;              // workspace slots per row: topk rounded up to 96
   int xcd_remap;

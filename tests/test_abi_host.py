@@ -136,13 +136,23 @@ def _bwd(lib, sh, ws_bytes, workspace=FAKE, null_dkv=False):
 
 
 def test_backward_argument_checks(lib):
-    # workspace formula: two bf16 [rows, topk rounded up to 96, h] arrays, up to 4096 rows
+    # workspace formula: per row two bf16 [topk rounded up to 96, h] arrays, the bf16
+    # [topk rounded up to 96, d_qk] contributions and topk list entries; per call 3 n_k + 1
+    # ints + slack
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    def row(topk, topkp):
+        return 2 * topkp * 128 * 2 + topkp * 576 * 2 + topk * 4
+
     sh = dsa._shape(n_q=5000, n_k=8192, h=128, d_qk=576, d_v=512, topk=2048, softmax_scale=0.1)
     n = ctypes.c_size_t(0)
     assert lib.dsa_sparse_attn_bwd_workspace_bytes(ctypes.byref(sh), ctypes.byref(n)) == dsa.DSA_OK
-    assert n.value == 4096 * 2 * 2112 * 128 * 2
-    assert dsa.dsa_sparse_attn_bwd_workspace_bytes(10, 100, 100) == 10 * 2 * 192 * 128 * 2
-    per_row = 2 * 2112 * 128 * 2
+    fixed = al((3 * 8192 + 1) * 4) + 8 * 256
+    assert n.value == fixed + 2048 * row(2048, 2112)
+    assert dsa.dsa_sparse_attn_bwd_workspace_bytes(10, 100, 100) == \
+        al((3 * 100 + 1) * 4) + 8 * 256 + 10 * row(100, 192)
+    per_row = fixed + row(2048, 2112)
     assert _bwd(lib, sh, per_row - 1) == dsa.DSA_ERR_WORKSPACE
     assert _bwd(lib, sh, per_row, workspace=None) == dsa.DSA_ERR_WORKSPACE
     assert _bwd(lib, sh, per_row, workspace=ctypes.c_void_p(0x1008)) == dsa.DSA_ERR_INVALID_ARG
