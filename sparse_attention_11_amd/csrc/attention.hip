@@ -131,25 +131,21 @@ __device__ __forceinline__ void tile_pv(const RowCtx& c, const uint16_t* tile, c
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[1][mt & 1] + off));
     return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
   };
-  bf16x8 vf[2][2];
-  vf[0][0] = vfrag(0, 0);
-  vf[0][1] = vfrag(1, 0);
+  // K-step outer, M tiles inner: consecutive MFMAs go to different accumulators (two
+  // back-to-back MFMAs into one accumulator would wait for each other)
+  constexpr int PD = 2;            // fragments read ahead of their MFMA
+  constexpr int NIT = 2 * C::MTV;
+  bf16x8 vf[PD + 1];
 #pragma unroll
-  for (int mt = 0; mt < C::MTV; ++mt) {
-    const int cur = mt & 1;
-    if (mt + 1 < C::MTV) {
-      vf[cur ^ 1][0] = vfrag(0, mt + 1);
-      vf[cur ^ 1][1] = vfrag(1, mt + 1);
-    }
-    o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][0], pf[0], o[mt], 0, 0, 0);
-    o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][1], pf[1], o[mt], 0, 0, 0);
+  for (int it = 0; it < PD; ++it) vf[it] = vfrag(it / C::MTV, it % C::MTV);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int kk = it / C::MTV, mt = it % C::MTV;
+    if (it + PD < NIT) vf[(it + PD) % (PD + 1)] = vfrag((it + PD) / C::MTV, (it + PD) % C::MTV);
+    o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[it % (PD + 1)], pf[kk], o[mt], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
-
-
-
-
 
 template <int H, int DQK, int DV>
 __device__ __forceinline__ void write_row(const AttnArgs& a, const RowCtx& c, const f32x16* o,
@@ -355,34 +351,23 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
   c.flags = flags;
   c.vm = vmring;
 
-  // tiles past the last valid slot are never gathered or computed
-  int last = -1;
-  for (int sl = c.tid; sl < a.topk; sl += C::NT) {
-    const int id = c.idx_row[sl];
-    if (id >= 0 && id < a.n_k) last = sl;
-  }
+  // Row prologue with few memory round trips: the staged part of Q goes to LDS by LDS DMA,
+  // the index scan (tiles past the last valid slot are never gathered or computed) has its
+  // loads in flight together, and the register part of Q travels across the barrier.
+  stage_q_tail<H, DQK, DV>(a, c, qlds);
+  int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
   if (c.lane == 0) s_last[c.wave] = last;
-
-  // stage q[row, :, DQR:] in LDS
-  if constexpr (C::DQL > 0) {
-    constexpr int CH = C::DQL / 8;
-    const uint16_t* qrow = a.q + (size_t)c.row * H * DQK + C::DQR;
-    for (int i = c.tid; i < H * CH; i += C::NT) {
-      const int hh = i / CH, cc = i % CH;
-      *reinterpret_cast<uint4*>(&qlds[hh * C::QROWE + cc * 8]) =
-          *reinterpret_cast<const uint4*>(qrow + (size_t)hh * DQK + cc * 8);
-    }
-  }
+  bf16x8 qf[C::KSR];
+  load_q<H, DQK, DV>(a, c, qf);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // staged Q landed (DMA is not tracked)
   __syncthreads();
   last = -1;
 #pragma unroll
   for (int w = 0; w < C::NW; ++w) last = max(last, s_last[w]);
   c.ntiles = (last + C::NK) / C::NK;
 
-  bf16x8 qf[C::KSR];
-  load_q<H, DQK, DV>(a, c, qf);
   // compiler-visible vmcnt(0) (exp/lgkm counters left alone): the Q loads are done before the
   // gather ring starts, so the compiler adds no waits for them inside the loop
   __builtin_amdgcn_s_waitcnt(0x0F70);

@@ -37,16 +37,13 @@ namespace {
 constexpr float kLog2e = 1.44269504088896340736f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // Number of 32-slot tiles up to the row's last valid index (block-wide; one barrier).
 template <int H, int DQK, int DV>
 __device__ __forceinline__ int row_tiles(const AttnBwdArgs& a, const RowCtx& c, int* s_last) {
   using C = AttnCfg<H, DQK, DV>;
-  int last = -1;
-  for (int sl = c.tid; sl < a.topk; sl += C::NT) {
-    const int id = c.idx_row[sl];
-    if (id >= 0 && id < a.n_k) last = sl;
-  }
+  int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
   if (c.lane == 0) s_last[c.wave] = last;
@@ -164,15 +161,7 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p(AttnBwdArgs a) {
   c.ntiles = row_tiles<H, DQK, DV>(a, c, s_last);
   if (c.ntiles == 0) return;   // nothing selected: the row has no P / dS and no dKV share
 
-  if constexpr (C::DQL > 0) {
-    constexpr int CH = C::DQL / 8;
-    const uint16_t* qrow = a.q + (size_t)c.row * H * DQK + C::DQR;
-    for (int i = c.tid; i < H * CH; i += C::NT) {
-      const int hh = i / CH, cc = i % CH;
-      *reinterpret_cast<uint4*>(&qlds[hh * C::QROWE + cc * 8]) =
-          *reinterpret_cast<const uint4*>(qrow + (size_t)hh * DQK + cc * 8);
-    }
-  }
+  stage_q_tail<H, DQK, DV>(a, c, qlds);
   bf16x8 qf[C::KSR];
   load_q<H, DQK, DV>(a, c, qf);
   // dY fragments (B operand of dP^T, same lane layout as Q) and D = rowsum(dY * out)
@@ -198,6 +187,7 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p(AttnBwdArgs a) {
   const float msub = mrow == kNegInf ? 0.f : mrow * kLog2e;   // scaled log2 units
   const float lrow = a.ssum[hrow];
   const float invl = lrow > 0.f ? 1.f / lrow : 0.f;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // staged Q landed (DMA is not tracked)
   __syncthreads();                        // staged Q visible
   __builtin_amdgcn_s_waitcnt(0x0F70);     // row loads done before the gather ring starts
 
@@ -215,22 +205,15 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p(AttnBwdArgs a) {
     if constexpr (C::FLAT) gather_tile_flat<H, DQK, DV>(a, c, ti, loff, wb[k]);
     else gather_tile_s<H, DQK, DV>(a, c, ti, c.buf[k]);
   };
-  uint16_t* prow = a.ws_p + (size_t)c.row * a.topkp * H + c.head;
-  uint16_t* drow = a.ws_ds + (size_t)c.row * a.topkp * H + c.head;
-  // results of the previous tile, stored at the start of the next step -- before that
-  // step's gather, so the vmcnt wait at its end still only has to spare the gather
-  uint16_t pend_p[16], pend_d[16];
-  int pend_t = -1;
-  auto flush = [&]() {
-    if (pend_t >= 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const size_t o = (size_t)(pend_t * C::NK + acc_key(r, c.g)) * H;
-        prow[o] = pend_p[r];
-        drow[o] = pend_d[r];
-      }
-    }
-  };
+  // P / dS stores: lanes of a head pair (hl, hl ^ 1) swap one value per register pair, so
+  // each lane writes both heads of one slot as one dword (8 dword stores per tensor and
+  // tile, issued from asm so the count before each barrier is exact)
+  const uint16_t* pbase = a.ws_p + (size_t)c.row * a.topkp * H;    // scalar row bases
+  const uint16_t* dbase = a.ws_ds + (size_t)c.row * a.topkp * H;
+  const bool odd = c.hl & 1;
+  const int hpair = c.wave * 32 + (c.hl & ~1);
+  constexpr int NST = 16;
+  static_assert(C::GOPS + 2 * NST < 64, "vmcnt range");
 
   const int ntiles = (c.ntiles + 2) / 3 * 3;
   const TI i0 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 0);
@@ -242,11 +225,10 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p(AttnBwdArgs a) {
     c.vm[0 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i0);
     c.vm[1 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i1);
   }
-  wait_vm_barrier<C::GOPS>();
+  wait_vm_barrier<0>();   // both first tiles, so the steady-state count holds from step 0
 
   auto step = [&](int t, int slot, const uint16_t* cur, int ahead2, TI& nxt2) {
     const TI i3 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, t + 3);
-    flush();
     gather(nxt2, ahead2);
     if (c.lane == 0) c.vm[((slot + 2) % 3) * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, nxt2);
     unsigned vmask = 0;
@@ -259,14 +241,34 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p(AttnBwdArgs a) {
       for (int r = 0; r < 16; ++r)
         if (!((vmask >> acc_key(r, c.g)) & 1u)) s[r] = kNegInf;
     }
+    uint32_t pb[16], db[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -msub)) * invl;
-      pend_p[r] = f32_to_bf16(p);
-      pend_d[r] = f32_to_bf16(a.scale * p * (dp[r] - D));
+      pb[r] = f32_to_bf16(p);
+      db[r] = f32_to_bf16(a.scale * p * (dp[r] - D));
     }
-    pend_t = t;
-    wait_vm_barrier<C::GOPS>();   // tile t+1 landed for every wave
+    // (every slot of the tile is stored, padding tiles too: they lie inside the row's padded
+    // area and are never read)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r0 = 2 * j, r1 = 2 * j + 1;
+      const uint32_t xp = odd ? pb[r0] : pb[r1];
+      const uint32_t xd = odd ? db[r0] : db[r1];
+      const uint32_t yp = (uint32_t)__builtin_amdgcn_mov_dpp((int)xp, 0xB1, 0xF, 0xF, false);
+      const uint32_t yd = (uint32_t)__builtin_amdgcn_mov_dpp((int)xd, 0xB1, 0xF, 0xF, false);
+      const uint32_t vp = odd ? (yp | (pb[r1] << 16)) : (pb[r0] | (yp << 16));
+      const uint32_t vd = odd ? (yd | (db[r1] << 16)) : (db[r0] | (yd << 16));
+      const int key = acc_key(odd ? r1 : r0, c.g);
+      const unsigned off = (unsigned)(((t * C::NK + key) * H + hpair) * 2);
+      const uint16_t* b0 = pbase;
+      const uint16_t* b1 = dbase;
+      asm volatile("global_store_dword %0, %1, %2" :: "v"(off), "v"(vp), "s"(b0) : "memory");
+      asm volatile("global_store_dword %0, %1, %2" :: "v"(off), "v"(vd), "s"(b1) : "memory");
+    }
+    // tile t+1 landed for every wave: after its gather come the previous and this step's
+    // stores and the gather of tile t+2
+    wait_vm_barrier<C::GOPS + 2 * NST>();
     nxt2 = i3;
   };
   for (int t = 0; t < ntiles; t += 3) {
@@ -274,8 +276,7 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p(AttnBwdArgs a) {
     step(t + 1, 1, c.buf[1], 0, i2);
     step(t + 2, 2, c.buf[2], 1, i2);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no gather may outlive the block
-  flush();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no gather or store may outlive the block
 }
 
 // ---------------------------------------------------------------------------------------
@@ -387,18 +388,17 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_dq(AttnBwdArgs a) {
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[k][1][mt & 1] + off));
         return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       };
-      bf16x8 kf[2][2];
-      kf[0][0] = kfrag(0, 0);
-      kf[0][1] = kfrag(1, 0);
+      // K-step outer, dim tiles inner (consecutive MFMAs into different accumulators), each
+      // fragment read two MFMAs ahead
+      constexpr int PD = 2, NIT = 2 * MTQ;
+      bf16x8 kf[PD + 1];
 #pragma unroll
-      for (int mt = 0; mt < MTQ; ++mt) {
-        const int cur = mt & 1;
-        if (mt + 1 < MTQ) {
-          kf[cur ^ 1][0] = kfrag(0, mt + 1);
-          kf[cur ^ 1][1] = kfrag(1, mt + 1);
-        }
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][0], bq[0], acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][1], bq[1], acc[mt], 0, 0, 0);
+      for (int it = 0; it < PD; ++it) kf[it] = kfrag(it / MTQ, it % MTQ);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int kk = it / MTQ, mt = it % MTQ;
+        if (it + PD < NIT) kf[(it + PD) % (PD + 1)] = kfrag((it + PD) / MTQ, (it + PD) % MTQ);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[it % (PD + 1)], bq[kk], acc[mt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       wait_vm_barrier<GOPS2>();
@@ -453,11 +453,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
   const int32_t* idx_row = a.idx + (size_t)row * a.topk;
-  int last = -1;
-  for (int sl = tid; sl < a.topk; sl += 256) {
-    const int id = idx_row[sl];
-    if (id >= 0 && id < a.n_k) last = sl;
-  }
+  int last = thread_last_valid<256>(idx_row, a.topk, a.n_k, tid);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
   if (lane == 0) s_last[wave] = last;
@@ -469,9 +465,12 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
   const int d0 = wave * DW;
   // fragments of Q^T[dim d0 + 16 nt + n, heads 32 kk + 8 G .. +7] and the same of dY
   bf16x8 qa[NT][KH], da[NT][KH];
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // uniform: DMA bases are scalars
+  const unsigned stage_lds = (unsigned)(size_t)(lds_u16_ptr_t)stage;
   {
-    const uint4* src = reinterpret_cast<const uint4*>(a.q + (size_t)row * H * DQK);
-    for (int i = tid; i < H * DQK / 8; i += 256) reinterpret_cast<uint4*>(stage)[i] = src[i];
+    static_assert((H * DQK * 2) % 1024 == 0 && (H * DV * 2) % 1024 == 0, "whole DMA pieces");
+    dma_copy_flat<NW>(stage_lds, a.q + (size_t)row * H * DQK, H * DQK * 2, wave_u, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -479,8 +478,8 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
       for (int kk = 0; kk < KH; ++kk)
         qa[nt][kk] = tr_frag(stage, DQK, 32 * kk + 8 * G, d0 + 16 * nt, n);
     __syncthreads();
-    const uint4* dsrc = reinterpret_cast<const uint4*>(a.dout + (size_t)row * H * DV);
-    for (int i = tid; i < H * DV / 8; i += 256) reinterpret_cast<uint4*>(stage)[i] = dsrc[i];
+    dma_copy_flat<NW>(stage_lds, a.dout + (size_t)row * H * DV, H * DV * 2, wave_u, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -498,7 +497,6 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
   // tensor wave / 2, slots 16 (wave % 2) .. +15), so every tile needs the barrier.
   constexpr int TILE_E = 2 * NK * H;   // bf16 elements per ring tile
   static_assert(3 * TILE_E <= H * DQK && H == 128, "ring fits the staging area");
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // uniform: DMA bases are scalars
   const uint16_t* tsrc0 = (wave_u >> 1) ? a.ws_ds : a.ws_p;
   const uint16_t* tsrc = tsrc0 + (size_t)row * a.topkp * H;
   unsigned doff[4];
@@ -508,7 +506,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
     const int c = (lane & 15) ^ (slot & 15);
     doff[i] = (unsigned)(slot * H * 2 + c * 16);
   }
-  const unsigned ring_lds = (unsigned)(size_t)(lds_u16_ptr_t)stage;
+  const unsigned ring_lds = stage_lds;
   const unsigned wdst = (unsigned)((wave_u >> 1) * NK * H * 2 + (wave_u & 1) * 16 * H * 2);
   auto dma_tile = [&](int t, int k) {
     const uint16_t* src = tsrc + (size_t)min(t, ntiles - 1) * NK * H;
@@ -524,28 +522,12 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
   };
 
   f32x4 acc[2][NT];
-  uint16_t* crow = a.ws_c + (size_t)row * a.topkp * DQK + d0 + 4 * G;
-  int pend_t = -1;
-  // store the previous tile's contributions (at the start of the next step, ahead of that
-  // step's DMA, so the vmcnt wait before each barrier only spares the DMA)
-  auto flush = [&]() {
-    if (pend_t >= 0 && pend_t < ntiles) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        uint16_t* dst = crow + (size_t)(pend_t * NK + 16 * mt + n) * DQK;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const uint32_t lo = (uint32_t)f32_to_bf16(acc[mt][nt][0]) |
-                              ((uint32_t)f32_to_bf16(acc[mt][nt][1]) << 16);
-          const uint32_t hi = (uint32_t)f32_to_bf16(acc[mt][nt][2]) |
-                              ((uint32_t)f32_to_bf16(acc[mt][nt][3]) << 16);
-          *reinterpret_cast<uint2*>(dst + 16 * nt) = make_uint2(lo, hi);
-        }
-      }
-    }
-  };
+  const uint16_t* cbase = a.ws_c + (size_t)row * a.topkp * DQK;   // scalar base of the row
+  // lane's byte offset of (slot n of the 16-slot group, dims d0 + 4 G ..): + slot / dim terms
+  const unsigned coff = (unsigned)((n * DQK + d0 + 4 * G) * 2);
+  constexpr int NST = 2 * NT;   // 8-byte stores per lane and tile (exact: issued from asm)
+  static_assert(2 * NST + 4 < 64, "vmcnt range");
   auto step = [&](int t, int k) {
-    flush();
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -562,31 +544,49 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
         bp[mt] = *(__attribute__((address_space(3))) const bf16x8*)(tb + e);
         bd[mt] = *(__attribute__((address_space(3))) const bf16x8*)(tb + NK * H + e);
       }
+      // (dims past DV have zero dY fragments: the product is issued anyway -- the wave
+      // owning them would otherwise only finish early, which buys nothing)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          // (dims past DV have zero dY fragments: the product is issued anyway -- the wave
-          // owning them would otherwise only finish early, which buys nothing)
+        for (int nt = 0; nt < NT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[nt][kk], bd[mt], acc[mt][nt], 0, 0, 0);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[nt][kk], bp[mt], acc[mt][nt], 0, 0, 0);
-        }
+    }
+    // every slot of the tile is stored (empty and padding slots too: they lie inside the
+    // row's padded area and are never listed), so the store count per step is fixed
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const unsigned off = coff + (unsigned)(((t * NK + 16 * mt) * DQK + 16 * nt) * 2);
+        const uint32_t lo = (uint32_t)f32_to_bf16(acc[mt][nt][0]) |
+                            ((uint32_t)f32_to_bf16(acc[mt][nt][1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(acc[mt][nt][2]) |
+                            ((uint32_t)f32_to_bf16(acc[mt][nt][3]) << 16);
+        const u32x2 d = {lo, hi};
+        const uint16_t* base = cbase;
+        asm volatile("global_store_dwordx2 %0, %1, %2" :: "v"(off), "v"(d), "s"(base) : "memory");
       }
     }
-    pend_t = t;
-    wait_vm_barrier<4>();   // tile t+1 landed for every wave
+    // tile t+1 landed for every wave: after its DMA come this and the previous step's
+    // stores and the DMA of tile t+2
+    wait_vm_barrier<2 * NST + 4>();
   };
   dma_tile(0, 0);
   dma_tile(1, 1);
-  wait_vm_barrier<4>();
+  wait_vm_barrier<0>();    // both first tiles, so the steady-state count holds from step 0
   const int npad = (ntiles + 2) / 3 * 3;
   for (int t = 0; t < npad; t += 3) {
     step(t, 0);
     step(t + 1, 1);
     step(t + 2, 2);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA may outlive the block
-  flush();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA or store may outlive the block
 }
 
 // Zero the per-key counters.

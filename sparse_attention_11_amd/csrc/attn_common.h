@@ -248,6 +248,62 @@ __device__ __forceinline__ void load_q(const Args& a, const RowCtx& c, bf16x8* q
   }
 }
 
+// The last slot index (slots tid, tid + NT, ...) of a row's index list that holds a valid
+// key, as seen by this thread (-1 if none).  The loads go out eight at a time with clamped
+// addresses, so a list of up to 8 * NT slots costs one memory round trip, not one per slot.
+template <int NT>
+__device__ __forceinline__ int thread_last_valid(const int32_t* idx_row, int topk, int n_k,
+                                                 int tid) {
+  int last = -1;
+  for (int base = 0; base * NT < topk; base += 8) {
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = idx_row[min((base + j) * NT + tid, topk - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sl = (base + j) * NT + tid;
+      if (sl < topk && v[j] >= 0 && v[j] < n_k) last = sl;
+    }
+  }
+  return last;
+}
+
+// Copy `bytes` (a multiple of 1024) from global `src` to LDS byte address `lds` by LDS DMA,
+// one 1 KB piece per wave instruction, pieces spread over the block's NW waves.  Completion
+// is not tracked by the compiler: wait with vmcnt before reading.
+template <int NW>
+__device__ __forceinline__ void dma_copy_flat(unsigned lds, const void* src, int bytes, int wave_u,
+                                              int lane) {
+  for (int i = wave_u; i < bytes / 1024; i += NW) {
+    const unsigned voff = (unsigned)i * 1024u + (unsigned)lane * 16u;
+    const unsigned m0v = lds + (unsigned)i * 1024u;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(m0v), "v"(voff), "s"(src) : "memory", "m0");
+  }
+}
+
+// Q[row, :, DQR:] into the padded LDS rows of `qlds` by LDS DMA (no registers held).  The
+// padding chunk at the end of each LDS row copies a harmless chunk of the same Q row.
+template <int H, int DQK, int DV, class Args>
+__device__ __forceinline__ void stage_q_tail(const Args& a, const RowCtx& c, uint16_t* qlds) {
+  using C = AttnCfg<H, DQK, DV>;
+  if constexpr (C::DQL > 0) {
+    constexpr int RC = C::QROWE / 8;                   // 16-byte chunks per padded LDS row
+    constexpr int NQI = (H * RC * 16 + 1023) / 1024;   // full-wave DMA pieces
+    static_assert(H * RC * 16 == NQI * 1024, "padded Q rows fill whole DMA pieces");
+    const uint16_t* qrow = a.q + (size_t)c.row * H * DQK;
+    const unsigned qlds_lds = (unsigned)(size_t)(lds_u16_ptr_t)qlds;
+    for (int i = c.wave_u; i < NQI; i += C::NW) {
+      const int f = i * 64 + c.lane;
+      const int hh = f / RC, ch = f - hh * RC;
+      const unsigned voff = (unsigned)((hh * DQK + C::DQR + (ch < RC - 1 ? ch * 8 : 0)) * 2);
+      const unsigned m0v = qlds_lds + (unsigned)i * 1024u;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(m0v), "v"(voff), "s"(qrow) : "memory", "m0");
+    }
+  }
+}
+
 }  // namespace
 
 }  // namespace dsa

@@ -137,19 +137,25 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
       // both 32-key sub-tiles are computed unconditionally (keys past the row's window are
       // only masked at the store), so the second sub-tile's MFMAs overlap the first one's
       // epilogue
-      f32x16 acc[kIdxKeys / 32][MT];
+      // K steps outer: the MT x 2 accumulators form independent chains, so consecutive MFMAs
+      // never wait for each other
+      constexpr int NT = kIdxKeys / 32;
+      f32x16 acc[NT][MT];
 #pragma unroll
-      for (int nt = 0; nt < kIdxKeys / 32; ++nt) {
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = (f32x16){};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 b =
-              *reinterpret_cast<const bf16x8*>(&sk[buf][(nt * 32 + hl) * ROW + ks * 16 + g * 8]);
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 b[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          b[nt] = *reinterpret_cast<const bf16x8*>(&sk[buf][(nt * 32 + hl) * ROW + ks * 16 + g * 8]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[mt][ks], b, acc[nt][mt], 0, 0, 0);
-        }
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[mt][ks], b[nt], acc[nt][mt], 0, 0, 0);
       }
 #pragma unroll
       for (int nt = 0; nt < kIdxKeys / 32; ++nt) {

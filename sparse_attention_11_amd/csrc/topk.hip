@@ -6,10 +6,13 @@
 // lower key index (-0.0 counts as +0.0) and emits the kept keys in ascending order.
 //
 // One workgroup per row.  The row's window (at most THREADS * ITEMS scores) is read once from
-// HBM, coalesced, into registers as order-preserving 32-bit keys.  Three radix passes over
-// digits of 12, 12 and 8 bits (LDS histograms, one LDS atomic per candidate, candidates
-// narrowing to those matching the prefix found so far) find the exact k-th largest key T and
-// how many keys equal to T are needed.  A single ballot / mbcnt compaction in key-index order
+// HBM, coalesced, into registers as order-preserving 32-bit keys.  Radix passes over digits
+// of up to 12 bits (LDS histograms, one LDS atomic per candidate, candidates narrowing to
+// those matching the prefix found so far) find the exact k-th largest key T and how many
+// keys equal to T are needed; once the threshold bin holds at most 256 keys, they are
+// gathered in LDS and T is found by counting, for each of them, the keys above it.  The digits cover only the bits below the common prefix of the
+// row's smallest and largest key: a row's scores share their leading bits, and digits taken
+// from those bits would send every key of the first pass to a handful of bins.  A single ballot / mbcnt compaction in key-index order
 // then writes every key > T and the first `need` keys == T straight to their output slot, so
 // the output comes out sorted by key index with no sort.  Rows whose window is not longer
 // than topk skip the selection and write the window plus -1 padding.
@@ -38,6 +41,9 @@ __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
   __shared__ uint32_t grp_eq[NE];
   __shared__ uint32_t scan_tmp[NW];
   __shared__ uint32_t found[2];
+  constexpr int CAP = 256;                // candidate set small enough for a direct rank count
+  __shared__ uint32_t cand[CAP];
+  __shared__ uint32_t ncand;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = blockIdx.x;
@@ -55,25 +61,56 @@ __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
     return;
   }
 
+  // unconditional loads (clamped index), so all of them are in flight at once
   uint32_t key[ITEMS];
 #pragma unroll
-  for (int j = 0; j < ITEMS; ++j) {
-    const int e = j * THREADS + tid;
-    key[j] = e < L ? order_key(src[e]) : 0u;
-  }
-
-  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)topk;
+  for (int j = 0; j < ITEMS; ++j) key[j] = __float_as_uint(src[min(j * THREADS + tid, L - 1)]);
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-    const int nbins = pass == 2 ? 256 : 4096;
+  for (int j = 0; j < ITEMS; ++j) key[j] = j * THREADS + tid < L ? order_key(__uint_as_float(key[j])) : 0u;
+
+  // The keys of one row usually share their leading bits (scores of a row lie in a narrow
+  // band): digits start below the common prefix of the row's min and max key, so the first
+  // histogram spreads over its bins instead of piling into a few.
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    if (j * THREADS + tid < L) {
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if (lane == 0) {
+    grp_gt[wave] = kmin;
+    grp_eq[wave] = kmax;
+  }
+  __syncthreads();
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    kmin = min(kmin, grp_gt[w]);
+    kmax = max(kmax, grp_eq[w]);
+  }
+  __syncthreads();
+  const int nbits = kmin == kmax ? 0 : 32 - __clz((int)(kmin ^ kmax));   // differing low bits
+  uint32_t pmask = nbits == 32 ? 0u : ~((1u << nbits) - 1u);
+  uint32_t prefix = kmin & pmask, krem = (uint32_t)topk;
+  for (int done = 0; done < nbits;) {   // block-uniform trip count (at most 3 passes)
+    const int width = min(12, nbits - done);
+    const int shift = nbits - done - width;
+    const int nbins = 1 << width;
+    const uint32_t dmask = (uint32_t)(nbins - 1);
     for (int b = tid; b < nbins; b += THREADS) hist[b] = 0u;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
       const int e = j * THREADS + tid;
-      if (e < L && (key[j] & pmask) == prefix)
-        atomicAdd(&hist[(key[j] >> shift) & (uint32_t)(nbins - 1)], 1u);
+      if (e < L && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
     }
     __syncthreads();
     // thread t owns chunk (nchunks-1-t) of consecutive bins, so the exclusive scan in thread
@@ -99,9 +136,40 @@ __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
     }
     __syncthreads();
     prefix |= found[0] << shift;
-    pmask |= (uint32_t)(nbins - 1) << shift;
+    pmask |= dmask << shift;
     krem -= found[1];
+    done += width;
+    const uint32_t nb = hist[found[0]];   // keys left in the threshold bin (block-uniform)
     __syncthreads();
+    if (done < nbits && nb <= (uint32_t)CAP) {
+      // few candidates left: gather them and find the krem-th largest by counting, for each
+      // candidate, the candidates above it and equal to it (instead of further passes)
+      if (tid == 0) ncand = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        const int e = j * THREADS + tid;
+        if (e < L && (key[j] & pmask) == prefix) cand[atomicAdd(&ncand, 1u)] = key[j];
+      }
+      __syncthreads();
+      for (int i = tid; i < (int)nb; i += THREADS) {
+        const uint32_t ki = cand[i];
+        uint32_t gt = 0, eq = 0;
+        for (int j = 0; j < (int)nb; ++j) {
+          const uint32_t kj = cand[j];
+          gt += kj > ki;
+          eq += kj == ki;
+        }
+        if (gt < krem && krem <= gt + eq) {   // tied candidates all write the same values
+          found[0] = ki;
+          found[1] = gt;
+        }
+      }
+      __syncthreads();
+      prefix = found[0];
+      krem -= found[1];
+      break;
+    }
   }
   const uint32_t T = prefix;   // the topk-th largest key
   const uint32_t need = krem;  // how many keys equal to T are kept (lowest indices first)
