@@ -57,30 +57,32 @@ __device__ __forceinline__ f32x16 tile_logits(const AttnArgs& a, const RowCtx& c
     abase[j] = ltile + arow_i * C::ROWE + (((2 * j + c.g) ^ asw) - 2 * j) * 8;
   auto arow_at = [&](int ks) { return abase[ks & 3] + ks * 16; };
   const uint16_t* qlrow = c.qlds + (C::DQL > 0 ? c.head % H : 0) * C::QROWE + c.g * 8;
-  // A fragments one group ahead of their MFMAs; sched_barrier bounds the live fragments
+  // A fragments (and, past the register part of Q, the staged Q fragments) are read one
+  // group of K steps ahead of their MFMAs; sched_barrier bounds the live fragments
   constexpr int QG = 3;                 // K steps per prefetch group (36 = 12 x 3)
   constexpr int NG = (C::KS + QG - 1) / QG;
-  bf16x8 af[2][QG];
-#pragma unroll
-  for (int u = 0; u < QG; ++u)
-    if (u < C::KS) af[0][u] = *(__attribute__((address_space(3))) const bf16x8*)(arow_at(u));
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const int cur = gi & 1;
-    if (gi + 1 < NG) {
-#pragma unroll
-      for (int u = 0; u < QG; ++u) {
-        const int ks = (gi + 1) * QG + u;
-        if (ks < C::KS) af[cur ^ 1][u] = *(__attribute__((address_space(3))) const bf16x8*)(arow_at(ks));
-      }
-    }
+  typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
+  bf16x8 af[2][QG], bt[2][QG];
+  auto fetch = [&](int gi, int buf) {
 #pragma unroll
     for (int u = 0; u < QG; ++u) {
       const int ks = gi * QG + u;
       if (ks < C::KS) {
-        bf16x8 bq;
-        if (ks < C::KSR) bq = qf[ks < C::KSR ? ks : 0];
-        else bq = *reinterpret_cast<const bf16x8*>(qlrow + (ks - C::KSR) * 16);
+        af[buf][u] = *(lds_cb8_t)(arow_at(ks));
+        if (ks >= C::KSR) bt[buf][u] = *reinterpret_cast<const bf16x8*>(qlrow + (ks - C::KSR) * 16);
+      }
+    }
+  };
+  fetch(0, 0);
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int cur = gi & 1;
+    if (gi + 1 < NG) fetch(gi + 1, cur ^ 1);
+#pragma unroll
+    for (int u = 0; u < QG; ++u) {
+      const int ks = gi * QG + u;
+      if (ks < C::KS) {
+        const bf16x8 bq = ks < C::KSR ? qf[ks < C::KSR ? ks : 0] : bt[cur][u];
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][u], bq, s, 0, 0, 0);
       }
     }
@@ -177,12 +179,13 @@ __device__ __forceinline__ void write_row(const AttnArgs& a, const RowCtx& c, co
   }
 }
 
-// Logits, probabilities and the output product of one tile.  Returns whether some head's
-// max exceeded the scaling max by more than the fast path's range.
+// Logits and probabilities of one tile for the wave's heads (pf: the lane's 16 keys as the
+// B operand of the value product).  Returns whether some head's max exceeded the scaling max
+// by more than the fast path's range.
 template <int H, int DQK, int DV>
-__device__ __forceinline__ bool tile_step(const AttnArgs& a, const RowCtx& c, const bf16x8* qf,
-                                          const uint16_t* tile, unsigned vmask, float& m_used,
-                                          float& m_true, float& lsum, f32x16* o) {
+__device__ __forceinline__ bool tile_probs(const AttnArgs& a, const RowCtx& c, const bf16x8* qf,
+                                           const uint16_t* tile, unsigned vmask, float& m_used,
+                                           float& m_true, float& lsum, bf16x8* pf) {
   float mx;
   f32x16 s = tile_logits<H, DQK, DV>(a, c, qf, tile, vmask, mx);
   m_true = fmaxf(m_true, mx);
@@ -192,7 +195,6 @@ __device__ __forceinline__ bool tile_step(const AttnArgs& a, const RowCtx& c, co
   const float msub = m_used == kNegInf ? 0.f : m_used;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  bf16x8 pf[2];
   float ls = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; r += 2) {
@@ -206,8 +208,85 @@ __device__ __forceinline__ bool tile_step(const AttnArgs& a, const RowCtx& c, co
     pf[r >> 3][(r & 7) + 1] = pk[1];
   }
   lsum += ls;
+  return over;
+}
+
+// Logits, probabilities and the output product of one tile (each wave: its own heads, all
+// value columns).
+template <int H, int DQK, int DV>
+__device__ __forceinline__ bool tile_step(const AttnArgs& a, const RowCtx& c, const bf16x8* qf,
+                                          const uint16_t* tile, unsigned vmask, float& m_used,
+                                          float& m_true, float& lsum, f32x16* o) {
+  bf16x8 pf[2];
+  const bool over = tile_probs<H, DQK, DV>(a, c, qf, tile, vmask, m_used, m_true, lsum, pf);
   tile_pv<H, DQK, DV>(c, tile, pf, o);
   return over;
+}
+
+// ---- column-split value product ------------------------------------------------------------
+// LDS probabilities of a tile: [head][32 keys] bf16, 16-byte chunk c (keys 8c .. 8c+7) of head
+// h stored at chunk c ^ ((h >> 2) & 3), so 16 lanes reading one chunk of 16 heads hit 16
+// different bank groups.
+__device__ __forceinline__ int pchunk(int head, int c) { return c ^ ((head >> 2) & 3); }
+
+// The owner lane (head hl of the wave's 32, half g) stores keys 8g..8g+7 and 16+8g..16+8g+7.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void store_probs(const RowCtx& c, uint16_t* pb, const bf16x8* pf) {
+  const int head = c.wave * 32 + c.hl;
+  typedef __attribute__((address_space(3))) bf16x8* lds_b8_t;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+    *(lds_b8_t)((lds_u16_ptr_t)pb + head * 32 + pchunk(head, 2 * kk + c.g) * 8) = pf[kk];
+}
+
+// O^T[col, head] += V^T P^T over one tile for the wave's DV / NW columns and all heads:
+// o[mt][nt] is the 32-column tile 4 wave + mt of the 32-head tile nt.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void pv_cols(const RowCtx& c, const uint16_t* tile, const uint16_t* pb,
+                                        f32x16 (&o)[4][4]) {
+  using C = AttnCfg<H, DQK, DV>;
+  typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
+  // B fragments: P^T[key, head], lane (head hl of tile nt, half g) takes keys 16 kk + 8 g ..
+  auto pfrag = [&](int kk, int nt) {
+    const int head = nt * 32 + c.hl;
+    return *(lds_cb8_t)((lds_cptr_t)pb + head * 32 + pchunk(head, 2 * kk + c.g) * 8);
+  };
+  // A fragments: V^T via the transposing read (addressing as in tile_pv), column tile
+  // 4 wave + mt
+  const int G = c.lane >> 4, i = c.lane & 15;
+  const int low = 2 * (G & 1) + ((i & 3) >> 1);
+  const lds_cptr_t ltile = (lds_cptr_t)tile;
+  lds_cptr_t vb[2][2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int r = (G >> 1) * 8 + (i >> 2) + hf * 4;
+    const int sw = C::SWZ ? swz(r) : 0;
+    const lds_cptr_t b = ltile + r * C::ROWE + ((low ^ (sw & 3)) * 8) + (i & 1) * 4 + c.wave * 4 * 32;
+    vb[hf][0] = b + (sw >> 2) * 32;
+    vb[hf][1] = b - (sw >> 2) * 32;
+  }
+  auto vfrag = [&](int kk, int mt) {
+    const int off = kk * 16 * C::ROWE + mt * 32;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[0][mt & 1] + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[1][mt & 1] + off));
+    return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  };
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    bf16x8 bp[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) bp[nt] = pfrag(kk, nt);
+    bf16x8 vf[2];
+    vf[0] = vfrag(kk, 0);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt + 1 < 4) vf[(mt + 1) & 1] = vfrag(kk, mt + 1);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[mt & 1], bp[nt], o[mt][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 }
 
 // Fast path: tiles in a 3-deep LDS ring (gathers of tiles t+1 and t+2 in flight while tile t
@@ -281,6 +360,108 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
   return true;
 }
 
+// Fast path with the column-split value product.  Same 3-deep gather ring as the plain fast
+// path (gathers of tiles t+1 and t+2 in flight while tile t is computed), but each step has
+// two halves: every wave computes the logits and probabilities of the tile for its 32 heads
+// and stores the probabilities in LDS; after a barrier every wave forms the output product
+// for its 128 value columns over all heads.  Each value element is then read from LDS once
+// per workgroup instead of once per wave.
+template <int H, int DQK, int DV, bool AL8>
+__device__ __forceinline__ bool accumulate_csplit(const AttnArgs& a, const RowCtx& c,
+                                                  const bf16x8* qf, uint16_t* pbuf, float* lbuf) {
+  using C = AttnCfg<H, DQK, DV>;
+  constexpr int RPW = C::RPW;
+  f32x16 o[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) o[mt][nt] = (f32x16){};
+  float m_used = kNegInf, m_true = kNegInf, lsum = 0.f;
+  bool overflow = false;
+  const int ntiles = (c.ntiles + 2) / 3 * 3;
+  using TI = TileIdx<H, DQK, DV>;
+  unsigned loff[C::NI];
+  unsigned wb[3];
+#pragma unroll
+  for (int i = 0; i < C::NI; ++i) loff[i] = flat_lane_offset<H, DQK, DV>(c, i);
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+    wb[k] = (unsigned)(size_t)(lds_u16_ptr_t)(c.buf[k]) + c.wave_u * (RPW * C::ROWE * 2);
+  auto gather = [&](const TI& ti, int k) { gather_tile_flat<H, DQK, DV>(a, c, ti, loff, wb[k]); };
+  const TI i0 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 0);
+  const TI i1 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 1);
+  TI i2 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 2);
+  gather(i0, 0);
+  gather(i1, 1);
+  if (c.lane == 0) {
+    c.vm[0 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i0);
+    c.vm[1 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i1);
+  }
+  wait_vm_barrier<C::GOPS>();          // tile 0 landed; tile 1 may be in flight
+
+  auto step = [&](int t, int slot, uint16_t* cur, int ahead2, TI& nxt2) {
+    const TI i3 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, t + 3);
+    gather(nxt2, ahead2);
+    if (c.lane == 0) c.vm[((slot + 2) % 3) * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, nxt2);
+    unsigned vmask = 0;
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) vmask |= c.vm[slot * C::NW + w] << (w * RPW);
+    bf16x8 pf[2];
+    const bool over = tile_probs<H, DQK, DV>(a, c, qf, cur, vmask, m_used, m_true, lsum, pf);
+    store_probs<H, DQK, DV>(c, pbuf, pf);
+    if (c.lane == 0) c.flags[(t & 1) * C::NW + c.wave] = __ballot(over) != 0ull;
+    // probabilities of every head visible (LDS only: the gathers stay in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    pv_cols<H, DQK, DV>(c, cur, pbuf, o);
+    wait_vm_barrier<C::GOPS>();        // tile t+1 landed for every wave; P and tile t free
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) overflow |= c.flags[(t & 1) * C::NW + w] != 0;
+    nxt2 = i3;
+  };
+  for (int t = 0; t < ntiles; t += 3) {
+    step(t, 0, c.buf[0], 2, i2);
+    step(t + 1, 1, c.buf[1], 0, i2);
+    step(t + 2, 2, c.buf[2], 1, i2);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no gather may outlive the block
+  if (overflow) return false;
+
+  // row sums of every head for the column owners
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(lsum), __float_as_int(lsum),
+                                                   false, false);
+  lsum = __int_as_float(pr[0]) + __int_as_float(pr[1]);
+  if (c.g == 0) lbuf[c.head] = lsum;
+  __syncthreads();
+  // o[mt][nt]: lane (head nt*32 + hl, half g), register r -> column
+  // 128 wave + 32 mt + (r / 4) * 8 + 4 g + r % 4
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int head = nt * 32 + c.hl;
+    const float l = lbuf[head];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* op = a.out + ((size_t)c.row * H + head) * DV + c.wave * 128;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int col = mt * 32 + q4 * 8 + c.g * 4;
+        const uint32_t lo = (uint32_t)f32_to_bf16(o[mt][nt][q4 * 4 + 0] * inv) |
+                            ((uint32_t)f32_to_bf16(o[mt][nt][q4 * 4 + 1] * inv) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(o[mt][nt][q4 * 4 + 2] * inv) |
+                            ((uint32_t)f32_to_bf16(o[mt][nt][q4 * 4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + col) = make_uint2(lo, hi);
+      }
+    }
+  }
+  if (c.g == 0) {
+    const size_t si = (size_t)c.row * H + c.head;
+    const bool any = m_true != kNegInf;
+    if (a.smax) a.smax[si] = any ? m_true * kLn2 : kNegInf;
+    if (a.ssum) a.ssum[si] = any ? lsum * exp2f(m_used - m_true) : 0.f;
+  }
+  return true;
+}
+
 // Exact path: scaling max fixed to the row max (computed beforehand), two buffers, full
 // waits; only runs for rows the fast path gave up on.
 template <int H, int DQK, int DV>
@@ -315,6 +496,8 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
   __shared__ __attribute__((aligned(16))) uint16_t kv1[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t kv2[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t qlds[C::QLDS];
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[C::PTILE];
+  __shared__ float lbuf[C::CSPLIT ? H : 1];
   __shared__ int flags[2 * C::NW];
   __shared__ unsigned vmring[3 * C::NW];
   __shared__ int s_last[C::NW];
@@ -385,8 +568,11 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
       __syncthreads();
     }
     accumulate_exact<H, DQK, DV>(a, c, qf, m_fix);
-  } else if (!accumulate_fast<H, DQK, DV, AL8>(a, c, qf) && c.tid == 0) {
-    a.out[(size_t)c.row * H * DV] = kOverflowMark;
+  } else {
+    bool done;
+    if constexpr (C::CSPLIT) done = accumulate_csplit<H, DQK, DV, AL8>(a, c, qf, pbuf, lbuf);
+    else done = accumulate_fast<H, DQK, DV, AL8>(a, c, qf);
+    if (!done && c.tid == 0) a.out[(size_t)c.row * H * DV] = kOverflowMark;
   }
   }
 }

@@ -64,6 +64,11 @@ struct AttnCfg {
   // vector-memory instructions one wave issues per tile gather
   static constexpr int GOPS = FLAT ? NI : RPW * ((CPR + 63) / 64);
   static_assert(GOPS < 64, "vmcnt range");
+  // Value product split by output columns: each wave owns DV / NW columns for all heads and
+  // reads the probabilities of every head from LDS (instead of each wave reading the whole
+  // value tile for its own heads).
+  static constexpr bool CSPLIT = H == 128 && DV == 512 && NW == 4;
+  static constexpr int PTILE = CSPLIT ? H * NK : 8;   // bf16 probabilities per tile
   static_assert(DQK % 16 == 0 && DV % 32 == 0 && DV <= DQK && DQR % 16 == 0, "head dims");
 };
 

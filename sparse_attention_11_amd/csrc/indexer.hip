@@ -69,11 +69,12 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   constexpr int KS = DI / 16;            // K steps of the 32x32x16 MFMA
   constexpr int ROW = DI + 8;            // LDS row in bf16 elements (16-byte pad)
   constexpr int CPR = DI / 8;            // 16-byte chunks per key row
-  constexpr int CH = kIdxKeys * CPR;     // chunks per stage
+  constexpr int KST = 2 * kIdxKeys;      // keys per LDS stage (two 64-key halves per barrier)
+  constexpr int CH = KST * CPR;          // chunks per stage
   constexpr int NT = kIdxWaves * 64;
   constexpr int PER = (CH + NT - 1) / NT;
   static_assert(DI % 16 == 0, "d_idx must be a multiple of 16");
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kIdxKeys * ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][KST * ROW];
 
   const RowInfo ri = indexer_row(a.segs);
   const int tid = threadIdx.x, lane = tid & 63, hl = lane & 31, g = lane >> 5;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   }
 
   float* out = a.scores + (size_t)ri.row * a.ld + (a.dense ? ri.k_lo : 0);
-  const int ntiles = (ri.L_blk + kIdxKeys - 1) / kIdxKeys;
+  const int ntiles = (ri.L_blk + KST - 1) / KST;
 
   uint4 pre[PER];
   auto fetch = [&](int t) {
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
     for (int p = 0; p < PER; ++p) {
       const int c = tid + p * NT;
       const int key = c / CPR, col = c % CPR;
-      const int kr = t * kIdxKeys + key;
+      const int kr = t * KST + key;
       pre[p] = make_uint4(0, 0, 0, 0);
       if (c < CH && kr < ri.L_blk)
         pre[p] = *reinterpret_cast<const uint4*>(ksrc + (size_t)(ri.k_lo + kr) * DI + col * 8);
@@ -133,12 +134,13 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntiles) fetch(t + 1);
-    if (ri.ok) {
+#pragma unroll
+    for (int hh = 0; hh < KST / kIdxKeys; ++hh) {
+    const int kb = t * KST + hh * kIdxKeys;   // first key of this 64-key half
+    if (ri.ok && kb <= ri.pos) {
       // both 32-key sub-tiles are computed unconditionally (keys past the row's window are
-      // only masked at the store), so the second sub-tile's MFMAs overlap the first one's
-      // epilogue
-      // K steps outer: the MT x 2 accumulators form independent chains, so consecutive MFMAs
-      // never wait for each other
+      // only masked at the store); K steps outer, so the MT x 2 accumulators form independent
+      // chains and consecutive MFMAs never wait for each other
       constexpr int NT = kIdxKeys / 32;
       f32x16 acc[NT][MT];
 #pragma unroll
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
         bf16x8 b[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          b[nt] = *reinterpret_cast<const bf16x8*>(&sk[buf][(nt * 32 + hl) * ROW + ks * 16 + g * 8]);
+          b[nt] = *reinterpret_cast<const bf16x8*>(&sk[buf][(hh * kIdxKeys + nt * 32 + hl) * ROW + ks * 16 + g * 8]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -165,9 +167,10 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
 #pragma unroll
           for (int r = 0; r < 16; ++r) s = relu_fma(acc[nt][mt][r], wv[mt][r], s);
         s = pair_sum(s);
-        const int key = t * kIdxKeys + nt * 32 + hl;
+        const int key = kb + nt * 32 + hl;
         if (g == 0 && key <= ri.pos) out[key] = s;
       }
+    }
     }
     if (t + 1 < ntiles) stash(buf ^ 1);
     __syncthreads();
