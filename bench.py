@@ -27,7 +27,16 @@ from sparse_attention_11_amd import dsa, inputs as I  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
-ATTN_SRC = os.path.join(ROOT, "sparse_attention_11_amd", "csrc", "attention.hip")
+# sources the sparse-attention kernel is built from: the counter record is valid for them only
+ATTN_SRCS = [os.path.join(ROOT, "sparse_attention_11_amd", "csrc", f)
+             for f in ("attention.hip", "attn_common.h", "dsa_device.h")]
+
+
+def attention_source_hash():
+    h = hashlib.sha256()
+    for f in ATTN_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def work(wl):
@@ -123,12 +132,44 @@ def traffic_entry():
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        h = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if t.get("attention_hip_sha256") == h:
+        if t.get("attention_source_sha256") == attention_source_hash():
             return float(t["hbm_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
         pass
     return None
+
+
+def _counter_rows(d, counter):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(rows)
+
+
+def write_traffic_record(fetch_dir, write_dir):
+    """HBM bytes per sparse-attention launch: FETCH_SIZE and WRITE_SIZE (KiB units as read)
+    scaled by what the same counters read for the 1 GiB device copy of the same run."""
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, name)
+        copies = [v for _, k, v in rows if "copyBuffer" in k or "copy" in k.lower()]
+        cal = max(copies)                         # the 1 GiB copy is the largest copy
+        attn = [v for _, k, v in rows if "k_sparse_attn<128, 576, 512, false" in k]
+        scale = float(1 << 30) / cal              # bytes per counter unit
+        out[name] = {"copy_reading": cal, "bytes_per_unit": scale,
+                     "attention_reading_avg": sum(attn) / len(attn), "launches": len(attn),
+                     "bytes_per_launch": sum(attn) / len(attn) * scale}
+    rec = {"attention_source_sha256": attention_source_hash(),
+           "hbm_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"]
+           + out["WRITE_SIZE"]["bytes_per_launch"],
+           "counters": out}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def main():
@@ -141,9 +182,16 @@ def main():
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the packed-varlen forward + backward timing")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM traffic record of the attention kernel from two "
+                         "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "'bench.py --calibrate-copy --no-stages' and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic_record(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only (got --gpus {args.gpus}); the CP "
               "all-gather and multi-GPU runs are not part of this build", file=sys.stderr)

@@ -388,17 +388,18 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_dq(AttnBwdArgs a) {
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[k][1][mt & 1] + off));
         return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       };
-      // K-step outer, dim tiles inner (consecutive MFMAs into different accumulators), each
-      // fragment read two MFMAs ahead
-      constexpr int PD = 2, NIT = 2 * MTQ;
-      bf16x8 kf[PD + 1];
+      bf16x8 kf[2][2];
+      kf[0][0] = kfrag(0, 0);
+      kf[0][1] = kfrag(1, 0);
 #pragma unroll
-      for (int it = 0; it < PD; ++it) kf[it] = kfrag(it / MTQ, it % MTQ);
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int kk = it / MTQ, mt = it % MTQ;
-        if (it + PD < NIT) kf[(it + PD) % (PD + 1)] = kfrag((it + PD) / MTQ, (it + PD) % MTQ);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[it % (PD + 1)], bq[kk], acc[mt], 0, 0, 0);
+      for (int mt = 0; mt < MTQ; ++mt) {
+        const int cur = mt & 1;
+        if (mt + 1 < MTQ) {
+          kf[cur ^ 1][0] = kfrag(0, mt + 1);
+          kf[cur ^ 1][1] = kfrag(1, mt + 1);
+        }
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][0], bq[0], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][1], bq[1], acc[mt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       wait_vm_barrier<GOPS2>();
