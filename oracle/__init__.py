@@ -24,4 +24,6 @@ from .dsa import (  # noqa: F401
     dsa_forward,
     attention_bwd_row,
     sparse_attn_bwd,
+    indexer_kl_row,
+    indexer_kl_loss_grad,
 )

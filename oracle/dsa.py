@@ -1,4 +1,5 @@
-"""Plain float64 oracle for the DSA forward (and sparse-attention backward) on one CP rank.
+"""Plain float64 oracle for the DSA forward (with the sparse-attention backward and the indexer
+KL loss) on one CP rank.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the bench's CPU-baseline
 leg, never by the product path.  Nothing here is blocked, fused or reordered beyond what the
@@ -13,7 +14,10 @@ Sources (four web pages on DeepSeek Sparse Attention and its context parallelism
   Flash Attention formula (softmax of q K_topk^T / sqrt(d)); section "SparseFlashAttentionGrad":
   the backward (Gather, recomputed P, dP = dY V^T, dS = P * (dP - FlashSoftmaxGrad(dY, out)),
   dQ = dS K_topk / sqrt(d), dK = ScatterAdd(dS^T Q / sqrt(d)), dV = P^T dY); section
-  "自定义CP策略": a CP rank's local queries must see the full all-gathered keys and values.
+  "自定义CP策略": a CP rank's local queries must see the full all-gathered keys and values;
+  section "SparseLightningIndexerGradKLLoss" also gives the indexer loss (KL divergence of the
+  indexer's softmax from the head-summed, L1-normalised attention probabilities) and its
+  gradients with respect to the index weights, queries and keys.
 * Page "CANN/torchtitan-npu融合算子适配", section "DSA": the indexer selects a small set of
   high-value token indices that the sparse multi-query attention then consumes.
 * Page "context_parallel.md" (HyperParallel CP guide), section "DSA CP": the indexer boundary
@@ -32,7 +36,10 @@ Readings where the pages are silent (each also listed in the design notes):
 * the value is the first ``d_v`` columns of the shared latent row, the rope part the rest;
 * ``softmax_max`` is the maximum scaled logit, ``softmax_sum`` the sum of exp(z - max);
 * FlashSoftmaxGrad(dY, out) is the row sum of dY * out;
-* fp8 indexer inputs: OCP e4m3fn with one fp32 scale per token row, scale = amax / 448.
+* fp8 indexer inputs: OCP e4m3fn with one fp32 scale per token row, scale = amax / 448;
+* indexer loss: the sum over tokens of each token's KL term over its selected slots (a
+  repeated key is one entry per slot), the target recomputed from the selected rows; ReLU
+  passes no gradient at exactly 0; the incoming loss gradient scales dI.
 """
 
 from __future__ import annotations
@@ -362,3 +369,79 @@ def sparse_attn_bwd(q, kv, idx, dout, scale: float, d_v: int):
         dq[i], sel, rows = attention_bwd_row(q[i], kv, idx[i], dout[i], scale, d_v)
         np.add.at(dkv, sel, rows)
     return dq, dkv
+
+
+# ----------------------------------------------------------------------------------------
+# indexer KL loss and its gradients
+# ----------------------------------------------------------------------------------------
+
+
+def indexer_kl_row(q_idx_i, k_idx, w_i, q_i, kv, idx_i, scale: float, loss_grad: float = 1.0):
+    """KL loss of one query token's indexer distribution and its gradients (page
+    "CANNTorchTitan: ...", section "SparseLightningIndexerGradKLLoss", the loss and gradient
+    formulas after the two top-k value formulas).
+
+    Over the token's selected keys (slots holding -1 are empty; a repeated key is one entry
+    per slot):
+      target   P[h, s] = softmax_s(scale * q[h] . kv[sel[s]]), the Sparse Flash Attention
+               probabilities; p = sum_h P[h, :], then divided by its L1 norm over the slots;
+      indexer  S = q_idx K_sel^T [h_idx, n] with K_sel = k_idx[sel] (S is the product of the
+               index queries and keys); I = sum_j w[j] ReLU(S[j, :]);
+      loss     = D_KL(p || softmax(I)) = sum_s p_s log(p_s / softmax(I)_s) (0 log 0 = 0);
+      dI       = loss_grad * (softmax(I) - p);
+      dW       = ReLU(S) dI  (for each index head j: sum_s dI_s ReLU(S[j, s]));
+      dS       = w[j] dI_s where S[j, s] > 0, else 0 (ReLU passes no gradient at 0);
+      dq_idx   = dS K_sel;   dK rows = dS^T q_idx (added into k_idx's selected rows).
+    The target carries no gradient.  loss_grad is the gradient arriving at this token's loss
+    term (1 for the plain sum over tokens).
+    Returns (loss, dq_idx_i [h_idx, d_idx], dw_i [h_idx], sel [n], dk_rows [n, d_idx])."""
+    q_idx_i = np.asarray(q_idx_i, dtype=np.float64)
+    w_i = np.asarray(w_i, dtype=np.float64)
+    idx_i = np.asarray(idx_i)
+    sel = idx_i[idx_i >= 0]
+    G, d = q_idx_i.shape
+    if sel.size == 0:
+        return 0.0, np.zeros((G, d)), np.zeros(G), sel, np.zeros((0, d))
+    # target distribution from the attention probabilities
+    K = np.asarray(kv, dtype=np.float64)[sel]
+    z = scale * (np.asarray(q_i, dtype=np.float64) @ K.T)      # [H, n]
+    e = np.exp(z - z.max(axis=1)[:, None])
+    P = e / e.sum(axis=1)[:, None]
+    p = P.sum(axis=0)
+    p = p / np.abs(p).sum()
+    # indexer distribution
+    Ki = np.asarray(k_idx, dtype=np.float64)[sel]              # [n, d]
+    S = q_idx_i @ Ki.T                                         # [G, n]
+    R = np.maximum(S, 0.0)
+    I = w_i @ R
+    lse = I.max() + np.log(np.sum(np.exp(I - I.max())))
+    logr = I - lse
+    r = np.exp(logr)
+    pos = p > 0
+    loss = float(np.sum(p[pos] * (np.log(p[pos]) - logr[pos])))
+    # gradients
+    dI = loss_grad * (r - p)
+    dw = R @ dI
+    dS = np.where(S > 0, w_i[:, None] * dI[None, :], 0.0)
+    dq = dS @ Ki
+    dk_rows = dS.T @ q_idx_i
+    return loss, dq, dw, sel, dk_rows
+
+
+def indexer_kl_loss_grad(q_idx, k_idx, w_idx, q, kv, idx, scale: float, loss_grad: float = 1.0):
+    """Row loop of ``indexer_kl_row``: per-token losses [n_q] (their sum is the loss of the
+    page's formula), dq_idx [n_q, h_idx, d_idx], dw [n_q, h_idx] and dk_idx [n_k, d_idx] (the
+    scatter-add of every row's key-row gradients)."""
+    q_idx = np.asarray(q_idx)
+    n_q, G, d = q_idx.shape
+    dk = np.zeros((np.asarray(k_idx).shape[0], d))
+    losses = np.zeros(n_q)
+    dq = np.zeros((n_q, G, d))
+    dw = np.zeros((n_q, G))
+    k64 = np.asarray(k_idx, dtype=np.float64)
+    kv64 = np.asarray(kv, dtype=np.float64)
+    for i in range(n_q):
+        losses[i], dq[i], dw[i], sel, rows = indexer_kl_row(q_idx[i], k64, w_idx[i], q[i], kv64,
+                                                            idx[i], scale, loss_grad)
+        np.add.at(dk, sel, rows)
+    return losses, dq, dw, dk

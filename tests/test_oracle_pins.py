@@ -447,6 +447,147 @@ def test_backward_matches_autograd_and_finite_differences():
         assert abs((f(q, kp) - f(q, km)) / (2 * eps) - dkv[s, d]) < 1e-6
 
 
+# ---------------------------------------------------------------------------------- indexer KL loss
+
+
+def _kl_case(seed, n_q=5, n_k=17, G=3, d=6, H=4, D=9, topk=6):
+    rng = np.random.default_rng(seed)
+    qi = rng.standard_normal((n_q, G, d))
+    ki = rng.standard_normal((n_k, d))
+    w = rng.uniform(-0.5, 1.0, (n_q, G))
+    q = rng.standard_normal((n_q, H, D))
+    kv = rng.standard_normal((n_k, D))
+    idx = np.full((n_q, topk), -1)
+    for i in range(n_q):
+        n = int(rng.integers(2, topk + 1))
+        idx[i, :n] = np.sort(rng.choice(n_k, n, replace=False))
+    return qi, ki, w, q, kv, idx
+
+
+def _sdpa_target(q_i, K, scale):
+    """Head-summed, L1-normalised attention probabilities via torch's attention with the
+    identity as values (each output row is then the probability row)."""
+    import torch.nn.functional as F
+    n = K.shape[0]
+    Q = torch.tensor(q_i)[None]                       # [1, H, D] as (batch, seq=H, dim)
+    Kt = torch.tensor(K)[None]
+    P = F.scaled_dot_product_attention(Q, Kt, torch.eye(n, dtype=torch.float64)[None],
+                                       scale=scale)[0]  # [H, n]
+    p = P.sum(0)
+    return (p / p.sum()).numpy()
+
+
+def test_indexer_kl_loss_matches_library_kl_and_attention():
+    """Loss value: scipy's relative entropy between the target (torch attention with identity
+    values, head-summed and normalised) and the softmax of the already pinned indexer score."""
+    from scipy.special import rel_entr, softmax
+    qi, ki, w, q, kv, idx = _kl_case(21)
+    scale = 0.41
+    losses, _, _, _ = O.indexer_kl_loss_grad(qi, ki, w, q, kv, idx, scale)
+    for i in range(qi.shape[0]):
+        sel = idx[i][idx[i] >= 0]
+        p = _sdpa_target(q[i], kv[sel], scale)
+        r = softmax(O.indexer_scores_row(qi[i], ki[sel], w[i]))
+        assert abs(losses[i] - float(np.sum(rel_entr(p, r)))) < 1e-12
+        assert losses[i] >= 0
+
+
+def test_indexer_kl_grads_match_autograd_and_finite_differences():
+    """Gradients of the summed loss with respect to the index weights, queries and keys: torch
+    autograd through its own KL divergence, and central differences of the oracle's loss.  The
+    case has a repeated key in one row (its two slots add into one key row)."""
+    import torch.nn.functional as F
+    qi, ki, w, q, kv, idx = _kl_case(22)
+    idx[3, :4] = [2, 2, 7, 11]
+    idx[3, 4:] = -1
+    scale, g = 0.33, 1.7
+    losses, dq, dw, dk = O.indexer_kl_loss_grad(qi, ki, w, q, kv, idx, scale, g)
+
+    QI = torch.tensor(qi, requires_grad=True)
+    KI = torch.tensor(ki, requires_grad=True)
+    W = torch.tensor(w, requires_grad=True)
+    total = 0
+    for i in range(qi.shape[0]):
+        sel = idx[i][idx[i] >= 0]
+        p = torch.tensor(_sdpa_target(q[i], kv[sel], scale))
+        K = KI.index_select(0, torch.tensor(sel))
+        I_ = (W[i][:, None] * torch.relu(QI[i] @ K.T)).sum(0)
+        total = total + F.kl_div(torch.log_softmax(I_, -1), p, reduction="sum")
+    assert abs(float(total.detach()) - float(losses.sum())) < 1e-12
+    (g * total).backward()
+    np.testing.assert_allclose(dq, QI.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dw, W.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, KI.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+    def f(qq, kk, ww):
+        return g * float(O.indexer_kl_loss_grad(qq, kk, ww, q, kv, idx, scale)[0].sum())
+
+    eps = 1e-6
+    for (i, j, c) in [(0, 0, 0), (3, 2, 5), (4, 1, 3)]:
+        a, b = qi.copy(), qi.copy()
+        a[i, j, c] += eps
+        b[i, j, c] -= eps
+        assert abs((f(a, ki, w) - f(b, ki, w)) / (2 * eps) - dq[i, j, c]) < 1e-6
+    for (i, j) in [(0, 1), (3, 0), (4, 2)]:
+        a, b = w.copy(), w.copy()
+        a[i, j] += eps
+        b[i, j] -= eps
+        assert abs((f(qi, ki, a) - f(qi, ki, b)) / (2 * eps) - dw[i, j]) < 1e-6
+    for (s, c) in [(2, 0), (7, 4), (11, 5)]:
+        a, b = ki.copy(), ki.copy()
+        a[s, c] += eps
+        b[s, c] -= eps
+        assert abs((f(qi, a, w) - f(qi, b, w)) / (2 * eps) - dk[s, c]) < 1e-6
+
+
+def test_indexer_kl_closed_forms():
+    """Zero attention query: uniform target, loss = logsumexp(I) - mean(I) - log n.  Zero index
+    query: uniform indexer distribution, loss = log n - entropy(target), and no gradient
+    reaches the index queries, weights or keys (every ReLU input is 0).  One selected key:
+    both distributions are the point mass, loss and gradients 0.  An empty row: all 0."""
+    from scipy.special import logsumexp
+    from scipy.stats import entropy
+    qi, ki, w, q, kv, idx = _kl_case(23)
+    scale = 0.5
+    losses, _, _, _ = O.indexer_kl_loss_grad(qi, ki, w, np.zeros_like(q), kv, idx, scale)
+    for i in range(qi.shape[0]):
+        sel = idx[i][idx[i] >= 0]
+        I_ = O.indexer_scores_row(qi[i], ki[sel], w[i])
+        assert abs(losses[i] - (logsumexp(I_) - I_.mean() - math.log(len(sel)))) < 1e-12
+    losses, dq, dw, dk = O.indexer_kl_loss_grad(np.zeros_like(qi), ki, w, q, kv, idx, scale)
+    for i in range(qi.shape[0]):
+        sel = idx[i][idx[i] >= 0]
+        p = _sdpa_target(q[i], kv[sel], scale)
+        assert abs(losses[i] - (math.log(len(sel)) - entropy(p))) < 1e-12
+    assert not dq.any() and not dw.any() and not dk.any()
+    idx1 = np.full_like(idx, -1)
+    idx1[:, 0] = 4
+    idx1[2, 0] = -1                    # an empty row
+    losses, dq, dw, dk = O.indexer_kl_loss_grad(qi, ki, w, q, kv, idx1, scale)
+    assert np.all(np.abs(losses) < 1e-15)
+    assert np.abs(dq).max() < 1e-15 and np.abs(dw).max() < 1e-15 and np.abs(dk).max() < 1e-15
+
+
+def test_indexer_kl_gradient_scale_and_slot_order():
+    """The incoming loss gradient scales every gradient and not the loss; permuting a row's
+    slots (holes included) changes nothing."""
+    qi, ki, w, q, kv, idx = _kl_case(24)
+    scale = 0.3
+    l1, dq1, dw1, dk1 = O.indexer_kl_loss_grad(qi, ki, w, q, kv, idx, scale, 1.0)
+    l2, dq2, dw2, dk2 = O.indexer_kl_loss_grad(qi, ki, w, q, kv, idx, scale, -2.5)
+    np.testing.assert_array_equal(l1, l2)
+    for a, b in [(dq1, dq2), (dw1, dw2), (dk1, dk2)]:
+        np.testing.assert_allclose(b, -2.5 * a, rtol=1e-13, atol=1e-15)
+    rng = np.random.default_rng(5)
+    perm = np.stack([rng.permutation(idx.shape[1]) for _ in range(idx.shape[0])])
+    idxp = np.take_along_axis(idx, perm, 1)
+    l3, dq3, dw3, dk3 = O.indexer_kl_loss_grad(qi, ki, w, q, kv, idxp, scale)
+    np.testing.assert_allclose(l3, l1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dq3, dq1, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dw3, dw1, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dk3, dk1, rtol=1e-10, atol=1e-13)
+
+
 # ---------------------------------------------------------------------------------- inputs
 
 
