@@ -193,6 +193,50 @@ dsa_status dsa_sparse_attn_bwd(const dsa_shape *shape, const void *q, const void
 dsa_status dsa_sparse_attn_bwd_workspace_bytes(const dsa_shape *shape, size_t *bytes);
 
 /*
+ * Indexer KL loss and its gradients (page "CANNTorchTitan: ...", section
+ * "SparseLightningIndexerGradKLLoss": the loss and gradient formulas that follow the indexer
+ * and Sparse Flash Attention top-k value formulas; the CP guide's indexer-loss boundary, which
+ * consumes softmax_max / softmax_sum).  For each row i, over its valid slots s (index
+ * k = topk_idx[i][s] in [0, n_k); a repeated key is one entry per slot):
+ *   P[h, s] = exp(softmax_scale * q[i,h,:] . kv[k,:] - softmax_max[i,h]) / softmax_sum[i,h]
+ *   p[s]    = sum_h P[h, s] / sum_{h,s'} P[h, s']           (target, L1-normalised)
+ *   S[j, s] = q_idx[i,j,:] . k_idx[k,:];   I[s] = sum_j w_idx[i,j] * ReLU(S[j, s])
+ *   loss_rows[i] = sum_s p[s] * (log p[s] - log softmax(I)[s])  (terms with p[s] = 0 are 0)
+ *   dI[s]   = loss_grad * (softmax(I)[s] - p[s])
+ *   dw_idx[i, j]  = sum_s dI[s] * ReLU(S[j, s])
+ *   dS[j, s] = w_idx[i,j] * dI[s] if S[j, s] > 0 else 0
+ *   dq_idx[i, j, :] = sum_s dS[j, s] * k_idx[k, :];   dk_idx[k, :] += sum_j dS[j, s] * q_idx[i, j, :]
+ * The target carries no gradient; loss_grad is the gradient arriving at each row's term (1 for
+ * the plain sum).  A row with no valid slot gets loss 0 and zero dq_idx / dw_idx.
+ *   q_idx [n_q, 64, 128] bf16, k_idx [n_k, 128] bf16, w_idx [n_q, 64] fp32,
+ *   q [n_q, 128, 576] bf16, kv [n_k, 576] bf16, topk_idx [n_q, topk] int32,
+ *   softmax_max / softmax_sum [n_q, 128] fp32 as written by the forward for these indices;
+ *   loss_rows [n_q] fp32 (written); loss [1] fp32 = sum of loss_rows in a fixed order (written;
+ *   may be NULL); dq_idx [n_q, 64, 128] bf16 and dw_idx [n_q, 64] fp32 (written);
+ *   dk_idx [n_k, 128] fp32 is ADDED to (the caller zeroes it), each key's sum in an order
+ *   that is not fixed.  Every row 0..n_q-1 is computed (segments are not used).
+ * Built for bf16 index tensors with (h_idx, d_idx, h, d_qk) = (64, 128, 128, 576) and
+ * 1 <= topk <= 2048 (else DSA_ERR_UNSUPPORTED); d_v is not used.  q_idx, k_idx, w_idx, q, kv,
+ * the statistics, dk_idx and the workspace must be 16-byte aligned, dq_idx 8-byte aligned
+ * (DSA_ERR_INVALID_ARG).  The workspace holds per-key counters and, for a chunk of rows, the
+ * bf16 key gradient of every slot and the per-key entry lists; rows are processed in chunks
+ * of as many rows as it fits (DSA_ERR_WORKSPACE if not even one).  Calls that update the same
+ * dk_idx must not overlap.  Products in bf16 MFMA with fp32 accumulation; softmax, logarithms
+ * and the loss in fp32.
+ */
+dsa_status dsa_indexer_kl_loss_grad(const dsa_shape *shape, const void *q_idx, const void *k_idx,
+                                    const float *w_idx, const void *q, const void *kv,
+                                    const int32_t *topk_idx, const float *softmax_max,
+                                    const float *softmax_sum, float loss_grad, float *loss_rows,
+                                    float *loss, void *dq_idx, float *dw_idx, float *dk_idx,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace size for dsa_indexer_kl_loss_grad that processes up to 2048 rows per pass:
+ * (256 * topk_p + 4 * topk) bytes per row, topk_p = topk rounded up to a multiple of 96, plus
+ * 4 * (3 * n_k + 1) bytes rounded up to 256 and 2 KiB of alignment slack. */
+dsa_status dsa_indexer_kl_workspace_bytes(const dsa_shape *shape, size_t *bytes);
+
+/*
  * Per-row (per-token) fp8 quantization for the fp8 indexer: for each of `rows` rows of
  * `cols` bf16 values, scale = amax(|row|) / 448 (1.0 for an all-zero row) and
  * code = e4m3fn(round-to-nearest-even(x / scale)), saturating at +-448; scale and x / scale

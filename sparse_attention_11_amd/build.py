@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 
-SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "attention.hip", "attention_bwd.hip", "quant.hip"]
+SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "attention.hip", "attention_bwd.hip", "indexer_kl.hip",
+           "quant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -22,6 +22,8 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int h, int d_qk, int d_v, int n
                               hipStream_t s);
 hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v, hipStream_t s);
 hipError_t launch_quant_fp8_rows(const QuantArgs& a, hipStream_t s);
+hipError_t launch_indexer_kl(const IdxKlArgs& a, const KeyListArgs& kl, hipStream_t s);
+hipError_t launch_loss_total(const float* loss, int n, float* out, hipStream_t s);
 }  // namespace dsa
 
 namespace {
@@ -267,6 +269,34 @@ dsa_status check_bwd_dims(const dsa_shape* s) {
   return DSA_OK;
 }
 
+// Indexer-loss workspace.  Per call: the per-key counters (as for the attention backward).
+// Per row of a chunk: the bf16 index-key gradient of every slot (slots padded to a multiple of
+// 96) and one list entry per slot.
+constexpr int kKlMaxTopk = 2048;   // the per-row target / indexer arrays live in LDS
+size_t kl_topkp(const dsa_shape* s) { return ((size_t)s->topk + 95) / 96 * 96; }
+size_t kl_row_bytes(const dsa_shape* s) { return kl_topkp(s) * 128 * 2 + (size_t)s->topk * 4; }
+size_t kl_fixed_bytes(const dsa_shape* s) {
+  return align_up(((size_t)3 * s->n_k + 1) * 4) + 8 * kAlign;
+}
+
+dsa_status check_kl_dims(const dsa_shape* s) {
+  if (s->idx_dtype != DSA_IDX_BF16)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer loss is built for bf16 index tensors only");
+  if (!(s->h_idx == 64 && s->d_idx == 128 && s->h == 128 && s->d_qk == 576))
+    return fail(DSA_ERR_UNSUPPORTED, "indexer loss built for (h_idx, d_idx, h, d_qk) = "
+                "(64, 128, 128, 576) only (got %d, %d, %d, %d)", s->h_idx, s->d_idx, s->h, s->d_qk);
+  if (s->topk < 1 || s->topk > kKlMaxTopk)
+    return fail(s->topk < 1 ? DSA_ERR_INVALID_ARG : DSA_ERR_UNSUPPORTED,
+                "indexer loss needs 1 <= topk <= %d (got %d)", kKlMaxTopk, s->topk);
+  if (!std::isfinite(s->softmax_scale))
+    return fail(DSA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if ((int64_t)s->n_k * s->d_qk * 2 > (int64_t)UINT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "latent KV of %d rows exceeds 4 GiB", s->n_k);
+  return DSA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -447,6 +477,106 @@ dsa_status dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void
     a.xcd_remap = rows % 8 == 0;
     hipError_t e = dsa::launch_sparse_attn_bwd(a, h, dqk, dv, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  }
+  return ok();
+}
+
+dsa_status dsa_indexer_kl_workspace_bytes(const dsa_shape* shape, size_t* bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (!shape) return fail(DSA_ERR_INVALID_ARG, "shape is NULL");
+  if (shape->n_q < 0 || shape->n_k < 0) return fail(DSA_ERR_INVALID_ARG, "negative n_q or n_k");
+  dsa_status st = check_kl_dims(shape);
+  if (st != DSA_OK) return st;
+  *bytes = kl_fixed_bytes(shape) + kl_row_bytes(shape) * (size_t)std::min(shape->n_q, kBwdChunkRows);
+  return ok();
+}
+
+dsa_status dsa_indexer_kl_loss_grad(const dsa_shape* shape, const void* q_idx, const void* k_idx,
+                                    const float* w_idx, const void* q, const void* kv,
+                                    const int32_t* topk_idx, const float* softmax_max,
+                                    const float* softmax_sum, float loss_grad, float* loss_rows,
+                                    float* loss, void* dq_idx, float* dw_idx, float* dk_idx,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape) return fail(DSA_ERR_INVALID_ARG, "shape is NULL");
+  if (shape->n_q < 0 || shape->n_k < 0) return fail(DSA_ERR_INVALID_ARG, "negative n_q or n_k");
+  dsa_status st = check_kl_dims(shape);
+  if (st != DSA_OK) return st;
+  if (!std::isfinite(loss_grad)) return fail(DSA_ERR_INVALID_ARG, "loss_grad is not finite");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (shape->n_q == 0) {
+    if (loss) {   // an empty sum (a kernel, so the call stays capturable in a graph)
+      hipError_t e = dsa::launch_loss_total(loss_rows, 0, loss, hs);
+      if (e != hipSuccess) return hip_fail(e, "loss sum launch");
+    }
+    return ok();
+  }
+  if (!q_idx || !k_idx || !w_idx || !q || !kv || !topk_idx || !softmax_max || !softmax_sum ||
+      !loss_rows || !dq_idx || !dw_idx || !dk_idx)
+    return fail(DSA_ERR_INVALID_ARG, "indexer loss tensor is NULL");
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(w_idx, 16) || !aligned(q, 16) ||
+      !aligned(kv, 16) || !aligned(softmax_max, 16) || !aligned(softmax_sum, 16) ||
+      !aligned(dk_idx, 16) || !aligned(workspace, 16) || !aligned(dq_idx, 8) ||
+      !aligned(topk_idx, 4) || !aligned(loss_rows, 4) || !aligned(dw_idx, 4))
+    return fail(DSA_ERR_INVALID_ARG, "indexer loss tensors, dk_idx and workspace must be "
+                "16-byte aligned (dq_idx 8-byte)");
+  const size_t per_row = kl_row_bytes(shape);
+  const size_t fixed = kl_fixed_bytes(shape);
+  const size_t fit = workspace && workspace_bytes > fixed ? (workspace_bytes - fixed) / per_row : 0;
+  if (fit == 0)
+    return fail(DSA_ERR_WORKSPACE, "workspace of at least %zu bytes (one row) needed, %zu given",
+                fixed + per_row, workspace ? workspace_bytes : (size_t)0);
+  const size_t max_rows = (size_t)INT32_MAX / (size_t)shape->topk;
+  const int chunk = (int)std::min({fit, (size_t)shape->n_q, max_rows});
+  const int topk = shape->topk;
+  const size_t topkp = kl_topkp(shape);
+  char* w = static_cast<char*>(workspace);
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    char* p = w + at;
+    at = align_up(at + bytes);
+    return p;
+  };
+  dsa::KeyListArgs kl = {};
+  kl.cnt = reinterpret_cast<int*>(take((size_t)shape->n_k * 4));
+  kl.off = reinterpret_cast<int*>(take(((size_t)shape->n_k + 1) * 4));
+  kl.cur = reinterpret_cast<int*>(take((size_t)shape->n_k * 4));
+  uint16_t* ws_c = reinterpret_cast<uint16_t*>(take((size_t)chunk * topkp * 128 * 2));
+  kl.list = reinterpret_cast<int*>(take((size_t)chunk * topk * 4));
+  if (at > workspace_bytes)
+    return fail(DSA_ERR_WORKSPACE, "internal workspace layout exceeds %zu bytes", workspace_bytes);
+  kl.n_k = shape->n_k;
+  kl.topk = topk;
+  dsa::IdxKlArgs a = {};
+  a.k_idx = static_cast<const uint16_t*>(k_idx);
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.ws_c = ws_c;
+  a.dk = dk_idx;
+  a.list = kl.list;
+  a.off = kl.off;
+  a.n_k = shape->n_k;
+  a.topk = topk;
+  a.topkp = (int)topkp;
+  a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
+  a.loss_grad = loss_grad;
+  for (int r0 = 0; r0 < shape->n_q; r0 += chunk) {
+    const int rows = std::min(chunk, shape->n_q - r0);
+    a.rows = kl.rows = rows;
+    a.q_idx = static_cast<const uint16_t*>(q_idx) + (size_t)r0 * 64 * 128;
+    a.w = w_idx + (size_t)r0 * 64;
+    a.q = static_cast<const uint16_t*>(q) + (size_t)r0 * 128 * 576;
+    a.idx = kl.idx = topk_idx + (size_t)r0 * topk;
+    a.smax = softmax_max + (size_t)r0 * 128;
+    a.ssum = softmax_sum + (size_t)r0 * 128;
+    a.loss = loss_rows + r0;
+    a.dq_idx = static_cast<uint16_t*>(dq_idx) + (size_t)r0 * 64 * 128;
+    a.dw = dw_idx + (size_t)r0 * 64;
+    a.xcd_remap = rows % 8 == 0;
+    hipError_t e = dsa::launch_indexer_kl(a, kl, hs);
+    if (e != hipSuccess) return hip_fail(e, "indexer loss launch");
+  }
+  if (loss) {
+    hipError_t e = dsa::launch_loss_total(loss_rows, shape->n_q, loss, hs);
+    if (e != hipSuccess) return hip_fail(e, "loss sum launch");
   }
   return ok();
 }

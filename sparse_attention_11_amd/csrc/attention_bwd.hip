@@ -39,54 +39,6 @@ constexpr float kLog2e = 1.44269504088896340736f;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-// Number of 32-slot tiles up to the row's last valid index (block-wide; one barrier).
-template <int H, int DQK, int DV>
-__device__ __forceinline__ int row_tiles(const AttnBwdArgs& a, const RowCtx& c, int* s_last) {
-  using C = AttnCfg<H, DQK, DV>;
-  int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
-  if (c.lane == 0) s_last[c.wave] = last;
-  __syncthreads();
-  last = -1;
-#pragma unroll
-  for (int w = 0; w < C::NW; ++w) last = max(last, s_last[w]);
-  return (last + C::NK) / C::NK;
-}
-
-__device__ __forceinline__ RowCtx make_ctx(const AttnBwdArgs& a, int row) {
-  RowCtx c;
-  c.row = row;
-  c.tid = threadIdx.x;
-  c.lane = c.tid & 63;
-  c.wave = c.tid >> 6;
-  c.wave_u = __builtin_amdgcn_readfirstlane(c.wave);
-  c.hl = c.lane & 31;
-  c.g = c.lane >> 5;
-  c.head = c.wave * 32 + c.hl;
-  c.idx_row = a.idx + (size_t)row * a.topk;
-  c.flags = nullptr;
-  c.vm = nullptr;
-  c.qlds = nullptr;
-  return c;
-}
-
-__device__ __forceinline__ int block_row(const AttnBwdArgs& a) {
-  int blk = blockIdx.x;
-  if (a.xcd_remap) blk = (blk & 7) * ((int)gridDim.x >> 3) + (blk >> 3);
-  return blk;
-}
-
-// Transposed fragment of a row-major LDS matrix with `cols` columns: within each 16-lane
-// group, lane i supplies row r0 + i/4 (r0 + 4 + i/4 for the second half), columns
-// c0 + 4 (i % 4) .. +3, and receives column c0 + i of rows r0 .. r0 + 7.
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* m, int cols, int r0, int c0, int i) {
-  const lds_cptr_t b = (lds_cptr_t)m + (r0 + (i >> 2)) * cols + c0 + (i & 3) * 4;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)b);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(b + 4 * cols));
-  return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-}
-
 // ---------------------------------------------------------------------------------------
 // k_attn_bwd_p: P and softmax_scale * dS per (row, slot, head)
 // ---------------------------------------------------------------------------------------
@@ -591,12 +543,12 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
 }
 
 // Zero the per-key counters.
-__global__ __launch_bounds__(256) void k_bwd_zero(AttnBwdArgs a) {
+__global__ __launch_bounds__(256) void k_keys_zero(KeyListArgs a) {
   for (int k = blockIdx.x * 256 + threadIdx.x; k < a.n_k; k += gridDim.x * 256) a.cnt[k] = 0;
 }
 
 // Count the valid (row, slot) entries of the chunk per key.
-__global__ __launch_bounds__(256) void k_bwd_count(AttnBwdArgs a) {
+__global__ __launch_bounds__(256) void k_keys_count(KeyListArgs a) {
   const long long total = (long long)a.rows * a.topk;
   for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total;
        e += (long long)gridDim.x * 256) {
@@ -606,7 +558,7 @@ __global__ __launch_bounds__(256) void k_bwd_count(AttnBwdArgs a) {
 }
 
 // off = exclusive prefix sum of cnt (off[n_k] = total), cur = off.  One workgroup.
-__global__ __launch_bounds__(1024) void k_bwd_scan(AttnBwdArgs a) {
+__global__ __launch_bounds__(1024) void k_keys_scan(KeyListArgs a) {
   __shared__ unsigned scratch[16];
   unsigned base = 0;
   for (int k0 = 0; k0 < a.n_k; k0 += 1024) {
@@ -624,7 +576,7 @@ __global__ __launch_bounds__(1024) void k_bwd_scan(AttnBwdArgs a) {
 }
 
 // list[cur[k]++] = row * topk + slot for every valid entry.
-__global__ __launch_bounds__(256) void k_bwd_scatter(AttnBwdArgs a) {
+__global__ __launch_bounds__(256) void k_keys_scatter(KeyListArgs a) {
   const long long total = (long long)a.rows * a.topk;
   for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total;
        e += (long long)gridDim.x * 256) {
@@ -689,17 +641,24 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(AttnBwdArgs a) {
 
 }  // namespace
 
+hipError_t launch_key_lists(const KeyListArgs& a, hipStream_t s) {
+  const long long entries = (long long)a.rows * a.topk;
+  if (entries == 0) return hipSuccess;
+  const int eg = (int)std::min<long long>((entries + 255) / 256, 8192);
+  k_keys_zero<<<std::min((a.n_k + 255) / 256, 1024), 256, 0, s>>>(a);
+  k_keys_count<<<eg, 256, 0, s>>>(a);
+  k_keys_scan<<<1, 1024, 0, s>>>(a);
+  k_keys_scatter<<<eg, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (!(h == 128 && d_qk == 576 && d_v == 512)) return hipErrorInvalidValue;
   const bool al8 = a.topk >= 8 && a.topk % 8 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 31) == 0;
-  const long long entries = (long long)a.rows * a.topk;
-  const int eg = (int)std::min<long long>((entries + 255) / 256, 8192);
-  // key lists of the chunk (only the indices are needed)
-  k_bwd_zero<<<std::min((a.n_k + 255) / 256, 1024), 256, 0, s>>>(a);
-  k_bwd_count<<<eg, 256, 0, s>>>(a);
-  k_bwd_scan<<<1, 1024, 0, s>>>(a);
-  k_bwd_scatter<<<eg, 256, 0, s>>>(a);
+  KeyListArgs kl = {a.idx, a.list, a.cnt, a.off, a.cur, a.rows, a.n_k, a.topk};
+  hipError_t e = launch_key_lists(kl, s);
+  if (e != hipSuccess) return e;
   if (al8) {
     k_attn_bwd_p<128, 576, 512, true><<<a.rows, 256, 0, s>>>(a);
     k_attn_bwd_dq<128, 576, 512, true><<<a.rows, 256, 0, s>>>(a);

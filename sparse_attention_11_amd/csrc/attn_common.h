@@ -273,6 +273,60 @@ __device__ __forceinline__ int thread_last_valid(const int32_t* idx_row, int top
   return last;
 }
 
+// Per-row context of a backward-style kernel (one workgroup per row of a chunk; the argument
+// struct has idx, topk and n_k).
+template <class Args>
+__device__ __forceinline__ RowCtx make_ctx(const Args& a, int row) {
+  RowCtx c;
+  c.row = row;
+  c.tid = threadIdx.x;
+  c.lane = c.tid & 63;
+  c.wave = c.tid >> 6;
+  c.wave_u = __builtin_amdgcn_readfirstlane(c.wave);
+  c.hl = c.lane & 31;
+  c.g = c.lane >> 5;
+  c.head = c.wave * 32 + c.hl;
+  c.idx_row = a.idx + (size_t)row * a.topk;
+  c.flags = nullptr;
+  c.vm = nullptr;
+  c.qlds = nullptr;
+  return c;
+}
+
+// Row of this workgroup; with xcd_remap (grid a multiple of 8) consecutive rows go to one
+// XCD (workgroups are dealt to the 8 XCDs round-robin), so rows that share keys share an L2.
+template <class Args>
+__device__ __forceinline__ int block_row(const Args& a) {
+  int blk = blockIdx.x;
+  if (a.xcd_remap) blk = (blk & 7) * ((int)gridDim.x >> 3) + (blk >> 3);
+  return blk;
+}
+
+// Number of 32-slot tiles up to the row's last valid index (block-wide; one barrier).
+template <int H, int DQK, int DV, class Args>
+__device__ __forceinline__ int row_tiles(const Args& a, const RowCtx& c, int* s_last) {
+  using C = AttnCfg<H, DQK, DV>;
+  int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if (c.lane == 0) s_last[c.wave] = last;
+  __syncthreads();
+  last = -1;
+#pragma unroll
+  for (int w = 0; w < C::NW; ++w) last = max(last, s_last[w]);
+  return (last + C::NK) / C::NK;
+}
+
+// Transposed fragment of a row-major LDS matrix with `cols` columns: within each 16-lane
+// group, lane i supplies row r0 + i/4 (r0 + 4 + i/4 for the second half), columns
+// c0 + 4 (i % 4) .. +3, and receives column c0 + i of rows r0 .. r0 + 7.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* m, int cols, int r0, int c0, int i) {
+  const lds_cptr_t b = (lds_cptr_t)m + (r0 + (i >> 2)) * cols + c0 + (i & 3) * 4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)b);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(b + 4 * cols));
+  return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
 // Copy `bytes` (a multiple of 1024) from global `src` to LDS byte address `lds` by LDS DMA,
 // one 1 KB piece per wave instruction, pieces spread over the block's NW waves.  Completion
 // is not tracked by the compiler: wait with vmcnt before reading.

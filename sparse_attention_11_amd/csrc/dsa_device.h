@@ -101,6 +101,44 @@ struct AttnBwdArgs {
   float scale, scale_log2;
 };
 
+// Indexer KL loss and its gradients over one chunk of query rows (pointers offset to the chunk).
+struct IdxKlArgs {
+  const uint16_t* q_idx;  // [rows, 64, 128] bf16 index queries
+  const uint16_t* k_idx;  // [n_k, 128] bf16 index keys
+  const float* w;         // [rows, 64] index weights
+  const uint16_t* q;      // [rows, 128, 576] bf16 attention queries
+  const uint16_t* kv;     // [n_k, 576] bf16 latent rows
+  const int32_t* idx;     // [rows, topk]
+  const float* smax;      // [rows, 128] forward softmax_max
+  const float* ssum;      // [rows, 128] forward softmax_sum
+  float* loss;            // [rows] per-row KL terms
+  uint16_t* dq_idx;       // [rows, 64, 128] bf16
+  float* dw;              // [rows, 64]
+  uint16_t* ws_c;         // [rows, topkp, 128] bf16 per-(row, slot) index-key gradients
+  float* dk;              // [n_k, 128] fp32, accumulated
+  const int* list;        // key lists of the chunk (see KeyListArgs)
+  const int* off;
+  int rows, n_k, topk;
+  int topkp;              // workspace slots per row: topk rounded up to 96
+  int xcd_remap;
+  float scale_log2;       // softmax_scale * log2(e)
+  float loss_grad;        // gradient arriving at each row's loss term
+};
+
+// Per-key entry lists of a chunk of top-k rows: every valid (row, slot) entry, as
+// row * topk + slot, grouped by key (off[k] .. off[k + 1] in list).
+struct KeyListArgs {
+  const int32_t* idx;     // [rows, topk]
+  int* list;              // [rows * topk]
+  int* cnt;               // [n_k]
+  int* off;               // [n_k + 1]
+  int* cur;               // [n_k]
+  int rows, n_k, topk;
+};
+
+// Builds the lists on stream s (counting sort; integer atomics on the counters only).
+hipError_t launch_key_lists(const KeyListArgs& a, hipStream_t s);
+
 struct QuantArgs {
   const uint16_t* x;
   uint8_t* y;

@@ -1,0 +1,548 @@
+// Indexer KL loss and its gradients on gfx950 MFMA.
+//
+// Page "CANNTorchTitan: DeepSeek-V3.2 32k长序列预训练昇腾优化实践", section
+// "SparseLightningIndexerGradKLLoss": for each query token the target distribution over its
+// selected keys is the Sparse Flash Attention probability summed over the query heads and
+// normalised to unit L1 norm; the indexer's distribution is the softmax of its top-k values
+// I = sum_j w_j ReLU(q_idx_j . k_idx); the loss is the KL divergence of the indexer's
+// distribution from the target, dI = softmax(I) - p, and the gradients of the index weights,
+// queries and keys follow through the ReLU, the key gradients being scatter-added into the
+// selected rows.  The attention probabilities are recomputed from the forward's softmax
+// statistics rather than stored.
+//
+// One workgroup per query row, four waves, 32 selected keys per tile, two passes over the
+// row's tiles:
+//   * Pass 1 gathers each tile's latent rows (576 wide) and index-key rows (128 wide) into
+//     LDS rings by LDS DMA.  The logits C[head, key] = Q K^T run on 32x32x16 MFMA with the
+//     wave's 32 heads x 576 dims of Q held in VGPRs (nothing else of that size is live, so Q
+//     needs no LDS staging here) in two accumulator chains; each lane owns one key and 16
+//     heads, so the head sum of the probabilities is lane-local up to one lane swap.  The
+//     same tile gives S[index head, key] on 16x16x32 MFMA (16 index heads per wave) and the
+//     weighted ReLU head sum.  Per-wave partial sums meet in LDS and are added in a fixed
+//     order into two per-row arrays (target mass, I), so the result is deterministic.
+//   * Between the passes the block forms softmax(I), the normalised target, the row's KL term
+//     and dI (stored over the target array).
+//   * Pass 2 gathers the index-key tiles again and recomputes S^T[key, index head].  dS, dW
+//     and dq_idx^T += K^T dS^T stay in registers (K^T read with the transposing LDS read; the
+//     MFMA's K order is the accumulator's key order, so dS feeds it without a shuffle).  dS
+//     is shared through LDS and each slot's key gradient dS^T q_idx is formed by the wave
+//     that owns 32 of its 128 dims and written as bf16 per (row, slot).
+//   * The per-slot key gradients are then summed per key (the chunk's entries grouped by key,
+//     16 lanes per key) and added to dk_idx: no float atomics.
+#include <algorithm>
+
+#include "attn_common.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kH = 128, kDQK = 576, kDV = 512;   // attention heads, latent row, value width
+constexpr int kG = 64, kDI = 128;                 // index heads, index head width
+using AC = AttnCfg<kH, kDQK, kDV>;
+using TI = TileIdx<kH, kDQK, kDV>;
+constexpr int NK = AC::NK;             // keys per tile (32)
+constexpr int kKs = kDQK / 16;         // K steps of the logits product
+constexpr int kMaxSlots = 2112;        // 66 tiles: topk <= 2048, rounded up to rings of 3 tiles
+constexpr int KT = NK * kDI;           // elements of an index-key tile (8 KB)
+constexpr int DSR = NK + 4;            // LDS row stride (elements) of the shared dS tile
+constexpr int GK = 2;                  // index-key gather instructions per wave and tile
+constexpr int NST = 4;                 // key-gradient stores per wave and tile
+constexpr float kLog2e = 1.44269504088896340736f;
+static_assert(AC::RPW == 8 && AC::FLAT, "tile split of the gathers");
+
+typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// x + x of the lane 16 (32) apart, in every lane (one lane swap between row pairs).
+__device__ __forceinline__ float pair16_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(p[0]) + __int_as_float(p[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(p[0]) + __int_as_float(p[1]);
+}
+
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+  return (unsigned)f32_to_bf16(lo) | ((unsigned)f32_to_bf16(hi) << 16);
+}
+
+// Block-wide sum / max over the 4 waves (two barriers).
+__device__ __forceinline__ float block_sum(float x, float* sb) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  if ((threadIdx.x & 63) == 0) sb[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const float r = (sb[0] + sb[1]) + (sb[2] + sb[3]);
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ float block_max(float x, float* sb) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  if ((threadIdx.x & 63) == 0) sb[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3]));
+  __syncthreads();
+  return r;
+}
+
+// The wave's 8 index-key rows of a tile (tile rows 8 w .. 8 w + 7) into an LDS tile of 256-B
+// rows by LDS DMA.  Instruction i copies rows 8 w + 4 i .. +3: lane L fills physical chunk
+// L % 16 of row 8 w + 4 i + L / 16, which holds logical chunk (L % 16) ^ (row % 16).  The XOR
+// makes 16 rows x one logical chunk (the MFMA operand reads) hit 16 different bank groups.
+// Empty slots copy row 0 (masked later).
+__device__ __forceinline__ void gather_ktile(const IdxKlArgs& a, const RowCtx& c, const TI& ti,
+                                             unsigned lds_tile) {
+  const int sub = c.lane >> 4, ch = c.lane & 15;
+  const bool b0 = c.lane & 16, b1 = c.lane & 32;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    // two selects on lane bits (an index expression would send the indices through scratch)
+    const int lo = b0 ? ti.v[4 * i + 1] : ti.v[4 * i];
+    const int hi = b0 ? ti.v[4 * i + 3] : ti.v[4 * i + 2];
+    int id = b1 ? hi : lo;
+    id = (unsigned)id < (unsigned)a.n_k ? id : 0;
+    const int r = c.wave * 8 + 4 * i + sub;
+    const unsigned voff = (unsigned)id * (kDI * 2u) + (unsigned)((ch ^ (r & 15)) * 16);
+    const unsigned m0v = lds_tile + (unsigned)((c.wave_u * 8 + 4 * i) * kDI * 2);
+    const uint16_t* base = a.k_idx;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
+  }
+}
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+template <bool AL8>
+__global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t kv0[AC::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv1[AC::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv2[AC::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kt0[KT];
+  __shared__ __attribute__((aligned(16))) uint16_t kt1[KT];
+  __shared__ __attribute__((aligned(16))) uint16_t kt2[KT];
+  __shared__ __attribute__((aligned(16))) float s_p[kMaxSlots];   // target mass, then dI
+  __shared__ __attribute__((aligned(16))) float s_i[kMaxSlots];   // indexer values I
+  __shared__ float s_red[2][2][4][NK];   // [tile parity][mass, I][wave][key]
+  __shared__ unsigned vmring[3 * 4];
+  __shared__ int s_last[4];
+  __shared__ float s_blk[4];
+
+  RowCtx c = make_ctx(a, block_row(a));
+  c.buf[0] = kv0;
+  c.buf[1] = kv1;
+  c.buf[2] = kv2;
+  c.vm = vmring;
+  c.ntiles = row_tiles<kH, kDQK, kDV>(a, c, s_last);
+  const int row = c.row;
+  if (c.ntiles == 0) {   // nothing selected: loss 0, no gradient (no key-list entries either)
+    uint4* dq = reinterpret_cast<uint4*>(a.dq_idx + (size_t)row * kG * kDI);
+    for (int j = c.tid; j < kG * kDI / 8; j += 256) dq[j] = make_uint4(0, 0, 0, 0);
+    if (c.tid < kG) a.dw[(size_t)row * kG + c.tid] = 0.f;
+    if (c.tid == 0) a.loss[row] = 0.f;
+    return;
+  }
+  const uint16_t* kts[3] = {kt0, kt1, kt2};
+  const int i16 = c.lane & 15, G = c.lane >> 4;
+
+  // ---- row operands
+  bf16x8 qf[kKs];   // Q of head wave*32 + hl, dims 16 ks + 8 g .. +7 (A of the logits)
+  {
+    const uint16_t* qp = a.q + ((size_t)row * kH + c.head) * kDQK + c.g * 8;
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 16));
+  }
+  // softmax statistics of the lane's 16 heads: accumulator register r holds head
+  // wave*32 + (r/4)*8 + 4 g + r%4
+  float msub[16], invl[16];
+  {
+    const size_t hb = (size_t)row * kH + c.wave * 32 + 4 * c.g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 mx = *reinterpret_cast<const float4*>(a.smax + hb + 8 * j);
+      const float4 sm = *reinterpret_cast<const float4*>(a.ssum + hb + 8 * j);
+      const float mv[4] = {mx.x, mx.y, mx.z, mx.w}, sv[4] = {sm.x, sm.y, sm.z, sm.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        msub[4 * j + u] = mv[u] == kNegInf ? 0.f : mv[u] * kLog2e;   // scaled log2 units
+        invl[4 * j + u] = sv[u] > 0.f ? 1.f / sv[u] : 0.f;
+      }
+    }
+  }
+  bf16x8 qi[4];   // index query of head 16 wave + i16, dims 32 s + 8 G .. +7
+  {
+    const uint16_t* p = a.q_idx + ((size_t)row * kG + 16 * c.wave + i16) * kDI + 8 * G;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qi[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p + 32 * s));
+  }
+  // weights of index heads 16 wave + 4 G + r (the S accumulator rows of this lane)
+  const float4 wq = *reinterpret_cast<const float4*>(a.w + (size_t)row * kG + 16 * c.wave + 4 * G);
+  // index-key tile: row i16 (and i16 + 16), logical chunk 4 s + G
+  int koff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) koff[s] = i16 * kDI + (((4 * s + G) ^ i16) * 8);
+
+  unsigned loff[AC::NI], wb[3], kb[3];
+#pragma unroll
+  for (int i = 0; i < AC::NI; ++i) loff[i] = flat_lane_offset<kH, kDQK, kDV>(c, i);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    wb[k] = lds_addr(c.buf[k]) + c.wave_u * (AC::RPW * AC::ROWE * 2);
+    kb[k] = lds_addr(kts[k]);
+  }
+  auto gather = [&](const TI& ti, int k) {
+    gather_tile_flat<kH, kDQK, kDV>(a, c, ti, loff, wb[k]);
+    gather_ktile(a, c, ti, kb[k]);
+  };
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // row loads done: the ring's counts are exact
+
+  // ---- pass 1: target mass and indexer values per slot
+  const int ntiles = (c.ntiles + 2) / 3 * 3;
+  {
+    const TI i0 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 0);
+    const TI i1 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 1);
+    TI i2 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 2);
+    gather(i0, 0);
+    gather(i1, 1);
+    if (c.lane == 0) {
+      c.vm[0 * 4 + c.wave] = tile_bits<kH, kDQK, kDV>(a, i0);
+      c.vm[1 * 4 + c.wave] = tile_bits<kH, kDQK, kDV>(a, i1);
+    }
+    wait_vm_barrier<0>();
+
+    auto step = [&](int t, int slot, int ahead2, TI& nxt2) {
+      const TI i3 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, t + 3);
+      gather(nxt2, ahead2);
+      if (c.lane == 0) c.vm[ahead2 * 4 + c.wave] = tile_bits<kH, kDQK, kDV>(a, nxt2);
+      // the previous tile's per-wave partials -> row arrays (one wave per tile, in turn)
+      if (t > 0 && c.wave_u == (t & 3) && c.lane < NK) {
+        const int pb = (t - 1) & 1;
+        const float m = (s_red[pb][0][0][c.lane] + s_red[pb][0][1][c.lane]) +
+                        (s_red[pb][0][2][c.lane] + s_red[pb][0][3][c.lane]);
+        const float v = (s_red[pb][1][0][c.lane] + s_red[pb][1][1][c.lane]) +
+                        (s_red[pb][1][2][c.lane] + s_red[pb][1][3][c.lane]);
+        s_p[(t - 1) * NK + c.lane] = m;
+        s_i[(t - 1) * NK + c.lane] = v;
+      }
+      unsigned vmask = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) vmask |= c.vm[slot * 4 + w] << (w * 8);
+
+      // logits C[head, key]: A = Q (VGPRs), B = latent row hl of the tile, chunk 2 ks + g
+      // (physical chunk (2 ks + g) ^ swz(hl)); even / odd K steps in two chains
+      f32x16 s0 = (f32x16){}, s1 = (f32x16){};
+      {
+        const lds_cptr_t lt = (lds_cptr_t)c.buf[slot];
+        const int sw = swz(c.hl);
+        lds_cptr_t bb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bb[j] = lt + c.hl * AC::ROWE + (((2 * j + c.g) ^ sw) - 2 * j) * 8;
+        auto at = [&](int ks) { return bb[ks & 3] + ks * 16; };
+        constexpr int QG = 4, NG = kKs / QG;
+        static_assert(kKs % QG == 0, "prefetch groups");
+        bf16x8 f[2][QG];
+#pragma unroll
+        for (int u = 0; u < QG; ++u) f[0][u] = *(lds_cb8_t)(at(u));
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          const int cur = gi & 1;
+          if (gi + 1 < NG) {
+#pragma unroll
+            for (int u = 0; u < QG; ++u) f[cur ^ 1][u] = *(lds_cb8_t)(at((gi + 1) * QG + u));
+          }
+#pragma unroll
+          for (int u = 0; u < QG; u += 2) {
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[gi * QG + u], f[cur][u], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[gi * QG + u + 1], f[cur][u + 1], s1, 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // probability mass of key hl over the lane's heads, then over the wave's 32 heads
+      float pm = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pm += __builtin_amdgcn_exp2f(fmaf(s0[r] + s1[r], a.scale_log2, -msub[r])) * invl[r];
+      pm = pair32_sum(pm);
+      if (!((vmask >> c.hl) & 1u)) pm = 0.f;
+
+      // indexer S[index head, key]: A = index-query rows, B = index-key rows i16, 16 + i16
+      f32x4 x0 = (f32x4){}, x1 = (f32x4){};
+      {
+        const lds_cptr_t kt = (lds_cptr_t)kts[slot];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 b0 = *(lds_cb8_t)(kt + koff[s]);
+          const bf16x8 b1 = *(lds_cb8_t)(kt + koff[s] + 16 * kDI);
+          x0 = mfma16(qi[s], b0, x0);
+          x1 = mfma16(qi[s], b1, x1);
+        }
+      }
+      // lane: key i16 (x0) / 16 + i16 (x1), index heads 16 wave + 4 G + r
+      float v0 = wq.x * fmaxf(x0[0], 0.f) + wq.y * fmaxf(x0[1], 0.f) +
+                 wq.z * fmaxf(x0[2], 0.f) + wq.w * fmaxf(x0[3], 0.f);
+      float v1 = wq.x * fmaxf(x1[0], 0.f) + wq.y * fmaxf(x1[1], 0.f) +
+                 wq.z * fmaxf(x1[2], 0.f) + wq.w * fmaxf(x1[3], 0.f);
+      v0 = pair32_sum(pair16_sum(v0));
+      v1 = pair32_sum(pair16_sum(v1));
+      if (c.lane < NK) {   // lane = key
+        const float v = c.lane < 16 ? v0 : v1;
+        s_red[t & 1][0][c.wave][c.lane] = pm;
+        s_red[t & 1][1][c.wave][c.lane] = ((vmask >> c.lane) & 1u) ? v : kNegInf;
+      }
+      // tile t+1 landed for every wave (only tile t+2's gathers may still be in flight)
+      wait_vm_barrier<AC::GOPS + GK>();
+      nxt2 = i3;
+    };
+    for (int t = 0; t < ntiles; t += 3) {
+      step(t, 0, 2, i2);
+      step(t + 1, 1, 0, i2);
+      step(t + 2, 2, 1, i2);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // gathers past the last tile
+  if (c.wave_u == 0 && c.lane < NK) {
+    const int t = ntiles - 1, pb = t & 1;
+    s_p[t * NK + c.lane] = (s_red[pb][0][0][c.lane] + s_red[pb][0][1][c.lane]) +
+                           (s_red[pb][0][2][c.lane] + s_red[pb][0][3][c.lane]);
+    s_i[t * NK + c.lane] = (s_red[pb][1][0][c.lane] + s_red[pb][1][1][c.lane]) +
+                           (s_red[pb][1][2][c.lane] + s_red[pb][1][3][c.lane]);
+  }
+  __syncthreads();
+
+  // ---- the row's distributions, KL term and dI
+  {
+    const int nsl = ntiles * NK;
+    float m = kNegInf;
+    for (int s = c.tid; s < nsl; s += 256) m = fmaxf(m, s_i[s]);
+    m = block_max(m, s_blk);
+    float se = 0.f, pt = 0.f;
+    for (int s = c.tid; s < nsl; s += 256) {
+      se += expf(s_i[s] - m);
+      pt += s_p[s];
+    }
+    se = block_sum(se, s_blk);
+    pt = block_sum(pt, s_blk);
+    const float lse = m + logf(se);
+    const float ipt = pt > 0.f ? 1.f / pt : 0.f;
+    float kl = 0.f;
+    for (int s = c.tid; s < nsl; s += 256) {
+      const float p = s_p[s] * ipt;
+      const float lr = s_i[s] - lse;       // log softmax(I); -inf at empty slots
+      if (p > 0.f) kl += p * (logf(p) - lr);
+      s_p[s] = a.loss_grad * (expf(lr) - p);
+    }
+    kl = block_sum(kl, s_blk);             // (its barriers also publish dI)
+    if (c.tid == 0) a.loss[row] = kl;
+  }
+
+  // ---- pass 2: dS, dW, dq_idx and the per-slot key gradients
+  // the row's index queries (64 x 128 bf16) staged in kv0 for the transposed reads
+  dma_copy_flat<4>(lds_addr(kv0), a.q_idx + (size_t)row * kG * kDI, kG * kDI * 2, c.wave_u, c.lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // A of the key gradient (q_idx^T): dims 32 wave + 16 mb + i16, index heads 32 ks + 8 G .. +7
+  bf16x8 qt[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qt[mb][ks] = tr_frag(kv0, kDI, 32 * ks + 8 * G, 32 * c.wave + 16 * mb, i16);
+  // dS[index head][key] of a tile, two buffers in kv1
+  auto dsb = [&](int par) { return kv1 + (par & 1) * (kG * DSR); };
+  const float wn = a.w[(size_t)row * kG + 16 * c.wave + i16];
+  // transposing reads of an index-key tile: rows (keys) 4 G + i16/4 (+16), columns 16 Mb + 4 (i16 % 4)
+  int toff[8];
+  {
+    const int r = 4 * G + (i16 >> 2), q4 = i16 & 3;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      toff[mb] = r * kDI + (((2 * mb + (q4 >> 1)) ^ (r & 15)) * 8) + (q4 & 1) * 4;
+  }
+  float dwacc = 0.f;
+  f32x4 dqa[8];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) dqa[mb] = (f32x4){};
+  const uint16_t* cbase = a.ws_c + (size_t)row * a.topkp * kDI;   // the row's slot gradients
+
+  // key gradients of tile u for this wave's 32 dims: C[dim, key] = q_idx^T dS over 64 heads
+  auto key_grad = [&](int u) {
+    const uint16_t* dsu = dsb(u);
+    f32x4 z[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) z[mb][0] = z[mb][1] = (f32x4){};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bf16x8 b = tr_frag(dsu, DSR, 32 * ks + 8 * G, 16 * nb, i16);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) z[mb][nb] = mfma16(qt[mb][ks], b, z[mb][nb]);
+      }
+    // lane: key 16 nb + i16, dims 32 wave + 16 mb + 4 G .. +3 -> one 8-byte store each
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const u32x2 v = {pack_bf16(z[mb][nb][0], z[mb][nb][1]), pack_bf16(z[mb][nb][2], z[mb][nb][3])};
+        const unsigned off = (unsigned)((((u * NK + 16 * nb + i16) * kDI) + 32 * c.wave + 16 * mb + 4 * G) * 2);
+        const uint16_t* b0 = cbase;
+        asm volatile("global_store_dwordx2 %0, %1, %2" :: "v"(off), "v"(v), "s"(b0) : "memory");
+      }
+  };
+
+  {
+    const TI j0 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 0);
+    const TI j1 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 1);
+    TI j2 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 2);
+    gather_ktile(a, c, j0, kb[0]);
+    gather_ktile(a, c, j1, kb[1]);
+    wait_vm_barrier<0>();
+
+    auto step = [&](int t, int slot, int ahead2, TI& nxt2) {
+      const TI j3 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, t + 3);
+      gather_ktile(a, c, nxt2, kb[ahead2]);
+      if (t > 0) key_grad(t - 1);
+      const lds_cptr_t kt = (lds_cptr_t)kts[slot];
+      // S^T[key, index head]: A = index-key rows i16 / 16 + i16, B = index-query rows
+      f32x4 y0 = (f32x4){}, y1 = (f32x4){};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a0 = *(lds_cb8_t)(kt + koff[s]);
+        const bf16x8 a1 = *(lds_cb8_t)(kt + koff[s] + 16 * kDI);
+        y0 = mfma16(a0, qi[s], y0);
+        y1 = mfma16(a1, qi[s], y1);
+      }
+      // lane: index head 16 wave + i16; keys 4 G + r (y0) and 16 + 4 G + r (y1)
+      const float4 e0 = *reinterpret_cast<const float4*>(s_p + t * NK + 4 * G);
+      const float4 e1 = *reinterpret_cast<const float4*>(s_p + t * NK + 16 + 4 * G);
+      const float d0[4] = {e0.x, e0.y, e0.z, e0.w}, d1[4] = {e1.x, e1.y, e1.z, e1.w};
+      float g0[4], g1[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dwacc += d0[r] * fmaxf(y0[r], 0.f) + d1[r] * fmaxf(y1[r], 0.f);
+        g0[r] = y0[r] > 0.f ? wn * d0[r] : 0.f;
+        g1[r] = y1[r] > 0.f ? wn * d1[r] : 0.f;
+      }
+      const unsigned p0 = pack_bf16(g0[0], g0[1]), p1 = pack_bf16(g0[2], g0[3]);
+      const unsigned p2 = pack_bf16(g1[0], g1[1]), p3 = pack_bf16(g1[2], g1[3]);
+      uint16_t* dst = dsb(t) + (16 * c.wave + i16) * DSR + 4 * G;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(p0, p1);
+      *reinterpret_cast<uint2*>(dst + 16) = make_uint2(p2, p3);
+      // dq_idx^T[dim, head] += K^T dS^T: the K order (keys 4 G .. +3, 16 + 4 G .. +3 in lane
+      // group G) is the accumulator order of dS, so dS is the B fragment as it stands
+      const bf16x8 bds = __builtin_bit_cast(bf16x8, make_uint4(p0, p1, p2, p3));
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const lds_cptr_t pa = kt + toff[mb];
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)pa);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(pa + 16 * kDI));
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        dqa[mb] = mfma16(ka, bds, dqa[mb]);
+      }
+      // tile t+1 landed; the dS tile is complete for every wave.  In flight: tile t+2's
+      // gathers and the previous tile's key-gradient stores.
+      wait_vm_barrier<GK + NST>();
+      nxt2 = j3;
+    };
+    for (int t = 0; t < ntiles; t += 3) {
+      step(t, 0, 2, j2);
+      step(t + 1, 1, 0, j2);
+      step(t + 2, 2, 1, j2);
+    }
+    key_grad(ntiles - 1);
+  }
+  // dq_idx: lane holds head 16 wave + i16, dims 16 mb + 4 G .. +3
+  {
+    uint16_t* dqp = a.dq_idx + ((size_t)row * kG + 16 * c.wave + i16) * kDI + 4 * G;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      *reinterpret_cast<uint2*>(dqp + 16 * mb) =
+          make_uint2(pack_bf16(dqa[mb][0], dqa[mb][1]), pack_bf16(dqa[mb][2], dqa[mb][3]));
+  }
+  dwacc = pair32_sum(pair16_sum(dwacc));
+  if (c.lane < 16) a.dw[(size_t)row * kG + 16 * c.wave + c.lane] = dwacc;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no gather or store may outlive the block
+}
+
+// dk[k] += sum of the key's slot gradients: 16 lanes per key, 8 dims (16 B) per lane, four
+// entries in flight; each key's sum is formed by one lane group, so the update is a plain
+// read-modify-write.
+__global__ __launch_bounds__(256) void k_idx_kl_reduce(IdxKlArgs a) {
+  const int k = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
+  if (k >= a.n_k) return;
+  const int beg = a.off[k], end = a.off[k + 1];
+  if (beg == end) return;
+  float s[8] = {};
+  auto add = [&](int e) {
+    const int r = e / a.topk, sl = e - r * a.topk;
+    const uint4 v = *reinterpret_cast<const uint4*>(a.ws_c + ((size_t)r * a.topkp + sl) * kDI + 8 * l);
+    const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[2 * j] += __uint_as_float(vv[j] << 16);
+      s[2 * j + 1] += __uint_as_float(vv[j] & 0xFFFF0000u);
+    }
+  };
+  int p = beg;
+  for (; p + 4 <= end; p += 4) {
+    const int e0 = a.list[p], e1 = a.list[p + 1], e2 = a.list[p + 2], e3 = a.list[p + 3];
+    add(e0);
+    add(e1);
+    add(e2);
+    add(e3);
+  }
+  for (; p < end; ++p) add(a.list[p]);
+  float4* d = reinterpret_cast<float4*>(a.dk + (size_t)k * kDI + 8 * l);
+  float4 x0 = d[0], x1 = d[1];
+  x0.x += s[0]; x0.y += s[1]; x0.z += s[2]; x0.w += s[3];
+  x1.x += s[4]; x1.y += s[5]; x1.z += s[6]; x1.w += s[7];
+  d[0] = x0;
+  d[1] = x1;
+}
+
+// out[0] = sum of loss[0 .. n) in a fixed order (fp64 partials), one workgroup.
+__global__ __launch_bounds__(1024) void k_loss_total(const float* loss, int n, float* out) {
+  __shared__ double part[16];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < n; i += 1024) acc += (double)loss[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int w = 0; w < 16; ++w) t += part[w];
+    out[0] = (float)t;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_indexer_kl(const IdxKlArgs& a, const KeyListArgs& kl, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  hipError_t e = launch_key_lists(kl, s);
+  if (e != hipSuccess) return e;
+  const bool al8 = a.topk >= 8 && a.topk % 8 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 31) == 0;
+  if (al8) k_idx_kl<true><<<a.rows, 256, 0, s>>>(a);
+  else k_idx_kl<false><<<a.rows, 256, 0, s>>>(a);
+  k_idx_kl_reduce<<<(a.n_k + 15) / 16, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_total(const float* loss, int n, float* out, hipStream_t s) {
+  k_loss_total<<<1, 1024, 0, s>>>(loss, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -58,6 +58,11 @@ _SIGS = {
                                            _P, _P, _P, ctypes.c_size_t, _P]),
     "dsa_sparse_attn_bwd_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(Shape),
                                                            ctypes.POINTER(ctypes.c_size_t)]),
+    "dsa_indexer_kl_loss_grad": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P,
+                                                _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P,
+                                                ctypes.c_size_t, _P]),
+    "dsa_indexer_kl_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(Shape),
+                                                      ctypes.POINTER(ctypes.c_size_t)]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -272,6 +277,60 @@ def dsa_sparse_attn_bwd(q, kv, topk_idx, out, dout, softmax_max, softmax_sum,
         _ptr(softmax_max), _ptr(softmax_sum), _ptr(dq), _ptr(dkv), _ptr(workspace),
         ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev, stream)))
     return dq, dkv
+
+
+def dsa_indexer_kl_workspace_bytes(n_q: int, n_k: int, topk: int) -> int:
+    sh = _shape(n_q=n_q, n_k=n_k, h_idx=64, d_idx=128, h=128, d_qk=576, d_v=512, topk=topk,
+                softmax_scale=1.0)
+    n = ctypes.c_size_t(0)
+    _check(load_library().dsa_indexer_kl_workspace_bytes(ctypes.byref(sh), ctypes.byref(n)))
+    return int(n.value)
+
+
+def dsa_indexer_kl_loss_grad(q_idx, k_idx, w_idx, q, kv, topk_idx, softmax_max, softmax_sum,
+                             softmax_scale: float, loss_grad: float = 1.0, dk_idx=None,
+                             workspace=None, stream=None):
+    """Indexer KL loss against the head-summed attention distribution, and its gradients.
+
+    Returns (loss fp32 [1], loss_rows fp32 [n_q], dq_idx bf16 [n_q,64,128], dw_idx fp32
+    [n_q,64], dk_idx fp32 [n_k,128]); a given ``dk_idx`` is accumulated into, a new one starts
+    at zero."""
+    _dev(q_idx, "q_idx", (torch.bfloat16,), 3)
+    _dev(k_idx, "k_idx", (torch.bfloat16,), 2)
+    _dev(w_idx, "w_idx", (torch.float32,), 2)
+    _dev(q, "q", (torch.bfloat16,), 3)
+    _dev(kv, "kv", (torch.bfloat16,), 2)
+    _dev(topk_idx, "topk_idx", (torch.int32,), 2)
+    _dev(softmax_max, "softmax_max", (torch.float32,), 2)
+    _dev(softmax_sum, "softmax_sum", (torch.float32,), 2)
+    n_q, h_idx, d_idx = q_idx.shape
+    n_k = k_idx.shape[0]
+    _, h, d_qk = q.shape
+    topk = topk_idx.shape[1]
+    if (k_idx.shape[1] != d_idx or w_idx.shape != (n_q, h_idx) or q.shape[0] != n_q
+            or kv.shape != (n_k, d_qk) or topk_idx.shape[0] != n_q
+            or softmax_max.shape != (n_q, h) or softmax_sum.shape != (n_q, h)):
+        raise ValueError("indexer loss tensor shapes do not match q_idx [n_q,h_idx,d_idx] / "
+                         "k_idx [n_k,d_idx] / q [n_q,h,d_qk] / kv [n_k,d_qk]")
+    dev = q.device
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    loss_rows = torch.empty(n_q, dtype=torch.float32, device=dev)
+    dq_idx = torch.empty(n_q, h_idx, d_idx, dtype=torch.bfloat16, device=dev)
+    dw_idx = torch.empty(n_q, h_idx, dtype=torch.float32, device=dev)
+    if dk_idx is None:
+        dk_idx = torch.zeros(n_k, d_idx, dtype=torch.float32, device=dev)
+    _dev(dk_idx, "dk_idx", (torch.float32,), 2)
+    sh = _shape(n_q=n_q, n_k=n_k, h_idx=h_idx, d_idx=d_idx, h=h, d_qk=d_qk, d_v=512, topk=topk,
+                softmax_scale=softmax_scale)
+    if workspace is None:
+        nb = dsa_indexer_kl_workspace_bytes(n_q, n_k, topk)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    _check(load_library().dsa_indexer_kl_loss_grad(
+        ctypes.byref(sh), _ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(kv),
+        _ptr(topk_idx), _ptr(softmax_max), _ptr(softmax_sum), ctypes.c_float(loss_grad),
+        _ptr(loss_rows), _ptr(loss), _ptr(dq_idx), _ptr(dw_idx), _ptr(dk_idx), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev, stream)))
+    return loss, loss_rows, dq_idx, dw_idx, dk_idx
 
 
 def dsa_forward(q_idx, k_idx, w_idx, q, kv, segments, topk: int, softmax_scale: float,

@@ -166,6 +166,61 @@ def test_backward_argument_checks(lib):
     assert _bwd(lib, empty, 0) == dsa.DSA_OK
 
 
+def _kl(lib, sh, ws_bytes, workspace=FAKE, null=None, misalign=None, loss_grad=1.0):
+    ptrs = {k: FAKE for k in ("q_idx", "k_idx", "w_idx", "q", "kv", "idx", "smax", "ssum",
+                              "loss_rows", "dq_idx", "dw_idx", "dk_idx")}
+    if null:
+        ptrs[null] = None
+    if misalign:
+        ptrs[misalign] = ctypes.c_void_p(0x1008)
+    return lib.dsa_indexer_kl_loss_grad(
+        ctypes.byref(sh), ptrs["q_idx"], ptrs["k_idx"], ptrs["w_idx"], ptrs["q"], ptrs["kv"],
+        ptrs["idx"], ptrs["smax"], ptrs["ssum"], ctypes.c_float(loss_grad), ptrs["loss_rows"],
+        None, ptrs["dq_idx"], ptrs["dw_idx"], ptrs["dk_idx"], workspace,
+        ctypes.c_size_t(ws_bytes), None)
+
+
+def test_indexer_kl_argument_checks(lib):
+    # workspace: per row the bf16 [topk rounded up to 96, 128] key gradients and topk list
+    # entries; per call 3 n_k + 1 ints + slack
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    def shape(**kw):
+        base = dict(n_q=5000, n_k=8192, h_idx=64, d_idx=128, h=128, d_qk=576, d_v=512, topk=2048,
+                    softmax_scale=0.1)
+        base.update(kw)
+        return dsa._shape(**base)
+
+    sh = shape()
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_indexer_kl_workspace_bytes(ctypes.byref(sh), ctypes.byref(n)) == dsa.DSA_OK
+    fixed = al((3 * 8192 + 1) * 4) + 8 * 256
+    assert n.value == fixed + 2048 * (2112 * 256 + 2048 * 4)
+    assert dsa.dsa_indexer_kl_workspace_bytes(10, 100, 100) == \
+        al((3 * 100 + 1) * 4) + 8 * 256 + 10 * (192 * 256 + 100 * 4)
+    per_row = fixed + 2112 * 256 + 2048 * 4
+    assert _kl(lib, sh, per_row - 1) == dsa.DSA_ERR_WORKSPACE
+    assert _kl(lib, sh, per_row, workspace=None) == dsa.DSA_ERR_WORKSPACE
+    for name in ("q_idx", "kv", "smax", "dk_idx", "loss_rows"):
+        assert _kl(lib, sh, per_row, null=name) == dsa.DSA_ERR_INVALID_ARG, name
+    for name in ("q_idx", "w_idx", "ssum", "dk_idx"):
+        assert _kl(lib, sh, per_row, misalign=name) == dsa.DSA_ERR_INVALID_ARG, name
+    assert _kl(lib, sh, per_row, workspace=ctypes.c_void_p(0x1008)) == dsa.DSA_ERR_INVALID_ARG
+    assert _kl(lib, sh, per_row, loss_grad=float("nan")) == dsa.DSA_ERR_INVALID_ARG
+    # built only for the DeepSeek-V3.2 shapes, bf16 index tensors and topk <= 2048
+    assert _kl(lib, shape(h_idx=4, d_idx=32), 1 << 30) == dsa.DSA_ERR_UNSUPPORTED
+    assert _kl(lib, shape(h=8, d_qk=80, d_v=64), 1 << 30) == dsa.DSA_ERR_UNSUPPORTED
+    assert _kl(lib, shape(topk=2049), 1 << 30) == dsa.DSA_ERR_UNSUPPORTED
+    assert _kl(lib, shape(topk=0), 1 << 30) == dsa.DSA_ERR_INVALID_ARG
+    fp8 = shape()
+    fp8.idx_dtype = dsa.DSA_IDX_FP8_E4M3
+    assert _kl(lib, fp8, 1 << 30) == dsa.DSA_ERR_UNSUPPORTED
+    assert "bf16" in dsa.dsa_last_error()
+    # nothing to do for zero rows (and no total requested)
+    assert _kl(lib, shape(n_q=0), 0, workspace=None) == dsa.DSA_OK
+
+
 def test_quantize_argument_checks(lib):
     assert lib.dsa_quantize_fp8_rows(FAKE, -1, 8, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
     assert lib.dsa_quantize_fp8_rows(FAKE, 0, 8, FAKE, FAKE, None) == dsa.DSA_OK
