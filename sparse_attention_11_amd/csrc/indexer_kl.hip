@@ -161,9 +161,10 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
     for (int ks = 0; ks < kKs; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 16));
   }
-  // softmax statistics of the lane's 16 heads: accumulator register r holds head
-  // wave*32 + (r/4)*8 + 4 g + r%4
-  float msub[16], invl[16];
+  // softmax statistics of the lane's 16 heads (accumulator register r holds head
+  // wave*32 + (r/4)*8 + 4 g + r%4), folded into one exponent bias per head:
+  // P = exp(z - max) / sum = exp2(z log2(e) - (max log2(e) + log2(sum)))
+  float bias[16];
   {
     const size_t hb = (size_t)row * kH + c.wave * 32 + 4 * c.g;
 #pragma unroll
@@ -172,10 +173,9 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
       const float4 sm = *reinterpret_cast<const float4*>(a.ssum + hb + 8 * j);
       const float mv[4] = {mx.x, mx.y, mx.z, mx.w}, sv[4] = {sm.x, sm.y, sm.z, sm.w};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        msub[4 * j + u] = mv[u] == kNegInf ? 0.f : mv[u] * kLog2e;   // scaled log2 units
-        invl[4 * j + u] = sv[u] > 0.f ? 1.f / sv[u] : 0.f;
-      }
+      for (int u = 0; u < 4; ++u)   // (a head without keys: bias +inf, P = 0)
+        bias[4 * j + u] = (sv[u] > 0.f && mv[u] != kNegInf) ? fmaf(mv[u], kLog2e, __log2f(sv[u]))
+                                                            : __builtin_huge_valf();
     }
   }
   bf16x8 qi[4];   // index query of head 16 wave + i16, dims 32 s + 8 G .. +7
@@ -204,10 +204,20 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
     gather_tile_flat<kH, kDQK, kDV>(a, c, ti, loff, wb[k]);
     gather_ktile(a, c, ti, kb[k]);
   };
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // row loads done: the ring's counts are exact
+  // row loads done (a wait the compiler sees, so it adds none inside the ring, where the
+  // counter also holds the in-flight gathers)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- pass 1: target mass and indexer values per slot
+  // Pipelined by one tile: while the matrix cores run tile t's logits, the wave issues the
+  // VALU epilogue of tile t-1 (probabilities, head sums, the indexer's ReLU head sums) between
+  // the MFMAs, so the epilogue does not serialise behind the product.  Q moves to AGPRs and
+  // the logits MFMAs (inline asm) read their A operand from there, which leaves the VGPRs to
+  // the LDS prefetch and the carried state of the previous tile.
   const int ntiles = (c.ntiles + 2) / 3 * 3;
+#pragma unroll
+  for (int ks = 0; ks < kKs; ++ks) asm volatile("" : "+a"(qf[ks]));
   {
     const TI i0 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 0);
     const TI i1 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 1);
@@ -220,86 +230,108 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
     }
     wait_vm_barrier<0>();
 
+    f32x16 sp0 = (f32x16){}, sp1 = (f32x16){};   // previous tile: logits (two chains)
+    f32x4 xp0 = (f32x4){}, xp1 = (f32x4){};      // previous tile: index scores
+    unsigned vmp = 0;                             // previous tile: validity bits
+    float pm = 0.f, v0 = 0.f, v1 = 0.f;
+    // unit u of the previous tile's epilogue (units 0 .. 23); the results land in
+    // s_red[(t-1) & 1] (at t = 0 a harmless all-empty tile -1)
+    auto epi = [&](int u, int t) {
+      if (u < 16) {
+        pm += __builtin_amdgcn_exp2f(fmaf(sp0[u] + sp1[u], a.scale_log2, -bias[u]));
+      } else if (u == 16) {
+        pm = pair32_sum(pm);
+      } else if (u == 17) {
+        v0 = wq.x * fmaxf(xp0[0], 0.f) + wq.y * fmaxf(xp0[1], 0.f) +
+             wq.z * fmaxf(xp0[2], 0.f) + wq.w * fmaxf(xp0[3], 0.f);
+      } else if (u == 18) {
+        v1 = wq.x * fmaxf(xp1[0], 0.f) + wq.y * fmaxf(xp1[1], 0.f) +
+             wq.z * fmaxf(xp1[2], 0.f) + wq.w * fmaxf(xp1[3], 0.f);
+      } else if (u == 19) {
+        v0 = pair16_sum(v0);
+      } else if (u == 20) {
+        v1 = pair16_sum(v1);
+      } else if (u == 21) {
+        v0 = pair32_sum(v0);
+      } else if (u == 22) {
+        v1 = pair32_sum(v1);
+      } else if (u == 23) {
+        // lane = key (lanes 32..63 repeat lanes 0..31 with equal values)
+        const int pb = (t - 1) & 1, key = c.lane & 31;
+        s_red[pb][0][c.wave][key] = ((vmp >> key) & 1u) ? pm : 0.f;
+        s_red[pb][1][c.wave][key] = ((vmp >> key) & 1u) ? ((c.lane & 16) ? v1 : v0) : kNegInf;
+        pm = 0.f;
+      }
+    };
+    auto lazy_sum = [&](int tt) {   // tile tt's per-wave partials -> row arrays
+      const int pb = tt & 1;
+      s_p[tt * NK + c.lane] = (s_red[pb][0][0][c.lane] + s_red[pb][0][1][c.lane]) +
+                              (s_red[pb][0][2][c.lane] + s_red[pb][0][3][c.lane]);
+      s_i[tt * NK + c.lane] = (s_red[pb][1][0][c.lane] + s_red[pb][1][1][c.lane]) +
+                              (s_red[pb][1][2][c.lane] + s_red[pb][1][3][c.lane]);
+    };
+
     auto step = [&](int t, int slot, int ahead2, TI& nxt2) {
       const TI i3 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, t + 3);
       gather(nxt2, ahead2);
       if (c.lane == 0) c.vm[ahead2 * 4 + c.wave] = tile_bits<kH, kDQK, kDV>(a, nxt2);
-      // the previous tile's per-wave partials -> row arrays (one wave per tile, in turn)
-      if (t > 0 && c.wave_u == (t & 3) && c.lane < NK) {
-        const int pb = (t - 1) & 1;
-        const float m = (s_red[pb][0][0][c.lane] + s_red[pb][0][1][c.lane]) +
-                        (s_red[pb][0][2][c.lane] + s_red[pb][0][3][c.lane]);
-        const float v = (s_red[pb][1][0][c.lane] + s_red[pb][1][1][c.lane]) +
-                        (s_red[pb][1][2][c.lane] + s_red[pb][1][3][c.lane]);
-        s_p[(t - 1) * NK + c.lane] = m;
-        s_i[(t - 1) * NK + c.lane] = v;
-      }
+      if (t >= 2 && c.wave_u == (t & 3) && c.lane < NK) lazy_sum(t - 2);
       unsigned vmask = 0;
 #pragma unroll
       for (int w = 0; w < 4; ++w) vmask |= c.vm[slot * 4 + w] << (w * 8);
 
-      // logits C[head, key]: A = Q (VGPRs), B = latent row hl of the tile, chunk 2 ks + g
-      // (physical chunk (2 ks + g) ^ swz(hl)); even / odd K steps in two chains
-      f32x16 s0 = (f32x16){}, s1 = (f32x16){};
-      {
-        const lds_cptr_t lt = (lds_cptr_t)c.buf[slot];
-        const int sw = swz(c.hl);
-        lds_cptr_t bb[4];
+      // logits C[head, key]: A = Q (AGPRs), B = latent row hl of the tile, chunk 2 ks + g
+      // (physical chunk (2 ks + g) ^ swz(hl)); even / odd K steps in two chains, PD
+      // fragments read ahead
+      const lds_cptr_t lt = (lds_cptr_t)c.buf[slot];
+      const int sw = swz(c.hl);
+      lds_cptr_t bb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bb[j] = lt + c.hl * AC::ROWE + (((2 * j + c.g) ^ sw) - 2 * j) * 8;
-        auto at = [&](int ks) { return bb[ks & 3] + ks * 16; };
-        constexpr int QG = 4, NG = kKs / QG;
-        static_assert(kKs % QG == 0, "prefetch groups");
-        bf16x8 f[2][QG];
+      for (int j = 0; j < 4; ++j) bb[j] = lt + c.hl * AC::ROWE + (((2 * j + c.g) ^ sw) - 2 * j) * 8;
+      auto at = [&](int ks) { return bb[ks & 3] + ks * 16; };
+      const lds_cptr_t kt = (lds_cptr_t)kts[slot];
+      constexpr int PD = 6;
+      bf16x8 f[PD], kf[8];
+      f32x16 s0, s1;
 #pragma unroll
-        for (int u = 0; u < QG; ++u) f[0][u] = *(lds_cb8_t)(at(u));
+      for (int i = 0; i < PD; ++i) f[i] = *(lds_cb8_t)(at(i));
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          const int cur = gi & 1;
-          if (gi + 1 < NG) {
-#pragma unroll
-            for (int u = 0; u < QG; ++u) f[cur ^ 1][u] = *(lds_cb8_t)(at((gi + 1) * QG + u));
-          }
-#pragma unroll
-          for (int u = 0; u < QG; u += 2) {
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[gi * QG + u], f[cur][u], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[gi * QG + u + 1], f[cur][u + 1], s1, 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < kKs; ++ks) {
+        const bf16x8 cur = f[ks % PD];
+        if (ks + PD < kKs) f[ks % PD] = *(lds_cb8_t)(at(ks + PD));
+        if (ks >= kKs - 8) {   // this tile's index-key fragments, ahead of the index product
+          const int j = ks - (kKs - 8);
+          kf[j] = *(lds_cb8_t)(kt + koff[j >> 1] + (j & 1) * 16 * kDI);
         }
+        const bf16x8 qa = qf[ks];
+        if (ks == 0) {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(s0) : "a"(qa), "v"(cur));
+        } else if (ks == 1) {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(s1) : "a"(qa), "v"(cur));
+        } else if (ks % 2 == 0) {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(s0) : "a"(qa), "v"(cur));
+        } else if (ks == kKs - 1) {
+          // the results are read by VALU next: wait out the MFMA write-to-read distance
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                       : "+a"(s1) : "a"(qa), "v"(cur));
+        } else {
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(s1) : "a"(qa), "v"(cur));
+        }
+        if (ks < 24) epi(ks, t);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // probability mass of key hl over the lane's heads, then over the wave's 32 heads
-      float pm = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        pm += __builtin_amdgcn_exp2f(fmaf(s0[r] + s1[r], a.scale_log2, -msub[r])) * invl[r];
-      pm = pair32_sum(pm);
-      if (!((vmask >> c.hl) & 1u)) pm = 0.f;
-
       // indexer S[index head, key]: A = index-query rows, B = index-key rows i16, 16 + i16
       f32x4 x0 = (f32x4){}, x1 = (f32x4){};
-      {
-        const lds_cptr_t kt = (lds_cptr_t)kts[slot];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 b0 = *(lds_cb8_t)(kt + koff[s]);
-          const bf16x8 b1 = *(lds_cb8_t)(kt + koff[s] + 16 * kDI);
-          x0 = mfma16(qi[s], b0, x0);
-          x1 = mfma16(qi[s], b1, x1);
-        }
+      for (int s = 0; s < 4; ++s) {
+        x0 = mfma16(qi[s], kf[2 * s], x0);
+        x1 = mfma16(qi[s], kf[2 * s + 1], x1);
       }
-      // lane: key i16 (x0) / 16 + i16 (x1), index heads 16 wave + 4 G + r
-      float v0 = wq.x * fmaxf(x0[0], 0.f) + wq.y * fmaxf(x0[1], 0.f) +
-                 wq.z * fmaxf(x0[2], 0.f) + wq.w * fmaxf(x0[3], 0.f);
-      float v1 = wq.x * fmaxf(x1[0], 0.f) + wq.y * fmaxf(x1[1], 0.f) +
-                 wq.z * fmaxf(x1[2], 0.f) + wq.w * fmaxf(x1[3], 0.f);
-      v0 = pair32_sum(pair16_sum(v0));
-      v1 = pair32_sum(pair16_sum(v1));
-      if (c.lane < NK) {   // lane = key
-        const float v = c.lane < 16 ? v0 : v1;
-        s_red[t & 1][0][c.wave][c.lane] = pm;
-        s_red[t & 1][1][c.wave][c.lane] = ((vmask >> c.lane) & 1u) ? v : kNegInf;
-      }
+      sp0 = s0;
+      sp1 = s1;
+      xp0 = x0;
+      xp1 = x1;
+      vmp = vmask;
       // tile t+1 landed for every wave (only tile t+2's gathers may still be in flight)
       wait_vm_barrier<AC::GOPS + GK>();
       nxt2 = i3;
@@ -309,14 +341,12 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
       step(t + 1, 1, 0, i2);
       step(t + 2, 2, 1, i2);
     }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // gathers past the last tile
-  if (c.wave_u == 0 && c.lane < NK) {
-    const int t = ntiles - 1, pb = t & 1;
-    s_p[t * NK + c.lane] = (s_red[pb][0][0][c.lane] + s_red[pb][0][1][c.lane]) +
-                           (s_red[pb][0][2][c.lane] + s_red[pb][0][3][c.lane]);
-    s_i[t * NK + c.lane] = (s_red[pb][1][0][c.lane] + s_red[pb][1][1][c.lane]) +
-                           (s_red[pb][1][2][c.lane] + s_red[pb][1][3][c.lane]);
+#pragma unroll
+    for (int u = 0; u < 24; ++u) epi(u, ntiles);   // the last tile's epilogue
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // gathers past the last tile
+    __syncthreads();
+    if (c.wave_u == 0 && c.lane < NK) lazy_sum(ntiles - 2);
+    if (c.wave_u == 1 && c.lane < NK) lazy_sum(ntiles - 1);
   }
   __syncthreads();
 
@@ -347,9 +377,11 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
   }
 
   // ---- pass 2: dS, dW, dq_idx and the per-slot key gradients
+  const float wn = a.w[(size_t)row * kG + 16 * c.wave + i16];
   // the row's index queries (64 x 128 bf16) staged in kv0 for the transposed reads
   dma_copy_flat<4>(lds_addr(kv0), a.q_idx + (size_t)row * kG * kDI, kG * kDI * 2, c.wave_u, c.lane);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   // A of the key gradient (q_idx^T): dims 32 wave + 16 mb + i16, index heads 32 ks + 8 G .. +7
   bf16x8 qt[2][2];
@@ -359,7 +391,6 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
     for (int ks = 0; ks < 2; ++ks) qt[mb][ks] = tr_frag(kv0, kDI, 32 * ks + 8 * G, 32 * c.wave + 16 * mb, i16);
   // dS[index head][key] of a tile, two buffers in kv1
   auto dsb = [&](int par) { return kv1 + (par & 1) * (kG * DSR); };
-  const float wn = a.w[(size_t)row * kG + 16 * c.wave + i16];
   // transposing reads of an index-key tile: rows (keys) 4 G + i16/4 (+16), columns 16 Mb + 4 (i16 % 4)
   int toff[8];
   {
