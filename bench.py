@@ -99,9 +99,10 @@ def cpu_baseline(wl, budget_s=15.0, max_rows=2048):
 
 
 def backward_stage(args, n=5):
-    """Sparse-attention backward on the packed varlen workload (8 documents, 32768 tokens):
-    the GPU forward supplies indices, output and softmax statistics; the backward (P / dS,
-    dQ, dKV kernels) is timed on its own with HIP events."""
+    """Training-side kernels on the packed varlen workload (8 documents, 32768 tokens): the
+    GPU forward supplies indices, output and softmax statistics; the sparse-attention backward
+    (P / dS, dQ, dKV kernels) and the indexer KL loss with its gradients are each timed on
+    their own with HIP events."""
     wl = I.workload(n)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
@@ -121,9 +122,27 @@ def backward_stage(args, n=5):
     n_sel = int((idx >= 0).sum())
     flop = 2.0 * wl.h * (3 * wl.d_qk + 2 * wl.d_v) * n_sel
     print(f"bench: backward {wl.name} {ms:.3f} ms", file=sys.stderr, flush=True)
-    return {"workload": wl.name, "ms": ms, "selected_keys": n_sel, "flop": flop,
-            "tflops": flop / (ms * 1e-3) / 1e12,
-            "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    rec = {"workload": wl.name, "ms": ms, "selected_keys": n_sel, "flop": flop,
+           "tflops": flop / (ms * 1e-3) / 1e12,
+           "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    del dq, ws
+    # indexer KL loss and its gradients on the same forward outputs: per selected slot the
+    # recomputed attention logits (2 h d_qk) and the index scores, dq_idx and dk_idx products
+    # (3 x 2 h_idx d_idx)
+    dk = torch.zeros(wl.n_k, wl.d_idx, dtype=torch.float32, device=dev)
+    kws = torch.empty(dsa.dsa_indexer_kl_workspace_bytes(wl.n_q, wl.n_k, wl.topk),
+                      dtype=torch.uint8, device=dev)
+
+    def kl():
+        dsa.dsa_indexer_kl_loss_grad(g["q_idx"], g["k_idx"], g["w_idx"], g["q"], g["kv"], idx,
+                                     smax, ssum, wl.softmax_scale, dk_idx=dk, workspace=kws)
+    kms = time_launches(kl, reps, stream)
+    kflop = 2.0 * n_sel * (wl.h * wl.d_qk + 3 * wl.h_idx * wl.d_idx)
+    print(f"bench: indexer KL loss + gradients {wl.name} {kms:.3f} ms", file=sys.stderr,
+          flush=True)
+    rec["indexer_kl"] = {"ms": kms, "flop": kflop, "tflops": kflop / (kms * 1e-3) / 1e12,
+                         "mfma_frac": kflop / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    return rec
 
 
 def traffic_entry():

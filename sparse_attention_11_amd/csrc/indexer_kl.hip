@@ -68,8 +68,11 @@ __device__ __forceinline__ float pair32_sum(float x) {
   return __int_as_float(p[0]) + __int_as_float(p[1]);
 }
 
+// two floats -> two round-to-nearest-even bf16 in one dword (one packed conversion)
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
-  return (unsigned)f32_to_bf16(lo) | ((unsigned)f32_to_bf16(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // Block-wide sum / max over the 4 waves (two barriers).
@@ -505,9 +508,9 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no gather or store may outlive the block
 }
 
-// dk[k] += sum of the key's slot gradients: 16 lanes per key, 8 dims (16 B) per lane, four
-// entries in flight; each key's sum is formed by one lane group, so the update is a plain
-// read-modify-write.
+// dk[k] += sum of the key's slot gradients: 16 lanes per key, 8 dims (16 B) per lane, eight
+// entries in flight (the slot gradients are read once: non-temporal loads); each key's sum is
+// formed by one lane group, so the update is a plain read-modify-write.
 __global__ __launch_bounds__(256) void k_idx_kl_reduce(IdxKlArgs a) {
   const int k = blockIdx.x * 16 + (threadIdx.x >> 4);
   const int l = threadIdx.x & 15;
@@ -515,25 +518,29 @@ __global__ __launch_bounds__(256) void k_idx_kl_reduce(IdxKlArgs a) {
   const int beg = a.off[k], end = a.off[k + 1];
   if (beg == end) return;
   float s[8] = {};
-  auto add = [&](int e) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  auto src = [&](int e) {
     const int r = e / a.topk, sl = e - r * a.topk;
-    const uint4 v = *reinterpret_cast<const uint4*>(a.ws_c + ((size_t)r * a.topkp + sl) * kDI + 8 * l);
-    const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+    return reinterpret_cast<const u32x4*>(a.ws_c + ((size_t)r * a.topkp + sl) * kDI + 8 * l);
+  };
+  auto add = [&](const u32x4& v) {
+    const uint32_t vv[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       s[2 * j] += __uint_as_float(vv[j] << 16);
       s[2 * j + 1] += __uint_as_float(vv[j] & 0xFFFF0000u);
     }
   };
+  constexpr int F = 8;
   int p = beg;
-  for (; p + 4 <= end; p += 4) {
-    const int e0 = a.list[p], e1 = a.list[p + 1], e2 = a.list[p + 2], e3 = a.list[p + 3];
-    add(e0);
-    add(e1);
-    add(e2);
-    add(e3);
+  for (; p + F <= end; p += F) {
+    u32x4 v[F];
+#pragma unroll
+    for (int j = 0; j < F; ++j) v[j] = __builtin_nontemporal_load(src(a.list[p + j]));
+#pragma unroll
+    for (int j = 0; j < F; ++j) add(v[j]);
   }
-  for (; p < end; ++p) add(a.list[p]);
+  for (; p < end; ++p) add(__builtin_nontemporal_load(src(a.list[p])));
   float4* d = reinterpret_cast<float4*>(a.dk + (size_t)k * kDI + 8 * l);
   float4 x0 = d[0], x1 = d[1];
   x0.x += s[0]; x0.y += s[1]; x0.z += s[2]; x0.w += s[3];
