@@ -219,7 +219,7 @@ dsa_status dsa_sparse_attn_bwd_workspace_bytes(const dsa_shape *shape, size_t *b
  * 1 <= topk <= 2048 (else DSA_ERR_UNSUPPORTED); d_v is not used.  q_idx, k_idx, w_idx, q, kv,
  * the statistics, dk_idx and the workspace must be 16-byte aligned, dq_idx 8-byte aligned
  * (DSA_ERR_INVALID_ARG).  The workspace holds per-key counters and, for a chunk of rows, the
- * bf16 key gradient of every slot and the per-key entry lists; rows are processed in chunks
+ * bf16 key gradient and fp32 dI of every slot and the per-key entry lists; rows are processed in chunks
  * of as many rows as it fits (DSA_ERR_WORKSPACE if not even one).  Calls that update the same
  * dk_idx must not overlap.  Products in bf16 MFMA with fp32 accumulation; softmax, logarithms
  * and the loss in fp32.
@@ -232,8 +232,8 @@ dsa_status dsa_indexer_kl_loss_grad(const dsa_shape *shape, const void *q_idx, c
                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace size for dsa_indexer_kl_loss_grad that processes up to 2048 rows per pass:
- * (256 * topk_p + 4 * topk) bytes per row, topk_p = topk rounded up to a multiple of 96, plus
- * 4 * (3 * n_k + 1) bytes rounded up to 256 and 2 KiB of alignment slack. */
+ * (260 * topk_p + 4 * topk) bytes per row, topk_p = topk rounded up to a multiple of 96, plus
+ * 4 * (3 * n_k + 1) bytes rounded up to 256, 1 KiB, and 2 KiB of alignment slack. */
 dsa_status dsa_indexer_kl_workspace_bytes(const dsa_shape *shape, size_t *bytes);
 
 /*

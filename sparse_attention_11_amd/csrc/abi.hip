@@ -270,13 +270,16 @@ dsa_status check_bwd_dims(const dsa_shape* s) {
 }
 
 // Indexer-loss workspace.  Per call: the per-key counters (as for the attention backward).
-// Per row of a chunk: the bf16 index-key gradient of every slot (slots padded to a multiple of
-// 96) and one list entry per slot.
+// Per row of a chunk: the bf16 index-key gradient and the fp32 dI of every slot (slots padded
+// to a multiple of 96; the dI array has 1 KB of slack for whole-piece LDS DMA reads) and one
+// list entry per slot.
 constexpr int kKlMaxTopk = 2048;   // the per-row target / indexer arrays live in LDS
 size_t kl_topkp(const dsa_shape* s) { return ((size_t)s->topk + 95) / 96 * 96; }
-size_t kl_row_bytes(const dsa_shape* s) { return kl_topkp(s) * 128 * 2 + (size_t)s->topk * 4; }
+size_t kl_row_bytes(const dsa_shape* s) {
+  return kl_topkp(s) * (128 * 2 + 4) + (size_t)s->topk * 4;
+}
 size_t kl_fixed_bytes(const dsa_shape* s) {
-  return align_up(((size_t)3 * s->n_k + 1) * 4) + 8 * kAlign;
+  return align_up(((size_t)3 * s->n_k + 1) * 4) + 1024 + 8 * kAlign;
 }
 
 dsa_status check_kl_dims(const dsa_shape* s) {
@@ -541,6 +544,7 @@ dsa_status dsa_indexer_kl_loss_grad(const dsa_shape* shape, const void* q_idx, c
   kl.off = reinterpret_cast<int*>(take(((size_t)shape->n_k + 1) * 4));
   kl.cur = reinterpret_cast<int*>(take((size_t)shape->n_k * 4));
   uint16_t* ws_c = reinterpret_cast<uint16_t*>(take((size_t)chunk * topkp * 128 * 2));
+  float* ws_di = reinterpret_cast<float*>(take((size_t)chunk * topkp * 4 + 1024));
   kl.list = reinterpret_cast<int*>(take((size_t)chunk * topk * 4));
   if (at > workspace_bytes)
     return fail(DSA_ERR_WORKSPACE, "internal workspace layout exceeds %zu bytes", workspace_bytes);
@@ -550,6 +554,7 @@ dsa_status dsa_indexer_kl_loss_grad(const dsa_shape* shape, const void* q_idx, c
   a.k_idx = static_cast<const uint16_t*>(k_idx);
   a.kv = static_cast<const uint16_t*>(kv);
   a.ws_c = ws_c;
+  a.ws_di = ws_di;
   a.dk = dk_idx;
   a.list = kl.list;
   a.off = kl.off;

@@ -115,6 +115,7 @@ struct IdxKlArgs {
   uint16_t* dq_idx;       // [rows, 64, 128] bf16
   float* dw;              // [rows, 64]
   uint16_t* ws_c;         // [rows, topkp, 128] bf16 per-(row, slot) index-key gradients
+  float* ws_di;           // [rows, topkp] fp32 dI per slot (+ 1 KB slack at the end)
   float* dk;              // [n_k, 128] fp32, accumulated
   const int* list;        // key lists of the chunk (see KeyListArgs)
   const int* off;

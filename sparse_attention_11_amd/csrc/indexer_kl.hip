@@ -48,6 +48,7 @@ constexpr int KT = NK * kDI;           // elements of an index-key tile (8 KB)
 constexpr int DSR = NK + 4;            // LDS row stride (elements) of the shared dS tile
 constexpr int GK = 2;                  // index-key gather instructions per wave and tile
 constexpr int NST = 4;                 // key-gradient stores per wave and tile
+constexpr int kDiLds = 2304;           // dI floats in LDS: 66 tiles x 32 rounded up to 1 KB pieces
 constexpr float kLog2e = 1.44269504088896340736f;
 static_assert(AC::RPW == 8 && AC::FLAT, "tile split of the gathers");
 
@@ -125,7 +126,7 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 }
 
 template <bool AL8>
-__global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
+__global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t kv0[AC::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t kv1[AC::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t kv2[AC::TILE];
@@ -146,10 +147,7 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
   c.vm = vmring;
   c.ntiles = row_tiles<kH, kDQK, kDV>(a, c, s_last);
   const int row = c.row;
-  if (c.ntiles == 0) {   // nothing selected: loss 0, no gradient (no key-list entries either)
-    uint4* dq = reinterpret_cast<uint4*>(a.dq_idx + (size_t)row * kG * kDI);
-    for (int j = c.tid; j < kG * kDI / 8; j += 256) dq[j] = make_uint4(0, 0, 0, 0);
-    if (c.tid < kG) a.dw[(size_t)row * kG + c.tid] = 0.f;
+  if (c.ntiles == 0) {   // nothing selected: loss 0 (the pass-2 kernel zeroes the gradients)
     if (c.tid == 0) a.loss[row] = 0.f;
     return;
   }
@@ -379,10 +377,62 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
     if (c.tid == 0) a.loss[row] = kl;
   }
 
-  // ---- pass 2: dS, dW, dq_idx and the per-slot key gradients
+  // dI of the row's slots -> workspace, for the pass-2 kernel
+  {
+    float* dst = a.ws_di + (size_t)row * a.topkp;
+    for (int sl = c.tid * 4; sl < ntiles * NK; sl += 256 * 4)
+      *reinterpret_cast<float4*>(dst + sl) = *reinterpret_cast<const float4*>(s_p + sl);
+  }
+}
+
+// Pass 2 (a kernel of its own: it needs 49 KB of LDS, so three workgroups share a CU and
+// one workgroup's waits overlap another's work).  One workgroup per row, four waves.  The
+// index-key tiles are gathered again and S^T[key, index head] recomputed; dS, dW and
+// dq_idx^T += K^T dS^T stay in registers (K^T from the transposing LDS read; the MFMA's K order
+// is the accumulator's key order, so dS is the B operand as it stands); dS is shared through
+// LDS and each wave forms the key gradient dS^T q_idx of its 32 of the 128 dims for every
+// slot, written as bf16 per (row, slot).
+template <bool AL8>
+__global__ __launch_bounds__(256, 3) void k_idx_kl_p2(IdxKlArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t kt0[KT];
+  __shared__ __attribute__((aligned(16))) uint16_t kt1[KT];
+  __shared__ __attribute__((aligned(16))) uint16_t kt2[KT];
+  __shared__ __attribute__((aligned(16))) uint16_t stage[kG * kDI];   // q_idx, then dS tiles
+  __shared__ __attribute__((aligned(16))) float s_di[kDiLds];        // dI of the row's slots
+  __shared__ int s_last[4];
+  static_assert(2 * kG * DSR <= kG * kDI, "two dS tiles fit in the staging area");
+
+  RowCtx c = make_ctx(a, block_row(a));
+  c.ntiles = row_tiles<kH, kDQK, kDV>(a, c, s_last);
+  const int row = c.row;
+  if (c.ntiles == 0) {   // nothing selected: no gradient
+    uint4* dq = reinterpret_cast<uint4*>(a.dq_idx + (size_t)row * kG * kDI);
+    for (int j = c.tid; j < kG * kDI / 8; j += 256) dq[j] = make_uint4(0, 0, 0, 0);
+    if (c.tid < kG) a.dw[(size_t)row * kG + c.tid] = 0.f;
+    return;
+  }
+  const int ntiles = (c.ntiles + 2) / 3 * 3;
+  const uint16_t* kts[3] = {kt0, kt1, kt2};
+  unsigned kb[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) kb[k] = lds_addr(kts[k]);
+  const int i16 = c.lane & 15, G = c.lane >> 4;
+  bf16x8 qi[4];   // index query of head 16 wave + i16, dims 32 s + 8 G .. +7
+  {
+    const uint16_t* p = a.q_idx + ((size_t)row * kG + 16 * c.wave + i16) * kDI + 8 * G;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qi[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p + 32 * s));
+  }
   const float wn = a.w[(size_t)row * kG + 16 * c.wave + i16];
-  // the row's index queries (64 x 128 bf16) staged in kv0 for the transposed reads
-  dma_copy_flat<4>(lds_addr(kv0), a.q_idx + (size_t)row * kG * kDI, kG * kDI * 2, c.wave_u, c.lane);
+  int koff[4];   // index-key tile: row i16 (and i16 + 16), logical chunk 4 s + G
+#pragma unroll
+  for (int s = 0; s < 4; ++s) koff[s] = i16 * kDI + (((4 * s + G) ^ i16) * 8);
+  // the row's index queries (64 x 128 bf16) and its dI (rounded up to whole 1 KB pieces; the
+  // workspace has the slack) by LDS DMA
+  dma_copy_flat<4>(lds_addr(stage), a.q_idx + (size_t)row * kG * kDI, kG * kDI * 2, c.wave_u, c.lane);
+  dma_copy_flat<4>(lds_addr(s_di), a.ws_di + (size_t)row * a.topkp, (ntiles * NK * 4 + 1023) & ~1023,
+                   c.wave_u, c.lane);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
@@ -391,9 +441,10 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qt[mb][ks] = tr_frag(kv0, kDI, 32 * ks + 8 * G, 32 * c.wave + 16 * mb, i16);
-  // dS[index head][key] of a tile, two buffers in kv1
-  auto dsb = [&](int par) { return kv1 + (par & 1) * (kG * DSR); };
+    for (int ks = 0; ks < 2; ++ks) qt[mb][ks] = tr_frag(stage, kDI, 32 * ks + 8 * G, 32 * c.wave + 16 * mb, i16);
+  __syncthreads();   // the staging area now holds the dS tiles
+  // dS[index head][key] of a tile, two buffers
+  auto dsb = [&](int par) { return stage + (par & 1) * (kG * DSR); };
   // transposing reads of an index-key tile: rows (keys) 4 G + i16/4 (+16), columns 16 Mb + 4 (i16 % 4)
   int toff[8];
   {
@@ -457,8 +508,8 @@ __global__ __launch_bounds__(256) void k_idx_kl(IdxKlArgs a) {
         y1 = mfma16(a1, qi[s], y1);
       }
       // lane: index head 16 wave + i16; keys 4 G + r (y0) and 16 + 4 G + r (y1)
-      const float4 e0 = *reinterpret_cast<const float4*>(s_p + t * NK + 4 * G);
-      const float4 e1 = *reinterpret_cast<const float4*>(s_p + t * NK + 16 + 4 * G);
+      const float4 e0 = *reinterpret_cast<const float4*>(s_di + t * NK + 4 * G);
+      const float4 e1 = *reinterpret_cast<const float4*>(s_di + t * NK + 16 + 4 * G);
       const float d0[4] = {e0.x, e0.y, e0.z, e0.w}, d1[4] = {e1.x, e1.y, e1.z, e1.w};
       float g0[4], g1[4];
 #pragma unroll
@@ -572,8 +623,13 @@ hipError_t launch_indexer_kl(const IdxKlArgs& a, const KeyListArgs& kl, hipStrea
   hipError_t e = launch_key_lists(kl, s);
   if (e != hipSuccess) return e;
   const bool al8 = a.topk >= 8 && a.topk % 8 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 31) == 0;
-  if (al8) k_idx_kl<true><<<a.rows, 256, 0, s>>>(a);
-  else k_idx_kl<false><<<a.rows, 256, 0, s>>>(a);
+  if (al8) {
+    k_idx_kl_p1<true><<<a.rows, 256, 0, s>>>(a);
+    k_idx_kl_p2<true><<<a.rows, 256, 0, s>>>(a);
+  } else {
+    k_idx_kl_p1<false><<<a.rows, 256, 0, s>>>(a);
+    k_idx_kl_p2<false><<<a.rows, 256, 0, s>>>(a);
+  }
   k_idx_kl_reduce<<<(a.n_k + 15) / 16, 256, 0, s>>>(a);
   return hipGetLastError();
 }

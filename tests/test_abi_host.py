@@ -181,8 +181,8 @@ def _kl(lib, sh, ws_bytes, workspace=FAKE, null=None, misalign=None, loss_grad=1
 
 
 def test_indexer_kl_argument_checks(lib):
-    # workspace: per row the bf16 [topk rounded up to 96, 128] key gradients and topk list
-    # entries; per call 3 n_k + 1 ints + slack
+    # workspace: per row the bf16 [topk rounded up to 96, 128] key gradients, the fp32 dI of
+    # those slots and topk list entries; per call 3 n_k + 1 ints, 1 KiB and alignment slack
     def al(x):
         return (x + 255) // 256 * 256
 
@@ -195,11 +195,11 @@ def test_indexer_kl_argument_checks(lib):
     sh = shape()
     n = ctypes.c_size_t(0)
     assert lib.dsa_indexer_kl_workspace_bytes(ctypes.byref(sh), ctypes.byref(n)) == dsa.DSA_OK
-    fixed = al((3 * 8192 + 1) * 4) + 8 * 256
-    assert n.value == fixed + 2048 * (2112 * 256 + 2048 * 4)
+    fixed = al((3 * 8192 + 1) * 4) + 1024 + 8 * 256
+    assert n.value == fixed + 2048 * (2112 * 260 + 2048 * 4)
     assert dsa.dsa_indexer_kl_workspace_bytes(10, 100, 100) == \
-        al((3 * 100 + 1) * 4) + 8 * 256 + 10 * (192 * 256 + 100 * 4)
-    per_row = fixed + 2112 * 256 + 2048 * 4
+        al((3 * 100 + 1) * 4) + 1024 + 8 * 256 + 10 * (192 * 260 + 100 * 4)
+    per_row = fixed + 2112 * 260 + 2048 * 4
     assert _kl(lib, sh, per_row - 1) == dsa.DSA_ERR_WORKSPACE
     assert _kl(lib, sh, per_row, workspace=None) == dsa.DSA_ERR_WORKSPACE
     for name in ("q_idx", "kv", "smax", "dk_idx", "loss_rows"):
