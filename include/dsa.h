@@ -98,8 +98,9 @@ int dsa_abi_version(void);
 const char *dsa_last_error(void);
 
 /*
- * Workspace bytes dsa_forward needs for `shape` (the per-row indexer scores of each row's
- * window, and the top-k indices when the caller does not keep them).  Host-only.
+ * Workspace bytes dsa_forward and dsa_indexer_topk need for `shape`: per row, slots of the
+ * longest window (rounded up to 64) for the candidate scores and for their keys, one count,
+ * and the top-k indices when the caller does not keep them.  Host-only.
  */
 dsa_status dsa_workspace_bytes(const dsa_shape *shape, size_t *bytes);
 
@@ -130,6 +131,22 @@ dsa_status dsa_topk_select(const dsa_shape *shape, const float *scores, int32_t 
                            void *stream);
 
 /*
+ * The indexer fused with the top-k (page "CANN/torchtitan-npu融合算子适配", section "DSA":
+ * the indexer operator returns the selected indices, not the scores): the same indices as
+ * dsa_indexer_scores followed by dsa_topk_select on the same inputs, bit for bit (the scores
+ * come from the same kernels), without writing every score.  Per row the indexer keeps a
+ * running lower bound of the row's k-th largest score and writes only the scores at or above
+ * it, with their keys, to `workspace`; the selection then runs over those candidates.
+ * topk_idx [n_q, topk] int32 receives, for every covered row, its kept keys in ascending order
+ * followed by -1.  workspace: dsa_workspace_bytes bytes.  Arguments and index dtypes as for
+ * dsa_indexer_scores; rows covered by no segment are left untouched.
+ */
+dsa_status dsa_indexer_topk(const dsa_shape *shape, const void *q_idx, const float *q_scale,
+                            const void *k_idx, const float *k_scale, const float *w_idx,
+                            int32_t *topk_idx, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
  * Sparse multi-query attention over gathered latent rows (page "CANNTorchTitan: ...",
  * Sparse Flash Attention formula; the CP guide's sparse-attention boundary with key = value
  * = the shared latent row under weight absorption, rope = its last d_qk - d_v columns):
@@ -147,10 +164,11 @@ dsa_status dsa_sparse_attn(const dsa_shape *shape, const void *q, const void *kv
                            float *softmax_sum, void *stream);
 
 /*
- * The fused DSA forward on one CP rank's share: indexer -> top-k -> sparse attention,
- * enqueued back to back on `stream` (the page "CANNTorchTitan: ..." section "自定义CP策略":
- * the CP forward is the plain forward over all-gathered keys).  Arguments as above; scores
- * live only in `workspace` (each row's window, never the full [n_q, n_k]).  topk_idx may be
+ * The fused DSA forward on one CP rank's share: the fused indexer + top-k
+ * (dsa_indexer_topk) -> sparse attention, enqueued back to back on `stream` (the page
+ * "CANNTorchTitan: ..." section "自定义CP策略": the CP forward is the plain forward over
+ * all-gathered keys).  Arguments as above; only candidate scores are written, to
+ * `workspace` (never the full [n_q, n_k]).  topk_idx may be
  * NULL (then the indices stay in the workspace), softmax_max / softmax_sum may be NULL.
  * Rows covered by no segment are left untouched.
  */

@@ -157,14 +157,19 @@ std::vector<dsa::SegTable> make_tables(const Plan& p, int rows_per_block) {
 // Row stride (floats) of the compact per-window score rows in the forward workspace.
 int64_t ws_score_ld(const Plan& p) { return (p.max_window + 63) / 64 * 64; }
 
+// Forward workspace: per row a slot array of the row-window stride for the candidate scores,
+// the same for their keys, the candidate count, then the indices.
 struct WsLayout {
-  size_t scores_off = 0, idx_off = 0, total = 0;
+  size_t scores_off = 0, ckey_off = 0, ccnt_off = 0, idx_off = 0, total = 0;
 };
 
 WsLayout ws_layout(const dsa_shape* s, const Plan& p) {
   WsLayout w;
+  const size_t slots = (size_t)s->n_q * (size_t)ws_score_ld(p);
   w.scores_off = 0;
-  w.idx_off = align_up((size_t)s->n_q * (size_t)ws_score_ld(p) * sizeof(float));
+  w.ckey_off = align_up(slots * sizeof(float));
+  w.ccnt_off = w.ckey_off + align_up(slots * sizeof(int32_t));
+  w.idx_off = w.ccnt_off + align_up((size_t)s->n_q * sizeof(int32_t));
   w.total = w.idx_off + align_up((size_t)s->n_q * (size_t)s->topk * sizeof(int32_t));
   return w;
 }
@@ -172,7 +177,7 @@ WsLayout ws_layout(const dsa_shape* s, const Plan& p) {
 dsa_status run_indexer(const dsa_shape* s, const Plan& p, const void* q_idx,
                        const float* q_scale, const void* k_idx, const float* k_scale,
                        const float* w_idx, float* scores, long long ld, int dense,
-                       hipStream_t st) {
+                       hipStream_t st, int32_t* cand_key = nullptr, int* cand_cnt = nullptr) {
   const bool fp8 = s->idx_dtype == DSA_IDX_FP8_E4M3;
   for (const dsa::SegTable& t : make_tables(p, dsa::indexer_rows_per_block())) {
     dsa::IndexerArgs a = {};
@@ -185,6 +190,9 @@ dsa_status run_indexer(const dsa_shape* s, const Plan& p, const void* q_idx,
     a.scores = scores;
     a.ld = ld;
     a.dense = dense;
+    a.cand_key = cand_key;
+    a.cand_cnt = cand_cnt;
+    a.topk = s->topk;
     hipError_t e = dsa::launch_indexer(a, s->h_idx, s->d_idx, fp8, st);
     if (e != hipSuccess) return hip_fail(e, "indexer launch");
   }
@@ -192,7 +200,8 @@ dsa_status run_indexer(const dsa_shape* s, const Plan& p, const void* q_idx,
 }
 
 dsa_status run_topk(const dsa_shape* s, const Plan& p, const float* scores, long long ld,
-                    int dense, int32_t* idx, hipStream_t st) {
+                    int dense, int32_t* idx, hipStream_t st, const int32_t* cand_key = nullptr,
+                    const int* cand_cnt = nullptr) {
   for (const dsa::SegTable& t : make_tables(p, 1)) {
     dsa::TopkArgs a = {};
     a.segs = t;
@@ -201,6 +210,8 @@ dsa_status run_topk(const dsa_shape* s, const Plan& p, const float* scores, long
     a.dense = dense;
     a.topk = s->topk;
     a.idx = idx;
+    a.cand_key = cand_key;
+    a.cand_cnt = cand_cnt;
     hipError_t e = dsa::launch_topk(a, (int)p.max_window, st);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
   }
@@ -267,6 +278,22 @@ dsa_status check_bwd_dims(const dsa_shape* s) {
     return fail(DSA_ERR_UNSUPPORTED, "attention backward built for (h, d_qk, d_v) = "
                 "(128, 576, 512) only (got %d, %d, %d)", s->h, s->d_qk, s->d_v);
   return DSA_OK;
+}
+
+// The fused indexer + top-k: candidate scores, keys and counts in the workspace, then the
+// selection over each row's candidates.
+dsa_status run_indexer_topk(const dsa_shape* s, const Plan& p, const void* q_idx,
+                            const float* q_scale, const void* k_idx, const float* k_scale,
+                            const float* w_idx, char* ws, const WsLayout& w, int32_t* idx,
+                            hipStream_t st) {
+  float* scores = reinterpret_cast<float*>(ws + w.scores_off);
+  int32_t* ckey = reinterpret_cast<int32_t*>(ws + w.ckey_off);
+  int* ccnt = reinterpret_cast<int*>(ws + w.ccnt_off);
+  const long long ld = ws_score_ld(p);
+  dsa_status e = run_indexer(s, p, q_idx, q_scale, k_idx, k_scale, w_idx, scores, ld, 0, st,
+                             ckey, ccnt);
+  if (e != DSA_OK) return e;
+  return run_topk(s, p, scores, ld, 0, idx, st, ckey, ccnt);
 }
 
 // Indexer-loss workspace.  Per call: the per-key counters (as for the attention backward).
@@ -381,14 +408,31 @@ dsa_status dsa_forward(const dsa_shape* shape, const void* q_idx, const float* q
                 workspace ? workspace_bytes : (size_t)0);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws + w.scores_off);
   int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + w.idx_off);
-  const long long ld = ws_score_ld(p);
-  if ((st = run_indexer(shape, p, q_idx, q_scale, k_idx, k_scale, w_idx, scores, ld, 0, hs)) != DSA_OK)
+  if ((st = run_indexer_topk(shape, p, q_idx, q_scale, k_idx, k_scale, w_idx, ws, w, idx, hs)) != DSA_OK)
     return st;
-  if ((st = run_topk(shape, p, scores, ld, 0, idx, hs)) != DSA_OK) return st;
   if ((st = run_attn(shape, &p, q, kv, idx, out, softmax_max, softmax_sum, hs)) != DSA_OK) return st;
   return ok();
+}
+
+dsa_status dsa_indexer_topk(const dsa_shape* shape, const void* q_idx, const float* q_scale,
+                            const void* k_idx, const float* k_scale, const float* w_idx,
+                            int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedSegs | kNeedIndexer | kNeedTopk, p);
+  if (st != DSA_OK) return st;
+  if (p.covered_rows == 0) return ok();
+  if ((st = check_idx_ptrs(shape, q_idx, q_scale, k_idx, k_scale, w_idx)) != DSA_OK) return st;
+  if (!topk_idx) return fail(DSA_ERR_INVALID_ARG, "topk_idx is NULL");
+  const WsLayout w = ws_layout(shape, p);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                workspace ? workspace_bytes : (size_t)0);
+  st = run_indexer_topk(shape, p, q_idx, q_scale, k_idx, k_scale, w_idx,
+                        static_cast<char*>(workspace), w, topk_idx,
+                        static_cast<hipStream_t>(stream));
+  return st == DSA_OK ? ok() : st;
 }
 
 dsa_status dsa_quantize_fp8_rows(const void* x_bf16, int64_t rows, int32_t cols, void* x_fp8,

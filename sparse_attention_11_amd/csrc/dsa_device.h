@@ -44,6 +44,12 @@ struct IndexerArgs {
   float* scores;          // row i at scores + i * ld (+ k_start when dense)
   long long ld;           // row stride of scores in elements
   int dense;              // 1: column = absolute key row; 0: column = key - k_start
+  // candidate mode (fused with the top-k): only scores that can still be in the row's top-k
+  // are written, compacted in key order to scores + i * ld, with their absolute key rows at
+  // cand_key + i * ld and their number at cand_cnt[i]
+  int32_t* cand_key;
+  int* cand_cnt;
+  int topk;
 };
 
 struct FillArgs {
@@ -60,7 +66,17 @@ struct TopkArgs {
   int dense;
   int topk;
   int32_t* idx;           // [n_q, topk]
+  const int32_t* cand_key;   // candidate mode: the rows' candidate keys and counts
+  const int* cand_cnt;
+  int cand_min;              // candidate mode: rows with at most this many are served elsewhere
 };
+
+// fp32 -> uint32 whose unsigned order is the float order; -0.0 is mapped like +0.0
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
 
 struct AttnArgs {
   SegTable segs;          // rows to compute when use_segs (else rows 0 .. grid-1)

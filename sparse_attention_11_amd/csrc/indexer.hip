@@ -15,6 +15,16 @@
 // each lane holds 16 heads of one key column per M tile, so ReLU * w and the head sum are
 // per-lane FMAs plus one exchange with the lane 32 apart (which holds the other 16 heads).
 // Causal work is uneven, so blocks of later (longer-window) rows are launched first.
+//
+// Candidate mode (the indexer fused with the top-k, page "CANN/torchtitan-npu融合算子适配",
+// section "DSA": the indexer operator hands out indices, not scores): each wave keeps, for its
+// row, a running lower bound tau of the row's k-th largest score and writes only the scores
+// >= tau (with their keys, compacted in key order); a score below tau is below the final k-th
+// largest, so the top-k of the candidates is the top-k of the window, ties included.  tau
+// comes from a 256-bin LDS histogram of the candidates' order-preserving keys (bins over a
+// range set by the row's first 32 scores, clamped at both ends): the lower edge of the highest
+// bin with at least k candidates at or above it.  Only candidates are counted, which keeps the
+// counts exact for every bin at or above tau's bin, the only ones the search reads.
 #include "dsa_device.h"
 
 namespace dsa {
@@ -41,6 +51,82 @@ struct RowInfo {
   bool ok;
 };
 
+// Per-row state of the candidate filter (one wave per row; all fields wave-uniform).
+struct CandRow {
+  uint32_t* hist;     // this wave's 256 LDS bins
+  float* cs;          // candidate scores of the row
+  int32_t* ck;        // candidate keys (absolute rows)
+  int n;              // candidates written so far
+  uint32_t base;      // order key of bin 0's upper part
+  int shift;          // bin width (log2) in order-key units
+  bool init;
+  uint32_t tau;       // order-key threshold (0: keep everything)
+};
+
+__device__ __forceinline__ void cand_begin(CandRow& c, uint32_t* hist_wave, float* cs, int32_t* ck) {
+  c.hist = hist_wave;
+  c.cs = cs;
+  c.ck = ck;
+  c.n = 0;
+  c.base = 0u;
+  c.shift = 0;
+  c.init = false;
+  c.tau = 0u;
+  *reinterpret_cast<uint4*>(hist_wave + 4 * (threadIdx.x & 63)) = make_uint4(0, 0, 0, 0);
+}
+
+// One 32-key group: lane (key key_abs, valid v) offers score s.
+__device__ __forceinline__ void cand_offer(CandRow& c, float s, int key_abs, bool v) {
+  const uint32_t ok = order_key(s);
+  if (!c.init) {   // bin range from the row's first group: its span over 64 of the 256 bins
+    uint32_t mn = v ? ok : 0xFFFFFFFFu, mx = v ? ok : 0u;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+    }
+    const uint32_t span = mx - mn;
+    c.base = mn;
+    c.shift = span == 0u ? 0 : max(0, 32 - __clz((int)span) - 6);
+    c.init = true;
+  }
+  const bool keep = v && ok >= c.tau;
+  const unsigned long long m = __ballot(keep);
+  if (keep) {
+    const int p = c.n + (int)lanes_below(m);
+    c.cs[p] = s;
+    c.ck[p] = key_abs;
+    const uint32_t d = ok < c.base ? 0u : min(255u, (ok - c.base) >> c.shift);
+    atomicAdd(&c.hist[d], 1u);
+  }
+  c.n += __popcll(m);
+}
+
+// Raise tau from the histogram (once k candidates exist).
+__device__ __forceinline__ void cand_update(CandRow& c, int k) {
+  if (c.n < k) return;
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's histogram atomics landed
+  const int lane = threadIdx.x & 63;
+  const uint4 h = *reinterpret_cast<const uint4*>(c.hist + 4 * lane);   // bins 4 lane .. +3
+  const uint32_t s4 = h.x + h.y + h.z + h.w;
+  uint32_t suf = s4;   // candidates in bins >= 4 lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = (uint32_t)__shfl_down((int)suf, o, 64);
+    if (lane + o < 64) suf += t;
+  }
+  const uint32_t s3 = suf - s4 + h.w, s2 = s3 + h.z, s1 = s2 + h.y, s0 = s1 + h.x;
+  const unsigned long long ball = __ballot(s0 >= (uint32_t)k);   // lanes 0 .. L* (nonzero: s0(0) = n)
+  const int lstar = 63 - __clzll(ball);
+  const int j = s3 >= (uint32_t)k ? 3 : s2 >= (uint32_t)k ? 2 : s1 >= (uint32_t)k ? 1 : 0;
+  const int b = 4 * lstar + __shfl(j, lstar, 64);
+  if (b > 0) {
+    const unsigned long long e = (unsigned long long)c.base + ((unsigned long long)b << c.shift);
+    c.tau = (uint32_t)min(e, 0xFFFFFFFFull);   // (a bin holding k candidates starts below 2^32)
+  }
+}
+
 __device__ __forceinline__ RowInfo indexer_row(const SegTable& segs) {
   RowInfo ri;
   const int blk = blockIdx.x;
@@ -63,7 +149,7 @@ __device__ __forceinline__ RowInfo indexer_row(const SegTable& segs) {
 
 // ------------------------------------------------------------------------------- bf16 ----
 
-template <int HI, int DI>
+template <int HI, int DI, bool CAND>
 __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) {
   constexpr int MT = (HI + 31) / 32;     // 32-head M tiles
   constexpr int KS = DI / 16;            // K steps of the 32x32x16 MFMA
@@ -75,6 +161,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   constexpr int PER = (CH + NT - 1) / NT;
   static_assert(DI % 16 == 0, "d_idx must be a multiple of 16");
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][KST * ROW];
+  __shared__ __attribute__((aligned(16))) uint32_t chist[CAND ? kIdxWaves * 256 : 4];
 
   const RowInfo ri = indexer_row(a.segs);
   const int tid = threadIdx.x, lane = tid & 63, hl = lane & 31, g = lane >> 5;
@@ -104,6 +191,9 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
 
   float* out = a.scores + (size_t)ri.row * a.ld + (a.dense ? ri.k_lo : 0);
   const int ntiles = (ri.L_blk + KST - 1) / KST;
+  CandRow cr;
+  if constexpr (CAND)
+    cand_begin(cr, chist + (tid >> 6) * 256, out, a.cand_key + (size_t)ri.row * a.ld);
 
   uint4 pre[PER];
   auto fetch = [&](int t) {
@@ -159,6 +249,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
           for (int mt = 0; mt < MT; ++mt)
             acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[mt][ks], b[nt], acc[nt][mt], 0, 0, 0);
       }
+      float sv[kIdxKeys / 32];
 #pragma unroll
       for (int nt = 0; nt < kIdxKeys / 32; ++nt) {
         float s = 0.f;
@@ -166,20 +257,30 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s = relu_fma(acc[nt][mt][r], wv[mt][r], s);
-        s = pair_sum(s);
-        const int key = kb + nt * 32 + hl;
-        if (g == 0 && key <= ri.pos) out[key] = s;
+        sv[nt] = pair_sum(s);   // (both lanes of the pair hold the sum)
       }
+      // lane (hl, g) takes key kb + 32 g + hl: 64 keys over the 64 lanes, in key order
+      static_assert(kIdxKeys == 64, "two 32-key groups per half-stage");
+      const int key = kb + 32 * g + hl;
+      const float sk_ = g ? sv[1] : sv[0];
+      if constexpr (CAND) cand_offer(cr, sk_, ri.k_lo + key, key <= ri.pos);
+      else if (key <= ri.pos) out[key] = sk_;
     }
+    }
+    if constexpr (CAND) {   // every fourth stage: the bound only needs to rise now and then
+      if (ri.ok && t * KST <= ri.pos && (t & 3) == 3) cand_update(cr, a.topk);
     }
     if (t + 1 < ntiles) stash(buf ^ 1);
     __syncthreads();
+  }
+  if constexpr (CAND) {
+    if (ri.ok && lane == 0) a.cand_cnt[ri.row] = cr.n;
   }
 }
 
 // -------------------------------------------------------------------------------- fp8 ----
 
-template <int HI, int DI>
+template <int HI, int DI, bool CAND>
 __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
   constexpr int MT = (HI + 31) / 32;
   constexpr int KS = (DI + 63) / 64;     // K steps of the 32x32x64 f8f6f4 MFMA (zero padded)
@@ -192,6 +293,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
   static_assert(DI % 16 == 0, "d_idx must be a multiple of 16");
   __shared__ __attribute__((aligned(16))) uint8_t sk[2][kIdxKeys * ROW];
   __shared__ float sks[2][kIdxKeys];
+  __shared__ __attribute__((aligned(16))) uint32_t chist[CAND ? kIdxWaves * 256 : 4];
 
   const RowInfo ri = indexer_row(a.segs);
   const int tid = threadIdx.x, lane = tid & 63, hl = lane & 31, g = lane >> 5;
@@ -238,6 +340,9 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
 
   float* out = a.scores + (size_t)ri.row * a.ld + (a.dense ? ri.k_lo : 0);
   const int ntiles = (ri.L_blk + kIdxKeys - 1) / kIdxKeys;
+  CandRow cr;
+  if constexpr (CAND)
+    cand_begin(cr, chist + (tid >> 6) * 256, out, a.cand_key + (size_t)ri.row * a.ld);
 
   uint4 pre[PER];
   float pres = 0.f;
@@ -302,12 +407,20 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
             for (int r = 0; r < 16; ++r) s = relu_fma(acc[mt][r], wv[mt][r], s);
           s = pair_sum(s);
           const int key = kbase + hl;
-          if (g == 0 && key <= ri.pos) out[key] = s * sks[buf][nt * 32 + hl];
+          const float sc = s * sks[buf][nt * 32 + hl];
+          if constexpr (CAND) cand_offer(cr, sc, ri.k_lo + key, g == 0 && key <= ri.pos);
+          else if (g == 0 && key <= ri.pos) out[key] = sc;
         }
+      }
+      if constexpr (CAND) {   // every eighth 64-key stage
+        if (t * kIdxKeys <= ri.pos && (t & 7) == 7) cand_update(cr, a.topk);
       }
     }
     if (t + 1 < ntiles) stash(buf ^ 1);
     __syncthreads();
+  }
+  if constexpr (CAND) {
+    if (ri.ok && lane == 0) a.cand_cnt[ri.row] = cr.n;
   }
 }
 
@@ -333,14 +446,27 @@ hipError_t launch_indexer(const IndexerArgs& a, int h_idx, int d_idx, bool fp8,
                           hipStream_t s) {
   const dim3 grid(a.segs.blk_off[a.segs.n]), block(kIdxWaves * 64);
   if (grid.x == 0) return hipSuccess;
+  const bool cand = a.cand_cnt != nullptr;
   if (!fp8) {
-    if (h_idx == 64 && d_idx == 128) k_indexer_bf16<64, 128><<<grid, block, 0, s>>>(a);
-    else if (h_idx == 4 && d_idx == 32) k_indexer_bf16<4, 32><<<grid, block, 0, s>>>(a);
-    else return hipErrorInvalidValue;
+    if (h_idx == 64 && d_idx == 128) {
+      if (cand) k_indexer_bf16<64, 128, true><<<grid, block, 0, s>>>(a);
+      else k_indexer_bf16<64, 128, false><<<grid, block, 0, s>>>(a);
+    } else if (h_idx == 4 && d_idx == 32) {
+      if (cand) k_indexer_bf16<4, 32, true><<<grid, block, 0, s>>>(a);
+      else k_indexer_bf16<4, 32, false><<<grid, block, 0, s>>>(a);
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else {
-    if (h_idx == 64 && d_idx == 128) k_indexer_fp8<64, 128><<<grid, block, 0, s>>>(a);
-    else if (h_idx == 4 && d_idx == 32) k_indexer_fp8<4, 32><<<grid, block, 0, s>>>(a);
-    else return hipErrorInvalidValue;
+    if (h_idx == 64 && d_idx == 128) {
+      if (cand) k_indexer_fp8<64, 128, true><<<grid, block, 0, s>>>(a);
+      else k_indexer_fp8<64, 128, false><<<grid, block, 0, s>>>(a);
+    } else if (h_idx == 4 && d_idx == 32) {
+      if (cand) k_indexer_fp8<4, 32, true><<<grid, block, 0, s>>>(a);
+      else k_indexer_fp8<4, 32, false><<<grid, block, 0, s>>>(a);
+    } else {
+      return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }

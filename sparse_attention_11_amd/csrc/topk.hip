@@ -20,18 +20,11 @@
 
 namespace dsa {
 
-namespace {
-
-// fp32 -> uint32 whose unsigned order is the float order; -0.0 is mapped like +0.0
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t b = __float_as_uint(f);
-  if (b == 0x80000000u) b = 0u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-}  // namespace
-
-template <int THREADS, int ITEMS>
+// CAND: the row's input is the candidate list the fused indexer wrote (scores compacted in
+// key order, their keys, their count) instead of the whole window.  The list holds every key
+// that can be in the top-k, in key order, so the same selection applies with the list
+// position standing in for the key index.
+template <int THREADS, int ITEMS, bool CAND>
 __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
   constexpr int NW = THREADS / 64;
   constexpr int NE = ITEMS * NW;          // (item, wave) compaction groups
@@ -51,13 +44,18 @@ __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
   const int r = a.segs.q_len[g] - 1 - (blk - a.segs.blk_off[g]);  // longer windows first
   const int row = a.segs.q_start[g] + r;
   const int k_lo = a.segs.k_start[g];
-  const int L = a.segs.pos0[g] + r + 1;
+  const int L = CAND ? a.cand_cnt[row] : a.segs.pos0[g] + r + 1;
+  // candidate mode with two launches: this configuration serves the rows whose candidates
+  // fit in it and that the smaller configuration before it could not hold
+  if (CAND && (L > THREADS * ITEMS || L <= a.cand_min)) return;
   const int topk = a.topk;
   const float* src = a.scores + (size_t)row * a.ld + (a.dense ? k_lo : 0);
+  const int32_t* ckey = CAND ? a.cand_key + (size_t)row * a.ld : nullptr;
   int32_t* dst = a.idx + (size_t)row * topk;
+  auto key_of = [&](int e) { return CAND ? ckey[e] : k_lo + e; };
 
   if (L <= topk) {
-    for (int t = tid; t < topk; t += THREADS) dst[t] = t < L ? k_lo + t : -1;
+    for (int t = tid; t < topk; t += THREADS) dst[t] = t < L ? key_of(t) : -1;
     return;
   }
 
@@ -209,18 +207,40 @@ __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
     const uint32_t n_gt = grp_gt[j * NW + wave] + lanes_below(mg);
     const uint32_t n_eq = grp_eq[j * NW + wave] + lanes_below(me);
     const uint32_t pos = n_gt + min(n_eq, need);
-    if ((gt || (eq && n_eq < need)) && pos < (uint32_t)topk) dst[pos] = k_lo + e;
+    if ((gt || (eq && n_eq < need)) && pos < (uint32_t)topk) dst[pos] = key_of(e);
   }
 }
 
-hipError_t launch_topk(const TopkArgs& a, int max_window, hipStream_t s) {
+template <bool CAND>
+hipError_t launch_topk_t(const TopkArgs& a, int max_window, hipStream_t s) {
   const dim3 grid(a.segs.blk_off[a.segs.n]);
   if (grid.x == 0) return hipSuccess;
-  if (max_window <= 2048) k_topk<256, 8><<<grid, 256, 0, s>>>(a);
-  else if (max_window <= 8192) k_topk<512, 16><<<grid, 512, 0, s>>>(a);
-  else if (max_window <= 32768) k_topk<1024, 32><<<grid, 1024, 0, s>>>(a);
-  else if (max_window <= 65536) k_topk<1024, 64><<<grid, 1024, 0, s>>>(a);
+  if (max_window <= 2048) k_topk<256, 8, CAND><<<grid, 256, 0, s>>>(a);
+  else if (max_window <= 8192) k_topk<512, 16, CAND><<<grid, 512, 0, s>>>(a);
+  else if (max_window <= 32768) k_topk<1024, 32, CAND><<<grid, 1024, 0, s>>>(a);
+  else if (max_window <= 65536) k_topk<1024, 64, CAND><<<grid, 1024, 0, s>>>(a);
   else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkArgs& a, int max_window, hipStream_t s) {
+  if (!a.cand_cnt) return launch_topk_t<false>(a, max_window, s);
+  // candidates: rows with at most 8192 go to a small configuration (several workgroups per
+  // CU), rows with up to 16384 to a middle one, the rest to the one sized for the longest
+  // window (each launch skips the rows another one serves)
+  if (max_window <= 8192) return launch_topk_t<true>(a, max_window, s);
+  const dim3 grid(a.segs.blk_off[a.segs.n]);
+  if (grid.x == 0) return hipSuccess;
+  TopkArgs t = a;
+  t.cand_min = 0;
+  k_topk<512, 16, true><<<grid, 512, 0, s>>>(t);
+  t.cand_min = 8192;
+  k_topk<512, 32, true><<<grid, 512, 0, s>>>(t);
+  if (max_window > 16384) {
+    t.cand_min = 16384;
+    hipError_t e = launch_topk_t<true>(t, max_window, s);
+    if (e != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 

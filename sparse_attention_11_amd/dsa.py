@@ -50,6 +50,8 @@ _SIGS = {
     "dsa_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)]),
     "dsa_indexer_scores": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P]),
     "dsa_topk_select": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P]),
+    "dsa_indexer_topk": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P,
+                                        ctypes.c_size_t, _P]),
     "dsa_sparse_attn": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P]),
     "dsa_forward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, ctypes.c_size_t, _P]),
@@ -205,6 +207,30 @@ def dsa_topk_select(scores, segments, topk: int, out=None, stream=None):
     sh = _shape(n_q=n_q, n_k=n_k, topk=topk, segments=segments)
     _check(load_library().dsa_topk_select(ctypes.byref(sh), _ptr(scores), _ptr(out),
                                           _stream(scores.device, stream)))
+    return out
+
+
+def dsa_indexer_topk(q_idx, k_idx, w_idx, segments, topk: int, q_scale=None, k_scale=None,
+                     out=None, workspace=None, stream=None):
+    """The indexer fused with the top-k: int32 [n_q, topk] indices (ascending, -1 padded) of
+    every covered row, the same as dsa_indexer_scores followed by dsa_topk_select."""
+    fp8, n_q, h_idx, d_idx = _idx_inputs(q_idx, k_idx, w_idx, q_scale, k_scale)
+    n_k = k_idx.shape[0]
+    dev = q_idx.device
+    if out is None:
+        out = torch.full((n_q, topk), -1, dtype=torch.int32, device=dev)
+    _dev(out, "out", (torch.int32,), 2)
+    sh = _shape(n_q=n_q, n_k=n_k, h_idx=h_idx, d_idx=d_idx, topk=topk,
+                idx_dtype=DSA_IDX_FP8_E4M3 if fp8 else DSA_IDX_BF16, segments=segments)
+    lib = load_library()
+    if workspace is None:
+        nbytes = ctypes.c_size_t(0)
+        _check(lib.dsa_workspace_bytes(ctypes.byref(sh), ctypes.byref(nbytes)))
+        workspace = torch.empty(max(1, nbytes.value), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", (torch.uint8,))
+    _check(lib.dsa_indexer_topk(ctypes.byref(sh), _ptr(q_idx), _ptr(q_scale), _ptr(k_idx),
+                                _ptr(k_scale), _ptr(w_idx), _ptr(out), _ptr(workspace),
+                                ctypes.c_size_t(workspace.numel()), _stream(dev, stream)))
     return out
 
 

@@ -54,12 +54,14 @@ def _ws(n_q, n_k, topk, segs):
 def test_workspace_bytes_formula(lib):
     def al(x):
         return (x + 255) // 256 * 256
+    # per row: candidate scores and keys in slots of the longest window (rounded up to 64),
+    # one count; then the indices
     st, n = _ws(16384, 32768, 2048, [(0, 16384, 0, 32768, 16384)])
     assert st == dsa.DSA_OK
-    assert n == al(16384 * 32768 * 4) + al(16384 * 2048 * 4)
+    assert n == 2 * al(16384 * 32768 * 4) + al(16384 * 4) + al(16384 * 2048 * 4)
     st, n = _ws(100, 300, 7, [(0, 60, 0, 100, 3), (60, 40, 100, 200, 150)])
     assert st == dsa.DSA_OK
-    assert n == al(100 * 192 * 4) + al(100 * 7 * 4)       # longest window 190 -> 192
+    assert n == 2 * al(100 * 192 * 4) + al(100 * 4) + al(100 * 7 * 4)   # longest window 190 -> 192
 
 
 @pytest.mark.parametrize("segs,n_q,n_k,why", [
@@ -127,6 +129,22 @@ def test_forward_workspace_checks(lib):
     assert _fwd(lib, need, workspace=None) == dsa.DSA_ERR_WORKSPACE
     # nothing to do: every segment is empty, returns OK without launching
     assert _fwd(lib, _ws(4, 4, 2, [(0, 0, 0, 4, 0)])[1], segs=((0, 0, 0, 4, 0),)) == dsa.DSA_OK
+
+
+def test_fused_indexer_topk_checks(lib):
+    def call(sh, ws_bytes, workspace=FAKE, idx=FAKE):
+        return lib.dsa_indexer_topk(ctypes.byref(sh), FAKE, None, FAKE, None, FAKE, idx,
+                                    workspace, ctypes.c_size_t(ws_bytes), None)
+    segs = [(0, 4, 0, 4, 0)]
+    sh = dsa._shape(n_q=4, n_k=4, h_idx=64, d_idx=128, topk=2, segments=segs)
+    need = _ws(4, 4, 2, segs)[1]
+    assert call(sh, need - 1) == dsa.DSA_ERR_WORKSPACE
+    assert call(sh, need, workspace=None) == dsa.DSA_ERR_WORKSPACE
+    assert call(sh, need, idx=None) == dsa.DSA_ERR_INVALID_ARG
+    bad = dsa._shape(n_q=4, n_k=4, h_idx=16, d_idx=128, topk=2, segments=segs)
+    assert call(bad, need) == dsa.DSA_ERR_UNSUPPORTED
+    empty = dsa._shape(n_q=4, n_k=4, h_idx=64, d_idx=128, topk=2, segments=[(0, 0, 0, 4, 0)])
+    assert call(empty, 0, workspace=None) == dsa.DSA_OK
 
 
 def _bwd(lib, sh, ws_bytes, workspace=FAKE, null_dkv=False):
