@@ -1,7 +1,7 @@
 """DSA forward benchmark on one MI355X: one CP rank's share of a 32K sequence.
 
-A step is one fused forward (indexer -> top-k -> sparse attention) over the whole local
-share, inputs resident in HBM.  Prints one JSON line: useful TFLOP/s of the step (indexer
+A step is one fused forward (indexer fused with the top-k -> sparse attention) over the
+whole local share, inputs resident in HBM.  Prints one JSON line: useful TFLOP/s of the step (indexer
 2*H_idx*d_idx per window key + attention 2*H*(d_qk+d_v) per selected key), queries/s, a
 roofline entry for the dominant kernel (sparse attention, MFMA-bound), per-stage timings and
 the CPU oracle's throughput on a bounded row sample.
@@ -266,6 +266,9 @@ def main():
         stages["topk_ms"] = time_launches(
             lambda: dsa.dsa_topk_select(scores, wl.segments, wl.topk, out=tk), reps, stream)
         del scores
+        stages["indexer_topk_fused_ms"] = time_launches(
+            lambda: dsa.dsa_indexer_topk(g["q_idx"], g["k_idx"], g["w_idx"], wl.segments,
+                                         wl.topk, out=tk, workspace=ws), reps, stream)
         stages["attention_ms"] = time_launches(
             lambda: dsa.dsa_sparse_attn(g["q"], g["kv"], idx, wl.softmax_scale, wl.d_v, out=out),
             reps, stream)
@@ -300,6 +303,7 @@ def main():
             "indexer_mfma_frac": W["f_idx"] / (ti * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "topk_ms": tt,
             "topk_gbs": W["topk_bytes"] / (tt * 1e-3) / 1e9,
+            "indexer_topk_fused_ms": stages["indexer_topk_fused_ms"],
             "attention_ms": t_attn,
             "attention_tflops": attn_tf,
             "attention_mfma_frac": attn_tf / PEAK_BF16_TFLOPS,
