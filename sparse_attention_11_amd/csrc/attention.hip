@@ -10,9 +10,9 @@
 // Mapping: one workgroup per query row, one wave per 32 query heads (4 waves for 128 heads,
 // one per SIMD), 32 selected keys per tile.
 //   * Gather: the tile's 32 latent rows are copied HBM -> LDS with global_load_lds (16 B per
-//     lane, no VGPR staging) into a ring of three tile buffers, so the gathers of the next two
-//     tiles overlap this tile's math.  Each wave copies whole rows, so the row base is a
-//     scalar (its index is read ahead through the scalar cache).  Rows are stored unpadded
+//     lane, no VGPR staging) into a ring of three tile buffers.  Each wave copies whole rows,
+//     so the row base is a scalar (the indices come in blocks of eight tiles through the
+//     vector-memory path, eight tiles ahead, and are moved to SGPRs).  Rows are stored unpadded
 //     with their 16-byte chunks XOR-swizzled by row, which keeps both the 16-row logits reads
 //     and the 4-row transposing value reads free of bank conflicts.  Empty slots gather row 0
 //     and are masked.
@@ -31,6 +31,13 @@
 //     transposing ds_read_b64_tr_b16) x P^T (B: the lane's bf16 probabilities, no shuffle).
 //     O^T is DV/32 M-tiles of 32 value columns; each lane owns one head's columns, so the
 //     final 1/l is lane-local.
+//   * Software pipeline (128 heads): with one wave per SIMD (the 128 x 512 fp32 accumulator
+//     of a row fills the register file) nothing hides a wave's own latencies, so each step
+//     interleaves two independent MFMA streams -- the logits of tile t+1 and the output
+//     product of tile t -- with the LDS operand reads, the gather of tile t+2 and the step's
+//     bookkeeping in their shadow; the softmax of tile t+1 runs under the second half of the
+//     output product.  One barrier per step.  The output accumulator is pinned to AGPRs and
+//     the logits accumulator to VGPRs (asm MFMAs), so no accumulator moves between the files.
 #include "attn_common.h"
 
 namespace dsa {
@@ -223,72 +230,6 @@ __device__ __forceinline__ bool tile_step(const AttnArgs& a, const RowCtx& c, co
   return over;
 }
 
-// ---- column-split value product ------------------------------------------------------------
-// LDS probabilities of a tile: [head][32 keys] bf16, 16-byte chunk c (keys 8c .. 8c+7) of head
-// h stored at chunk c ^ ((h >> 2) & 3), so 16 lanes reading one chunk of 16 heads hit 16
-// different bank groups.
-__device__ __forceinline__ int pchunk(int head, int c) { return c ^ ((head >> 2) & 3); }
-
-// The owner lane (head hl of the wave's 32, half g) stores keys 8g..8g+7 and 16+8g..16+8g+7.
-template <int H, int DQK, int DV>
-__device__ __forceinline__ void store_probs(const RowCtx& c, uint16_t* pb, const bf16x8* pf) {
-  const int head = c.wave * 32 + c.hl;
-  typedef __attribute__((address_space(3))) bf16x8* lds_b8_t;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-    *(lds_b8_t)((lds_u16_ptr_t)pb + head * 32 + pchunk(head, 2 * kk + c.g) * 8) = pf[kk];
-}
-
-// O^T[col, head] += V^T P^T over one tile for the wave's DV / NW columns and all heads:
-// o[mt][nt] is the 32-column tile 4 wave + mt of the 32-head tile nt.
-template <int H, int DQK, int DV>
-__device__ __forceinline__ void pv_cols(const RowCtx& c, const uint16_t* tile, const uint16_t* pb,
-                                        f32x16 (&o)[4][4]) {
-  using C = AttnCfg<H, DQK, DV>;
-  typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
-  // B fragments: P^T[key, head], lane (head hl of tile nt, half g) takes keys 16 kk + 8 g ..
-  auto pfrag = [&](int kk, int nt) {
-    const int head = nt * 32 + c.hl;
-    return *(lds_cb8_t)((lds_cptr_t)pb + head * 32 + pchunk(head, 2 * kk + c.g) * 8);
-  };
-  // A fragments: V^T via the transposing read (addressing as in tile_pv), column tile
-  // 4 wave + mt
-  const int G = c.lane >> 4, i = c.lane & 15;
-  const int low = 2 * (G & 1) + ((i & 3) >> 1);
-  const lds_cptr_t ltile = (lds_cptr_t)tile;
-  lds_cptr_t vb[2][2];
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int r = (G >> 1) * 8 + (i >> 2) + hf * 4;
-    const int sw = C::SWZ ? swz(r) : 0;
-    const lds_cptr_t b = ltile + r * C::ROWE + ((low ^ (sw & 3)) * 8) + (i & 1) * 4 + c.wave * 4 * 32;
-    vb[hf][0] = b + (sw >> 2) * 32;
-    vb[hf][1] = b - (sw >> 2) * 32;
-  }
-  auto vfrag = [&](int kk, int mt) {
-    const int off = kk * 16 * C::ROWE + mt * 32;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[0][mt & 1] + off));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[1][mt & 1] + off));
-    return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-  };
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    bf16x8 bp[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) bp[nt] = pfrag(kk, nt);
-    bf16x8 vf[2];
-    vf[0] = vfrag(kk, 0);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (mt + 1 < 4) vf[(mt + 1) & 1] = vfrag(kk, mt + 1);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[mt & 1], bp[nt], o[mt][nt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-}
-
 // Fast path: tiles in a 3-deep LDS ring (gathers of tiles t+1 and t+2 in flight while tile t
 // is computed).  The loop is unrolled by three so every buffer is a distinct LDS object with
 // a static role: the compiler then only waits for the gather of the buffer it reads, and
@@ -360,25 +301,191 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
   return true;
 }
 
-// Fast path with the column-split value product.  Same 3-deep gather ring as the plain fast
-// path (gathers of tiles t+1 and t+2 in flight while tile t is computed), but each step has
-// two halves: every wave computes the logits and probabilities of the tile for its 32 heads
-// and stores the probabilities in LDS; after a barrier every wave forms the output product
-// for its 128 value columns over all heads.  Each value element is then read from LDS once
-// per workgroup instead of once per wave.
+// ---- software-pipelined fast path ----------------------------------------------------------
+// One step of the pipelined loop.  The logits of tile kt (32 keys x the wave's 32 heads) are
+// interleaved with the output product of the previous tile vt, whose probabilities arrive in
+// pf; then the probabilities of kt are formed (returned in pf) while the second half of that
+// output product runs.  The gather of a later tile goes out piece by piece between the
+// MFMAs (gti: its slot indices for this wave's rows, wbg: LDS address of the wave's first row
+// in the destination buffer), and the bookkeeping of the step runs in their shadow: this
+// wave's validity bits of the gathered tile go to vmw, the bits of kt (every wave's) are read
+// from vmr.  Each lane owns one head's value columns, as in tile_pv.  Returns whether some
+// head's max outgrew the scaling range.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, const bf16x8* qf,
+                                          lds_cptr_t ktile, const unsigned* vmr, lds_cptr_t vtile,
+                                          bf16x8* pf, f32x16* o, float& m_used, float& m_true,
+                                          float& lsum, const TileIdx<H, DQK, DV>& gti,
+                                          unsigned* vmw, const unsigned* loff, unsigned wbg) {
+  using C = AttnCfg<H, DQK, DV>;
+  typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
+  unsigned so[C::RPW];                     // byte offsets of the gathered rows in kv
+#pragma unroll
+  for (int j = 0; j < C::RPW; ++j)
+    so[j] = (unsigned)gti.v[j] < (unsigned)a.n_k ? (unsigned)gti.v[j] * (C::CPR * 16u) : 0u;
+  unsigned vmw_in[C::NW];
+  // logits operands: addressing as in tile_logits
+  const int arow_i = key_perm(c.hl);
+  const int asw = C::SWZ ? swz(arow_i) : 0;
+  lds_cptr_t abase[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    abase[j] = ktile + arow_i * C::ROWE + (((2 * j + c.g) ^ asw) - 2 * j) * 8;
+  const uint16_t* qlrow = c.qlds + c.head * C::QROWE + c.g * 8;
+  constexpr int QG = 3;                    // K steps per prefetch group
+  constexpr int NG = C::KS / QG;
+  static_assert(C::KS % QG == 0, "logits K steps");
+  bf16x8 af[2][QG], bt[2][QG];
+  auto fetch = [&](int gi, int buf) {
+#pragma unroll
+    for (int u = 0; u < QG; ++u) {
+      const int ks = gi * QG + u;
+      af[buf][u] = *(lds_cb8_t)(abase[ks & 3] + ks * 16);
+      if (ks >= C::KSR) bt[buf][u] = *reinterpret_cast<const bf16x8*>(qlrow + (ks - C::KSR) * 16);
+    }
+  };
+  // value operands: addressing as in tile_pv
+  const int G = c.lane >> 4, i = c.lane & 15;
+  const int low = 2 * (G & 1) + ((i & 3) >> 1);
+  lds_cptr_t vb[2][2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int r = (G >> 1) * 8 + (i >> 2) + hf * 4;
+    const int sw = C::SWZ ? swz(r) : 0;
+    const lds_cptr_t b = vtile + r * C::ROWE + ((low ^ (sw & 3)) * 8) + (i & 1) * 4;
+    vb[hf][0] = b + (sw >> 2) * 32;
+    vb[hf][1] = b - (sw >> 2) * 32;
+  }
+  auto vfrag = [&](int j) {
+    const int kk = j / C::MTV, mt = j % C::MTV;
+    const int off = kk * 16 * C::ROWE + mt * 32;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[0][mt & 1] + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[1][mt & 1] + off));
+    return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  };
+  constexpr int NP = 2 * C::MTV;           // output-product MFMAs per tile
+  constexpr int NPA = NP / 2;              // of which interleaved with the logits
+  constexpr int PD = 2;                    // value fragments read ahead of their MFMA
+  bf16x8 vf[PD + 1];
+  // the accumulator stays in AGPRs (the logits accumulator and every operand in VGPRs): an
+  // asm MFMA pins it there, so the register allocator never swaps accumulators between the
+  // two files.  Only MFMAs read it until the row ends.
+  auto pv = [&](int j) {
+    if (j + PD < NP) vf[(j + PD) % (PD + 1)] = vfrag(j + PD);
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+a"(o[j % C::MTV]) : "v"(vf[j % (PD + 1)]), "v"(pf[j / C::MTV]));
+  };
+  // one piece (1 KB) of the wave's share of the next gather
+  auto gather_piece = [&](int gi) {
+    const int j0 = gi * 64 / C::CPR;
+    const int b = (j0 + 1) * C::CPR - 64 * gi;
+    unsigned ro = so[j0];
+    if (b < 64) ro = c.lane >= b ? so[j0 + 1] : ro;
+    const unsigned voff = loff[gi] + ro;
+    const unsigned m0v = wbg + (unsigned)gi * 1024u;
+    const uint16_t* base = a.kv;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
+  };
+
+  f32x16 s;
+  fetch(0, 0);
+#pragma unroll
+  for (int j = 0; j < PD; ++j) vf[j] = vfrag(j);
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int cur = gi & 1;
+    if (gi + 1 < NG) fetch(gi + 1, cur ^ 1);
+#pragma unroll
+    for (int u = 0; u < QG; ++u) {
+      const int ks = gi * QG + u;
+      const bf16x8 bq = ks < C::KSR ? qf[ks < C::KSR ? ks : 0] : bt[cur][u];
+      // the logits accumulator is pinned to VGPRs (the AGPRs hold the output accumulator);
+      // VALU reads it after the last step: wait out the MFMA write-to-read distance there
+      if (ks == 0)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(af[cur][u]), "v"(bq));
+      else if (ks == C::KS - 1)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+v"(s) : "v"(af[cur][u]), "v"(bq));
+      else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(af[cur][u]), "v"(bq));
+      if (ks >= 2 && ks < 2 + C::NI) gather_piece(ks - 2);
+#pragma unroll
+      for (int j = ks * NPA / C::KS; j < (ks + 1) * NPA / C::KS; ++j) pv(j);
+    }
+    if (gi == 4 && c.lane == 0) *vmw = tile_bits<H, DQK, DV>(a, gti);
+    if (gi == 5) {
+#pragma unroll
+      for (int w = 0; w < C::NW; ++w) vmw_in[w] = vmr[w];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  unsigned vmask = 0;
+#pragma unroll
+  for (int w = 0; w < C::NW; ++w) vmask |= vmw_in[w] << (w * C::RPW);
+
+  // probabilities of kt (as in tile_logits / tile_probs), interleaved with the second half
+  // of the output product of vt
+  if (vmask != 0xFFFFFFFFu) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (!((vmask >> acc_key(r, c.g)) & 1u)) s[r] = kNegInf;
+  }
+  float m = kNegInf;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m = fmaxf(m, s[r]);
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(m), __float_as_int(m), false, false);
+  const float mx = fmaxf(__int_as_float(pr[0]), __int_as_float(pr[1])) * a.scale_log2;
+  pv(NPA + 0);
+  pv(NPA + 1);
+  pv(NPA + 2);
+  pv(NPA + 3);
+  __builtin_amdgcn_sched_barrier(0);
+  m_true = fmaxf(m_true, mx);
+  if (m_used == kNegInf) m_used = mx;
+  const bool over = mx > m_used + kOverflowLog2;
+  const float msub = m_used == kNegInf ? 0.f : m_used;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float ls = 0.f;
+  bf16x8 pn[2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int r = 4 * q; r < 4 * q + 4; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -msub));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], a.scale_log2, -msub));
+      const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
+      ls = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, ls, false);
+      pn[r >> 3][r & 7] = pk[0];
+      pn[r >> 3][(r & 7) + 1] = pk[1];
+    }
+#pragma unroll
+    for (int j = NPA + 4 + 3 * q; j < NPA + 7 + 3 * q; ++j) pv(j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  static_assert(NPA + 4 + 3 * 4 == NP, "every output-product MFMA issued once");
+  lsum += ls;
+  pf[0] = pn[0];
+  pf[1] = pn[1];
+  return over;
+}
+
+// Pipelined fast path.  Same 3-deep LDS ring as the other fast paths, used one tile later:
+// step t forms the output product of tile t and the logits of tile t+1 while the gather of
+// tile t+2 is in flight, then waits for that gather and meets the other waves at the step's
+// only barrier.  The probabilities of tile 0 are formed before the loop; the last step's
+// logits run over the empty tile past the row's last valid slot (every key masked).
 template <int H, int DQK, int DV, bool AL8>
-__device__ __forceinline__ bool accumulate_csplit(const AttnArgs& a, const RowCtx& c,
-                                                  const bf16x8* qf, uint16_t* pbuf, float* lbuf) {
+__device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx& c,
+                                                const bf16x8* qf, int ib_cur, int ib_nxt) {
   using C = AttnCfg<H, DQK, DV>;
   constexpr int RPW = C::RPW;
-  f32x16 o[4][4];
+  f32x16 o[C::MTV];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) o[mt][nt] = (f32x16){};
+  for (int mt = 0; mt < C::MTV; ++mt) o[mt] = (f32x16){};
   float m_used = kNegInf, m_true = kNegInf, lsum = 0.f;
   bool overflow = false;
-  const int ntiles = (c.ntiles + 2) / 3 * 3;
   using TI = TileIdx<H, DQK, DV>;
   unsigned loff[C::NI];
   unsigned wb[3];
@@ -387,78 +494,69 @@ __device__ __forceinline__ bool accumulate_csplit(const AttnArgs& a, const RowCt
 #pragma unroll
   for (int k = 0; k < 3; ++k)
     wb[k] = (unsigned)(size_t)(lds_u16_ptr_t)(c.buf[k]) + c.wave_u * (RPW * C::ROWE * 2);
-  auto gather = [&](const TI& ti, int k) { gather_tile_flat<H, DQK, DV>(a, c, ti, loff, wb[k]); };
-  const TI i0 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 0);
-  const TI i1 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 1);
-  TI i2 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 2);
-  gather(i0, 0);
-  gather(i1, 1);
+  auto tile_mask = [&](int slot) {
+    unsigned vmask = 0;
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) vmask |= c.vm[slot * C::NW + w] << (w * RPW);
+    return vmask;
+  };
+  // index blocks (eight tiles each) of the tiles the loop gathers: ib_cur holds the block of
+  // tile t+2 at step t, ib_nxt the block after it
+  const TI i0 = tile_idx_from_block<H, DQK, DV>(ib_cur, 0);
+  const TI i1 = tile_idx_from_block<H, DQK, DV>(ib_cur, 1);
+  gather_tile_flat<H, DQK, DV>(a, c, i0, loff, wb[0]);
+  gather_tile_flat<H, DQK, DV>(a, c, i1, loff, wb[1]);
   if (c.lane == 0) {
     c.vm[0 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i0);
     c.vm[1 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i1);
   }
   wait_vm_barrier<C::GOPS>();          // tile 0 landed; tile 1 may be in flight
+  bf16x8 pf[2];
+  // overflow of this wave's heads, combined over the waves once the row is done
+  bool over_any = tile_probs<H, DQK, DV>(a, c, qf, c.buf[0], tile_mask(0), m_used, m_true, lsum,
+                                         pf);
+  wait_vm_barrier<0>();                // tile 1 landed
 
-  auto step = [&](int t, int slot, uint16_t* cur, int ahead2, TI& nxt2) {
-    const TI i3 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, t + 3);
-    gather(nxt2, ahead2);
-    if (c.lane == 0) c.vm[((slot + 2) % 3) * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, nxt2);
-    unsigned vmask = 0;
-#pragma unroll
-    for (int w = 0; w < C::NW; ++w) vmask |= c.vm[slot * C::NW + w] << (w * RPW);
-    bf16x8 pf[2];
-    const bool over = tile_probs<H, DQK, DV>(a, c, qf, cur, vmask, m_used, m_true, lsum, pf);
-    store_probs<H, DQK, DV>(c, pbuf, pf);
-    if (c.lane == 0) c.flags[(t & 1) * C::NW + c.wave] = __ballot(over) != 0ull;
-    // probabilities of every head visible (LDS only: the gathers stay in flight)
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    pv_cols<H, DQK, DV>(c, cur, pbuf, o);
-    wait_vm_barrier<C::GOPS>();        // tile t+1 landed for every wave; P and tile t free
-#pragma unroll
-    for (int w = 0; w < C::NW; ++w) overflow |= c.flags[(t & 1) * C::NW + w] != 0;
-    nxt2 = i3;
+  // step t: output product of t (slot sv) with the logits of t+1 (slot sk) and the gather of
+  // t+2 (slot sg, free since the previous step's barrier)
+  auto step = [&](int t, lds_cptr_t bv, lds_cptr_t bk, unsigned wbg, int sk, int sg) {
+    const int u = t + 2;
+    if ((u & 7) == 0) ib_cur = ib_nxt;
+    const TI nxt2 = tile_idx_from_block<H, DQK, DV>(ib_cur, u);
+    if ((u & 7) == 0) ib_nxt = load_idx_block<H, DQK, DV>(a, c, u / 8 + 1);   // read 8 tiles on
+    over_any |= pipe_tile<H, DQK, DV>(a, c, qf, bk, c.vm + sk * C::NW, bv, pf, o, m_used, m_true,
+                                      lsum, nxt2, c.vm + sg * C::NW + c.wave, loff, wbg);
+    wait_vm_barrier<0>();              // tile t+2 landed for every wave; tile t free
   };
-  for (int t = 0; t < ntiles; t += 3) {
-    step(t, 0, c.buf[0], 2, i2);
-    step(t + 1, 1, c.buf[1], 0, i2);
-    step(t + 2, 2, c.buf[2], 1, i2);
+  // one step per loop iteration, the ring slots (LDS addresses, gather bases and slot numbers)
+  // rotating in registers: the accumulator keeps its registers across iterations, and no
+  // indexed private array (scratch memory) is involved
+  lds_cptr_t bv = (lds_cptr_t)c.buf[0], bk = (lds_cptr_t)c.buf[1], bg = (lds_cptr_t)c.buf[2];
+  unsigned wv = wb[0], wk = wb[1], wg = wb[2];
+  int sv = 0, sk = 1, sg = 2;
+  for (int t = 0; t < c.ntiles; ++t) {
+    step(t, bv, bk, wg, sk, sg);
+    const lds_cptr_t b0 = bv;
+    bv = bk;
+    bk = bg;
+    bg = b0;
+    const unsigned w0 = wv;
+    wv = wk;
+    wk = wg;
+    wg = w0;
+    const int s0 = sv;
+    sv = sk;
+    sk = sg;
+    sg = s0;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no gather may outlive the block
-  if (overflow) return false;
-
-  // row sums of every head for the column owners
-  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(lsum), __float_as_int(lsum),
-                                                   false, false);
-  lsum = __int_as_float(pr[0]) + __int_as_float(pr[1]);
-  if (c.g == 0) lbuf[c.head] = lsum;
+  // no gather may outlive the block; the accumulator's last MFMA writes are read by VALU next
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  if (c.lane == 0) c.flags[c.wave] = __ballot(over_any) != 0ull;
   __syncthreads();
-  // o[mt][nt]: lane (head nt*32 + hl, half g), register r -> column
-  // 128 wave + 32 mt + (r / 4) * 8 + 4 g + r % 4
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int head = nt * 32 + c.hl;
-    const float l = lbuf[head];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* op = a.out + ((size_t)c.row * H + head) * DV + c.wave * 128;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int col = mt * 32 + q4 * 8 + c.g * 4;
-        const uint32_t lo = (uint32_t)f32_to_bf16(o[mt][nt][q4 * 4 + 0] * inv) |
-                            ((uint32_t)f32_to_bf16(o[mt][nt][q4 * 4 + 1] * inv) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(o[mt][nt][q4 * 4 + 2] * inv) |
-                            ((uint32_t)f32_to_bf16(o[mt][nt][q4 * 4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + col) = make_uint2(lo, hi);
-      }
-    }
-  }
-  if (c.g == 0) {
-    const size_t si = (size_t)c.row * H + c.head;
-    const bool any = m_true != kNegInf;
-    if (a.smax) a.smax[si] = any ? m_true * kLn2 : kNegInf;
-    if (a.ssum) a.ssum[si] = any ? lsum * exp2f(m_used - m_true) : 0.f;
-  }
+  for (int w = 0; w < C::NW; ++w) overflow |= c.flags[w] != 0;
+  if (overflow) return false;
+  write_row<H, DQK, DV>(a, c, o, lsum, m_used, m_true);
   return true;
 }
 
@@ -496,8 +594,6 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
   __shared__ __attribute__((aligned(16))) uint16_t kv1[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t kv2[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t qlds[C::QLDS];
-  __shared__ __attribute__((aligned(16))) uint16_t pbuf[C::PTILE];
-  __shared__ float lbuf[C::CSPLIT ? H : 1];
   __shared__ int flags[2 * C::NW];
   __shared__ unsigned vmring[3 * C::NW];
   __shared__ int s_last[C::NW];
@@ -543,6 +639,12 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
   if (c.lane == 0) s_last[c.wave] = last;
   bf16x8 qf[C::KSR];
+  // the pipelined path's first two index blocks travel with the Q loads
+  int ib0 = 0, ib1 = 0;
+  if constexpr (C::PIPE && !EXACT) {
+    ib0 = load_idx_block<H, DQK, DV>(a, c, 0);
+    ib1 = load_idx_block<H, DQK, DV>(a, c, 1);
+  }
   load_q<H, DQK, DV>(a, c, qf);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // staged Q landed (DMA is not tracked)
   __syncthreads();
@@ -570,7 +672,7 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
     accumulate_exact<H, DQK, DV>(a, c, qf, m_fix);
   } else {
     bool done;
-    if constexpr (C::CSPLIT) done = accumulate_csplit<H, DQK, DV, AL8>(a, c, qf, pbuf, lbuf);
+    if constexpr (C::PIPE) done = accumulate_pipe<H, DQK, DV, AL8>(a, c, qf, ib0, ib1);
     else done = accumulate_fast<H, DQK, DV, AL8>(a, c, qf);
     if (!done && c.tid == 0) a.out[(size_t)c.row * H * DV] = kOverflowMark;
   }

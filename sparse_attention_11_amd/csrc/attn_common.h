@@ -64,11 +64,9 @@ struct AttnCfg {
   // vector-memory instructions one wave issues per tile gather
   static constexpr int GOPS = FLAT ? NI : RPW * ((CPR + 63) / 64);
   static_assert(GOPS < 64, "vmcnt range");
-  // Value product split by output columns: each wave owns DV / NW columns for all heads and
-  // reads the probabilities of every head from LDS (instead of each wave reading the whole
-  // value tile for its own heads).
-  static constexpr bool CSPLIT = H == 128 && DV == 512 && NW == 4;
-  static constexpr int PTILE = CSPLIT ? H * NK : 8;   // bf16 probabilities per tile
+  // Software-pipelined fast path: the logits of tile t+1 are interleaved with the output
+  // product of tile t (each wave: its own heads, all value columns), one barrier per tile.
+  static constexpr bool PIPE = H == 128 && DV == 512 && NW == 4 && FLAT && NI <= KS;
   static_assert(DQK % 16 == 0 && DV % 32 == 0 && DV <= DQK && DQR % 16 == 0, "head dims");
 };
 
@@ -158,6 +156,30 @@ __device__ __forceinline__ TileIdx<H, DQK, DV> load_tile_idx_s(const Args& a,
       r.v[j] = slot < a.topk ? v : -1;
     }
   }
+  return r;
+}
+
+// The slot indices of tiles 8 blk .. 8 blk + 7 for this wave's rows, one VGPR per wave through
+// the vector-memory path: lane l holds slot (8 blk + l/8) NK + wave RPW + l%8 (-1 past topk).
+// Scalar loads share lgkmcnt with LDS reads and may return out of order, so while one is
+// outstanding every LDS operand wait becomes a full drain that also waits out the scalar
+// load's memory latency; this load counts against vmcnt, in order with the gathers, and a
+// block is fetched eight tiles before its first use.
+template <int H, int DQK, int DV, class Args>
+__device__ __forceinline__ int load_idx_block(const Args& a, const RowCtx& c, int blk) {
+  using C = AttnCfg<H, DQK, DV>;
+  static_assert(C::RPW == 8, "eight slots per wave and tile");
+  const int slot = (blk * 8 + (c.lane >> 3)) * C::NK + c.wave_u * C::RPW + (c.lane & 7);
+  return slot < a.topk ? c.idx_row[slot] : -1;
+}
+
+// The indices of tile u (block u / 8 in `ib`) as scalars; the block's load must have completed.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ TileIdx<H, DQK, DV> tile_idx_from_block(int ib, int u) {
+  TileIdx<H, DQK, DV> r;
+#pragma unroll
+  for (int j = 0; j < AttnCfg<H, DQK, DV>::RPW; ++j)
+    r.v[j] = __builtin_amdgcn_readlane(ib, (u & 7) * 8 + j);
   return r;
 }
 
