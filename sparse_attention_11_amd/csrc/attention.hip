@@ -456,6 +456,9 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
       const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -msub));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], a.scale_log2, -msub));
       const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
+      // pinned here, between the output-product MFMAs (pure arithmetic would otherwise sink
+      // past them to its use at the end of the step)
+      asm volatile("" :: "v"(pk));
       ls = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, ls, false);
       pn[r >> 3][r & 7] = pk[0];
       pn[r >> 3][(r & 7) + 1] = pk[1];
