@@ -186,6 +186,54 @@ __device__ __forceinline__ void write_row(const AttnArgs& a, const RowCtx& c, co
   }
 }
 
+// write_row through LDS: the wave's 32 output rows (bf16, 1 KB each) are assembled in `stage`
+// (32 KB of LDS no other wave uses any more), then each row leaves as one fully coalesced
+// 1 KB store, instead of 64 stores per wave that each touch 32 rows 16 bytes at a time.  In
+// `stage` the 16-byte chunk ch of head row hl sits at chunk ch ^ hl: the 8-byte writes of the
+// 32 heads of one column block then spread over the banks.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void write_row_staged(const AttnArgs& a, const RowCtx& c,
+                                                 const f32x16* o, float lsum, float m_used,
+                                                 float m_true, uint16_t* stage) {
+  using C = AttnCfg<H, DQK, DV>;
+  static_assert(H % 32 == 0 && DV == 512, "staged rows are 1 KB, 64 chunks");
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(lsum), __float_as_int(lsum),
+                                                   false, false);
+  lsum = __int_as_float(pr[0]) + __int_as_float(pr[1]);
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) u32x2* lds_u2_t;
+  typedef __attribute__((address_space(3))) const u32x4* lds_cu4_t;
+  const lds_u16_ptr_t srow = (lds_u16_ptr_t)stage + c.hl * DV;
+#pragma unroll
+  for (int mt = 0; mt < C::MTV; ++mt) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int ch = mt * 4 + q4;                       // logical 16-byte chunk (8 columns)
+      const uint32_t lo = (uint32_t)f32_to_bf16(o[mt][q4 * 4 + 0] * inv) |
+                          ((uint32_t)f32_to_bf16(o[mt][q4 * 4 + 1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(o[mt][q4 * 4 + 2] * inv) |
+                          ((uint32_t)f32_to_bf16(o[mt][q4 * 4 + 3] * inv) << 16);
+      *(lds_u2_t)(srow + (ch ^ c.hl) * 8 + c.g * 4) = (u32x2){lo, hi};
+    }
+  }
+  // each instruction: one head row, lane L carries logical chunk L (own wave's writes only,
+  // so the LDS counter orders them)
+  uint16_t* obase = a.out + ((size_t)c.row * H + c.wave * 32) * DV;
+#pragma unroll 4
+  for (int h = 0; h < 32; ++h) {
+    const u32x4 v = *(lds_cu4_t)((lds_u16_ptr_t)stage + h * DV + (c.lane ^ h) * 8);
+    *reinterpret_cast<u32x4*>(obase + (size_t)h * DV + c.lane * 8) = v;
+  }
+  if (c.g == 0) {
+    const size_t si = (size_t)c.row * H + c.head;
+    const bool any = m_true != kNegInf;
+    if (a.smax) a.smax[si] = any ? m_true * kLn2 : kNegInf;
+    if (a.ssum) a.ssum[si] = any ? lsum * exp2f(m_used - m_true) : 0.f;
+  }
+}
+
 // Logits and probabilities of one tile for the wave's heads (pf: the lane's 16 keys as the
 // B operand of the value product).  Returns whether some head's max exceeded the scaling max
 // by more than the fast path's range.
@@ -559,7 +607,12 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
 #pragma unroll
   for (int w = 0; w < C::NW; ++w) overflow |= c.flags[w] != 0;
   if (overflow) return false;
-  write_row<H, DQK, DV>(a, c, o, lsum, m_used, m_true);
+  // the ring and the staged Q are free (every wave is past the loop): 32 KB per wave
+  static_assert(C::TILE >= 32 * DV && C::QLDS >= 32 * DV && C::NW == 4, "staging space");
+  const lds_cptr_t stg = c.wave_u == 0 ? (lds_cptr_t)c.buf[0]
+                       : (c.wave_u == 1 ? (lds_cptr_t)c.buf[1]
+                       : (c.wave_u == 2 ? (lds_cptr_t)c.buf[2] : (lds_cptr_t)c.qlds));
+  write_row_staged<H, DQK, DV>(a, c, o, lsum, m_used, m_true, (uint16_t*)stg);
   return true;
 }
 
