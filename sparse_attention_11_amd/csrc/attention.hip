@@ -553,8 +553,8 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
   };
   // index blocks (eight tiles each) of the tiles the loop gathers: ib_cur holds the block of
   // tile t+2 at step t, ib_nxt the block after it
-  const TI i0 = tile_idx_from_block<H, DQK, DV>(ib_cur, 0);
-  const TI i1 = tile_idx_from_block<H, DQK, DV>(ib_cur, 1);
+  const TI i0 = tile_idx_from_block<H, DQK, DV>(a, c, ib_cur, 0);
+  const TI i1 = tile_idx_from_block<H, DQK, DV>(a, c, ib_cur, 1);
   gather_tile_flat<H, DQK, DV>(a, c, i0, loff, wb[0]);
   gather_tile_flat<H, DQK, DV>(a, c, i1, loff, wb[1]);
   if (c.lane == 0) {
@@ -573,7 +573,7 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
   auto step = [&](int t, lds_cptr_t bv, lds_cptr_t bk, unsigned wbg, int sk, int sg) {
     const int u = t + 2;
     if ((u & 7) == 0) ib_cur = ib_nxt;
-    const TI nxt2 = tile_idx_from_block<H, DQK, DV>(ib_cur, u);
+    const TI nxt2 = tile_idx_from_block<H, DQK, DV>(a, c, ib_cur, u);
     if ((u & 7) == 0) ib_nxt = load_idx_block<H, DQK, DV>(a, c, u / 8 + 1);   // read 8 tiles on
     over_any |= pipe_tile<H, DQK, DV>(a, c, qf, bk, c.vm + sk * C::NW, bv, pf, o, m_used, m_true,
                                       lsum, nxt2, c.vm + sg * C::NW + c.wave, loff, wbg);
@@ -638,24 +638,13 @@ __device__ __forceinline__ void accumulate_exact(const AttnArgs& a, const RowCtx
   write_row<H, DQK, DV>(a, c, o, lsum, m_used, m_true);
 }
 
-}  // namespace
-
-// EXACT = false: the fast path over blocks = rows (a block per row).
-// EXACT = true: a grid-stride pass that recomputes only rows the fast path marked, with the
-// row max found first so nothing can overflow.
+// One row of the fast path or of the exact pass (block index bi of nblk; the LDS arrays are
+// the kernel's).
 template <int H, int DQK, int DV, bool EXACT, bool AL8>
-__global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a) {
+__device__ __forceinline__ void attn_row(const AttnArgs& a, int bi, int nblk, uint16_t* kv0,
+                                         uint16_t* kv1, uint16_t* kv2, uint16_t* qlds, int* flags,
+                                         unsigned* vmring, int* s_last) {
   using C = AttnCfg<H, DQK, DV>;
-  __shared__ __attribute__((aligned(16))) uint16_t kv0[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t kv1[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t kv2[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t qlds[C::QLDS];
-  __shared__ int flags[2 * C::NW];
-  __shared__ unsigned vmring[3 * C::NW];
-  __shared__ int s_last[C::NW];
-
-  const int nblk = EXACT ? a.nrows : (int)gridDim.x;
-  for (int bi = EXACT ? (int)blockIdx.x : 0; bi < (EXACT ? nblk : 1); bi += (int)gridDim.x) {
   // XCD-aware row order: consecutive blocks go to different XCDs; give each XCD a contiguous
   // run of rows (neighbouring queries tend to select neighbouring keys).
   int blk = EXACT ? bi : (int)blockIdx.x;
@@ -669,7 +658,7 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
   }
   if (EXACT) {
     __syncthreads();   // the previous row's LDS use is over
-    if (a.out[(size_t)c.row * H * DV] != kOverflowMark) continue;
+    if (a.out[(size_t)c.row * H * DV] != kOverflowMark) return;
   }
   c.tid = threadIdx.x;
   c.lane = c.tid & 63;
@@ -686,22 +675,22 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
   c.flags = flags;
   c.vm = vmring;
 
-  // Row prologue with few memory round trips: the staged part of Q goes to LDS by LDS DMA,
-  // the index scan (tiles past the last valid slot are never gathered or computed) has its
-  // loads in flight together, and the register part of Q travels across the barrier.
+  // Row prologue in one memory round trip: the staged part of Q goes to LDS by LDS DMA, and
+  // the pipelined path's first two index blocks, the register part of Q and the index scan
+  // (tiles past the last valid slot are never gathered or computed) are all issued before
+  // anything waits.
   stage_q_tail<H, DQK, DV>(a, c, qlds);
-  int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
-  if (c.lane == 0) s_last[c.wave] = last;
-  bf16x8 qf[C::KSR];
-  // the pipelined path's first two index blocks travel with the Q loads
   int ib0 = 0, ib1 = 0;
   if constexpr (C::PIPE && !EXACT) {
     ib0 = load_idx_block<H, DQK, DV>(a, c, 0);
     ib1 = load_idx_block<H, DQK, DV>(a, c, 1);
   }
+  bf16x8 qf[C::KSR];
   load_q<H, DQK, DV>(a, c, qf);
+  int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if (c.lane == 0) s_last[c.wave] = last;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // staged Q landed (DMA is not tracked)
   __syncthreads();
   last = -1;
@@ -732,6 +721,34 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
     else done = accumulate_fast<H, DQK, DV, AL8>(a, c, qf);
     if (!done && c.tid == 0) a.out[(size_t)c.row * H * DV] = kOverflowMark;
   }
+}
+
+}  // namespace
+
+// EXACT = false: the fast path over blocks = rows (a block per row).
+// EXACT = true: a grid-stride pass that recomputes only rows the fast path marked, with the
+// row max found first so nothing can overflow.
+template <int H, int DQK, int DV, bool EXACT, bool AL8>
+__global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a) {
+  using C = AttnCfg<H, DQK, DV>;
+  __shared__ __attribute__((aligned(16))) uint16_t kv0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv1[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv2[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[C::QLDS];
+  __shared__ int flags[2 * C::NW];
+  __shared__ unsigned vmring[3 * C::NW];
+  __shared__ int s_last[C::NW];
+
+  const int nblk = EXACT ? a.nrows : (int)gridDim.x;
+  // one row per block on the fast path (no loop around it: per-lane values would be hoisted
+  // out of a loop and spilled, and their reloads would add memory round trips to the row
+  // prologue); the exact pass walks the rows in a grid-stride loop
+  if constexpr (EXACT) {
+    for (int bi = (int)blockIdx.x; bi < nblk; bi += (int)gridDim.x)
+      attn_row<H, DQK, DV, EXACT, AL8>(a, bi, nblk, kv0, kv1, kv2, qlds, flags, vmring, s_last);
+  } else {
+    attn_row<H, DQK, DV, EXACT, AL8>(a, (int)blockIdx.x, nblk, kv0, kv1, kv2, qlds, flags, vmring,
+                                     s_last);
   }
 }
 

@@ -92,7 +92,9 @@ template <int H, int DQK, int DV, class Args>
 __device__ __forceinline__ void gather_row(const Args& a, const RowCtx& c, int id, int key,
                                            uint16_t* dst) {
   using C = AttnCfg<H, DQK, DV>;
-  id = (id < 0 || id >= a.n_k) ? 0 : id;   // empty slot: any in-bounds row, masked later
+  // empty slot: any in-bounds row, masked later; the id is wave-uniform (one row per call),
+  // made explicit so the row base is an SGPR pair as the DMA's address operand requires
+  id = __builtin_amdgcn_readfirstlane((id < 0 || id >= a.n_k) ? 0 : id);
   const uint16_t* src = a.kv + (size_t)id * DQK;
   const unsigned sw16 = C::SWZ ? (unsigned)swz(key) * 16u : 0u;
   const unsigned voff = ((unsigned)c.lane * 16u) ^ sw16;
@@ -165,21 +167,30 @@ __device__ __forceinline__ TileIdx<H, DQK, DV> load_tile_idx_s(const Args& a,
 // outstanding every LDS operand wait becomes a full drain that also waits out the scalar
 // load's memory latency; this load counts against vmcnt, in order with the gathers, and a
 // block is fetched eight tiles before its first use.
+// The load is unconditional (address clamped to the row): a select on the loaded value would
+// make the compiler wait for the load right here; slots past topk are masked when the block
+// is read.
 template <int H, int DQK, int DV, class Args>
 __device__ __forceinline__ int load_idx_block(const Args& a, const RowCtx& c, int blk) {
   using C = AttnCfg<H, DQK, DV>;
   static_assert(C::RPW == 8, "eight slots per wave and tile");
   const int slot = (blk * 8 + (c.lane >> 3)) * C::NK + c.wave_u * C::RPW + (c.lane & 7);
-  return slot < a.topk ? c.idx_row[slot] : -1;
+  return c.idx_row[min(slot, a.topk - 1)];
 }
 
-// The indices of tile u (block u / 8 in `ib`) as scalars; the block's load must have completed.
-template <int H, int DQK, int DV>
-__device__ __forceinline__ TileIdx<H, DQK, DV> tile_idx_from_block(int ib, int u) {
+// The indices of tile u (block u / 8 in `ib`) as scalars, -1 past topk; the block's load must
+// have completed.
+template <int H, int DQK, int DV, class Args>
+__device__ __forceinline__ TileIdx<H, DQK, DV> tile_idx_from_block(const Args& a, const RowCtx& c,
+                                                                   int ib, int u) {
+  using C = AttnCfg<H, DQK, DV>;
   TileIdx<H, DQK, DV> r;
+  const int s0 = u * C::NK + c.wave_u * C::RPW;
 #pragma unroll
-  for (int j = 0; j < AttnCfg<H, DQK, DV>::RPW; ++j)
-    r.v[j] = __builtin_amdgcn_readlane(ib, (u & 7) * 8 + j);
+  for (int j = 0; j < C::RPW; ++j) {
+    const int v = __builtin_amdgcn_readlane(ib, (u & 7) * 8 + j);
+    r.v[j] = s0 + j < a.topk ? v : -1;
+  }
   return r;
 }
 
