@@ -218,6 +218,56 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
     }
   };
 
+  // Per 64-key half: the contraction (32 MFMAs into acc), then the epilogue.  The two waves of
+  // a SIMD (w and w + 4) would otherwise reach their epilogues together and leave the matrix
+  // pipe idle meanwhile; the upper four waves run each epilogue one half late (after the
+  // barrier, at the start of the next half), so one wave's MFMAs overlap the other's
+  // epilogue.  The late epilogue needs no more registers: it finishes with acc before the
+  // next contraction starts.
+  constexpr int NTK = kIdxKeys / 32;
+  f32x16 acc[NTK][MT];
+  auto mma = [&](int buf, int hh) {
+    // both 32-key sub-tiles are computed unconditionally (keys past the row's window are
+    // only masked at the store); K steps outer, so the MT x 2 accumulators form independent
+    // chains and consecutive MFMAs never wait for each other
+#pragma unroll
+    for (int nt = 0; nt < NTK; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 b[NTK];
+#pragma unroll
+      for (int nt = 0; nt < NTK; ++nt)
+        b[nt] = *reinterpret_cast<const bf16x8*>(&sk[buf][(hh * kIdxKeys + nt * 32 + hl) * ROW + ks * 16 + g * 8]);
+#pragma unroll
+      for (int nt = 0; nt < NTK; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[mt][ks], b[nt], acc[nt][mt], 0, 0, 0);
+    }
+  };
+  auto epi = [&](int kb) {   // kb: first key of the half
+    float sv[NTK];
+#pragma unroll
+    for (int nt = 0; nt < NTK; ++nt) {
+      float s = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s = relu_fma(acc[nt][mt][r], wv[mt][r], s);
+      sv[nt] = pair_sum(s);   // (both lanes of the pair hold the sum)
+    }
+    // lane (hl, g) takes key kb + 32 g + hl: 64 keys over the 64 lanes, in key order
+    static_assert(kIdxKeys == 64, "two 32-key groups per half-stage");
+    const int key = kb + 32 * g + hl;
+    const float sk_ = g ? sv[1] : sv[0];
+    if constexpr (CAND) cand_offer(cr, sk_, ri.k_lo + key, key <= ri.pos);
+    else if (key <= ri.pos) out[key] = sk_;
+  };
+  const bool lag = (tid >> 6) >= kIdxWaves / 2;   // wave-uniform
+  int pkb = -1;                                   // half whose epilogue is pending (lag waves)
+
   fetch(0);
   stash(0);
   __syncthreads();
@@ -226,46 +276,19 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
     if (t + 1 < ntiles) fetch(t + 1);
 #pragma unroll
     for (int hh = 0; hh < KST / kIdxKeys; ++hh) {
-    const int kb = t * KST + hh * kIdxKeys;   // first key of this 64-key half
-    if (ri.ok && kb <= ri.pos) {
-      // both 32-key sub-tiles are computed unconditionally (keys past the row's window are
-      // only masked at the store); K steps outer, so the MT x 2 accumulators form independent
-      // chains and consecutive MFMAs never wait for each other
-      constexpr int NT = kIdxKeys / 32;
-      f32x16 acc[NT][MT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = (f32x16){};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 b[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          b[nt] = *reinterpret_cast<const bf16x8*>(&sk[buf][(hh * kIdxKeys + nt * 32 + hl) * ROW + ks * 16 + g * 8]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[mt][ks], b[nt], acc[nt][mt], 0, 0, 0);
+      const int kb = t * KST + hh * kIdxKeys;   // first key of this 64-key half
+      const bool act = ri.ok && kb <= ri.pos;
+      if (lag) {
+        if (pkb >= 0) epi(pkb);
+        pkb = -1;
+        if (act) {
+          mma(buf, hh);
+          pkb = kb;
+        }
+      } else if (act) {
+        mma(buf, hh);
+        epi(kb);
       }
-      float sv[kIdxKeys / 32];
-#pragma unroll
-      for (int nt = 0; nt < kIdxKeys / 32; ++nt) {
-        float s = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s = relu_fma(acc[nt][mt][r], wv[mt][r], s);
-        sv[nt] = pair_sum(s);   // (both lanes of the pair hold the sum)
-      }
-      // lane (hl, g) takes key kb + 32 g + hl: 64 keys over the 64 lanes, in key order
-      static_assert(kIdxKeys == 64, "two 32-key groups per half-stage");
-      const int key = kb + 32 * g + hl;
-      const float sk_ = g ? sv[1] : sv[0];
-      if constexpr (CAND) cand_offer(cr, sk_, ri.k_lo + key, key <= ri.pos);
-      else if (key <= ri.pos) out[key] = sk_;
-    }
     }
     if constexpr (CAND) {   // every fourth stage: the bound only needs to rise now and then
       if (ri.ok && t * KST <= ri.pos && (t & 3) == 3) cand_update(cr, a.topk);
@@ -273,6 +296,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
     if (t + 1 < ntiles) stash(buf ^ 1);
     __syncthreads();
   }
+  if (pkb >= 0) epi(pkb);
   if constexpr (CAND) {
     if (ri.ok && lane == 0) a.cand_cnt[ri.row] = cr.n;
   }
