@@ -68,6 +68,31 @@ def time_launches(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
+def per_step_timing(step, stream, reps, cold_reps=5, scratch_bytes=512 << 20):
+    """Each forward step timed on its own (HIP events on the launch stream): median and min
+    with the caches warm (steps back to back), and with them cold (a 512 MB buffer, twice the
+    256 MB MALL, is overwritten before each timed step; the fill is outside the timed span)."""
+    def one(before=None):
+        if before is not None:
+            before()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+    warm = [one() for _ in range(reps)]
+    scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device=torch.device("cuda:0"))
+    cold = [one(lambda i=i: scratch.fill_(i & 0xFF)) for i in range(cold_reps)]
+    del scratch
+    return {"warm": {"median_ms": float(np.median(warm)), "min_ms": float(np.min(warm)),
+                     "steps": reps},
+            "cold": {"median_ms": float(np.median(cold)), "min_ms": float(np.min(cold)),
+                     "steps": cold_reps,
+                     "flush": "512 MB buffer overwritten before each timed step"}}
+
+
 def cpu_baseline(wl, budget_s=15.0, max_rows=2048):
     """The float64 oracle on a seeded sample of the workload's rows, on the host cores."""
     import oracle
@@ -254,6 +279,14 @@ def main():
     ms = t0.elapsed_time(t1) / args.steps
     print(f"bench: forward {ms:.3f} ms/step", file=sys.stderr, flush=True)
     idx = res[1]
+    # (left out of the counter runs: cold steps would change the per-launch averages there;
+    # an auxiliary figure, so a failure here is reported in the line instead of ending the run)
+    timing = None
+    if not args.calibrate_copy:
+        try:
+            timing = per_step_timing(step, stream, reps=max(3, min(args.steps, 10)))
+        except Exception as e:  # noqa: BLE001
+            timing = {"error": f"{type(e).__name__}: {e}"}
 
     stages = {}
     if not args.no_stages:
@@ -294,6 +327,7 @@ def main():
                    "d_qk": wl.d_qk, "d_v": wl.d_v, "parallelism": "one CP rank's share"},
         "queries_per_s": wl.n_q / (ms * 1e-3),
         "useful_tflop": (W["f_idx"] + W["f_attn"]) / 1e12,
+        "step_timing": timing,
     }
     if stages:
         ti, tt = stages["indexer_ms"], stages["topk_ms"]
