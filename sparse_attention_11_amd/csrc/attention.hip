@@ -354,23 +354,19 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
 // interleaved with the output product of the previous tile vt, whose probabilities arrive in
 // pf; then the probabilities of kt are formed (returned in pf) while the second half of that
 // output product runs.  The gather of a later tile goes out piece by piece between the
-// MFMAs (gti: its slot indices for this wave's rows, wbg: LDS address of the wave's first row
-// in the destination buffer), and the bookkeeping of the step runs in their shadow: this
-// wave's validity bits of the gathered tile go to vmw, the bits of kt (every wave's) are read
-// from vmr.  Each lane owns one head's value columns, as in tile_pv.  Returns whether some
+// MFMAs (so: byte offsets in kv of this wave's rows of it, wbg: LDS address of the wave's
+// first row in the destination buffer), and the bookkeeping of the step runs in their shadow:
+// this wave's validity bits of the gathered tile (gbits) go to vmw, the bits of kt (every
+// wave's) are read from vmr.  Each lane owns one head's value columns, as in tile_pv.  Returns whether some
 // head's max outgrew the scaling range.
 template <int H, int DQK, int DV>
 __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, const bf16x8* qf,
                                           lds_cptr_t ktile, const unsigned* vmr, lds_cptr_t vtile,
                                           bf16x8* pf, f32x16* o, float& m_used, float& m_true,
-                                          float& lsum, const TileIdx<H, DQK, DV>& gti,
+                                          float& lsum, const unsigned* so, unsigned gbits,
                                           unsigned* vmw, const unsigned* loff, unsigned wbg) {
   using C = AttnCfg<H, DQK, DV>;
   typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
-  unsigned so[C::RPW];                     // byte offsets of the gathered rows in kv
-#pragma unroll
-  for (int j = 0; j < C::RPW; ++j)
-    so[j] = (unsigned)gti.v[j] < (unsigned)a.n_k ? (unsigned)gti.v[j] * (C::CPR * 16u) : 0u;
   unsigned vmw_in[C::NW];
   // logits operands: addressing as in tile_logits
   const int arow_i = key_perm(c.hl);
@@ -461,7 +457,7 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
 #pragma unroll
       for (int j = ks * NPA / C::KS; j < (ks + 1) * NPA / C::KS; ++j) pv(j);
     }
-    if (gi == 4 && c.lane == 0) *vmw = tile_bits<H, DQK, DV>(a, gti);
+    if (gi == 4 && c.lane == 0) *vmw = gbits;
     if (gi == 5) {
 #pragma unroll
       for (int w = 0; w < C::NW; ++w) vmw_in[w] = vmr[w];
@@ -537,7 +533,6 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
   for (int mt = 0; mt < C::MTV; ++mt) o[mt] = (f32x16){};
   float m_used = kNegInf, m_true = kNegInf, lsum = 0.f;
   bool overflow = false;
-  using TI = TileIdx<H, DQK, DV>;
   unsigned loff[C::NI];
   unsigned wb[3];
 #pragma unroll
@@ -551,15 +546,19 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
     for (int w = 0; w < C::NW; ++w) vmask |= c.vm[slot * C::NW + w] << (w * RPW);
     return vmask;
   };
-  // index blocks (eight tiles each) of the tiles the loop gathers: ib_cur holds the block of
-  // tile t+2 at step t, ib_nxt the block after it
-  const TI i0 = tile_idx_from_block<H, DQK, DV>(a, c, ib_cur, 0);
-  const TI i1 = tile_idx_from_block<H, DQK, DV>(a, c, ib_cur, 1);
-  gather_tile_flat<H, DQK, DV>(a, c, i0, loff, wb[0]);
-  gather_tile_flat<H, DQK, DV>(a, c, i1, loff, wb[1]);
+  // index blocks (eight tiles each) of the tiles the loop gathers: gcur holds the block of
+  // tile t+2 at step t, converted to row offsets and validity bits; ib_nxt the raw block after it
+  GatherBlk gcur = gather_blk<H, DQK, DV>(a, c, ib_cur, 0);
+  {
+    unsigned so0[RPW], so1[RPW];
+    tile_offsets<H, DQK, DV>(gcur, 0, so0);
+    tile_offsets<H, DQK, DV>(gcur, 1, so1);
+    gather_tile_flat_so<H, DQK, DV>(a, c, so0, loff, wb[0]);
+    gather_tile_flat_so<H, DQK, DV>(a, c, so1, loff, wb[1]);
+  }
   if (c.lane == 0) {
-    c.vm[0 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i0);
-    c.vm[1 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i1);
+    c.vm[0 * C::NW + c.wave] = tile_vbits(gcur, 0);
+    c.vm[1 * C::NW + c.wave] = tile_vbits(gcur, 1);
   }
   wait_vm_barrier<C::GOPS>();          // tile 0 landed; tile 1 may be in flight
   bf16x8 pf[2];
@@ -572,11 +571,13 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
   // t+2 (slot sg, free since the previous step's barrier)
   auto step = [&](int t, lds_cptr_t bv, lds_cptr_t bk, unsigned wbg, int sk, int sg) {
     const int u = t + 2;
-    if ((u & 7) == 0) ib_cur = ib_nxt;
-    const TI nxt2 = tile_idx_from_block<H, DQK, DV>(a, c, ib_cur, u);
+    if ((u & 7) == 0) gcur = gather_blk<H, DQK, DV>(a, c, ib_nxt, u / 8);
+    unsigned so[RPW];
+    tile_offsets<H, DQK, DV>(gcur, u, so);
+    const unsigned gbits = tile_vbits(gcur, u);
     if ((u & 7) == 0) ib_nxt = load_idx_block<H, DQK, DV>(a, c, u / 8 + 1);   // read 8 tiles on
     over_any |= pipe_tile<H, DQK, DV>(a, c, qf, bk, c.vm + sk * C::NW, bv, pf, o, m_used, m_true,
-                                      lsum, nxt2, c.vm + sg * C::NW + c.wave, loff, wbg);
+                                      lsum, so, gbits, c.vm + sg * C::NW + c.wave, loff, wbg);
     wait_vm_barrier<0>();              // tile t+2 landed for every wave; tile t free
   };
   // one step per loop iteration, the ring slots (LDS addresses, gather bases and slot numbers)

@@ -194,6 +194,39 @@ __device__ __forceinline__ TileIdx<H, DQK, DV> tile_idx_from_block(const Args& a
   return r;
 }
 
+// An index block (see load_idx_block) turned, once per eight tiles, into what the gather needs:
+// each lane's byte offset of its slot's latent row in kv (0 for a slot past topk or an index
+// outside [0, n_k): such rows are gathered from row 0 and masked), and the validity ballot,
+// whose byte b holds the bits of tile 8 blk + b for this wave's rows.  Per tile the gather
+// then needs eight lane reads and a shift, not a compare-and-select chain per slot.
+struct GatherBlk {
+  unsigned off;
+  uint64_t bits;
+};
+
+template <int H, int DQK, int DV, class Args>
+__device__ __forceinline__ GatherBlk gather_blk(const Args& a, const RowCtx& c, int raw, int blk) {
+  using C = AttnCfg<H, DQK, DV>;
+  const int slot = (blk * 8 + (c.lane >> 3)) * C::NK + c.wave_u * C::RPW + (c.lane & 7);
+  const bool ok = slot < a.topk && (unsigned)raw < (unsigned)a.n_k;
+  GatherBlk g;
+  g.off = ok ? (unsigned)raw * (C::CPR * 16u) : 0u;
+  g.bits = __ballot(ok);
+  return g;
+}
+
+// Row byte offsets (scalars) of this wave's rows of tile u, from the block holding u.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void tile_offsets(const GatherBlk& g, int u, unsigned* so) {
+  static_assert(AttnCfg<H, DQK, DV>::RPW == 8, "eight slots per wave and tile");
+#pragma unroll
+  for (int j = 0; j < 8; ++j) so[j] = __builtin_amdgcn_readlane(g.off, (u & 7) * 8 + j);
+}
+
+__device__ __forceinline__ unsigned tile_vbits(const GatherBlk& g, int u) {
+  return (unsigned)(g.bits >> ((u & 7) * 8)) & 0xFFu;
+}
+
 // Validity bits of this wave's slots of a tile (bit j: row wave*RPW + j).
 template <int H, int DQK, int DV, class Args>
 __device__ __forceinline__ unsigned tile_bits(const Args& a, const TileIdx<H, DQK, DV>& ti) {
@@ -233,18 +266,14 @@ __device__ __forceinline__ unsigned flat_lane_offset(const RowCtx& c, int i) {
   return (unsigned)(ch ^ sw) * 16u;
 }
 
-// Flat gather of this wave's rows of a tile.  wb: LDS byte address of the wave's first row.
-// The row offsets are scalars; each lane picks the one of the (at most two) rows its chunk
-// falls in.  Empty slots copy row 0 (masked later).
+// Flat gather of this wave's rows of a tile.  wb: LDS byte address of the wave's first row;
+// so: byte offsets of the rows in kv, scalars (0 for empty slots: row 0 is copied and masked
+// later).  Each lane picks the one of the (at most two) rows its chunk falls in.
 template <int H, int DQK, int DV, class Args>
-__device__ __forceinline__ void gather_tile_flat(const Args& a, const RowCtx& c,
-                                                 const TileIdx<H, DQK, DV>& ti,
-                                                 const unsigned* loff, unsigned wb) {
+__device__ __forceinline__ void gather_tile_flat_so(const Args& a, const RowCtx& c,
+                                                    const unsigned* so, const unsigned* loff,
+                                                    unsigned wb) {
   using C = AttnCfg<H, DQK, DV>;
-  unsigned so[C::RPW];
-#pragma unroll
-  for (int j = 0; j < C::RPW; ++j)
-    so[j] = (unsigned)ti.v[j] < (unsigned)a.n_k ? (unsigned)ti.v[j] * (C::CPR * 16u) : 0u;
   static_for<C::NI>([&](auto I) {
     constexpr int i = decltype(I)::value;
     constexpr int j0 = i * 64 / C::CPR;              // row of lane 0
@@ -258,6 +287,19 @@ __device__ __forceinline__ void gather_tile_flat(const Args& a, const RowCtx& c,
     asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3"
                  :: "s"(m0v), "n"(i * 1024), "v"(voff), "s"(base) : "memory", "m0", "scc");
   });
+}
+
+// The same from the tile's slot indices (-1 or out of range: empty).
+template <int H, int DQK, int DV, class Args>
+__device__ __forceinline__ void gather_tile_flat(const Args& a, const RowCtx& c,
+                                                 const TileIdx<H, DQK, DV>& ti,
+                                                 const unsigned* loff, unsigned wb) {
+  using C = AttnCfg<H, DQK, DV>;
+  unsigned so[C::RPW];
+#pragma unroll
+  for (int j = 0; j < C::RPW; ++j)
+    so[j] = (unsigned)ti.v[j] < (unsigned)a.n_k ? (unsigned)ti.v[j] * (C::CPR * 16u) : 0u;
+  gather_tile_flat_so<H, DQK, DV>(a, c, so, loff, wb);
 }
 
 // Wait until at most N of this wave's vector-memory instructions are outstanding, then meet
