@@ -54,18 +54,23 @@ def work(wl):
                 topk_bytes=float(L.sum() * 4 + L.size * wl.topk * 4))
 
 
-def time_launches(fn, reps, stream):
-    """Average duration of fn() over reps launches, HIP events on the launch stream."""
+def time_launches(fn, reps, stream, trials=3):
+    """Average duration of fn() over reps back-to-back launches, HIP events on the launch
+    stream; the median of `trials` such averages (one slow stretch of the box does not set the
+    figure; every launch of the median trial counts)."""
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     fn()
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(reps):
-        fn()
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / reps
+    avg = []
+    for _ in range(trials):
+        start.record(stream)
+        for _ in range(reps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        avg.append(start.elapsed_time(end) / reps)
+    return float(np.median(avg))
 
 
 def per_step_timing(step, stream, reps, cold_reps=5, scratch_bytes=512 << 20):

@@ -745,8 +745,26 @@ __global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn(AttnArgs a
   // out of a loop and spilled, and their reloads would add memory round trips to the row
   // prologue); the exact pass walks the rows in a grid-stride loop
   if constexpr (EXACT) {
-    for (int bi = (int)blockIdx.x; bi < nblk; bi += (int)gridDim.x)
-      attn_row<H, DQK, DV, EXACT, AL8>(a, bi, nblk, kv0, kv1, kv2, qlds, flags, vmring, s_last);
+    // block b owns rows b, b + G, b + 2G, ... (G = gridDim.x); their marks are checked C::NT
+    // at a time, one per thread, so a group with no marked row (the normal case) costs one
+    // load per thread
+    const int G = (int)gridDim.x;
+    for (int j0 = 0; (int)blockIdx.x + j0 * G < nblk; j0 += C::NT) {
+      const int bi = (int)blockIdx.x + (j0 + (int)threadIdx.x) * G;
+      bool marked = false;
+      if (bi < nblk) {
+        int row = bi;
+        if (a.use_segs) {
+          const int g = seg_of_block(a.segs, bi);
+          row = a.segs.q_start[g] + (bi - a.segs.blk_off[g]);
+        }
+        marked = a.out[(size_t)row * H * DV] == kOverflowMark;
+      }
+      if (!__syncthreads_or(marked)) continue;
+      for (int k = 0; k < C::NT && (int)blockIdx.x + (j0 + k) * G < nblk; ++k)
+        attn_row<H, DQK, DV, EXACT, AL8>(a, (int)blockIdx.x + (j0 + k) * G, nblk, kv0, kv1, kv2,
+                                         qlds, flags, vmring, s_last);
+    }
   } else {
     attn_row<H, DQK, DV, EXACT, AL8>(a, (int)blockIdx.x, nblk, kv0, kv1, kv2, qlds, flags, vmring,
                                      s_last);

@@ -225,6 +225,34 @@ def test_sparse_attn_large_logit_growth_takes_exact_path():
                     atol=atol)
 
 
+def test_forward_large_logit_growth_exact_path_deepseek_dims():
+    """DeepSeek-V3.2 dims, two segments, every window selected whole: latent row 200 is aligned
+    with head 0 of row 0 and lies past the row's first tile, so the fast path gives the row up
+    and the exact pass (which scans the rows' marks in parallel) recomputes it.  The fused
+    forward and the standalone attention on its indices both match the oracle."""
+    _need_gpu()
+    wl = I.workload(2).with_(n_q=64, n_k=256, topk=256, seed=777, with_dout=False,
+                             segments=((0, 32, 0, 256, 200), (32, 32, 0, 256, 224)))
+    x = I.generate(wl)
+    x["kv"][200] = (x["q"][0, 0].float() * 8).to(torch.bfloat16)
+    g = {k: v.cuda() for k, v in x.items()}
+    out, idx, smax, ssum = dsa.dsa_forward(g["q_idx"], g["k_idx"], g["w_idx"], g["q"], g["kv"],
+                                           wl.segments, wl.topk, wl.softmax_scale, wl.d_v)
+    out2, smax2, ssum2 = dsa.dsa_sparse_attn(g["q"], g["kv"], idx, wl.softmax_scale, wl.d_v)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy().astype(np.int64)
+    # topk covers every window: each row selects exactly its window
+    k_lo, L = _windows(wl, np.arange(wl.n_q))
+    for r in range(wl.n_q):
+        assert np.array_equal(np.sort(gi[r][gi[r] >= 0]), np.arange(k_lo[r], k_lo[r] + L[r]))
+    ro, rm, rs = O.sparse_attn(f64(x["q"]), f64(x["kv"]), gi, wl.softmax_scale, wl.d_v)
+    assert rm[0, 0] - np.median(rm) > 64 * math.log(2), "case does not overflow"
+    atol = 2e-2 + 2.0 ** -9 * float(x["kv"][:, :wl.d_v].float().abs().max())
+    for o, m, s_ in ((out, smax, ssum), (out2, smax2, ssum2)):
+        check_attention(o.float().cpu().numpy(), m.cpu().numpy(), s_.cpu().numpy(), ro, rm, rs,
+                        atol=atol)
+
+
 # ------------------------------------------------------------------------- fused forward ----
 
 def _check_forward(wl, x, out, idx, smax, ssum, rows, ref, max_flip_frac=0.2):
