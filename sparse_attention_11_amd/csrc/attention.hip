@@ -359,7 +359,12 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
 // this wave's validity bits of the gathered tile (gbits) go to vmw, the bits of kt (every
 // wave's) are read from vmr.  Each lane owns one head's value columns, as in tile_pv.  Returns whether some
 // head's max outgrew the scaling range.
-template <int H, int DQK, int DV>
+// MODE: kStepFull as above; kStepNoGather for the step whose later tile would lie past the
+// row's last valid slot (nothing to gather); kStepPvOnly for the row's last step: the output
+// product of vt alone (there is no later tile to form logits for).
+constexpr int kStepFull = 0, kStepNoGather = 1, kStepPvOnly = 2;
+
+template <int H, int DQK, int DV, int MODE>
 __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, const bf16x8* qf,
                                           lds_cptr_t ktile, const unsigned* vmr, lds_cptr_t vtile,
                                           bf16x8* pf, f32x16* o, float& m_used, float& m_true,
@@ -432,17 +437,24 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
                  :: "s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
   };
 
+  constexpr bool LOGITS = MODE != kStepPvOnly;
+  constexpr bool GATHER = MODE == kStepFull;
   f32x16 s;
-  fetch(0, 0);
+  if constexpr (LOGITS) fetch(0, 0);
 #pragma unroll
   for (int j = 0; j < PD; ++j) vf[j] = vfrag(j);
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     const int cur = gi & 1;
-    if (gi + 1 < NG) fetch(gi + 1, cur ^ 1);
+    if (LOGITS && gi + 1 < NG) fetch(gi + 1, cur ^ 1);
 #pragma unroll
     for (int u = 0; u < QG; ++u) {
       const int ks = gi * QG + u;
+      if constexpr (!LOGITS) {
+#pragma unroll
+        for (int j = ks * NPA / C::KS; j < (ks + 1) * NPA / C::KS; ++j) pv(j);
+        continue;
+      }
       const bf16x8 bq = ks < C::KSR ? qf[ks < C::KSR ? ks : 0] : bt[cur][u];
       // the logits accumulator is pinned to VGPRs (the AGPRs hold the output accumulator);
       // VALU reads it after the last step: wait out the MFMA write-to-read distance there
@@ -453,16 +465,21 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
                      : "+v"(s) : "v"(af[cur][u]), "v"(bq));
       else
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(af[cur][u]), "v"(bq));
-      if (ks >= 2 && ks < 2 + C::NI) gather_piece(ks - 2);
+      if (GATHER && ks >= 2 && ks < 2 + C::NI) gather_piece(ks - 2);
 #pragma unroll
       for (int j = ks * NPA / C::KS; j < (ks + 1) * NPA / C::KS; ++j) pv(j);
     }
-    if (gi == 4 && c.lane == 0) *vmw = gbits;
-    if (gi == 5) {
+    if (GATHER && gi == 4 && c.lane == 0) *vmw = gbits;
+    if (LOGITS && gi == 5) {
 #pragma unroll
       for (int w = 0; w < C::NW; ++w) vmw_in[w] = vmr[w];
     }
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (!LOGITS) {
+#pragma unroll
+    for (int j = NPA; j < NP; ++j) pv(j);
+    return false;
   }
   unsigned vmask = 0;
 #pragma unroll
@@ -568,17 +585,24 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
   wait_vm_barrier<0>();                // tile 1 landed
 
   // step t: output product of t (slot sv) with the logits of t+1 (slot sk) and the gather of
-  // t+2 (slot sg, free since the previous step's barrier)
-  auto step = [&](int t, lds_cptr_t bv, lds_cptr_t bk, unsigned wbg, int sk, int sg) {
-    const int u = t + 2;
-    if ((u & 7) == 0) gcur = gather_blk<H, DQK, DV>(a, c, ib_nxt, u / 8);
-    unsigned so[RPW];
-    tile_offsets<H, DQK, DV>(gcur, u, so);
-    const unsigned gbits = tile_vbits(gcur, u);
-    if ((u & 7) == 0) ib_nxt = load_idx_block<H, DQK, DV>(a, c, u / 8 + 1);   // read 8 tiles on
-    over_any |= pipe_tile<H, DQK, DV>(a, c, qf, bk, c.vm + sk * C::NW, bv, pf, o, m_used, m_true,
-                                      lsum, so, gbits, c.vm + sg * C::NW + c.wave, loff, wbg);
-    wait_vm_barrier<0>();              // tile t+2 landed for every wave; tile t free
+  // t+2 (slot sg, free since the previous step's barrier).  Tiles past the row's last valid
+  // slot are neither gathered nor computed: step ntiles-2 gathers nothing, and the last step
+  // is the output product of tile ntiles-1 alone.
+  auto step = [&](auto mode, int t, lds_cptr_t bv, lds_cptr_t bk, unsigned wbg, int sk, int sg) {
+    constexpr int MODE = decltype(mode)::value;
+    unsigned so[RPW] = {};
+    unsigned gbits = 0u;
+    if constexpr (MODE == kStepFull) {
+      const int u = t + 2;
+      if ((u & 7) == 0) gcur = gather_blk<H, DQK, DV>(a, c, ib_nxt, u / 8);
+      tile_offsets<H, DQK, DV>(gcur, u, so);
+      gbits = tile_vbits(gcur, u);
+      if ((u & 7) == 0) ib_nxt = load_idx_block<H, DQK, DV>(a, c, u / 8 + 1);   // 8 tiles on
+    }
+    over_any |= pipe_tile<H, DQK, DV, MODE>(a, c, qf, bk, c.vm + sk * C::NW, bv, pf, o, m_used,
+                                            m_true, lsum, so, gbits,
+                                            c.vm + sg * C::NW + c.wave, loff, wbg);
+    if constexpr (MODE != kStepPvOnly) wait_vm_barrier<0>();   // tile t+2 landed; t free
   };
   // one step per loop iteration, the ring slots (LDS addresses, gather bases and slot numbers)
   // rotating in registers: the accumulator keeps its registers across iterations, and no
@@ -586,8 +610,7 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
   lds_cptr_t bv = (lds_cptr_t)c.buf[0], bk = (lds_cptr_t)c.buf[1], bg = (lds_cptr_t)c.buf[2];
   unsigned wv = wb[0], wk = wb[1], wg = wb[2];
   int sv = 0, sk = 1, sg = 2;
-  for (int t = 0; t < c.ntiles; ++t) {
-    step(t, bv, bk, wg, sk, sg);
+  auto rotate = [&]() {
     const lds_cptr_t b0 = bv;
     bv = bk;
     bk = bg;
@@ -600,7 +623,16 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
     sv = sk;
     sk = sg;
     sg = s0;
+  };
+  for (int t = 0; t < c.ntiles - 2; ++t) {
+    step(std::integral_constant<int, kStepFull>{}, t, bv, bk, wg, sk, sg);
+    rotate();
   }
+  if (c.ntiles >= 2) {
+    step(std::integral_constant<int, kStepNoGather>{}, c.ntiles - 2, bv, bk, wg, sk, sg);
+    rotate();
+  }
+  if (c.ntiles >= 1) step(std::integral_constant<int, kStepPvOnly>{}, c.ntiles - 1, bv, bk, wg, sk, sg);
   // no gather may outlive the block; the accumulator's last MFMA writes are read by VALU next
   asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   if (c.lane == 0) c.flags[c.wave] = __ballot(over_any) != 0ull;
