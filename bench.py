@@ -3,8 +3,9 @@
 A step is one fused forward (indexer fused with the top-k -> sparse attention) over the
 whole local share, inputs resident in HBM.  Prints one JSON line: useful TFLOP/s of the step (indexer
 2*H_idx*d_idx per window key + attention 2*H*(d_qk+d_v) per selected key), queries/s, a
-roofline entry for the dominant kernel (sparse attention, MFMA-bound), per-stage timings and
-the CPU oracle's throughput on a bounded row sample.
+roofline entry for the dominant kernel (sparse attention, MFMA-bound), per-stage timings, the
+head-tail CP-degree-8 share with its indexer in bf16 and in fp8, the training-side kernels on
+the packed varlen workload, and the CPU oracle's throughput on a bounded row sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
 """
@@ -25,6 +26,7 @@ sys.path.insert(0, ROOT)
 from sparse_attention_11_amd import dsa, inputs as I  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 # sources the sparse-attention kernel is built from: the counter record is valid for them only
@@ -173,6 +175,43 @@ def backward_stage(args, n=5):
     rec["indexer_kl"] = {"ms": kms, "flop": kflop, "tflops": kflop / (kms * 1e-3) / 1e12,
                          "mfma_frac": kflop / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     return rec
+
+
+def head_tail_stage(args):
+    """The CP-degree-8 head-tail share (two 2048-query chunks against 32768 keys): the fused
+    indexer + top-k with bf16 index inputs and with e4m3 codes and per-token scales (quantized
+    on the GPU, outside the timed span), and the whole bf16 forward, each timed on its own."""
+    wl = I.workload(4).with_(with_dout=False)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    g = I.generate(wl, device=dev, gen_device="cuda")
+    W = work(wl)
+    reps = max(3, min(args.steps, 10))
+    qc, qs = dsa.dsa_quantize_fp8_rows(g["q_idx"])
+    kc, ks = dsa.dsa_quantize_fp8_rows(g["k_idx"])
+    tk = torch.empty(wl.n_q, wl.topk, dtype=torch.int32, device=dev)
+    ws = torch.empty(dsa.dsa_workspace_bytes(wl.n_q, wl.n_k, wl.topk, wl.segments),
+                     dtype=torch.uint8, device=dev)
+    bf = time_launches(lambda: dsa.dsa_indexer_topk(g["q_idx"], g["k_idx"], g["w_idx"],
+                                                    wl.segments, wl.topk, out=tk, workspace=ws),
+                       reps, stream)
+    f8 = time_launches(lambda: dsa.dsa_indexer_topk(qc, kc, g["w_idx"], wl.segments, wl.topk,
+                                                    q_scale=qs, k_scale=ks, out=tk, workspace=ws),
+                       reps, stream)
+    out = torch.empty(wl.n_q, wl.h, wl.d_v, dtype=torch.bfloat16, device=dev)
+    fw = time_launches(lambda: dsa.dsa_forward(g["q_idx"], g["k_idx"], g["w_idx"], g["q"],
+                                               g["kv"], wl.segments, wl.topk, wl.softmax_scale,
+                                               wl.d_v, out=out, workspace=ws), reps, stream)
+    print(f"bench: head-tail {wl.name}: indexer+top-k bf16 {bf:.3f} ms, fp8 {f8:.3f} ms, "
+          f"forward {fw:.3f} ms", file=sys.stderr, flush=True)
+    fi = W["f_idx"]
+    return {"workload": wl.name,
+            "indexer_topk_bf16_ms": bf, "indexer_topk_bf16_tflops": fi / (bf * 1e-3) / 1e12,
+            "indexer_topk_fp8_ms": f8, "indexer_topk_fp8_tflops": fi / (f8 * 1e-3) / 1e12,
+            "indexer_topk_fp8_frac_of_fp8_peak": fi / (f8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+            "forward_bf16_ms": fw,
+            "forward_tflops": (W["f_idx"] + W["f_attn"]) / (fw * 1e-3) / 1e12,
+            "forward_queries_per_s": wl.n_q / (fw * 1e-3)}
 
 
 def traffic_entry():
@@ -353,6 +392,8 @@ def main():
                             "achieved": attn_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": attn_tf / PEAK_BF16_TFLOPS, "traffic": traffic,
                             "per_launch_flop": W["f_attn"]}
+    if stages:
+        line["head_tail"] = head_tail_stage(args)
     if not args.no_backward:
         line["backward"] = backward_stage(args)
     if not args.no_cpu_baseline:
