@@ -230,9 +230,10 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
     return *reinterpret_cast<const bf16x8*>(
         &sk[buf][(hh * kIdxKeys + nt * 32 + hl) * ROW + ks * 16 + g * 8]);
   };
-  // b0: the first K step's key fragments, read by the caller ahead of an epilogue so their
-  // LDS latency is hidden behind it
-  auto mma = [&](int buf, int hh, const bf16x8* b0) {
+  // b0: the first PF K steps' key fragments, read by the caller ahead of an epilogue so
+  // their LDS latency is hidden behind it
+  constexpr int PF = 2;
+  auto mma = [&](int buf, int hh, const bf16x8 (*b0)[NTK]) {
     // both 32-key sub-tiles are computed unconditionally (keys past the row's window are
     // only masked at the store); K steps outer, so the MT x 2 accumulators form independent
     // chains and consecutive MFMAs never wait for each other
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 b[NTK];
 #pragma unroll
-      for (int nt = 0; nt < NTK; ++nt) b[nt] = ks == 0 ? b0[nt] : bfrag(buf, hh, ks, nt);
+      for (int nt = 0; nt < NTK; ++nt) b[nt] = ks < PF ? b0[ks < PF ? ks : 0][nt] : bfrag(buf, hh, ks, nt);
 #pragma unroll
       for (int nt = 0; nt < NTK; ++nt)
 #pragma unroll
@@ -279,16 +280,18 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntiles) fetch(t + 1);
-    bf16x8 bn[NTK];   // non-lag waves: the second half's first fragments
+    bf16x8 bn[PF][NTK];   // non-lag waves: the second half's first fragments
 #pragma unroll
     for (int hh = 0; hh < KST / kIdxKeys; ++hh) {
       const int kb = t * KST + hh * kIdxKeys;   // first key of this 64-key half
       const bool act = ri.ok && kb <= ri.pos;
       if (lag) {
-        bf16x8 b0[NTK];
+        bf16x8 b0[PF][NTK];
         if (act)
 #pragma unroll
-          for (int nt = 0; nt < NTK; ++nt) b0[nt] = bfrag(buf, hh, 0, nt);
+          for (int k = 0; k < PF; ++k)
+#pragma unroll
+            for (int nt = 0; nt < NTK; ++nt) b0[k][nt] = bfrag(buf, hh, k, nt);
         if (pkb >= 0) epi(pkb);
         pkb = -1;
         if (act) {
@@ -296,13 +299,17 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
           pkb = kb;
         }
       } else if (act) {
-        bf16x8 b0[NTK];
+        bf16x8 b0[PF][NTK];
 #pragma unroll
-        for (int nt = 0; nt < NTK; ++nt) b0[nt] = hh == 0 ? bfrag(buf, hh, 0, nt) : bn[nt];
+        for (int k = 0; k < PF; ++k)
+#pragma unroll
+          for (int nt = 0; nt < NTK; ++nt) b0[k][nt] = hh == 0 ? bfrag(buf, hh, k, nt) : bn[k][nt];
         mma(buf, hh, b0);
         if (hh + 1 < KST / kIdxKeys && kb + kIdxKeys <= ri.pos)
 #pragma unroll
-          for (int nt = 0; nt < NTK; ++nt) bn[nt] = bfrag(buf, hh + 1, 0, nt);
+          for (int k = 0; k < PF; ++k)
+#pragma unroll
+            for (int nt = 0; nt < NTK; ++nt) bn[k][nt] = bfrag(buf, hh + 1, k, nt);
         epi(kb);
       }
     }
