@@ -185,18 +185,48 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP, with no LDS round trip: row shifts
+// by 1, 2, 4 and 8 within each 16-lane row, then the last lane of each row broadcast into the
+// rows above it (lanes a shift or broadcast does not reach add 0).
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned x) {
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  x += (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return x;
+}
+
+// Minimum and maximum over the 64 lanes of a wave (the same DPP pattern; lanes it does not
+// reach take the identity), returned to every lane.
+__device__ __forceinline__ unsigned wave_min_u32(unsigned x) {
+  const int I = -1;
+  x = min(x, (unsigned)__builtin_amdgcn_update_dpp(I, (int)x, 0x111, 0xF, 0xF, false));
+  x = min(x, (unsigned)__builtin_amdgcn_update_dpp(I, (int)x, 0x112, 0xF, 0xF, false));
+  x = min(x, (unsigned)__builtin_amdgcn_update_dpp(I, (int)x, 0x114, 0xF, 0xF, false));
+  x = min(x, (unsigned)__builtin_amdgcn_update_dpp(I, (int)x, 0x118, 0xF, 0xF, false));
+  x = min(x, (unsigned)__builtin_amdgcn_update_dpp(I, (int)x, 0x142, 0xA, 0xF, false));
+  x = min(x, (unsigned)__builtin_amdgcn_update_dpp(I, (int)x, 0x143, 0xC, 0xF, false));
+  return (unsigned)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ unsigned wave_max_u32(unsigned x) {
+  x = max(x, (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false));
+  x = max(x, (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false));
+  x = max(x, (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false));
+  x = max(x, (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false));
+  x = max(x, (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false));
+  x = max(x, (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false));
+  return (unsigned)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 // Block-wide exclusive prefix sum of one value per thread; `scratch` holds NW words of LDS.
 // Returns the exclusive prefix; `total` receives the block sum.  Contains two barriers.
 template <int NW>
 __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* scratch,
                                                     unsigned& total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  unsigned x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    unsigned t = __shfl_up(x, o, 64);
-    if (lane >= o) x += t;
-  }
+  const unsigned x = wave_incl_scan(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
   unsigned before = 0, tot = 0;

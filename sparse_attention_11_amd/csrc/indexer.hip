@@ -110,16 +110,8 @@ __device__ __forceinline__ void cand_update(CandRow& c, int k) {
   const int lane = threadIdx.x & 63;
   const uint4 h = *reinterpret_cast<const uint4*>(c.hist + 4 * lane);   // bins 4 lane .. +3
   const uint32_t s4 = h.x + h.y + h.z + h.w;
-  // candidates in bins >= 4 lane: the total minus an inclusive prefix sum over the lanes, the
-  // prefix sum by DPP (row shifts 1, 2, 4, 8 within each 16-lane row, then the last lane of
-  // the rows below broadcast into the rows above), no LDS round trip
-  uint32_t pre = s4;
-  pre += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pre, 0x111, 0xF, 0xF, false);   // row_shr:1
-  pre += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pre, 0x112, 0xF, 0xF, false);   // row_shr:2
-  pre += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pre, 0x114, 0xF, 0xF, false);   // row_shr:4
-  pre += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pre, 0x118, 0xF, 0xF, false);   // row_shr:8
-  pre += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pre, 0x142, 0xA, 0xF, false);   // row_bcast:15
-  pre += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pre, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  // candidates in bins >= 4 lane: the total minus an inclusive prefix sum over the lanes
+  const uint32_t pre = wave_incl_scan(s4);
   const uint32_t suf = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + s4;
   const uint32_t s3 = suf - s4 + h.w, s2 = s3 + h.z, s1 = s2 + h.y, s0 = s1 + h.x;
   const unsigned long long ball = __ballot(s0 >= (uint32_t)k);   // lanes 0 .. L* (nonzero: s0(0) = n)

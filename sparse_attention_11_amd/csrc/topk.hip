@@ -77,11 +77,8 @@ __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
       kmax = max(kmax, key[j]);
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
   if (lane == 0) {
     grp_gt[wave] = kmin;
     grp_eq[wave] = kmax;
