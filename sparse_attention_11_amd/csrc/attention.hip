@@ -721,8 +721,7 @@ __device__ __forceinline__ void attn_row(const AttnArgs& a, int bi, int nblk, ui
   bf16x8 qf[C::KSR];
   load_q<H, DQK, DV>(a, c, qf);
   int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  last = (int)wave_max_u32((unsigned)(last + 1)) - 1;   // (last >= -1)
   if (c.lane == 0) s_last[c.wave] = last;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // staged Q landed (DMA is not tracked)
   __syncthreads();

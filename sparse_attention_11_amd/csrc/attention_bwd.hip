@@ -407,8 +407,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
   const int n = lane & 15, G = lane >> 4;
   const int32_t* idx_row = a.idx + (size_t)row * a.topk;
   int last = thread_last_valid<256>(idx_row, a.topk, a.n_k, tid);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  last = (int)wave_max_u32((unsigned)(last + 1)) - 1;   // (last >= -1)
   if (lane == 0) s_last[wave] = last;
   __syncthreads();
   last = max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3]));

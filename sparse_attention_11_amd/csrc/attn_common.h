@@ -382,8 +382,7 @@ template <int H, int DQK, int DV, class Args>
 __device__ __forceinline__ int row_tiles(const Args& a, const RowCtx& c, int* s_last) {
   using C = AttnCfg<H, DQK, DV>;
   int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  last = (int)wave_max_u32((unsigned)(last + 1)) - 1;   // (last >= -1)
   if (c.lane == 0) s_last[c.wave] = last;
   __syncthreads();
   last = -1;

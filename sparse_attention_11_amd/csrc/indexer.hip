@@ -79,12 +79,7 @@ __device__ __forceinline__ void cand_begin(CandRow& c, uint32_t* hist_wave, floa
 __device__ __forceinline__ void cand_offer(CandRow& c, float s, int key_abs, bool v) {
   const uint32_t ok = order_key(s);
   if (!c.init) {   // bin range from the row's first group: its span over 64 of the 256 bins
-    uint32_t mn = v ? ok : 0xFFFFFFFFu, mx = v ? ok : 0u;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-    }
+    const uint32_t mn = wave_min_u32(v ? ok : 0xFFFFFFFFu), mx = wave_max_u32(v ? ok : 0u);
     const uint32_t span = mx - mn;
     c.base = mn;
     c.shift = span == 0u ? 0 : max(0, 32 - __clz((int)span) - 6);
@@ -117,7 +112,7 @@ __device__ __forceinline__ void cand_update(CandRow& c, int k) {
   const unsigned long long ball = __ballot(s0 >= (uint32_t)k);   // lanes 0 .. L* (nonzero: s0(0) = n)
   const int lstar = 63 - __clzll(ball);
   const int j = s3 >= (uint32_t)k ? 3 : s2 >= (uint32_t)k ? 2 : s1 >= (uint32_t)k ? 1 : 0;
-  const int b = 4 * lstar + __shfl(j, lstar, 64);
+  const int b = 4 * lstar + __builtin_amdgcn_readlane(j, lstar);
   if (b > 0) {
     const unsigned long long e = (unsigned long long)c.base + ((unsigned long long)b << c.shift);
     c.tau = (uint32_t)min(e, 0xFFFFFFFFull);   // (a bin holding k candidates starts below 2^32)
