@@ -59,10 +59,19 @@ __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
     return;
   }
 
-  // unconditional loads (clamped index), so all of them are in flight at once
+  // unconditional loads (clamped index), so all of them are in flight at once; in candidate
+  // mode the candidates' key indices come with them (read here, not at the output writes,
+  // where each would be a dependent memory round trip) where the registers allow: not in the
+  // 1024-thread configurations, which have 128 VGPRs per lane
+  constexpr bool PRE = CAND && THREADS <= 512;
   uint32_t key[ITEMS];
+  int32_t ckv[PRE ? ITEMS : 1];
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) key[j] = __float_as_uint(src[min(j * THREADS + tid, L - 1)]);
+  if constexpr (PRE) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) ckv[j] = ckey[min(j * THREADS + tid, L - 1)];
+  }
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) key[j] = j * THREADS + tid < L ? order_key(__uint_as_float(key[j])) : 0u;
 
@@ -204,7 +213,8 @@ __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
     const uint32_t n_gt = grp_gt[j * NW + wave] + lanes_below(mg);
     const uint32_t n_eq = grp_eq[j * NW + wave] + lanes_below(me);
     const uint32_t pos = n_gt + min(n_eq, need);
-    if ((gt || (eq && n_eq < need)) && pos < (uint32_t)topk) dst[pos] = key_of(e);
+    if ((gt || (eq && n_eq < need)) && pos < (uint32_t)topk)
+      dst[pos] = PRE ? ckv[PRE ? j : 0] : key_of(e);
   }
 }
 
