@@ -61,9 +61,10 @@ __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
 
   // unconditional loads (clamped index), so all of them are in flight at once; in candidate
   // mode the candidates' key indices come with them (read here, not at the output writes,
-  // where each would be a dependent memory round trip) where the registers allow: not in the
-  // 1024-thread configurations, which have 128 VGPRs per lane
-  constexpr bool PRE = CAND && THREADS <= 512;
+  // where each would be a dependent memory round trip) where the registers allow: at most 16
+  // items per thread (with 32 the extra registers cost the 512-thread tier its second
+  // workgroup per CU, and the 1024-thread tiers have only 128 VGPRs per lane)
+  constexpr bool PRE = CAND && THREADS <= 512 && ITEMS <= 16;
   uint32_t key[ITEMS];
   int32_t ckv[PRE ? ITEMS : 1];
 #pragma unroll
