@@ -364,12 +364,34 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
 // product of vt alone (there is no later tile to form logits for).
 constexpr int kStepFull = 0, kStepNoGather = 1, kStepPvOnly = 2;
 
+// Value fragment j of a tile (the first two of a tile are read ahead, across the step's
+// barrier; addressing as in pipe_tile's vfrag).
+template <int H, int DQK, int DV>
+__device__ __forceinline__ bf16x8 vfrag_of(const RowCtx& c, lds_cptr_t tile, int j) {
+  using C = AttnCfg<H, DQK, DV>;
+  const int G = c.lane >> 4, i = c.lane & 15;
+  const int low = 2 * (G & 1) + ((i & 3) >> 1);
+  const int kk = j / C::MTV, mt = j % C::MTV;
+  lds_cptr_t p[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int r = (G >> 1) * 8 + (i >> 2) + hf * 4;
+    const int sw = C::SWZ ? swz(r) : 0;
+    const lds_cptr_t b = tile + r * C::ROWE + ((low ^ (sw & 3)) * 8) + (i & 1) * 4;
+    p[hf] = ((mt & 1) ? b - (sw >> 2) * 32 : b + (sw >> 2) * 32) + kk * 16 * C::ROWE + mt * 32;
+  }
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)p[0]);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)p[1]);
+  return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
 template <int H, int DQK, int DV, int MODE>
 __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, const bf16x8* qf,
                                           lds_cptr_t ktile, const unsigned* vmr, lds_cptr_t vtile,
                                           bf16x8* pf, f32x16* o, float& m_used, float& m_true,
                                           float& lsum, const unsigned* so, unsigned gbits,
-                                          unsigned* vmw, const unsigned* loff, unsigned wbg) {
+                                          unsigned* vmw, const unsigned* loff, unsigned wbg,
+                                          bf16x8* vcarry) {
   using C = AttnCfg<H, DQK, DV>;
   typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
   unsigned vmw_in[C::NW];
@@ -441,8 +463,14 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
   constexpr bool GATHER = MODE == kStepFull;
   f32x16 s;
   if constexpr (LOGITS) fetch(0, 0);
-#pragma unroll
-  for (int j = 0; j < PD; ++j) vf[j] = vfrag(j);
+  // the tile's first two value fragments were read before the step's barrier
+  static_assert(PD == 2, "two carried value fragments");
+  vf[0] = vcarry[0];
+  vf[1] = vcarry[1];
+  // the first output-product MFMA goes ahead of the logits: its operands are in registers,
+  // so it covers the LDS latency of the first key fragments
+  constexpr int NPRE = LOGITS ? 1 : 0;
+  if constexpr (LOGITS) pv(0);
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     const int cur = gi & 1;
@@ -467,7 +495,8 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(af[cur][u]), "v"(bq));
       if (GATHER && ks >= 2 && ks < 2 + C::NI) gather_piece(ks - 2);
 #pragma unroll
-      for (int j = ks * NPA / C::KS; j < (ks + 1) * NPA / C::KS; ++j) pv(j);
+      for (int j = ks * NPA / C::KS; j < (ks + 1) * NPA / C::KS; ++j)
+        if (j >= NPRE) pv(j);
     }
     if (GATHER && gi == 4 && c.lane == 0) *vmw = gbits;
     if (LOGITS && gi == 5) {
@@ -532,6 +561,10 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
   lsum += ls;
   pf[0] = pn[0];
   pf[1] = pn[1];
+  // the next step's output product is of kt: its first value fragments are read now, ahead
+  // of the barrier
+  vcarry[0] = vfrag_of<H, DQK, DV>(c, ktile, 0);
+  vcarry[1] = vfrag_of<H, DQK, DV>(c, ktile, 1);
   return over;
 }
 
@@ -588,6 +621,9 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
   // t+2 (slot sg, free since the previous step's barrier).  Tiles past the row's last valid
   // slot are neither gathered nor computed: step ntiles-2 gathers nothing, and the last step
   // is the output product of tile ntiles-1 alone.
+  // the first two value fragments of the tile whose output product comes next
+  bf16x8 vcarry[2] = {vfrag_of<H, DQK, DV>(c, (lds_cptr_t)c.buf[0], 0),
+                      vfrag_of<H, DQK, DV>(c, (lds_cptr_t)c.buf[0], 1)};
   auto step = [&](auto mode, int t, lds_cptr_t bv, lds_cptr_t bk, unsigned wbg, int sk, int sg) {
     constexpr int MODE = decltype(mode)::value;
     unsigned so[RPW] = {};
@@ -601,7 +637,7 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
     }
     over_any |= pipe_tile<H, DQK, DV, MODE>(a, c, qf, bk, c.vm + sk * C::NW, bv, pf, o, m_used,
                                             m_true, lsum, so, gbits,
-                                            c.vm + sg * C::NW + c.wave, loff, wbg);
+                                            c.vm + sg * C::NW + c.wave, loff, wbg, vcarry);
     if constexpr (MODE != kStepPvOnly) wait_vm_barrier<0>();   // tile t+2 landed; t free
   };
   // one step per loop iteration, the ring slots (LDS addresses, gather bases and slot numbers)
