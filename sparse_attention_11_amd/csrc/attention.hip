@@ -467,10 +467,13 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
   static_assert(PD == 2, "two carried value fragments");
   vf[0] = vcarry[0];
   vf[1] = vcarry[1];
-  // the first output-product MFMA goes ahead of the logits: its operands are in registers,
-  // so it covers the LDS latency of the first key fragments
-  constexpr int NPRE = LOGITS ? 1 : 0;
-  if constexpr (LOGITS) pv(0);
+  // the first two output-product MFMAs go ahead of the logits: their operands are in
+  // registers, so they cover the LDS latency of the first key fragments
+  constexpr int NPRE = LOGITS ? 2 : 0;
+  if constexpr (LOGITS) {
+    pv(0);
+    pv(1);
+  }
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     const int cur = gi & 1;
