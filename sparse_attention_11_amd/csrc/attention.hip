@@ -364,24 +364,28 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
 // product of vt alone (there is no later tile to form logits for).
 constexpr int kStepFull = 0, kStepNoGather = 1, kStepPvOnly = 2;
 
-// Value fragment j of a tile (the first two of a tile are read ahead, across the step's
-// barrier; addressing as in pipe_tile's vfrag).
+// Lane offsets (elements, from a tile's base) of the first two value fragments of a tile,
+// [fragment][half]: the addressing of pipe_tile's vfrag for fragments 0 and 1, computed once
+// per row; those two fragments of each tile are read ahead, across the step's barrier.
 template <int H, int DQK, int DV>
-__device__ __forceinline__ bf16x8 vfrag_of(const RowCtx& c, lds_cptr_t tile, int j) {
+__device__ __forceinline__ void vcarry_offsets(const RowCtx& c, unsigned (*vo)[2]) {
   using C = AttnCfg<H, DQK, DV>;
   const int G = c.lane >> 4, i = c.lane & 15;
   const int low = 2 * (G & 1) + ((i & 3) >> 1);
-  const int kk = j / C::MTV, mt = j % C::MTV;
-  lds_cptr_t p[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const int r = (G >> 1) * 8 + (i >> 2) + hf * 4;
     const int sw = C::SWZ ? swz(r) : 0;
-    const lds_cptr_t b = tile + r * C::ROWE + ((low ^ (sw & 3)) * 8) + (i & 1) * 4;
-    p[hf] = ((mt & 1) ? b - (sw >> 2) * 32 : b + (sw >> 2) * 32) + kk * 16 * C::ROWE + mt * 32;
+    const int b = r * C::ROWE + ((low ^ (sw & 3)) * 8) + (i & 1) * 4;
+    vo[0][hf] = (unsigned)(b + (sw >> 2) * 32);        // fragment 0: mt 0
+    vo[1][hf] = (unsigned)(b - (sw >> 2) * 32 + 32);   // fragment 1: mt 1
   }
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)p[0]);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)p[1]);
+}
+
+template <int H, int DQK, int DV>
+__device__ __forceinline__ bf16x8 vfrag_at(lds_cptr_t tile, const unsigned* vo) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(tile + vo[0]));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(tile + vo[1]));
   return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 }
 
@@ -391,7 +395,7 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
                                           bf16x8* pf, f32x16* o, float& m_used, float& m_true,
                                           float& lsum, const unsigned* so, unsigned gbits,
                                           unsigned* vmw, const unsigned* loff, unsigned wbg,
-                                          bf16x8* vcarry) {
+                                          bf16x8* vcarry, const unsigned (*vco)[2]) {
   using C = AttnCfg<H, DQK, DV>;
   typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
   unsigned vmw_in[C::NW];
@@ -566,8 +570,8 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
   pf[1] = pn[1];
   // the next step's output product is of kt: its first value fragments are read now, ahead
   // of the barrier
-  vcarry[0] = vfrag_of<H, DQK, DV>(c, ktile, 0);
-  vcarry[1] = vfrag_of<H, DQK, DV>(c, ktile, 1);
+  vcarry[0] = vfrag_at<H, DQK, DV>(ktile, vco[0]);
+  vcarry[1] = vfrag_at<H, DQK, DV>(ktile, vco[1]);
   return over;
 }
 
@@ -625,8 +629,10 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
   // slot are neither gathered nor computed: step ntiles-2 gathers nothing, and the last step
   // is the output product of tile ntiles-1 alone.
   // the first two value fragments of the tile whose output product comes next
-  bf16x8 vcarry[2] = {vfrag_of<H, DQK, DV>(c, (lds_cptr_t)c.buf[0], 0),
-                      vfrag_of<H, DQK, DV>(c, (lds_cptr_t)c.buf[0], 1)};
+  unsigned vco[2][2];
+  vcarry_offsets<H, DQK, DV>(c, vco);
+  bf16x8 vcarry[2] = {vfrag_at<H, DQK, DV>((lds_cptr_t)c.buf[0], vco[0]),
+                      vfrag_at<H, DQK, DV>((lds_cptr_t)c.buf[0], vco[1])};
   auto step = [&](auto mode, int t, lds_cptr_t bv, lds_cptr_t bk, unsigned wbg, int sk, int sg) {
     constexpr int MODE = decltype(mode)::value;
     unsigned so[RPW] = {};
@@ -640,7 +646,8 @@ __device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx&
     }
     over_any |= pipe_tile<H, DQK, DV, MODE>(a, c, qf, bk, c.vm + sk * C::NW, bv, pf, o, m_used,
                                             m_true, lsum, so, gbits,
-                                            c.vm + sg * C::NW + c.wave, loff, wbg, vcarry);
+                                            c.vm + sg * C::NW + c.wave, loff, wbg, vcarry,
+                                            vco);
     if constexpr (MODE != kStepPvOnly) wait_vm_barrier<0>();   // tile t+2 landed; t free
   };
   // one step per loop iteration, the ring slots (LDS addresses, gather bases and slot numbers)
