@@ -418,39 +418,49 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntiles) fetch(t + 1);
-    if (ri.ok) {
+    const int kb = t * kIdxKeys;   // first key of the stage
+    if (ri.ok && kb <= ri.pos) {
+      // both 32-key sub-tiles (keys past the row's window are masked at the store), then one
+      // epilogue for the 64 keys: lane (hl, g) takes key kb + 32 g + hl, so the filter and
+      // the store run once per 64 keys, on every lane
+      f32x16 acc[2][MT];
 #pragma unroll
-      for (int nt = 0; nt < kIdxKeys / 32; ++nt) {
-        const int kbase = t * kIdxKeys + nt * 32;
-        if (kbase <= ri.pos) {
-          f32x16 acc[MT];
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x16){};
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = (f32x16){};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const uint8_t* bp = &sk[buf][(nt * 32 + hl) * ROW + ks * 64 + g * 32];
-            const uint4 b0 = *reinterpret_cast<const uint4*>(bp);
-            const uint4 b1 = *reinterpret_cast<const uint4*>(bp + 16);
-            const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                             (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+      for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              // formats: A and B e4m3 (0); block scales 127 = 2^0
-              acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qf[mt][ks], b, acc[mt],
-                                                                        0, 0, 0, 127, 0, 127);
-          }
-          float s = 0.f;
+        for (int nt = 0; nt < 2; ++nt) {
+          const uint8_t* bp = &sk[buf][(nt * 32 + hl) * ROW + ks * 64 + g * 32];
+          const uint4 b0 = *reinterpret_cast<const uint4*>(bp);
+          const uint4 b1 = *reinterpret_cast<const uint4*>(bp + 16);
+          const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                           (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s = relu_fma(acc[mt][r], wv[mt][r], s);
-          s = pair_sum(s);
-          const int key = kbase + hl;
-          const float sc = s * sks[buf][nt * 32 + hl];
-          if constexpr (CAND) cand_offer(cr, sc, ri.k_lo + key, g == 0 && key <= ri.pos);
-          else if (g == 0 && key <= ri.pos) out[key] = sc;
+            // formats: A and B e4m3 (0); block scales 127 = 2^0
+            acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                qf[mt][ks], b, acc[nt][mt], 0, 0, 0, 127, 0, 127);
         }
       }
+      float sv[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float s = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s = relu_fma(acc[nt][mt][r], wv[mt][r], s);
+        sv[nt] = pair_sum(s);   // (both lanes of the pair hold the sum)
+      }
+      static_assert(kIdxKeys == 64, "two 32-key sub-tiles per stage");
+      const int key = kb + 32 * g + hl;
+      const float sc = (g ? sv[1] : sv[0]) * sks[buf][32 * g + hl];
+      if constexpr (CAND) cand_offer(cr, sc, ri.k_lo + key, key <= ri.pos);
+      else if (key <= ri.pos) out[key] = sc;
+    }
+    if (ri.ok) {
       if constexpr (CAND) {   // every eighth 64-key stage
         if (t * kIdxKeys <= ri.pos && (t & 7) == 7) cand_update(cr, a.topk);
       }
