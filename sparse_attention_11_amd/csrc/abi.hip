@@ -594,6 +594,7 @@ dsa_status dsa_indexer_kl_loss_grad(const dsa_shape* shape, const void* q_idx, c
     return fail(DSA_ERR_WORKSPACE, "internal workspace layout exceeds %zu bytes", workspace_bytes);
   kl.n_k = shape->n_k;
   kl.topk = topk;
+  kl.topkp = (int)topkp;
   dsa::IdxKlArgs a = {};
   a.k_idx = static_cast<const uint16_t*>(k_idx);
   a.kv = static_cast<const uint16_t*>(kv);

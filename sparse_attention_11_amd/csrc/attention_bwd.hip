@@ -574,13 +574,17 @@ __global__ __launch_bounds__(1024) void k_keys_scan(KeyListArgs a) {
   if (threadIdx.x == 0) a.off[a.n_k] = (int)base;
 }
 
-// list[cur[k]++] = row * topk + slot for every valid entry.
+// list[cur[k]++] = row * topkp + slot for every valid entry: the entry's row in the
+// per-(row, slot) workspaces, so the reductions read it with no division.
 __global__ __launch_bounds__(256) void k_keys_scatter(KeyListArgs a) {
   const long long total = (long long)a.rows * a.topk;
   for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total;
        e += (long long)gridDim.x * 256) {
     const int k = a.idx[e];
-    if ((unsigned)k < (unsigned)a.n_k) a.list[atomicAdd(&a.cur[k], 1)] = (int)e;
+    if ((unsigned)k < (unsigned)a.n_k) {
+      const int r = (int)(e / a.topk), sl = (int)(e - (long long)r * a.topk);
+      a.list[atomicAdd(&a.cur[k], 1)] = r * a.topkp + sl;
+    }
   }
 }
 
@@ -598,8 +602,7 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(AttnBwdArgs a) {
   float s0[8] = {}, s1[8] = {};
   const bool tail = lane < 8;
   auto add = [&](int e) {
-    const int r = e / a.topk, sl = e - r * a.topk;
-    const uint16_t* src = a.ws_c + ((size_t)r * a.topkp + sl) * DQK;
+    const uint16_t* src = a.ws_c + (size_t)e * DQK;
     const uint4 v = *reinterpret_cast<const uint4*>(src + 8 * lane);
     uint4 w = make_uint4(0, 0, 0, 0);
     if (tail) w = *reinterpret_cast<const uint4*>(src + 512 + 8 * lane);
@@ -655,7 +658,7 @@ hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v
   if (a.rows == 0) return hipSuccess;
   if (!(h == 128 && d_qk == 576 && d_v == 512)) return hipErrorInvalidValue;
   const bool al8 = a.topk >= 8 && a.topk % 8 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 31) == 0;
-  KeyListArgs kl = {a.idx, a.list, a.cnt, a.off, a.cur, a.rows, a.n_k, a.topk};
+  KeyListArgs kl = {a.idx, a.list, a.cnt, a.off, a.cur, a.rows, a.n_k, a.topk, a.topkp};
   hipError_t e = launch_key_lists(kl, s);
   if (e != hipSuccess) return e;
   if (al8) {

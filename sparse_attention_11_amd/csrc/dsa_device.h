@@ -151,6 +151,7 @@ struct KeyListArgs {
   int* off;               // [n_k + 1]
   int* cur;               // [n_k]
   int rows, n_k, topk;
+  int topkp;              // slot stride of the per-(row, slot) workspaces the lists index
 };
 
 // Builds the lists on stream s (counting sort; integer atomics on the counters only).

@@ -570,9 +570,8 @@ __global__ __launch_bounds__(256) void k_idx_kl_reduce(IdxKlArgs a) {
   if (beg == end) return;
   float s[8] = {};
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  auto src = [&](int e) {
-    const int r = e / a.topk, sl = e - r * a.topk;
-    return reinterpret_cast<const u32x4*>(a.ws_c + ((size_t)r * a.topkp + sl) * kDI + 8 * l);
+  auto src = [&](int e) {   // e: the slot's row in the workspace (row * topkp + slot)
+    return reinterpret_cast<const u32x4*>(a.ws_c + (size_t)e * kDI + 8 * l);
   };
   auto add = [&](const u32x4& v) {
     const uint32_t vv[4] = {v[0], v[1], v[2], v[3]};
