@@ -357,8 +357,9 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
 // MFMAs (so: byte offsets in kv of this wave's rows of it, wbg: LDS address of the wave's
 // first row in the destination buffer), and the bookkeeping of the step runs in their shadow:
 // this wave's validity bits of the gathered tile (gbits) go to vmw, the bits of kt (every
-// wave's) are read from vmr.  Each lane owns one head's value columns, as in tile_pv.  Returns whether some
-// head's max outgrew the scaling range.
+// wave's) are read from vmr.  Each lane owns one head's value columns, as in tile_pv.
+// vcarry: the first two value fragments of vt on entry (read before the barrier), those of kt
+// on return.  Returns whether some head's max outgrew the scaling range.
 // MODE: kStepFull as above; kStepNoGather for the step whose later tile would lie past the
 // row's last valid slot (nothing to gather); kStepPvOnly for the row's last step: the output
 // product of vt alone (there is no later tile to form logits for).
