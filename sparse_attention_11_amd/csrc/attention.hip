@@ -408,7 +408,7 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
   for (int j = 0; j < 4; ++j)
     abase[j] = ktile + arow_i * C::ROWE + (((2 * j + c.g) ^ asw) - 2 * j) * 8;
   const uint16_t* qlrow = c.qlds + c.head * C::QROWE + c.g * 8;
-  constexpr int QG = 3;                    // K steps per prefetch group
+  constexpr int QG = 2;                    // K steps per prefetch group
   constexpr int NG = C::KS / QG;
   static_assert(C::KS % QG == 0, "logits K steps");
   bf16x8 af[2][QG], bt[2][QG];
