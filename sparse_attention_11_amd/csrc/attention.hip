@@ -440,7 +440,8 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
     return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
   };
   constexpr int NP = 2 * C::MTV;           // output-product MFMAs per tile
-  constexpr int NPA = NP / 2;              // of which interleaved with the logits
+  constexpr int NPA = 20;                  // of which interleaved with the logits
+  constexpr int NPQ = (NP - NPA - 4) / 4;  // per quarter of the softmax
   constexpr int PD = 2;                    // value fragments read ahead of their MFMA
   bf16x8 vf[PD + 1];
   // the accumulator stays in AGPRs (the logits accumulator and every operand in VGPRs): an
@@ -562,10 +563,10 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
       pn[r >> 3][(r & 7) + 1] = pk[1];
     }
 #pragma unroll
-    for (int j = NPA + 4 + 3 * q; j < NPA + 7 + 3 * q; ++j) pv(j);
+    for (int j = NPA + 4 + NPQ * q; j < NPA + 4 + NPQ * (q + 1); ++j) pv(j);
     __builtin_amdgcn_sched_barrier(0);
   }
-  static_assert(NPA + 4 + 3 * 4 == NP, "every output-product MFMA issued once");
+  static_assert(NPA + 4 + NPQ * 4 == NP, "every output-product MFMA issued once");
   lsum += ls;
   pf[0] = pn[0];
   pf[1] = pn[1];
