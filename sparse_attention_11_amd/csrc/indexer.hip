@@ -461,8 +461,8 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
       else if (key <= ri.pos) out[key] = sc;
     }
     if (ri.ok) {
-      if constexpr (CAND) {   // every eighth 64-key stage
-        if (t * kIdxKeys <= ri.pos && (t & 7) == 7) cand_update(cr, a.topk);
+      if constexpr (CAND) {   // every fourth 64-key stage
+        if (t * kIdxKeys <= ri.pos && (t & 3) == 3) cand_update(cr, a.topk);
       }
     }
     if (t + 1 < ntiles) stash(buf ^ 1);
