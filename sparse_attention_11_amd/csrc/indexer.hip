@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
         epi(kb);
       }
     }
-    if constexpr (CAND) {   // every fourth stage: the bound only needs to rise now and then
+    if constexpr (CAND) {   // every second stage: the bound only needs to rise now and then
       if (ri.ok && t * KST <= ri.pos && (t & 1) == 1) cand_update(cr, a.topk);
     }
     if (t + 1 < ntiles) stash(buf ^ 1);
