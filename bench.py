@@ -28,16 +28,25 @@ from sparse_attention_11_amd import dsa, inputs as I  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
-# sources the sparse-attention kernel is built from: the counter record is valid for them only
-ATTN_SRCS = [os.path.join(ROOT, "sparse_attention_11_amd", "csrc", f)
-             for f in ("attention.hip", "attn_common.h", "dsa_device.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+_CSRC = os.path.join(ROOT, "sparse_attention_11_amd", "csrc")
+# kernel families of the forward whose HBM bytes the counter record holds, the sources each is
+# built from (the record is valid for those sources only) and the name prefix of its kernels
+# in the profiler's dispatch table
+TRAFFIC_KERNELS = {
+    "attention": (("attention.hip", "attn_common.h", "dsa_device.h"),
+                  ("k_sparse_attn<128, 576, 512, false",)),
+    "indexer_candidates": (("indexer.hip", "dsa_device.h"), ("k_indexer_bf16<64, 128, true>",)),
+    "topk_candidates": (("topk.hip", "dsa_device.h"),
+                        ("k_topk<256, 8, true>", "k_topk<512, 16, true>", "k_topk<512, 32, true>",
+                         "k_topk<1024, 32, true>")),
+}
 
 
-def attention_source_hash():
+def source_hash(files):
     h = hashlib.sha256()
-    for f in ATTN_SRCS:
-        h.update(open(f, "rb").read())
+    for f in files:
+        h.update(open(os.path.join(_CSRC, f), "rb").read())
     return h.hexdigest()
 
 
@@ -125,7 +134,7 @@ def cpu_baseline(wl, budget_s=15.0, max_rows=2048):
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "queries_per_s": len(done) / dt,
+            "kind": "oracle", "queries_per_s": len(done) / dt, "cpu_model": host_cpu_model(),
             "sample": f"{len(done)} seeded random rows of {wl.name} (indexer over each row's "
                       f"window, top-k, attention), float64 NumPy, {dt:.1f} s"}
 
@@ -214,17 +223,20 @@ def head_tail_stage(args):
             "forward_queries_per_s": wl.n_q / (fw * 1e-3)}
 
 
-def traffic_entry():
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was
-    taken on the current attention kernel source."""
+def traffic_record():
+    """Counter-based HBM bytes per forward of each kernel family (see TRAFFIC_KERNELS), for the
+    families whose sources are unchanged since the counters were taken; {} without a record."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        if t.get("attention_source_sha256") == attention_source_hash():
-            return float(t["hbm_bytes_per_launch"])
-    except (OSError, ValueError, KeyError):
-        pass
-    return None
+    except (OSError, ValueError):
+        return {}
+    out = {}
+    for fam, (srcs, _) in TRAFFIC_KERNELS.items():
+        e = t.get("kernels", {}).get(fam)
+        if e and e.get("source_sha256") == source_hash(srcs):
+            out[fam] = e
+    return out
 
 
 def _counter_rows(d, counter):
@@ -238,26 +250,71 @@ def _counter_rows(d, counter):
     return sorted(rows)
 
 
-def write_traffic_record(fetch_dir, write_dir):
-    """HBM bytes per sparse-attention launch: FETCH_SIZE and WRITE_SIZE (KiB units as read)
-    scaled by what the same counters read for the 1 GiB device copy of the same run."""
-    out = {}
+def write_traffic_record(fetch_dir, write_dir, steps):
+    """HBM bytes per forward of each kernel family: FETCH_SIZE and WRITE_SIZE (KiB-like units
+    as read) scaled by what the same counters read for the 1 GiB device copy of the same run,
+    summed over the family's dispatches and divided by the forwards run (warm-up + timed)."""
+    scale, rows = {}, {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = _counter_rows(d, name)
-        copies = [v for _, k, v in rows if "copyBuffer" in k or "copy" in k.lower()]
-        cal = max(copies)                         # the 1 GiB copy is the largest copy
-        attn = [v for _, k, v in rows if "k_sparse_attn<128, 576, 512, false" in k]
-        scale = float(1 << 30) / cal              # bytes per counter unit
-        out[name] = {"copy_reading": cal, "bytes_per_unit": scale,
-                     "attention_reading_avg": sum(attn) / len(attn), "launches": len(attn),
-                     "bytes_per_launch": sum(attn) / len(attn) * scale}
-    rec = {"attention_source_sha256": attention_source_hash(),
-           "hbm_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"]
-           + out["WRITE_SIZE"]["bytes_per_launch"],
-           "counters": out}
+        rows[name] = _counter_rows(d, name)
+        copies = [v for _, k, v in rows[name] if "copyBuffer" in k or "copy" in k.lower()]
+        scale[name] = float(1 << 30) / max(copies)   # bytes per unit: the largest copy is 1 GiB
+    rec = {"forwards": steps, "bytes_per_unit": scale, "kernels": {}}
+    for fam, (srcs, prefixes) in TRAFFIC_KERNELS.items():
+        e = {"source_sha256": source_hash(srcs), "kernels": list(prefixes)}
+        for name in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals = [v for _, k, v in rows[name] if any(p in k for p in prefixes)]
+            e[name] = {"dispatches": len(vals),
+                       "bytes_per_forward": sum(vals) * scale[name] / steps}
+        e["hbm_bytes_per_forward"] = e["FETCH_SIZE"]["bytes_per_forward"] + \
+            e["WRITE_SIZE"]["bytes_per_forward"]
+        rec["kernels"][fam] = e
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
+
+
+def kernel_times(fn, reps):
+    """Average duration (ms) of every GPU kernel fn() launches, per call of fn, from the
+    profiler's device activity trace (the HIP runtime's own dispatch timestamps); None when
+    the trace is not available."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        fn()
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for _ in range(reps):
+                fn()
+            torch.cuda.synchronize()
+        out = {}
+        for e in prof.key_averages():
+            tot = getattr(e, "device_time_total", None)
+            if tot is None:
+                tot = getattr(e, "cuda_time_total", 0.0)
+            if tot and e.key.startswith(("dsa::", "void dsa::")):
+                out[e.key.replace("void ", "")] = tot / 1000.0 / reps
+        return out or None
+    except Exception as ex:  # noqa: BLE001
+        print(f"bench: kernel trace unavailable ({type(ex).__name__}: {ex})", file=sys.stderr)
+        return None
+
+
+def _family_ms(ktimes, fam):
+    if not ktimes:
+        return None
+    prefixes = TRAFFIC_KERNELS[fam][1]
+    t = sum(v for k, v in ktimes.items() if any(p in k for p in prefixes))
+    return t or None
+
+
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -271,14 +328,15 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the packed-varlen forward + backward timing")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write the HBM traffic record of the attention kernel from two "
+                    help="write the HBM traffic record of the forward's kernels from two "
                          "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
-                         "'bench.py --calibrate-copy --no-stages' and exit")
+                         "'bench.py --calibrate-copy --no-stages --no-backward' with the same "
+                         "--steps/--warmup, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.traffic_from:
-        write_traffic_record(*args.traffic_from)
+        write_traffic_record(*args.traffic_from, steps=args.steps + args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only (got --gpus {args.gpus}); the CP "
@@ -349,6 +407,9 @@ def main():
         stages["attention_ms"] = time_launches(
             lambda: dsa.dsa_sparse_attn(g["q"], g["kv"], idx, wl.softmax_scale, wl.d_v, out=out),
             reps, stream)
+        # per-kernel durations of one forward (the profiler's dispatch timestamps): the
+        # candidate-mode indexer and the top-k tiers are two kernels inside one fused call
+        stages["kernels_ms"] = kernel_times(step, reps)
     t_attn = stages.get("attention_ms")
     attn_tf = W["f_attn"] / (t_attn * 1e-3) / 1e12 if t_attn else None
 
@@ -372,22 +433,51 @@ def main():
         "queries_per_s": wl.n_q / (ms * 1e-3),
         "useful_tflop": (W["f_idx"] + W["f_attn"]) / 1e12,
         "step_timing": timing,
+        "workspace_bytes": int(ws.numel()),
     }
     if stages:
         ti, tt = stages["indexer_ms"], stages["topk_ms"]
+        kt = stages["kernels_ms"]
+        t_ic = _family_ms(kt, "indexer_candidates")
+        t_tk = _family_ms(kt, "topk_candidates")
+        t_ak = _family_ms(kt, "attention")
+        tr = traffic_record()
+
+        def gbs(fam, t_ms, minus=0.0, part="hbm_bytes_per_forward"):
+            e = tr.get(fam)
+            if not e or not t_ms:
+                return None
+            b = (e[part]["bytes_per_forward"] if part != "hbm_bytes_per_forward" else e[part])
+            return (b - minus) / (t_ms * 1e-3) / 1e9
+        q_bytes = wl.n_q * wl.h * wl.d_qk * 2.0
+        idx_bytes = wl.n_q * wl.topk * 4.0
         line["stages"] = {
-            "indexer_ms_incl_minus_inf_fill": ti,
-            "indexer_tflops": W["f_idx"] / (ti * 1e-3) / 1e12,
-            "indexer_mfma_frac": W["f_idx"] / (ti * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "topk_ms": tt,
-            "topk_gbs": W["topk_bytes"] / (tt * 1e-3) / 1e9,
+            "dense_indexer_ms_incl_minus_inf_fill": ti,
+            "dense_indexer_tflops": W["f_idx"] / (ti * 1e-3) / 1e12,
+            "dense_indexer_mfma_frac": W["f_idx"] / (ti * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "dense_topk_ms": tt,
+            "dense_topk_logical_gbs": W["topk_bytes"] / (tt * 1e-3) / 1e9,
             "indexer_topk_fused_ms": stages["indexer_topk_fused_ms"],
+            "indexer_candidates_kernel_ms": t_ic,
+            "indexer_candidates_tflops": W["f_idx"] / (t_ic * 1e-3) / 1e12 if t_ic else None,
+            "indexer_candidates_mfma_frac":
+                W["f_idx"] / (t_ic * 1e-3) / 1e12 / PEAK_BF16_TFLOPS if t_ic else None,
+            "topk_candidates_kernels_ms": t_tk,
+            # HBM bytes from the rocprofv3 FETCH_SIZE / WRITE_SIZE record of these kernels
+            # (null when their sources changed since it was taken) over their live duration
+            "topk_candidates_hbm_gbs": gbs("topk_candidates", t_tk),
             "attention_ms": t_attn,
+            "attention_kernel_ms": t_ak,
             "attention_tflops": attn_tf,
             "attention_mfma_frac": attn_tf / PEAK_BF16_TFLOPS,
-            "kv_gather_gbs": W["gather_bytes"] / (t_attn * 1e-3) / 1e9,
+            "attention_hbm_gbs": gbs("attention", t_ak),
+            # the attention kernel's fetched bytes less its compulsory reads (q, indices):
+            # the latent-row gather's traffic past L2 (HBM and the MALL behind it)
+            "kv_gather_hbm_gbs": gbs("attention", t_ak, q_bytes + idx_bytes, "FETCH_SIZE"),
+            "kv_gather_logical_gbs": W["gather_bytes"] / (t_attn * 1e-3) / 1e9,
+            "kernels_ms": kt,
         }
-        traffic = traffic_entry()
+        traffic = tr["attention"]["hbm_bytes_per_forward"] if "attention" in tr else None
         line["roofline"] = {"bound": "mfma", "kernel": "k_sparse_attn (sparse MQA attention)",
                             "achieved": attn_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": attn_tf / PEAK_BF16_TFLOPS, "traffic": traffic,

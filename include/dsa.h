@@ -28,6 +28,10 @@
  *     host synchronisation.  A failed launch returns DSA_ERR_HIP.  Device-side faults surface
  *     at the caller's next synchronisation.  dsa_last_error() describes the last non-OK status
  *     of the calling thread.  No C++ exception crosses this interface.
+ *   - Alignment: the kernels read and write rows in 16-byte pieces, so q_idx, k_idx, q, kv,
+ *     out, dout, dq, dkv and workspaces must be 16-byte aligned; index lists, scores, weights,
+ *     scales and softmax statistics 4-byte aligned (bf16 quantizer input 2-byte).  A
+ *     misaligned pointer is DSA_ERR_INVALID_ARG, naming the argument.
  *   - Supported dimensions (anything else is DSA_ERR_UNSUPPORTED):
  *       indexer (h_idx, d_idx) in {(4, 32), (64, 128)};
  *       attention (h, d_qk, d_v) in {(8, 80, 64), (128, 576, 512)};
@@ -98,9 +102,16 @@ int dsa_abi_version(void);
 const char *dsa_last_error(void);
 
 /*
- * Workspace bytes dsa_forward and dsa_indexer_topk need for `shape`: per row, slots of the
- * longest window (rounded up to 64) for the candidate scores and for their keys, one count,
- * and the top-k indices when the caller does not keep them.  Host-only.
+ * Workspace bytes dsa_forward and dsa_indexer_topk use by default for `shape`: one candidate
+ * count per row, the [n_q, topk] indices (used when the caller does not keep them), then
+ * `cap` candidate slots per row, as fp32 scores and, in a second region, 16-bit window
+ * offsets of their keys; each region starts on a 256-byte boundary:
+ *     round256(4 n_q) + round256(4 n_q topk) + round256(4 n_q cap) + round256(2 n_q cap),
+ *     cap = min(W, max(T + 192, round64(ceil(4.5 topk))))
+ * with W the longest window and T topk, both rounded up to a multiple of 64.  A smaller
+ * workspace is accepted down to cap = min(W, T + 192) (the calls use the most slots it holds);
+ * rows whose candidates outgrow their slots are compacted in place, so fewer slots cost time,
+ * not results.  Host-only.
  */
 dsa_status dsa_workspace_bytes(const dsa_shape *shape, size_t *bytes);
 
@@ -136,10 +147,13 @@ dsa_status dsa_topk_select(const dsa_shape *shape, const float *scores, int32_t 
  * dsa_indexer_scores followed by dsa_topk_select on the same inputs, bit for bit (the scores
  * come from the same kernels), without writing every score.  Per row the indexer keeps a
  * running lower bound of the row's k-th largest score and writes only the scores at or above
- * it, with their keys, to `workspace`; the selection then runs over those candidates.
+ * it, with their keys, to the row's candidate slots in `workspace`; when they would outgrow
+ * the slots the row finds its k-th largest candidate and keeps only what can still be
+ * selected.  The selection then runs over those candidates.
  * topk_idx [n_q, topk] int32 receives, for every covered row, its kept keys in ascending order
- * followed by -1.  workspace: dsa_workspace_bytes bytes.  Arguments and index dtypes as for
- * dsa_indexer_scores; rows covered by no segment are left untouched.
+ * followed by -1.  workspace: dsa_workspace_bytes bytes or fewer, down to the minimum stated
+ * there (DSA_ERR_WORKSPACE below it).  Arguments and index dtypes as for dsa_indexer_scores;
+ * rows covered by no segment are left untouched.
  */
 dsa_status dsa_indexer_topk(const dsa_shape *shape, const void *q_idx, const float *q_scale,
                             const void *k_idx, const float *k_scale, const float *w_idx,
@@ -168,7 +182,7 @@ dsa_status dsa_sparse_attn(const dsa_shape *shape, const void *q, const void *kv
  * (dsa_indexer_topk) -> sparse attention, enqueued back to back on `stream` (the page
  * "CANNTorchTitan: ..." section "自定义CP策略": the CP forward is the plain forward over
  * all-gathered keys).  Arguments as above; only candidate scores are written, to
- * `workspace` (never the full [n_q, n_k]).  topk_idx may be
+ * `workspace` (never the full [n_q, n_k]; sizes as for dsa_indexer_topk).  topk_idx may be
  * NULL (then the indices stay in the workspace), softmax_max / softmax_sum may be NULL.
  * Rows covered by no segment are left untouched.
  */

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -154,30 +155,65 @@ std::vector<dsa::SegTable> make_tables(const Plan& p, int rows_per_block) {
   return out;
 }
 
-// Row stride (floats) of the compact per-window score rows in the forward workspace.
-int64_t ws_score_ld(const Plan& p) { return (p.max_window + 63) / 64 * 64; }
+// Forward workspace: the candidate count of every row, the indices (used when the caller
+// does not keep them), then for every row `cap` candidate slots: fp32 scores, and in a second
+// region their keys as 16-bit window offsets.  The expected number of candidates a row's
+// running bound lets through is about topk (1 + ln(window / topk)); the default gives a row
+// 4.5 topk slots (at most the longest window rounded up to 64), enough for windows to about
+// 30 topk without a compaction; a smaller workspace gives fewer slots, down to topk + 192
+// (the indexer's room check between stages keeps 192 free), and rows compact more often.
+constexpr int64_t kCandRoom = 192;
+int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
+int64_t cand_cap_max(const dsa_shape* s, const Plan& p) {
+  const int64_t k = s->topk;
+  return std::min(round64(p.max_window), std::max(round64(k) + kCandRoom, round64((9 * k + 1) / 2)));
+}
+int64_t cand_cap_min(const dsa_shape* s, const Plan& p) {
+  return std::min(round64(p.max_window), round64(s->topk) + kCandRoom);
+}
 
-// Forward workspace: per row a slot array of the row-window stride for the candidate scores,
-// the same for their keys, the candidate count, then the indices.
 struct WsLayout {
-  size_t scores_off = 0, ckey_off = 0, ccnt_off = 0, idx_off = 0, total = 0;
+  size_t ccnt_off = 0, idx_off = 0, scores_off = 0, ckey_off = 0, total = 0;
+  int64_t cap = 0;
 };
 
-WsLayout ws_layout(const dsa_shape* s, const Plan& p) {
+WsLayout ws_layout_cap(const dsa_shape* s, int64_t cap) {
   WsLayout w;
-  const size_t slots = (size_t)s->n_q * (size_t)ws_score_ld(p);
-  w.scores_off = 0;
-  w.ckey_off = align_up(slots * sizeof(float));
-  w.ccnt_off = w.ckey_off + align_up(slots * sizeof(int32_t));
-  w.idx_off = w.ccnt_off + align_up((size_t)s->n_q * sizeof(int32_t));
-  w.total = w.idx_off + align_up((size_t)s->n_q * (size_t)s->topk * sizeof(int32_t));
+  const size_t n = (size_t)s->n_q;
+  w.cap = cap;
+  w.ccnt_off = 0;
+  w.idx_off = align_up(n * sizeof(int32_t));
+  w.scores_off = w.idx_off + align_up(n * (size_t)s->topk * sizeof(int32_t));
+  w.ckey_off = w.scores_off + align_up(n * (size_t)cap * sizeof(float));
+  w.total = w.ckey_off + align_up(n * (size_t)cap * sizeof(uint16_t));
   return w;
+}
+
+WsLayout ws_layout(const dsa_shape* s, const Plan& p) { return ws_layout_cap(s, cand_cap_max(s, p)); }
+
+// The layout with the most candidate slots per row that `bytes` holds (cap 0: not even
+// cap_min fits).
+WsLayout ws_layout_for(const dsa_shape* s, const Plan& p, size_t bytes) {
+  const int64_t hi = cand_cap_max(s, p), lo = cand_cap_min(s, p);
+  WsLayout w = ws_layout_cap(s, hi);
+  if (w.total <= bytes) return w;
+  const WsLayout base = ws_layout_cap(s, 0);
+  const size_t per = (size_t)s->n_q * (sizeof(float) + sizeof(uint16_t));
+  int64_t cap = bytes > base.total && per > 0 ? (int64_t)((bytes - base.total) / per) / 64 * 64 : 0;
+  cap = std::min(cap, hi);
+  while (cap >= lo && ws_layout_cap(s, cap).total > bytes) cap -= 64;   // region rounding
+  if (cap < lo) {
+    WsLayout none = ws_layout_cap(s, lo);
+    none.cap = 0;
+    return none;
+  }
+  return ws_layout_cap(s, cap);
 }
 
 dsa_status run_indexer(const dsa_shape* s, const Plan& p, const void* q_idx,
                        const float* q_scale, const void* k_idx, const float* k_scale,
                        const float* w_idx, float* scores, long long ld, int dense,
-                       hipStream_t st, int32_t* cand_key = nullptr, int* cand_cnt = nullptr) {
+                       hipStream_t st, uint16_t* cand_key = nullptr, int* cand_cnt = nullptr) {
   const bool fp8 = s->idx_dtype == DSA_IDX_FP8_E4M3;
   for (const dsa::SegTable& t : make_tables(p, dsa::indexer_rows_per_block())) {
     dsa::IndexerArgs a = {};
@@ -200,7 +236,7 @@ dsa_status run_indexer(const dsa_shape* s, const Plan& p, const void* q_idx,
 }
 
 dsa_status run_topk(const dsa_shape* s, const Plan& p, const float* scores, long long ld,
-                    int dense, int32_t* idx, hipStream_t st, const int32_t* cand_key = nullptr,
+                    int dense, int32_t* idx, hipStream_t st, const uint16_t* cand_key = nullptr,
                     const int* cand_cnt = nullptr) {
   for (const dsa::SegTable& t : make_tables(p, 1)) {
     dsa::TopkArgs a = {};
@@ -287,9 +323,9 @@ dsa_status run_indexer_topk(const dsa_shape* s, const Plan& p, const void* q_idx
                             const float* w_idx, char* ws, const WsLayout& w, int32_t* idx,
                             hipStream_t st) {
   float* scores = reinterpret_cast<float*>(ws + w.scores_off);
-  int32_t* ckey = reinterpret_cast<int32_t*>(ws + w.ckey_off);
+  uint16_t* ckey = reinterpret_cast<uint16_t*>(ws + w.ckey_off);
   int* ccnt = reinterpret_cast<int*>(ws + w.ccnt_off);
-  const long long ld = ws_score_ld(p);
+  const long long ld = w.cap;
   dsa_status e = run_indexer(s, p, q_idx, q_scale, k_idx, k_scale, w_idx, scores, ld, 0, st,
                              ckey, ccnt);
   if (e != DSA_OK) return e;
@@ -327,6 +363,36 @@ dsa_status check_kl_dims(const dsa_shape* s) {
 
 bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
+// Pointer alignment the kernels' vector loads and stores need: {pointer, bytes, name}; NULL
+// pointers (optional outputs) pass.
+struct AlignReq {
+  const void* p;
+  size_t a;
+  const char* name;
+};
+
+dsa_status check_align(std::initializer_list<AlignReq> reqs) {
+  for (const AlignReq& r : reqs)
+    if (r.p && !aligned(r.p, r.a))
+      return fail(DSA_ERR_INVALID_ARG, "%s must be %zu-byte aligned", r.name, r.a);
+  return DSA_OK;
+}
+
+// Index-side tensors: q_idx / k_idx rows are read in 16-byte pieces.
+dsa_status check_idx_align(const void* q_idx, const float* q_scale, const void* k_idx,
+                           const float* k_scale, const float* w_idx) {
+  return check_align({{q_idx, 16, "q_idx"}, {k_idx, 16, "k_idx"}, {w_idx, 4, "w_idx"},
+                      {q_scale, 4, "q_scale"}, {k_scale, 4, "k_scale"}});
+}
+
+// Attention-side tensors: q and kv rows are gathered / staged in 16-byte pieces and output
+// rows leave in 16-byte pieces.
+dsa_status check_attn_align(const void* q, const void* kv, const int32_t* idx, const void* out,
+                            const float* smax, const float* ssum) {
+  return check_align({{q, 16, "q"}, {kv, 16, "kv"}, {idx, 4, "topk_idx"}, {out, 16, "out"},
+                      {smax, 4, "softmax_max"}, {ssum, 4, "softmax_sum"}});
+}
+
 }  // namespace
 
 extern "C" {
@@ -353,6 +419,8 @@ dsa_status dsa_indexer_scores(const dsa_shape* shape, const void* q_idx, const f
   if (p.covered_rows == 0) return ok();
   if ((st = check_idx_ptrs(shape, q_idx, q_scale, k_idx, k_scale, w_idx)) != DSA_OK) return st;
   if (!scores) return fail(DSA_ERR_INVALID_ARG, "scores is NULL");
+  if ((st = check_idx_align(q_idx, q_scale, k_idx, k_scale, w_idx)) != DSA_OK) return st;
+  if ((st = check_align({{scores, 4, "scores"}})) != DSA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   for (const dsa::SegTable& t : make_tables(p, 1)) {
     dsa::FillArgs f = {};
@@ -374,6 +442,7 @@ dsa_status dsa_topk_select(const dsa_shape* shape, const float* scores, int32_t*
   if (st != DSA_OK) return st;
   if (p.covered_rows == 0) return ok();
   if (!scores || !topk_idx) return fail(DSA_ERR_INVALID_ARG, "scores or topk_idx is NULL");
+  if ((st = check_align({{scores, 4, "scores"}, {topk_idx, 4, "topk_idx"}})) != DSA_OK) return st;
   st = run_topk(shape, p, scores, shape->n_k, 1, topk_idx, static_cast<hipStream_t>(stream));
   return st == DSA_OK ? ok() : st;
 }
@@ -386,6 +455,7 @@ dsa_status dsa_sparse_attn(const dsa_shape* shape, const void* q, const void* kv
   if (st != DSA_OK) return st;
   if (shape->n_q == 0) return ok();
   if (!q || !kv || !topk_idx || !out) return fail(DSA_ERR_INVALID_ARG, "attention tensor is NULL");
+  if ((st = check_attn_align(q, kv, topk_idx, out, softmax_max, softmax_sum)) != DSA_OK) return st;
   st = run_attn(shape, nullptr, q, kv, topk_idx, out, softmax_max, softmax_sum,
                 static_cast<hipStream_t>(stream));
   return st == DSA_OK ? ok() : st;
@@ -402,10 +472,13 @@ dsa_status dsa_forward(const dsa_shape* shape, const void* q_idx, const float* q
   if (p.covered_rows == 0) return ok();   // nothing to do: no pointer is read
   if ((st = check_idx_ptrs(shape, q_idx, q_scale, k_idx, k_scale, w_idx)) != DSA_OK) return st;
   if (!q || !kv || !out) return fail(DSA_ERR_INVALID_ARG, "attention tensor is NULL");
-  const WsLayout w = ws_layout(shape, p);
-  if (!workspace || workspace_bytes < w.total)
-    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+  if ((st = check_idx_align(q_idx, q_scale, k_idx, k_scale, w_idx)) != DSA_OK) return st;
+  if ((st = check_attn_align(q, kv, topk_idx, out, softmax_max, softmax_sum)) != DSA_OK) return st;
+  const WsLayout w = ws_layout_for(shape, p, workspace ? workspace_bytes : 0);
+  if (!workspace || w.cap == 0)
+    return fail(DSA_ERR_WORKSPACE, "workspace of at least %zu bytes needed, %zu given", w.total,
                 workspace ? workspace_bytes : (size_t)0);
+  if ((st = check_align({{workspace, 16, "workspace"}})) != DSA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + w.idx_off);
@@ -425,10 +498,13 @@ dsa_status dsa_indexer_topk(const dsa_shape* shape, const void* q_idx, const flo
   if (p.covered_rows == 0) return ok();
   if ((st = check_idx_ptrs(shape, q_idx, q_scale, k_idx, k_scale, w_idx)) != DSA_OK) return st;
   if (!topk_idx) return fail(DSA_ERR_INVALID_ARG, "topk_idx is NULL");
-  const WsLayout w = ws_layout(shape, p);
-  if (!workspace || workspace_bytes < w.total)
-    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+  if ((st = check_idx_align(q_idx, q_scale, k_idx, k_scale, w_idx)) != DSA_OK) return st;
+  if ((st = check_align({{topk_idx, 4, "topk_idx"}})) != DSA_OK) return st;
+  const WsLayout w = ws_layout_for(shape, p, workspace ? workspace_bytes : 0);
+  if (!workspace || w.cap == 0)
+    return fail(DSA_ERR_WORKSPACE, "workspace of at least %zu bytes needed, %zu given", w.total,
                 workspace ? workspace_bytes : (size_t)0);
+  if ((st = check_align({{workspace, 16, "workspace"}})) != DSA_OK) return st;
   st = run_indexer_topk(shape, p, q_idx, q_scale, k_idx, k_scale, w_idx,
                         static_cast<char*>(workspace), w, topk_idx,
                         static_cast<hipStream_t>(stream));
@@ -441,6 +517,8 @@ dsa_status dsa_quantize_fp8_rows(const void* x_bf16, int64_t rows, int32_t cols,
   if (rows > 0x7fffffff) return fail(DSA_ERR_UNSUPPORTED, "more than 2^31-1 rows");
   if (rows == 0) return ok();
   if (!x_bf16 || !x_fp8 || !scale) return fail(DSA_ERR_INVALID_ARG, "quantize tensor is NULL");
+  dsa_status st = check_align({{x_bf16, 2, "x_bf16"}, {scale, 4, "scale"}});
+  if (st != DSA_OK) return st;
   dsa::QuantArgs a = {};
   a.x = static_cast<const uint16_t*>(x_bf16);
   a.y = static_cast<uint8_t*>(x_fp8);
@@ -476,17 +554,19 @@ dsa_status dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void
     return fail(DSA_ERR_INVALID_ARG, "attention backward tensor is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(dkv) % 16 != 0)
     return fail(DSA_ERR_INVALID_ARG, "workspace and dkv must be 16-byte aligned");
+  if ((st = check_attn_align(q, kv, topk_idx, out, softmax_max, softmax_sum)) != DSA_OK) return st;
+  if ((st = check_align({{dout, 16, "dout"}, {dq, 16, "dq"}})) != DSA_OK) return st;
   const size_t per_row = bwd_row_bytes(shape);
   const size_t fixed = bwd_fixed_bytes(shape);
   const size_t fit = workspace && workspace_bytes > fixed ? (workspace_bytes - fixed) / per_row : 0;
   if (fit == 0)
     return fail(DSA_ERR_WORKSPACE, "workspace of at least %zu bytes (one row) needed, %zu given",
                 fixed + per_row, workspace ? workspace_bytes : (size_t)0);
-  // list entries are row * topk + slot within a chunk: keep them below 2^31
-  const size_t max_rows = (size_t)INT32_MAX / (size_t)shape->topk;
+  // list entries are row * topkp + slot within a chunk: keep them below 2^31
+  const size_t topkp = bwd_topkp(shape);
+  const size_t max_rows = (size_t)INT32_MAX / topkp;
   const int chunk = (int)std::min({fit, (size_t)shape->n_q, max_rows});
   const int h = shape->h, dqk = shape->d_qk, dv = shape->d_v, topk = shape->topk;
-  const size_t topkp = bwd_topkp(shape);
   char* w = static_cast<char*>(workspace);
   size_t at = 0;
   auto take = [&](size_t bytes) {
@@ -572,10 +652,11 @@ dsa_status dsa_indexer_kl_loss_grad(const dsa_shape* shape, const void* q_idx, c
   if (fit == 0)
     return fail(DSA_ERR_WORKSPACE, "workspace of at least %zu bytes (one row) needed, %zu given",
                 fixed + per_row, workspace ? workspace_bytes : (size_t)0);
-  const size_t max_rows = (size_t)INT32_MAX / (size_t)shape->topk;
+  // list entries are row * topkp + slot within a chunk: keep them below 2^31
+  const size_t topkp = kl_topkp(shape);
+  const size_t max_rows = (size_t)INT32_MAX / topkp;
   const int chunk = (int)std::min({fit, (size_t)shape->n_q, max_rows});
   const int topk = shape->topk;
-  const size_t topkp = kl_topkp(shape);
   char* w = static_cast<char*>(workspace);
   size_t at = 0;
   auto take = [&](size_t bytes) {

@@ -45,9 +45,11 @@ struct IndexerArgs {
   long long ld;           // row stride of scores in elements
   int dense;              // 1: column = absolute key row; 0: column = key - k_start
   // candidate mode (fused with the top-k): only scores that can still be in the row's top-k
-  // are written, compacted in key order to scores + i * ld, with their absolute key rows at
-  // cand_key + i * ld and their number at cand_cnt[i]
-  int32_t* cand_key;
+  // are written, compacted in key order to scores + i * ld (ld = the row's candidate slots),
+  // with their keys as offsets in the row's window (a window holds at most 65536 keys) at
+  // cand_key + i * ld and their number at cand_cnt[i]; a row whose candidates would outgrow
+  // its ld slots is compacted in place
+  uint16_t* cand_key;
   int* cand_cnt;
   int topk;
 };
@@ -66,7 +68,7 @@ struct TopkArgs {
   int dense;
   int topk;
   int32_t* idx;           // [n_q, topk]
-  const int32_t* cand_key;   // candidate mode: the rows' candidate keys and counts
+  const uint16_t* cand_key;  // candidate mode: the rows' candidate keys (window offsets), counts
   const int* cand_cnt;
   int cand_min;              // candidate mode: rows with at most this many are served elsewhere
 };
@@ -107,7 +109,7 @@ struct AttnBwdArgs {
   uint16_t* dq;           // [rows, H, DQK] bf16
   float* dkv;             // [n_k, DQK] fp32, accumulated
   uint16_t* ws_c;         // [rows, topkp, DQK] bf16 per-(row, slot) dKV contributions
-  int* list;              // [rows * topk] (row * topk + slot) entries grouped by key
+  int* list;              // [rows * topk] (row * topkp + slot) entries grouped by key
   int* cnt;               // [n_k] entries per key
   int* off;               // [n_k + 1] first entry of each key in `list`
   int* cur;               // [n_k] fill cursor
@@ -143,7 +145,7 @@ struct IdxKlArgs {
 };
 
 // Per-key entry lists of a chunk of top-k rows: every valid (row, slot) entry, as
-// row * topk + slot, grouped by key (off[k] .. off[k + 1] in list).
+// row * topkp + slot, grouped by key (off[k] .. off[k + 1] in list).
 struct KeyListArgs {
   const int32_t* idx;     // [rows, topk]
   int* list;              // [rows * topk]

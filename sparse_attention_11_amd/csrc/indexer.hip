@@ -24,7 +24,9 @@
 // comes from a 256-bin LDS histogram of the candidates' order-preserving keys (bins over a
 // range set by the row's first 32 scores, clamped at both ends): the lower edge of the highest
 // bin with at least k candidates at or above it.  Only candidates are counted, which keeps the
-// counts exact for every bin at or above tau's bin, the only ones the search reads.
+// counts exact for every bin at or above tau's bin, the only ones the search reads.  A row has
+// a fixed number of candidate slots; when the next group might not fit, the wave finds the
+// k-th largest candidate exactly and compacts its list in place to what can still be selected.
 #include "dsa_device.h"
 
 namespace dsa {
@@ -33,6 +35,11 @@ namespace {
 
 constexpr int kIdxWaves = 8;    // query rows (waves) per workgroup
 constexpr int kIdxKeys = 64;    // keys per LDS stage
+// Candidate slots a bf16 row keeps free after its room check between stages: the late
+// waves' pending 64-key group plus the next stage's two (the fp8 kernel offers one group per
+// stage and keeps kIdxKeys free).  A row's slots must number at least topk + this many, or
+// hold the row's whole window.
+constexpr int kRoomBf16 = 3 * kIdxKeys;
 
 // ReLU(x) * w + s with ReLU as one integer max on the fp32 bits: a set sign bit (negative
 // values and -0.0) makes the integer negative, so the result is +0 exactly as max(x, 0).
@@ -55,19 +62,22 @@ struct RowInfo {
 struct CandRow {
   uint32_t* hist;     // this wave's 256 LDS bins
   float* cs;          // candidate scores of the row
-  int32_t* ck;        // candidate keys (absolute rows)
+  uint16_t* ck;       // candidate keys (offsets in the row's window)
   int n;              // candidates written so far
+  int cap;            // candidate slots of the row
   uint32_t base;      // order key of bin 0's upper part
   int shift;          // bin width (log2) in order-key units
   bool init;
   uint32_t tau;       // order-key threshold (0: keep everything)
 };
 
-__device__ __forceinline__ void cand_begin(CandRow& c, uint32_t* hist_wave, float* cs, int32_t* ck) {
+__device__ __forceinline__ void cand_begin(CandRow& c, uint32_t* hist_wave, float* cs,
+                                           uint16_t* ck, int cap) {
   c.hist = hist_wave;
   c.cs = cs;
   c.ck = ck;
   c.n = 0;
+  c.cap = cap;
   c.base = 0u;
   c.shift = 0;
   c.init = false;
@@ -75,8 +85,178 @@ __device__ __forceinline__ void cand_begin(CandRow& c, uint32_t* hist_wave, floa
   *reinterpret_cast<uint4*>(hist_wave + 4 * (threadIdx.x & 63)) = make_uint4(0, 0, 0, 0);
 }
 
-// One 32-key group: lane (key key_abs, valid v) offers score s.
-__device__ __forceinline__ void cand_offer(CandRow& c, float s, int key_abs, bool v) {
+// The highest of the wave's 256 bins b with at least `need` entries in bins >= b (the lane
+// holds bins 4 lane .. 4 lane + 3; the bins must hold at least `need` in total): returns b,
+// with the count in the bins above b in `above` and b's own count in `cnt`.
+__device__ __forceinline__ int hist_crossing(const uint32_t* hist, uint32_t need, uint32_t& above,
+                                             uint32_t& cnt) {
+  const int lane = threadIdx.x & 63;
+  const uint4 h = *reinterpret_cast<const uint4*>(hist + 4 * lane);
+  const uint32_t s4 = h.x + h.y + h.z + h.w;
+  // entries in bins >= 4 lane: the total minus an inclusive prefix sum over the lanes
+  const uint32_t pre = wave_incl_scan(s4);
+  const uint32_t suf = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + s4;
+  const uint32_t s3 = suf - s4 + h.w, s2 = s3 + h.z, s1 = s2 + h.y, s0 = s1 + h.x;
+  const unsigned long long ball = __ballot(s0 >= need);   // lanes 0 .. L*
+  const int lstar = 63 - __clzll(ball);
+  const int j = s3 >= need ? 3 : s2 >= need ? 2 : s1 >= need ? 1 : 0;
+  const uint32_t ab = j == 3 ? suf - s4 : j == 2 ? s3 : j == 1 ? s2 : s1;
+  const uint32_t cn = j == 3 ? h.w : j == 2 ? h.z : j == 1 ? h.y : h.x;
+  above = (uint32_t)__builtin_amdgcn_readlane((int)ab, lstar);
+  cnt = (uint32_t)__builtin_amdgcn_readlane((int)cn, lstar);
+  return 4 * lstar + __builtin_amdgcn_readlane(j, lstar);
+}
+
+constexpr int kCB = 2;   // candidate groups of 64 loaded together by the compaction (more
+                         // would push the indexer's main loop past its registers)
+
+// Order keys of candidates j0 + 64 u + lane, u < kCB (0 past n), loaded together.
+__device__ __forceinline__ void cand_keys(const CandRow& c, int j0, int n, uint32_t* ok) {
+  const int lane = threadIdx.x & 63;
+  float v[kCB];
+#pragma unroll
+  for (int u = 0; u < kCB; ++u) v[u] = c.cs[min(j0 + 64 * u + lane, n - 1)];
+#pragma unroll
+  for (int u = 0; u < kCB; ++u) ok[u] = j0 + 64 * u + lane < n ? order_key(v[u]) : 0u;
+}
+
+// Room for the next stage when the row's slots are nearly full.  The k-th largest candidate
+// key T lies in the histogram's crossing bin; when that bin is a bounded one (neither the
+// clamped bottom nor top bin) its range is exact, otherwise the search starts from the
+// candidates' min and max.  Radix passes over the stored candidates (the wave's 256 bins,
+// 8-bit digits of the offset into the current range) narrow the range until it is small
+// enough to keep whole, or down to T itself.  The list is then rewritten in place, in key
+// order, keeping every key at or above the range (when narrowed to T: every key above T, then
+// the first keys equal to T up to k in all; later equal keys lose the tie to lower ones), and
+// the histogram is rebuilt over what is kept.  Only keys that can no longer be in the row's
+// top-k are dropped: k kept keys lie at or above the new bound and each precedes every later
+// key.  n >= k on entry; the list ends with at most k + (cap - margin - k) / 2 entries.
+__device__ __forceinline__ void cand_compact(CandRow& c, int k, int margin) {
+  const int lane = threadIdx.x & 63;
+  const int n = c.n;
+  // this wave's candidate stores complete before its lanes read each other's entries
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  // keeping a whole range is enough once the list then holds at most this many
+  const uint32_t limit = (uint32_t)k + (uint32_t)max(0, c.cap - margin - k) / 2u;
+  uint32_t above, cnt;
+  const int b = hist_crossing(c.hist, (uint32_t)k, above, cnt);
+  const uint4 h4 = *reinterpret_cast<const uint4*>(c.hist + 4 * lane);
+  const unsigned long long nz = __ballot((h4.x | h4.y | h4.z | h4.w) != 0u);
+  const int hl_ = 63 - __clzll(nz);   // highest lane with a nonempty bin (n >= k > 0)
+  const uint4 ht = *reinterpret_cast<const uint4*>(c.hist + 4 * hl_);
+  const int hb = 4 * hl_ + (ht.w ? 3 : ht.z ? 2 : ht.y ? 1 : 0);   // highest nonempty bin
+  uint32_t lo, mxk;   // the range [lo, lo + 2^w) holds T; mxk >= every key
+  int w;
+  uint32_t krem;      // keys still to take from inside the range
+  if (b >= 1 && hb <= 254) {
+    lo = c.base + ((uint32_t)b << c.shift);   // (bin b holds keys, so its edge is below 2^32)
+    w = c.shift;
+    krem = (uint32_t)k - above;
+    const unsigned long long top =
+        (unsigned long long)c.base + ((unsigned long long)(hb + 1) << c.shift) - 1ull;
+    mxk = top > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)top;
+  } else {
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int j0 = 0; j0 < n; j0 += 64 * kCB) {
+      uint32_t ok[kCB];
+      cand_keys(c, j0, n, ok);
+#pragma unroll
+      for (int u = 0; u < kCB; ++u) {
+        if (j0 + 64 * u + lane < n) {
+          mn = min(mn, ok[u]);
+          mx = max(mx, ok[u]);
+        }
+      }
+    }
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    lo = mn;
+    mxk = mx;
+    w = mn == mx ? 0 : 32 - __clz((int)(mx - mn));   // 2^w > mx - mn
+    krem = (uint32_t)k;
+    cnt = (uint32_t)n;
+  }
+  uint4* hq = reinterpret_cast<uint4*>(c.hist + 4 * lane);
+  while (w > 0 && (uint32_t)k - krem + cnt > limit) {
+    const int width = min(8, w);
+    const int shift = w - width;
+    __builtin_amdgcn_wave_barrier();
+    *hq = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_wave_barrier();
+    for (int j0 = 0; j0 < n; j0 += 64 * kCB) {
+      uint32_t ok[kCB];
+      cand_keys(c, j0, n, ok);
+#pragma unroll
+      for (int u = 0; u < kCB; ++u) {
+        const uint32_t off = ok[u] - lo;
+        if (j0 + 64 * u + lane < n && ok[u] >= lo && (w >= 32 || (off >> w) == 0u))
+          atomicAdd(&c.hist[off >> shift], 1u);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint32_t ab;
+    const int d = hist_crossing(c.hist, krem, ab, cnt);
+    lo += (uint32_t)d << shift;
+    krem -= ab;
+    w = shift;
+  }
+  const bool exact = w == 0 && (uint32_t)k - krem + cnt > limit;   // keep only k
+  const uint32_t lo32 = lo;
+  // the new histogram: the kept keys span [lo, mxk] over bins 0 .. 127 (bins above are
+  // headroom for larger later scores; both ends clamp)
+  const uint32_t span = mxk - lo;
+  const int nshift = span == 0u ? 0 : max(0, 32 - __clz((int)span) - 7);
+  __builtin_amdgcn_wave_barrier();
+  *hq = make_uint4(0, 0, 0, 0);
+  __builtin_amdgcn_wave_barrier();
+  int m = 0;
+  uint32_t eqseen = 0;
+  for (int j0 = 0; j0 < n; j0 += 64 * kCB) {
+    float v[kCB];
+    uint16_t kk[kCB];
+#pragma unroll
+    for (int u = 0; u < kCB; ++u) {
+      const int j = min(j0 + 64 * u + lane, n - 1);
+      v[u] = c.cs[j];
+      kk[u] = c.ck[j];
+    }
+    // both groups are loaded before the first store: the stores go to positions at or
+    // below these, and below every later load
+#pragma unroll
+    for (int u = 0; u < kCB; ++u) {
+      const bool in = j0 + 64 * u + lane < n;
+      const uint32_t ok = order_key(v[u]);
+      bool keep;
+      if (exact) {
+        const bool eq = in && ok == lo32;
+        const unsigned long long me = __ballot(eq);
+        keep = (in && ok > lo32) || (eq && eqseen + lanes_below(me) < krem);
+        eqseen += (uint32_t)__popcll(me);
+      } else {
+        keep = in && ok >= lo32;
+      }
+      const unsigned long long mk = __ballot(keep);
+      if (keep) {
+        const int p = m + (int)lanes_below(mk);
+        c.cs[p] = v[u];
+        c.ck[p] = kk[u];
+        atomicAdd(&c.hist[min(255u, (ok - lo32) >> nshift)], 1u);
+      }
+      m += __popcll(mk);
+    }
+  }
+  c.n = m;
+  c.base = lo32;
+  c.shift = nshift;
+  c.init = true;
+  // exact: a later key equal to T loses the tie to the k kept keys
+  c.tau = exact ? (lo32 == 0xFFFFFFFFu ? lo32 : lo32 + 1u) : max(c.tau, lo32);
+}
+
+// One 64-lane group: lane (window offset key, valid v) offers score s.
+__device__ __forceinline__ void cand_offer(CandRow& c, float s, int key, bool v, int k) {
   const uint32_t ok = order_key(s);
   if (!c.init) {   // bin range from the row's first group: its span over 64 of the 256 bins
     const uint32_t mn = wave_min_u32(v ? ok : 0xFFFFFFFFu), mx = wave_max_u32(v ? ok : 0u);
@@ -90,11 +270,17 @@ __device__ __forceinline__ void cand_offer(CandRow& c, float s, int key_abs, boo
   if (keep) {
     const int p = c.n + (int)lanes_below(m);
     c.cs[p] = s;
-    c.ck[p] = key_abs;
+    c.ck[p] = (uint16_t)key;
     const uint32_t d = ok < c.base ? 0u : min(255u, (ok - c.base) >> c.shift);
     atomicAdd(&c.hist[d], 1u);
   }
   c.n += __popcll(m);
+}
+
+// Whether the row must compact before offering up to `margin` more keys (slots fewer than
+// k + margin hold the row's whole window, so everything fits).  Wave-uniform.
+__device__ __forceinline__ bool cand_full(const CandRow& c, int k, int margin) {
+  return c.n > c.cap - margin && c.n >= k && c.cap >= k + margin;
 }
 
 // Raise tau from the histogram (once k candidates exist).
@@ -102,20 +288,12 @@ __device__ __forceinline__ void cand_update(CandRow& c, int k) {
   if (c.n < k) return;
   __builtin_amdgcn_wave_barrier();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's histogram atomics landed
-  const int lane = threadIdx.x & 63;
-  const uint4 h = *reinterpret_cast<const uint4*>(c.hist + 4 * lane);   // bins 4 lane .. +3
-  const uint32_t s4 = h.x + h.y + h.z + h.w;
-  // candidates in bins >= 4 lane: the total minus an inclusive prefix sum over the lanes
-  const uint32_t pre = wave_incl_scan(s4);
-  const uint32_t suf = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + s4;
-  const uint32_t s3 = suf - s4 + h.w, s2 = s3 + h.z, s1 = s2 + h.y, s0 = s1 + h.x;
-  const unsigned long long ball = __ballot(s0 >= (uint32_t)k);   // lanes 0 .. L* (nonzero: s0(0) = n)
-  const int lstar = 63 - __clzll(ball);
-  const int j = s3 >= (uint32_t)k ? 3 : s2 >= (uint32_t)k ? 2 : s1 >= (uint32_t)k ? 1 : 0;
-  const int b = 4 * lstar + __builtin_amdgcn_readlane(j, lstar);
+  uint32_t above, cnt;
+  const int b = hist_crossing(c.hist, (uint32_t)k, above, cnt);
   if (b > 0) {
     const unsigned long long e = (unsigned long long)c.base + ((unsigned long long)b << c.shift);
-    c.tau = (uint32_t)min(e, 0xFFFFFFFFull);   // (a bin holding k candidates starts below 2^32)
+    // (a bin holding k candidates starts below 2^32)
+    c.tau = max(c.tau, (uint32_t)min(e, 0xFFFFFFFFull));
   }
 }
 
@@ -185,7 +363,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   const int ntiles = (ri.L_blk + KST - 1) / KST;
   CandRow cr;
   if constexpr (CAND)
-    cand_begin(cr, chist + (tid >> 6) * 256, out, a.cand_key + (size_t)ri.row * a.ld);
+    cand_begin(cr, chist + (tid >> 6) * 256, out, a.cand_key + (size_t)ri.row * a.ld, (int)a.ld);
 
   uint4 pre[PER];
   auto fetch = [&](int t) {
@@ -260,7 +438,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
     static_assert(kIdxKeys == 64, "two 32-key groups per half-stage");
     const int key = kb + 32 * g + hl;
     const float sk_ = g ? sv[1] : sv[0];
-    if constexpr (CAND) cand_offer(cr, sk_, ri.k_lo + key, key <= ri.pos);
+    if constexpr (CAND) cand_offer(cr, sk_, key, key <= ri.pos, a.topk);
     else if (key <= ri.pos) out[key] = sk_;
   };
   const bool lag = (tid >> 6) >= kIdxWaves / 2;   // wave-uniform
@@ -310,6 +488,16 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
     }
     if (t + 1 < ntiles) stash(buf ^ 1);
     __syncthreads();
+    // Room for what comes before the next check: the late waves' pending group, flushed here
+    // when the row compacts (then nothing but the query fragments and weights is live, so
+    // the compaction's registers cost the loop nothing), and the next stage's two groups.
+    if constexpr (CAND) {
+      if (ri.ok && cand_full(cr, a.topk, kRoomBf16)) {
+        if (pkb >= 0) epi(pkb);
+        pkb = -1;
+        cand_compact(cr, a.topk, kRoomBf16);
+      }
+    }
   }
   if (pkb >= 0) epi(pkb);
   if constexpr (CAND) {
@@ -381,7 +569,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
   const int ntiles = (ri.L_blk + kIdxKeys - 1) / kIdxKeys;
   CandRow cr;
   if constexpr (CAND)
-    cand_begin(cr, chist + (tid >> 6) * 256, out, a.cand_key + (size_t)ri.row * a.ld);
+    cand_begin(cr, chist + (tid >> 6) * 256, out, a.cand_key + (size_t)ri.row * a.ld, (int)a.ld);
 
   uint4 pre[PER];
   float pres = 0.f;
@@ -457,7 +645,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
       static_assert(kIdxKeys == 64, "two 32-key sub-tiles per stage");
       const int key = kb + 32 * g + hl;
       const float sc = (g ? sv[1] : sv[0]) * sks[buf][32 * g + hl];
-      if constexpr (CAND) cand_offer(cr, sc, ri.k_lo + key, key <= ri.pos);
+      if constexpr (CAND) cand_offer(cr, sc, key, key <= ri.pos, a.topk);
       else if (key <= ri.pos) out[key] = sc;
     }
     if (ri.ok) {
@@ -467,6 +655,9 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
     }
     if (t + 1 < ntiles) stash(buf ^ 1);
     __syncthreads();
+    if constexpr (CAND) {   // the next stage offers one 64-key group
+      if (ri.ok && cand_full(cr, a.topk, kIdxKeys)) cand_compact(cr, a.topk, kIdxKeys);
+    }
   }
   if constexpr (CAND) {
     if (ri.ok && lane == 0) a.cand_cnt[ri.row] = cr.n;

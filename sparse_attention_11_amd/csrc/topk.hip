@@ -21,7 +21,7 @@
 namespace dsa {
 
 // CAND: the row's input is the candidate list the fused indexer wrote (scores compacted in
-// key order, their keys, their count) instead of the whole window.  The list holds every key
+// key order, their keys as window offsets, their count) instead of the whole window.  The list holds every key
 // that can be in the top-k, in key order, so the same selection applies with the list
 // position standing in for the key index.
 template <int THREADS, int ITEMS, bool CAND>
@@ -50,9 +50,9 @@ __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
   if (CAND && (L > THREADS * ITEMS || L <= a.cand_min)) return;
   const int topk = a.topk;
   const float* src = a.scores + (size_t)row * a.ld + (a.dense ? k_lo : 0);
-  const int32_t* ckey = CAND ? a.cand_key + (size_t)row * a.ld : nullptr;
+  const uint16_t* ckey = CAND ? a.cand_key + (size_t)row * a.ld : nullptr;
   int32_t* dst = a.idx + (size_t)row * topk;
-  auto key_of = [&](int e) { return CAND ? ckey[e] : k_lo + e; };
+  auto key_of = [&](int e) { return CAND ? k_lo + (int)ckey[e] : k_lo + e; };
 
   if (L <= topk) {
     for (int t = tid; t < topk; t += THREADS) dst[t] = t < L ? key_of(t) : -1;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(THREADS) void k_topk(TopkArgs a) {
   for (int j = 0; j < ITEMS; ++j) key[j] = __float_as_uint(src[min(j * THREADS + tid, L - 1)]);
   if constexpr (PRE) {
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) ckv[j] = ckey[min(j * THREADS + tid, L - 1)];
+    for (int j = 0; j < ITEMS; ++j) ckv[j] = k_lo + (int)ckey[min(j * THREADS + tid, L - 1)];
   }
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) key[j] = j * THREADS + tid < L ? order_key(__uint_as_float(key[j])) : 0u;
@@ -233,21 +233,27 @@ hipError_t launch_topk_t(const TopkArgs& a, int max_window, hipStream_t s) {
 
 hipError_t launch_topk(const TopkArgs& a, int max_window, hipStream_t s) {
   if (!a.cand_cnt) return launch_topk_t<false>(a, max_window, s);
-  // candidates: rows with at most 8192 go to a small configuration (several workgroups per
-  // CU), rows with up to 16384 to a middle one, the rest to the one sized for the longest
-  // window (each launch skips the rows another one serves)
-  if (max_window <= 8192) return launch_topk_t<true>(a, max_window, s);
+  // candidates (at most a.ld per row): rows with at most 8192 go to a small configuration
+  // (several workgroups per CU), rows with up to 16384 to a middle one, the rest (up to
+  // 32768) to a large one; each launch skips the rows another one serves
   const dim3 grid(a.segs.blk_off[a.segs.n]);
   if (grid.x == 0) return hipSuccess;
+  const long long cap = a.ld;
+  if (cap > 32768) return hipErrorInvalidValue;
   TopkArgs t = a;
   t.cand_min = 0;
+  if (cap <= 2048) {
+    k_topk<256, 8, true><<<grid, 256, 0, s>>>(t);
+    return hipGetLastError();
+  }
   k_topk<512, 16, true><<<grid, 512, 0, s>>>(t);
-  t.cand_min = 8192;
-  k_topk<512, 32, true><<<grid, 512, 0, s>>>(t);
-  if (max_window > 16384) {
+  if (cap > 8192) {
+    t.cand_min = 8192;
+    k_topk<512, 32, true><<<grid, 512, 0, s>>>(t);
+  }
+  if (cap > 16384) {
     t.cand_min = 16384;
-    hipError_t e = launch_topk_t<true>(t, max_window, s);
-    if (e != hipSuccess) return e;
+    k_topk<1024, 32, true><<<grid, 1024, 0, s>>>(t);
   }
   return hipGetLastError();
 }

@@ -263,6 +263,68 @@ def test_topk_whole_window_when_short():
     assert list(O.topk_row(s, 7, 5)) == [7, 8, 9, -1, -1]
 
 
+def test_topk_select_hand_built_multi_segment_windows():
+    """topk_select over a dense score matrix with two segments and an uncovered row, worked by
+    hand: each row's window starts at its segment's first key and holds pos0 + r + 1 keys."""
+    ninf = -np.inf
+    # n_q = 5 rows, n_k = 8 keys; segment A: rows 0-1, keys 1.., pos0 1 (windows {1,2}, {1,2,3});
+    # row 2 uncovered; segment B: rows 3-4, keys 5.., pos0 0 (windows {5}, {5,6})
+    segs = [(0, 2, 1, 4, 1), (3, 2, 5, 3, 0)]
+    S = np.array([
+        [9.0, 1.0, 2.0, 7.0, 7.0, 7.0, 7.0, 7.0],     # window keys 1,2 -> scores 1, 2
+        [9.0, 3.0, 3.0, 5.0, 9.0, 9.0, 9.0, 9.0],     # window keys 1,2,3 -> 3, 3, 5
+        [ninf] * 8,                                    # uncovered
+        [9.0, 9.0, 9.0, 9.0, 9.0, -4.0, 8.0, 8.0],    # window key 5 -> -4
+        [0.0, 0.0, 0.0, 0.0, 0.0, -1.0, -0.0, 8.0],   # window keys 5,6 -> -1, -0
+    ])
+    full = O.topk_select(S, segs, 2)
+    # row 1: keys 1 and 2 tie at 3 below key 3's 5, so the lower key 1 goes with key 3
+    want = np.array([[1, 2], [1, 3], [-1, -1], [5, -1], [5, 6]])
+    assert np.array_equal(full, want)
+    # topk 1: the largest score of each window; row 4 picks -0 (key 6) over -1
+    assert np.array_equal(O.topk_select(S, segs, 1)[:, 0], [2, 3, -1, 5, 6])
+    # a row subset, out of order and with the uncovered row: score row o is local row rows[o]
+    rows = np.array([4, 0, 2, 1])
+    got = O.topk_select(S[rows], segs, 2, n_q=5, rows=rows)
+    assert np.array_equal(got, want[rows])
+    with pytest.raises(ValueError):
+        O.topk_select(S[rows], segs, 2, rows=rows)          # n_q is required with rows
+
+
+def test_row_subsets_equal_rows_of_full_call():
+    """The rows= paths of indexer_scores, topk_select, sparse_attn and dsa_forward give exactly
+    the matching rows of the full call, on a multi-segment share with uncovered rows, for a row
+    subset in arbitrary order (a wrong map from output row o to local row rows[o] fails)."""
+    n_q, n_k, topk, dv, scale = 30, 50, 6, 8, 0.3
+    p = _small_problem(31, n_q, n_k=n_k)
+    # rows 10..13 uncovered; two segments with different key ranges and positions
+    segs = [(0, 10, 0, 30, 12), (14, 16, 30, 20, 3)]
+    full = O.dsa_forward(p["q_idx"], p["k_idx"], p["w"], p["q"], p["kv"], segs, topk, scale, dv)
+    rows = np.array([29, 3, 11, 14, 0, 21, 12, 9])
+    sub = O.dsa_forward(p["q_idx"], p["k_idx"], p["w"], p["q"], p["kv"], segs, topk, scale, dv,
+                        rows=rows)
+    for key in ("scores", "idx", "out", "softmax_max", "softmax_sum"):
+        assert np.array_equal(sub[key], full[key][rows]), key
+    sc = O.indexer_scores(p["q_idx"], p["k_idx"], p["w"], segs, rows=rows)
+    assert np.array_equal(sc, full["scores"][rows])
+    # uncovered rows: all -inf scores, no selection, empty attention
+    unc = np.isin(rows, [10, 11, 12, 13])
+    assert np.all(np.isneginf(sc[unc])) and np.all(sub["idx"][unc] == -1)
+    assert np.all(sub["out"][unc] == 0) and np.all(sub["softmax_sum"][unc] == 0)
+    tk = O.topk_select(full["scores"][rows], segs, topk, n_q=n_q, rows=rows)
+    assert np.array_equal(tk, full["idx"][rows])
+    assert np.array_equal(O.topk_select(full["scores"], segs, topk), full["idx"])
+    o, m, s_ = O.sparse_attn(p["q"], p["kv"], full["idx"], scale, dv, rows=rows)
+    assert np.array_equal(o, full["out"][rows])
+    assert np.array_equal(m, full["softmax_max"][rows]) and np.array_equal(s_, full["softmax_sum"][rows])
+    # and each covered row's selection is topk_row over its own window
+    k_lo, L = O.row_windows(segs, n_q, n_k)
+    for o_, i in enumerate(rows):
+        if L[i] > 0:
+            win = full["scores"][i, k_lo[i]:k_lo[i] + L[i]]
+            assert np.array_equal(sub["idx"][o_], O.topk_row(win, int(k_lo[i]), topk))
+
+
 # ---------------------------------------------------------------------------------- attention
 
 
