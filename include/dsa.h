@@ -268,6 +268,28 @@ dsa_status dsa_indexer_kl_loss_grad(const dsa_shape *shape, const void *q_idx, c
  * 4 * (3 * n_k + 1) bytes rounded up to 256, 1 KiB, and 2 KiB of alignment slack. */
 dsa_status dsa_indexer_kl_workspace_bytes(const dsa_shape *shape, size_t *bytes);
 
+/* Bytes of the fixed device array dsa_forward_noalloc works in (one per GPU). */
+#define DSA_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/*
+ * dsa_forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Arguments, results and errors are
+ * those of dsa_forward without the workspace (the same kernels run, so the results are the
+ * same bit for bit).  The workspace is a device array of DSA_NOALLOC_SCRATCH_BYTES bytes that
+ * the library holds on every GPU it runs on until the process ends; the local rows go through
+ * it in consecutive passes of as many rows as it holds with the default candidate slots
+ * (DSA_ERR_UNSUPPORTED if not even one row's workspace fits).  Nothing in it needs to start
+ * at zero.  The call allocates no device memory and does not synchronise; its first call on a
+ * device looks up that device's array address (make it before any graph capture).  `stream`
+ * must belong to the current device (DSA_ERR_INVALID_ARG otherwise).  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller.
+ */
+dsa_status dsa_forward_noalloc(const dsa_shape *shape, const void *q_idx, const float *q_scale,
+                               const void *k_idx, const float *k_scale, const float *w_idx,
+                               const void *q, const void *kv, void *out, int32_t *topk_idx,
+                               float *softmax_max, float *softmax_sum, void *stream);
+
 /*
  * Per-row (per-token) fp8 quantization for the fp8 indexer: for each of `rows` rows of
  * `cols` bf16 values, scale = amax(|row|) / 448 (1.0 for an all-zero row) and

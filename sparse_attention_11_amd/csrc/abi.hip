@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -393,6 +394,62 @@ dsa_status check_attn_align(const void* q, const void* kv, const int32_t* idx, c
                       {smax, 4, "softmax_max"}, {ssum, 4, "softmax_sum"}});
 }
 
+// ---- the allocation-free forward ---------------------------------------------------------
+// For callers that cannot allocate device memory: the forward's workspace is this fixed array
+// (each GPU the library runs on holds its own copy until the process ends).  Host code never
+// passes the array's name to a kernel or copy (in host code it is a stand-in, not a device
+// address): the device address comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kNoallocScratchBytes = (size_t)DSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the current device (the stream's device must be the
+// current one).
+dsa_status scratch_address(hipStream_t st, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (st) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(st, &sd);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sd != dev)
+      return fail(DSA_ERR_INVALID_ARG, "the stream belongs to device %d, device %d is current",
+                  (int)sd, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DSA_ERR_UNSUPPORTED, "device %d beyond the %d this library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+// The segments of local rows [r0, r1), renumbered from r0 (empty pieces dropped).
+std::vector<dsa_segment> clip_segments(const Plan& p, int r0, int r1) {
+  std::vector<dsa_segment> out;
+  for (const dsa_segment& g : p.segs) {
+    const int a = std::max(g.q_start, r0), b = std::min(g.q_start + g.q_len, r1);
+    if (a >= b) continue;
+    dsa_segment c = g;
+    c.q_start = a - r0;
+    c.q_len = b - a;
+    c.pos0 = g.pos0 + (a - g.q_start);
+    out.push_back(c);
+  }
+  return out;
+}
+
 }  // namespace
 
 extern "C" {
@@ -708,6 +765,68 @@ dsa_status dsa_indexer_kl_loss_grad(const dsa_shape* shape, const void* q_idx, c
   if (loss) {
     hipError_t e = dsa::launch_loss_total(loss_rows, shape->n_q, loss, hs);
     if (e != hipSuccess) return hip_fail(e, "loss sum launch");
+  }
+  return ok();
+}
+
+dsa_status dsa_forward_noalloc(const dsa_shape* shape, const void* q_idx, const float* q_scale,
+                               const void* k_idx, const float* k_scale, const float* w_idx,
+                               const void* q, const void* kv, void* out, int32_t* topk_idx,
+                               float* softmax_max, float* softmax_sum, void* stream) {
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedSegs | kNeedIndexer | kNeedTopk | kNeedAttn, p);
+  if (st != DSA_OK) return st;
+  if (p.covered_rows == 0) return ok();
+  if ((st = check_idx_ptrs(shape, q_idx, q_scale, k_idx, k_scale, w_idx)) != DSA_OK) return st;
+  if (!q || !kv || !out) return fail(DSA_ERR_INVALID_ARG, "attention tensor is NULL");
+  if ((st = check_idx_align(q_idx, q_scale, k_idx, k_scale, w_idx)) != DSA_OK) return st;
+  if ((st = check_attn_align(q, kv, topk_idx, out, softmax_max, softmax_sum)) != DSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void* base = nullptr;
+  if ((st = scratch_address(hs, &base)) != DSA_OK) return st;
+  // rows per pass: as many as the scratch holds with the default candidate slots of the
+  // whole share (a pass's own windows are no longer)
+  const int64_t cap = cand_cap_max(shape, p);
+  dsa_shape one = *shape;
+  one.n_q = 1;
+  const size_t per_row = ws_layout_cap(&one, cap).total;
+  int64_t rows = (int64_t)(kNoallocScratchBytes / per_row);
+  dsa_shape sub = *shape;
+  for (; rows > 1; --rows) {   // region rounding: at most a few steps
+    sub.n_q = (int32_t)std::min<int64_t>(rows, shape->n_q);
+    if (ws_layout_cap(&sub, cap).total <= kNoallocScratchBytes) break;
+  }
+  rows = std::max<int64_t>(1, std::min<int64_t>(rows, shape->n_q));
+  for (int64_t r0 = 0; r0 < shape->n_q; r0 += rows) {
+    const int r1 = (int)std::min<int64_t>(r0 + rows, shape->n_q);
+    std::vector<dsa_segment> segs = clip_segments(p, (int)r0, r1);
+    if (segs.empty()) continue;
+    sub = *shape;
+    sub.n_q = r1 - (int)r0;
+    sub.segs = segs.data();
+    sub.n_segs = (int32_t)segs.size();
+    Plan sp;
+    if ((st = check_shape(&sub, kNeedSegs | kNeedIndexer | kNeedTopk | kNeedAttn, sp)) != DSA_OK)
+      return st;
+    const WsLayout w = ws_layout_for(&sub, sp, kNoallocScratchBytes);
+    if (w.cap == 0)
+      return fail(DSA_ERR_UNSUPPORTED, "one row's workspace (%zu bytes) exceeds the %zu-byte "
+                  "scratch of the allocation-free forward", w.total, kNoallocScratchBytes);
+    char* ws = static_cast<char*>(base);
+    const size_t qi_row = (size_t)shape->h_idx * shape->d_idx *
+                          (shape->idx_dtype == DSA_IDX_FP8_E4M3 ? 1 : 2);
+    const char* qi = static_cast<const char*>(q_idx) + (size_t)r0 * qi_row;
+    const float* qs = q_scale ? q_scale + r0 : nullptr;
+    const float* wi = w_idx + (size_t)r0 * shape->h_idx;
+    const char* qq = static_cast<const char*>(q) + (size_t)r0 * shape->h * shape->d_qk * 2;
+    char* oo = static_cast<char*>(out) + (size_t)r0 * shape->h * shape->d_v * 2;
+    int32_t* idx = topk_idx ? topk_idx + (size_t)r0 * shape->topk
+                            : reinterpret_cast<int32_t*>(ws + w.idx_off);
+    float* sm = softmax_max ? softmax_max + (size_t)r0 * shape->h : nullptr;
+    float* ss = softmax_sum ? softmax_sum + (size_t)r0 * shape->h : nullptr;
+    if ((st = run_indexer_topk(&sub, sp, qi, qs, k_idx, k_scale, wi, ws, w, idx, hs)) != DSA_OK)
+      return st;
+    if ((st = run_attn(&sub, &sp, qq, kv, idx, oo, sm, ss, hs)) != DSA_OK) return st;
   }
   return ok();
 }

@@ -55,6 +55,8 @@ _SIGS = {
     "dsa_sparse_attn": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P]),
     "dsa_forward": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, ctypes.c_size_t, _P]),
+    "dsa_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, _P]),
     "dsa_quantize_fp8_rows": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
     "dsa_sparse_attn_bwd": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P,
                                            _P, _P, _P, ctypes.c_size_t, _P]),
@@ -393,6 +395,36 @@ def dsa_forward(q_idx, k_idx, w_idx, q, kv, segments, topk: int, softmax_scale: 
                            _ptr(smax), _ptr(ssum), _ptr(workspace),
                            ctypes.c_size_t(workspace.numel()), _stream(dev, stream)))
     return out, idx, smax, ssum
+
+
+def dsa_forward_noalloc(q_idx, k_idx, w_idx, q, kv, segments, topk: int, softmax_scale: float,
+                        d_v: int, out, topk_idx=None, softmax_max=None, softmax_sum=None,
+                        q_scale=None, k_scale=None, stream=None):
+    """dsa_forward with the library's fixed per-GPU scratch as its workspace: every output is
+    given by the caller (topk_idx / softmax_max / softmax_sum may be None) and nothing is
+    allocated.  Returns (out, topk_idx, softmax_max, softmax_sum)."""
+    fp8, n_q, h_idx, d_idx = _idx_inputs(q_idx, k_idx, w_idx, q_scale, k_scale)
+    _dev(q, "q", (torch.bfloat16,), 3)
+    _dev(kv, "kv", (torch.bfloat16,), 2)
+    _dev(out, "out", (torch.bfloat16,), 3)
+    n_k = k_idx.shape[0]
+    _, h, d_qk = q.shape
+    if q.shape[0] != n_q or kv.shape != (n_k, d_qk) or tuple(out.shape) != (n_q, h, d_v):
+        raise ValueError("q [n_q,h,d_qk] / kv [n_k,d_qk] / out [n_q,h,d_v] do not match")
+    for t, name, shp in ((topk_idx, "topk_idx", (n_q, topk)), (softmax_max, "softmax_max", (n_q, h)),
+                         (softmax_sum, "softmax_sum", (n_q, h))):
+        if t is not None:
+            _dev(t, name, (torch.int32,) if name == "topk_idx" else (torch.float32,), 2)
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name} must be {shp}")
+    sh = _shape(n_q=n_q, n_k=n_k, h_idx=h_idx, d_idx=d_idx, h=h, d_qk=d_qk, d_v=d_v, topk=topk,
+                softmax_scale=softmax_scale,
+                idx_dtype=DSA_IDX_FP8_E4M3 if fp8 else DSA_IDX_BF16, segments=segments)
+    _check(load_library().dsa_forward_noalloc(
+        ctypes.byref(sh), _ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w_idx),
+        _ptr(q), _ptr(kv), _ptr(out), _ptr(topk_idx), _ptr(softmax_max), _ptr(softmax_sum),
+        _stream(q.device, stream)))
+    return out, topk_idx, softmax_max, softmax_sum
 
 
 def dsa_quantize_fp8_rows(x, out=None, scale=None, stream=None):
