@@ -247,6 +247,9 @@ __device__ __forceinline__ void cand_compact(CandRow& c, int k, int margin) {
       m += __popcll(mk);
     }
   }
+  // the rewrite's stores complete here: the stage loop around this rarely taken path then
+  // carries no pending stores whose registers the next operand reads would have to wait for
+  __builtin_amdgcn_s_waitcnt(0);
   c.n = m;
   c.base = lo32;
   c.shift = nshift;
@@ -275,6 +278,55 @@ __device__ __forceinline__ void cand_offer(CandRow& c, float s, int key, bool v,
     atomicAdd(&c.hist[d], 1u);
   }
   c.n += __popcll(m);
+}
+
+// A 64-lane group marked as candidates (bookkeeping and histogram done) whose list writes are
+// still to be issued: writing them at the end of the stage, after the key stage's loads have
+// landed, keeps the stage loop's waits on those loads from also waiting on fresh stores.
+struct CandPend {
+  float s;
+  uint32_t key;
+  int p;                    // the lane's list slot (kept lanes)
+  unsigned long long m;     // kept lanes
+  bool valid;
+};
+
+__device__ __forceinline__ void cand_mark(CandRow& c, float s, int key, bool v, int k,
+                                          CandPend& pd) {
+  (void)k;
+  const uint32_t ok = order_key(s);
+  if (!c.init) {   // bin range from the row's first group: its span over 64 of the 256 bins
+    const uint32_t mn = wave_min_u32(v ? ok : 0xFFFFFFFFu), mx = wave_max_u32(v ? ok : 0u);
+    const uint32_t span = mx - mn;
+    c.base = mn;
+    c.shift = span == 0u ? 0 : max(0, 32 - __clz((int)span) - 6);
+    c.init = true;
+  }
+  const bool keep = v && ok >= c.tau;
+  const unsigned long long m = __ballot(keep);
+  // the previous group's registers stay reserved until now, so no asynchronous load ever
+  // lands in a register a pending store still reads
+  asm volatile("" :: "v"(pd.s), "v"(pd.key), "v"(pd.p));
+  pd.s = s;
+  pd.key = (uint32_t)key;
+  pd.p = c.n + (int)lanes_below(m);
+  pd.m = m;
+  pd.valid = true;
+  if (keep) {
+    const uint32_t d = ok < c.base ? 0u : min(255u, (ok - c.base) >> c.shift);
+    atomicAdd(&c.hist[d], 1u);
+  }
+  c.n += __popcll(m);
+}
+
+__device__ __forceinline__ void cand_flush(const CandRow& c, CandPend& pd) {
+  if (pd.valid) {
+    if ((pd.m >> (threadIdx.x & 63)) & 1ull) {
+      c.cs[pd.p] = pd.s;
+      c.ck[pd.p] = (uint16_t)pd.key;
+    }
+    pd.valid = false;
+  }
 }
 
 // Whether the row must compact before offering up to `margin` more keys (slots fewer than
@@ -323,18 +375,22 @@ template <int HI, int DI, bool CAND>
 __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) {
   constexpr int MT = (HI + 31) / 32;     // 32-head M tiles
   constexpr int KS = DI / 16;            // K steps of the 32x32x16 MFMA
-  constexpr int ROW = DI + 8;            // LDS row in bf16 elements (16-byte pad)
   constexpr int CPR = DI / 8;            // 16-byte chunks per key row
+  constexpr int SWM = CPR >= 8 ? 7 : CPR - 1;   // chunk swizzle mask (by row)
   constexpr int KST = 2 * kIdxKeys;      // keys per LDS stage (two 64-key halves per barrier)
-  constexpr int CH = KST * CPR;          // chunks per stage
-  constexpr int NT = kIdxWaves * 64;
-  constexpr int PER = (CH + NT - 1) / NT;
-  static_assert(DI % 16 == 0, "d_idx must be a multiple of 16");
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][KST * ROW];
+  constexpr int TILE = KST * DI;         // elements per stage buffer
+  constexpr int NPC = TILE * 2 / 1024;   // 1 KB LDS-DMA pieces per stage
+  constexpr int PPW = NPC / kIdxWaves;   // pieces per wave
+  constexpr int RPP = 1024 / (DI * 2);   // key rows per piece
+  static_assert(DI % 16 == 0 && NPC % kIdxWaves == 0 && CPR * RPP == 64, "stage layout");
+  // key rows unpadded; physical chunk c of row r holds logical chunk c ^ (r & SWM), so the
+  // 16-row key fragments read without bank conflicts
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][TILE];
   __shared__ __attribute__((aligned(16))) uint32_t chist[CAND ? kIdxWaves * 256 : 4];
 
   const RowInfo ri = indexer_row(a.segs);
   const int tid = threadIdx.x, lane = tid & 63, hl = lane & 31, g = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(a.q_idx);
   const uint16_t* ksrc = reinterpret_cast<const uint16_t*>(a.k_idx);
 
@@ -365,26 +421,23 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   if constexpr (CAND)
     cand_begin(cr, chist + (tid >> 6) * 256, out, a.cand_key + (size_t)ri.row * a.ld, (int)a.ld);
 
-  uint4 pre[PER];
-  auto fetch = [&](int t) {
+  // Stage t's key rows go HBM -> LDS by LDS DMA (no registers held; the compiler never waits
+  // on these loads, the stage loop does): piece i of a stage is rows i RPP .. i RPP + RPP - 1,
+  // lane L fills physical chunk L % CPR of row i RPP + L / CPR.  Rows past the block's
+  // windows copy the union's last key: finite values whose scores the epilogue masks.
+  typedef __attribute__((address_space(3))) uint16_t* lds_u16_t;
+  const unsigned sk_lds = (unsigned)(size_t)(lds_u16_t)&sk[0][0];
+  auto fetch = [&](int t, int buf) {
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int c = tid + p * NT;
-      const int key = c / CPR, col = c % CPR;
-      const int kr = t * KST + key;
-      pre[p] = make_uint4(0, 0, 0, 0);
-      if (c < CH && kr < ri.L_blk)
-        pre[p] = *reinterpret_cast<const uint4*>(ksrc + (size_t)(ri.k_lo + kr) * DI + col * 8);
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int c = tid + p * NT;
-      if (c < CH) {
-        const int key = c / CPR, col = c % CPR;
-        *reinterpret_cast<uint4*>(&sk[buf][key * ROW + col * 8]) = pre[p];
-      }
+    for (int j = 0; j < PPW; ++j) {
+      const int i = wave_u + kIdxWaves * j;
+      const int r = i * RPP + lane / CPR;
+      const int c = (lane % CPR) ^ (r & SWM);
+      const int kr = min(t * KST + r, ri.L_blk - 1);
+      const unsigned voff = (unsigned)(ri.k_lo + kr) * (unsigned)(DI * 2) + (unsigned)c * 16u;
+      const unsigned m0v = sk_lds + (unsigned)(buf * TILE * 2 + i * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(m0v), "v"(voff), "s"(ksrc) : "memory", "m0");
     }
   };
 
@@ -396,13 +449,14 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   // next contraction starts.
   constexpr int NTK = kIdxKeys / 32;
   f32x16 acc[NTK][MT];
+  const int swz = hl & SWM;   // rows nt * 32 + hl of a half keep hl's swizzle
   auto bfrag = [&](int buf, int hh, int ks, int nt) {
     return *reinterpret_cast<const bf16x8*>(
-        &sk[buf][(hh * kIdxKeys + nt * 32 + hl) * ROW + ks * 16 + g * 8]);
+        &sk[buf][(hh * kIdxKeys + nt * 32 + hl) * DI + (((2 * ks + g) ^ swz) * 8)]);
   };
   // b0: the first PF K steps' key fragments, read by the caller ahead of an epilogue so
   // their LDS latency is hidden behind it
-  constexpr int PF = 2;
+  constexpr int PF = CAND ? 1 : 2;
   auto mma = [&](int buf, int hh, const bf16x8 (*b0)[NTK]) {
     // both 32-key sub-tiles are computed unconditionally (keys past the row's window are
     // only masked at the store); K steps outer, so the MT x 2 accumulators form independent
@@ -423,7 +477,12 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
           acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[mt][ks], b[nt], acc[nt][mt], 0, 0, 0);
     }
   };
-  auto epi = [&](int kb) {   // kb: first key of the half
+  // The epilogue's output (candidate marks, or the dense scores) is written at the end of the
+  // stage, after the stage's DMA has landed: no wait of the stage loop then covers a fresh store
+  CandPend pend[KST / kIdxKeys];   // per half of a stage
+#pragma unroll
+  for (int i = 0; i < KST / kIdxKeys; ++i) pend[i] = CandPend{0.f, 0u, 0, 0ull, false};
+  auto epi = [&](int kb, int slot) {   // kb: first key of the half
     float sv[NTK];
 #pragma unroll
     for (int nt = 0; nt < NTK; ++nt) {
@@ -438,18 +497,36 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
     static_assert(kIdxKeys == 64, "two 32-key groups per half-stage");
     const int key = kb + 32 * g + hl;
     const float sk_ = g ? sv[1] : sv[0];
-    if constexpr (CAND) cand_offer(cr, sk_, key, key <= ri.pos, a.topk);
-    else if (key <= ri.pos) out[key] = sk_;
+    if constexpr (CAND) {
+      cand_mark(cr, sk_, key, key <= ri.pos, a.topk, pend[slot]);
+    } else {
+      CandPend& pd = pend[slot];
+      asm volatile("" :: "v"(pd.s), "v"(pd.key));   // (see cand_mark)
+      pd.s = sk_;
+      pd.key = (uint32_t)key;
+      pd.valid = true;
+    }
+  };
+  auto flush = [&]() {
+#pragma unroll
+    for (int i = 0; i < KST / kIdxKeys; ++i) {
+      if constexpr (CAND) {
+        cand_flush(cr, pend[i]);
+      } else if (pend[i].valid) {
+        if ((int)pend[i].key <= ri.pos) out[pend[i].key] = pend[i].s;
+        pend[i].valid = false;
+      }
+    }
   };
   const bool lag = (tid >> 6) >= kIdxWaves / 2;   // wave-uniform
   int pkb = -1;                                   // half whose epilogue is pending (lag waves)
 
-  fetch(0);
-  stash(0);
+  fetch(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): stage 0 and the query loads landed
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1);
+    if (t + 1 < ntiles) fetch(t + 1, buf ^ 1);
     bf16x8 bn[PF][NTK];   // non-lag waves: the second half's first fragments
 #pragma unroll
     for (int hh = 0; hh < KST / kIdxKeys; ++hh) {
@@ -462,7 +539,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
           for (int k = 0; k < PF; ++k)
 #pragma unroll
             for (int nt = 0; nt < NTK; ++nt) b0[k][nt] = bfrag(buf, hh, k, nt);
-        if (pkb >= 0) epi(pkb);
+        if (pkb >= 0) epi(pkb, hh);
         pkb = -1;
         if (act) {
           mma(buf, hh, b0);
@@ -480,26 +557,31 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
           for (int k = 0; k < PF; ++k)
 #pragma unroll
             for (int nt = 0; nt < NTK; ++nt) bn[k][nt] = bfrag(buf, hh + 1, k, nt);
-        epi(kb);
+        epi(kb, hh);
       }
     }
     if constexpr (CAND) {   // every second stage: the bound only needs to rise now and then
       if (ri.ok && t * KST <= ri.pos && (t & 1) == 1) cand_update(cr, a.topk);
     }
-    if (t + 1 < ntiles) stash(buf ^ 1);
+    // this wave's pieces of the next stage have landed (the stage issued no other memory
+    // operation: its writes follow), then every wave's, at the barrier
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    flush();
     __syncthreads();
     // Room for what comes before the next check: the late waves' pending group, flushed here
     // when the row compacts (then nothing but the query fragments and weights is live, so
     // the compaction's registers cost the loop nothing), and the next stage's two groups.
     if constexpr (CAND) {
       if (ri.ok && cand_full(cr, a.topk, kRoomBf16)) {
-        if (pkb >= 0) epi(pkb);
+        if (pkb >= 0) epi(pkb, 0);
         pkb = -1;
+        flush();
         cand_compact(cr, a.topk, kRoomBf16);
       }
     }
   }
-  if (pkb >= 0) epi(pkb);
+  if (pkb >= 0) epi(pkb, 0);
+  flush();
   if constexpr (CAND) {
     if (ri.ok && lane == 0) a.cand_cnt[ri.row] = cr.n;
   }
