@@ -376,15 +376,15 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   constexpr int MT = (HI + 31) / 32;     // 32-head M tiles
   constexpr int KS = DI / 16;            // K steps of the 32x32x16 MFMA
   constexpr int CPR = DI / 8;            // 16-byte chunks per key row
-  constexpr int SWM = CPR >= 8 ? 7 : CPR - 1;   // chunk swizzle mask (by row)
+  constexpr int SWM = CPR - 1;           // chunk swizzle mask (by row)
   constexpr int KST = 2 * kIdxKeys;      // keys per LDS stage (two 64-key halves per barrier)
   constexpr int TILE = KST * DI;         // elements per stage buffer
   constexpr int NPC = TILE * 2 / 1024;   // 1 KB LDS-DMA pieces per stage
   constexpr int PPW = NPC / kIdxWaves;   // pieces per wave
   constexpr int RPP = 1024 / (DI * 2);   // key rows per piece
   static_assert(DI % 16 == 0 && NPC % kIdxWaves == 0 && CPR * RPP == 64, "stage layout");
-  // key rows unpadded; physical chunk c of row r holds logical chunk c ^ (r & SWM), so the
-  // 16-row key fragments read without bank conflicts
+  // key rows unpadded; physical chunk c of row r holds logical chunk c ^ (r & SWM): the 16
+  // rows a 128-bit fragment read serves together then fall in 16 distinct bank groups
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][TILE];
   __shared__ __attribute__((aligned(16))) uint32_t chist[CAND ? kIdxWaves * 256 : 4];
 
@@ -435,7 +435,9 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
       const int c = (lane % CPR) ^ (r & SWM);
       const int kr = min(t * KST + r, ri.L_blk - 1);
       const unsigned voff = (unsigned)(ri.k_lo + kr) * (unsigned)(DI * 2) + (unsigned)c * 16u;
-      const unsigned m0v = sk_lds + (unsigned)(buf * TILE * 2 + i * 1024);
+      // (wave-uniform; readfirstlane makes it a scalar, as M0 requires)
+      const unsigned m0v = (unsigned)__builtin_amdgcn_readfirstlane(
+          (int)(sk_lds + (unsigned)(buf * TILE * 2 + i * 1024)));
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                    :: "s"(m0v), "v"(voff), "s"(ksrc) : "memory", "m0");
     }
@@ -449,10 +451,13 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   // next contraction starts.
   constexpr int NTK = kIdxKeys / 32;
   f32x16 acc[NTK][MT];
-  const int swz = hl & SWM;   // rows nt * 32 + hl of a half keep hl's swizzle
+  // rows nt * 32 + hl of a half keep hl's swizzle; per K step one lane offset, the rest
+  // (buffer, half, sub-tile) are immediate offsets of the read
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = hl * DI + (((2 * ks + g) ^ (hl & SWM)) * 8);
   auto bfrag = [&](int buf, int hh, int ks, int nt) {
-    return *reinterpret_cast<const bf16x8*>(
-        &sk[buf][(hh * kIdxKeys + nt * 32 + hl) * DI + (((2 * ks + g) ^ swz) * 8)]);
+    return *reinterpret_cast<const bf16x8*>(&sk[buf][(hh * kIdxKeys + nt * 32) * DI + koff[ks]]);
   };
   // b0: the first PF K steps' key fragments, read by the caller ahead of an epilogue so
   // their LDS latency is hidden behind it
