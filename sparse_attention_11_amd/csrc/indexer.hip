@@ -599,18 +599,23 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
   constexpr int MT = (HI + 31) / 32;
   constexpr int KS = (DI + 63) / 64;     // K steps of the 32x32x64 f8f6f4 MFMA (zero padded)
   constexpr int DP = KS * 64;            // padded width in bytes
-  constexpr int ROW = DP + 16;           // LDS row in bytes (16-byte pad)
-  constexpr int CPR = DP / 16;
-  constexpr int CH = kIdxKeys * CPR;
-  constexpr int NT = kIdxWaves * 64;
-  constexpr int PER = (CH + NT - 1) / NT;
-  static_assert(DI % 16 == 0, "d_idx must be a multiple of 16");
-  __shared__ __attribute__((aligned(16))) uint8_t sk[2][kIdxKeys * ROW];
+  constexpr int CPR = DP / 16;           // 16-byte chunks per LDS row
+  constexpr int RPW = 256 / DP;          // rows per 256-byte bank window
+  constexpr int TILE = kIdxKeys * DP;    // bytes per stage buffer
+  constexpr int NPC = TILE / 1024;       // 1 KB LDS-DMA pieces per stage
+  constexpr int RPP = 1024 / DP;         // key rows per piece
+  static_assert(DI % 16 == 0 && NPC <= kIdxWaves && CPR * RPP == 64, "stage layout");
+  // key rows unpadded, physical chunk c of row r holds logical chunk c ^ ((r / RPW) % CPR): the
+  // 16 rows a 128-bit fragment read serves together fall in 16 distinct bank groups.  Logical
+  // chunks past d_idx (zero padding of the K dimension) repeat the row's first chunks: finite
+  // values the zero query chunks multiply away.
+  __shared__ __attribute__((aligned(16))) uint8_t sk[2][TILE];
   __shared__ float sks[2][kIdxKeys];
   __shared__ __attribute__((aligned(16))) uint32_t chist[CAND ? kIdxWaves * 256 : 4];
 
   const RowInfo ri = indexer_row(a.segs);
   const int tid = threadIdx.x, lane = tid & 63, hl = lane & 31, g = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q_idx);
   const uint8_t* ksrc = reinterpret_cast<const uint8_t*>(a.k_idx);
 
@@ -658,41 +663,47 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
   if constexpr (CAND)
     cand_begin(cr, chist + (tid >> 6) * 256, out, a.cand_key + (size_t)ri.row * a.ld, (int)a.ld);
 
-  uint4 pre[PER];
+  // Stage t's key rows by LDS DMA (piece i = rows i RPP .., lane L fills physical chunk L % CPR
+  // of row i RPP + L / CPR; rows past the block's windows copy the union's last key), and the
+  // stage's key scales through a register (one per thread of the first 64, index clamped the
+  // same way), written to LDS at the end of the stage.
+  typedef __attribute__((address_space(3))) uint8_t* lds_u8_t;
+  const unsigned sk_lds = (unsigned)(size_t)(lds_u8_t)&sk[0][0];
   float pres = 0.f;
-  auto fetch = [&](int t) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int c = tid + p * NT;
-      const int key = c / CPR, col = c % CPR;
-      const int kr = t * kIdxKeys + key;
-      pre[p] = make_uint4(0, 0, 0, 0);
-      if (c < CH && kr < ri.L_blk && col * 16 < DI)
-        pre[p] = *reinterpret_cast<const uint4*>(ksrc + (size_t)(ri.k_lo + kr) * DI + col * 16);
+  auto fetch = [&](int t, int buf) {
+    if (wave_u < NPC) {
+      const int i = wave_u;
+      const int r = i * RPP + lane / CPR;
+      const int lc = (lane % CPR) ^ ((r / RPW) % CPR);
+      const int kr = min(t * kIdxKeys + r, ri.L_blk - 1);
+      const unsigned voff = (unsigned)(ri.k_lo + kr) * (unsigned)DI + (unsigned)(lc % (DI / 16)) * 16u;
+      const unsigned m0v = (unsigned)__builtin_amdgcn_readfirstlane(
+          (int)(sk_lds + (unsigned)(buf * TILE + i * 1024)));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(m0v), "v"(voff), "s"(ksrc) : "memory", "m0");
     }
-    if (tid < kIdxKeys) {
-      const int kr = t * kIdxKeys + tid;
-      pres = kr < ri.L_blk ? a.k_scale[ri.k_lo + kr] : 0.f;
-    }
+    if (tid < kIdxKeys) pres = a.k_scale[ri.k_lo + min(t * kIdxKeys + tid, ri.L_blk - 1)];
   };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int c = tid + p * NT;
-      if (c < CH) {
-        const int key = c / CPR, col = c % CPR;
-        *reinterpret_cast<uint4*>(&sk[buf][key * ROW + col * 16]) = pre[p];
-      }
-    }
+  auto stash_scale = [&](int buf) {
     if (tid < kIdxKeys) sks[buf][tid] = pres;
   };
+  CandPend pend = CandPend{0.f, 0u, 0, 0ull, false};
+  auto flush = [&]() {
+    if constexpr (CAND) {
+      cand_flush(cr, pend);
+    } else if (pend.valid) {
+      if ((int)pend.key <= ri.pos) out[pend.key] = pend.s;
+      pend.valid = false;
+    }
+  };
 
-  fetch(0);
-  stash(0);
+  fetch(0, 0);
+  stash_scale(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): stage 0 landed
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1);
+    if (t + 1 < ntiles) fetch(t + 1, buf ^ 1);
     const int kb = t * kIdxKeys;   // first key of the stage
     if (ri.ok && kb <= ri.pos) {
       // both 32-key sub-tiles (keys past the row's window are masked at the store), then one
@@ -707,9 +718,11 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const uint8_t* bp = &sk[buf][(nt * 32 + hl) * ROW + ks * 64 + g * 32];
-          const uint4 b0 = *reinterpret_cast<const uint4*>(bp);
-          const uint4 b1 = *reinterpret_cast<const uint4*>(bp + 16);
+          const int row = nt * 32 + hl;
+          const int sw = (row / RPW) % CPR;
+          const uint8_t* rp = &sk[buf][row * DP];
+          const uint4 b0 = *reinterpret_cast<const uint4*>(rp + (((ks * 4 + 2 * g) ^ sw) * 16));
+          const uint4 b1 = *reinterpret_cast<const uint4*>(rp + (((ks * 4 + 2 * g + 1) ^ sw) * 16));
           const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
                            (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
 #pragma unroll
@@ -732,15 +745,25 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
       static_assert(kIdxKeys == 64, "two 32-key sub-tiles per stage");
       const int key = kb + 32 * g + hl;
       const float sc = (g ? sv[1] : sv[0]) * sks[buf][32 * g + hl];
-      if constexpr (CAND) cand_offer(cr, sc, key, key <= ri.pos, a.topk);
-      else if (key <= ri.pos) out[key] = sc;
+      if constexpr (CAND) {
+        cand_mark(cr, sc, key, key <= ri.pos, a.topk, pend);
+      } else {
+        asm volatile("" :: "v"(pend.s), "v"(pend.key));   // (see cand_mark)
+        pend.s = sc;
+        pend.key = (uint32_t)key;
+        pend.valid = true;
+      }
     }
     if (ri.ok) {
       if constexpr (CAND) {   // every fourth 64-key stage
         if (t * kIdxKeys <= ri.pos && (t & 3) == 3) cand_update(cr, a.topk);
       }
     }
-    if (t + 1 < ntiles) stash(buf ^ 1);
+    // the next stage's rows and scales landed (the stage's own writes follow), then every
+    // wave's, at the barrier
+    stash_scale(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    flush();
     __syncthreads();
     if constexpr (CAND) {   // the next stage offers one 64-key group
       if (ri.ok && cand_full(cr, a.topk, kIdxKeys)) cand_compact(cr, a.topk, kIdxKeys);
