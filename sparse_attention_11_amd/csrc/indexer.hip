@@ -610,7 +610,9 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
   // chunks past d_idx (zero padding of the K dimension) repeat the row's first chunks: finite
   // values the zero query chunks multiply away.
   __shared__ __attribute__((aligned(16))) uint8_t sk[2][TILE];
-  __shared__ float sks[2][kIdxKeys];
+  // key scales of three stages: a late epilogue reads its stage's while other waves already
+  // write the scales of the stage after next
+  __shared__ float sks[3][kIdxKeys];
   __shared__ __attribute__((aligned(16))) uint32_t chist[CAND ? kIdxWaves * 256 : 4];
 
   const RowInfo ri = indexer_row(a.segs);
@@ -684,8 +686,8 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
     }
     if (tid < kIdxKeys) pres = a.k_scale[ri.k_lo + min(t * kIdxKeys + tid, ri.L_blk - 1)];
   };
-  auto stash_scale = [&](int buf) {
-    if (tid < kIdxKeys) sks[buf][tid] = pres;
+  auto stash_scale = [&](int sbuf) {
+    if (tid < kIdxKeys) sks[sbuf][tid] = pres;
   };
   CandPend pend = CandPend{0.f, 0u, 0, 0ull, false};
   auto flush = [&]() {
@@ -697,6 +699,63 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
     }
   };
 
+  // Per stage: the contraction (both 32-key sub-tiles, 8 MFMAs), then one epilogue for the
+  // 64 keys (lane (hl, g) takes key kb + 32 g + hl, so the filter and the writes run once per
+  // 64 keys on every lane).  The two waves of a SIMD (w and w + 4) would reach their
+  // epilogues together and leave the matrix pipe idle; the upper four waves run each
+  // epilogue one stage late (after the barrier, before their next contraction), so one wave's
+  // MFMAs overlap the other's epilogue.  Stage t's key scales are in sks[t % 3].
+  f32x16 acc[2][MT];
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int row = nt * 32 + hl;
+        const int sw = (row / RPW) % CPR;
+        const uint8_t* rp = &sk[buf][row * DP];
+        const uint4 b0 = *reinterpret_cast<const uint4*>(rp + (((ks * 4 + 2 * g) ^ sw) * 16));
+        const uint4 b1 = *reinterpret_cast<const uint4*>(rp + (((ks * 4 + 2 * g + 1) ^ sw) * 16));
+        const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                         (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          // formats: A and B e4m3 (0); block scales 127 = 2^0
+          acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              qf[mt][ks], b, acc[nt][mt], 0, 0, 0, 127, 0, 127);
+      }
+    }
+  };
+  auto epi = [&](int kb, int sbuf) {
+    float sv[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float s = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s = relu_fma(acc[nt][mt][r], wv[mt][r], s);
+      sv[nt] = pair_sum(s);   // (both lanes of the pair hold the sum)
+    }
+    static_assert(kIdxKeys == 64, "two 32-key sub-tiles per stage");
+    const int key = kb + 32 * g + hl;
+    const float sc = (g ? sv[1] : sv[0]) * sks[sbuf][32 * g + hl];
+    if constexpr (CAND) {
+      cand_mark(cr, sc, key, key <= ri.pos, a.topk, pend);
+    } else {
+      asm volatile("" :: "v"(pend.s), "v"(pend.key));   // (see cand_mark)
+      pend.s = sc;
+      pend.key = (uint32_t)key;
+      pend.valid = true;
+    }
+  };
+  const bool lag = (tid >> 6) >= kIdxWaves / 2;   // wave-uniform
+  int pkb = -1;                                   // stage whose epilogue is pending (lag waves)
+
   fetch(0, 0);
   stash_scale(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): stage 0 landed
@@ -705,54 +764,17 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
     const int buf = t & 1;
     if (t + 1 < ntiles) fetch(t + 1, buf ^ 1);
     const int kb = t * kIdxKeys;   // first key of the stage
-    if (ri.ok && kb <= ri.pos) {
-      // both 32-key sub-tiles (keys past the row's window are masked at the store), then one
-      // epilogue for the 64 keys: lane (hl, g) takes key kb + 32 g + hl, so the filter and
-      // the store run once per 64 keys, on every lane
-      f32x16 acc[2][MT];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = (f32x16){};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int row = nt * 32 + hl;
-          const int sw = (row / RPW) % CPR;
-          const uint8_t* rp = &sk[buf][row * DP];
-          const uint4 b0 = *reinterpret_cast<const uint4*>(rp + (((ks * 4 + 2 * g) ^ sw) * 16));
-          const uint4 b1 = *reinterpret_cast<const uint4*>(rp + (((ks * 4 + 2 * g + 1) ^ sw) * 16));
-          const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                           (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            // formats: A and B e4m3 (0); block scales 127 = 2^0
-            acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                qf[mt][ks], b, acc[nt][mt], 0, 0, 0, 127, 0, 127);
-        }
+    const bool act = ri.ok && kb <= ri.pos;
+    if (lag) {
+      if (pkb >= 0) epi(pkb, (t + 2) % 3);   // stage t - 1
+      pkb = -1;
+      if (act) {
+        mma(buf);
+        pkb = kb;
       }
-      float sv[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float s = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s = relu_fma(acc[nt][mt][r], wv[mt][r], s);
-        sv[nt] = pair_sum(s);   // (both lanes of the pair hold the sum)
-      }
-      static_assert(kIdxKeys == 64, "two 32-key sub-tiles per stage");
-      const int key = kb + 32 * g + hl;
-      const float sc = (g ? sv[1] : sv[0]) * sks[buf][32 * g + hl];
-      if constexpr (CAND) {
-        cand_mark(cr, sc, key, key <= ri.pos, a.topk, pend);
-      } else {
-        asm volatile("" :: "v"(pend.s), "v"(pend.key));   // (see cand_mark)
-        pend.s = sc;
-        pend.key = (uint32_t)key;
-        pend.valid = true;
-      }
+    } else if (act) {
+      mma(buf);
+      epi(kb, t % 3);
     }
     if (ri.ok) {
       if constexpr (CAND) {   // every fourth 64-key stage
@@ -761,14 +783,22 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
     }
     // the next stage's rows and scales landed (the stage's own writes follow), then every
     // wave's, at the barrier
-    stash_scale(buf ^ 1);
+    stash_scale((t + 1) % 3);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     flush();
     __syncthreads();
-    if constexpr (CAND) {   // the next stage offers one 64-key group
-      if (ri.ok && cand_full(cr, a.topk, kIdxKeys)) cand_compact(cr, a.topk, kIdxKeys);
+    // the next check comes after the late waves' pending group and the next stage's group
+    if constexpr (CAND) {
+      if (ri.ok && cand_full(cr, a.topk, 2 * kIdxKeys)) {
+        if (pkb >= 0) epi(pkb, t % 3);
+        pkb = -1;
+        flush();
+        cand_compact(cr, a.topk, 2 * kIdxKeys);
+      }
     }
   }
+  if (pkb >= 0) epi(pkb, (ntiles - 1) % 3);
+  flush();
   if constexpr (CAND) {
     if (ri.ok && lane == 0) a.cand_cnt[ri.row] = cr.n;
   }
