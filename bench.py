@@ -35,7 +35,7 @@ _CSRC = os.path.join(ROOT, "sparse_attention_11_amd", "csrc")
 # in the profiler's dispatch table
 TRAFFIC_KERNELS = {
     "attention": (("attention.hip", "attn_common.h", "dsa_device.h"),
-                  ("k_sparse_attn<128, 576, 512, false",)),
+                  ("k_sparse_attn_ring<128, 576, 512>",)),
     "indexer_candidates": (("indexer.hip", "dsa_device.h"), ("k_indexer_bf16<64, 128, true>",)),
     "topk_candidates": (("topk.hip", "dsa_device.h"),
                         ("k_topk<256, 8, true>", "k_topk<512, 16, true>", "k_topk<512, 32, true>",
@@ -478,7 +478,7 @@ def main():
             "kernels_ms": kt,
         }
         traffic = tr["attention"]["hbm_bytes_per_forward"] if "attention" in tr else None
-        line["roofline"] = {"bound": "mfma", "kernel": "k_sparse_attn (sparse MQA attention)",
+        line["roofline"] = {"bound": "mfma", "kernel": "k_sparse_attn_ring (sparse MQA attention)",
                             "achieved": attn_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": attn_tf / PEAK_BF16_TFLOPS, "traffic": traffic,
                             "per_launch_flop": W["f_attn"]}

@@ -10,17 +10,13 @@
 // Mapping: one workgroup per query row, one wave per 32 query heads (4 waves for 128 heads,
 // one per SIMD), 32 selected keys per tile.
 //   * Gather: the tile's 32 latent rows are copied HBM -> LDS with global_load_lds (16 B per
-//     lane, no VGPR staging) into a ring of three tile buffers.  Each wave copies whole rows,
-//     so the row base is a scalar (the indices come in blocks of eight tiles through the
-//     vector-memory path, eight tiles ahead, and are moved to SGPRs).  Rows are stored unpadded
-//     with their 16-byte chunks XOR-swizzled by row, which keeps both the 16-row logits reads
-//     and the 4-row transposing value reads free of bank conflicts.  Empty slots gather row 0
-//     and are masked.
-//   * Logits: S^T[key, head] = K_tile (A, from LDS) x Q^T (B) on v_mfma_f32_32x32x16_bf16.
-//     The first 416 Q dims stay in VGPRs for the whole row, the rest are staged once in LDS
-//     (Q and the 512-wide accumulator do not both fit in registers otherwise).  A rows
-//     are fed in a fixed key permutation so that each lane's 16 accumulators come out as two
-//     runs of 8 consecutive keys of one head -- the B-operand layout of the next product.
+//     lane, no VGPR staging).  Each wave copies whole rows, so the row base is a scalar.  Rows
+//     are stored unpadded with their 16-byte chunks XOR-swizzled by row, which keeps both the
+//     16-row logits reads and the 4-row transposing value reads free of bank conflicts.  Empty
+//     slots gather row 0 and are masked.
+//   * Logits: S^T[key, head] = K_tile (A, from LDS) x Q^T (B) on v_mfma_f32_32x32x16_bf16.  A
+//     rows are fed in a fixed key permutation so that each lane's 16 accumulators come out as
+//     two runs of 8 consecutive keys of one head -- the B-operand layout of the next product.
 //   * Softmax per lane (a lane pair holds one head), exp2 with the scale folded in.  The
 //     scaling max is the first valid tile's max; p = exp2(z - m) may exceed 1 (fp32 / bf16
 //     keep their relative precision), and only growth past 2^64 is treated as overflow: the
@@ -31,13 +27,17 @@
 //     transposing ds_read_b64_tr_b16) x P^T (B: the lane's bf16 probabilities, no shuffle).
 //     O^T is DV/32 M-tiles of 32 value columns; each lane owns one head's columns, so the
 //     final 1/l is lane-local.
-//   * Software pipeline (128 heads): with one wave per SIMD (the 128 x 512 fp32 accumulator
-//     of a row fills the register file) nothing hides a wave's own latencies, so each step
-//     interleaves two independent MFMA streams -- the logits of tile t+1 and the output
-//     product of tile t -- with the LDS operand reads, the gather of tile t+2 and the step's
+//   * 128 heads (k_sparse_attn_ring): the 128 x 512 fp32 accumulator of a row fills the AGPRs
+//     and all of Q the VGPRs, one wave per SIMD, so nothing hides a wave's own latencies: each
+//     step interleaves two independent MFMA streams -- the logits of tile t+1 and the output
+//     product of tile t -- with the LDS operand reads, the gather of tile t+3 and the step's
 //     bookkeeping in their shadow; the softmax of tile t+1 runs under the second half of the
-//     output product.  One barrier per step.  The output accumulator is pinned to AGPRs and
-//     the logits accumulator to VGPRs (asm MFMAs), so no accumulator moves between the files.
+//     output product.  Four tile buffers (a gather has two steps to land), the slot indices
+//     in an LDS ring filled by LDS DMA, one barrier per step.  The output accumulator is
+//     pinned to AGPRs and the logits accumulator to VGPRs (asm MFMAs), so no accumulator
+//     moves between the files.
+//   * Other shapes and the exact pass: three tile buffers, the Q dims past the first 416 staged
+//     once in LDS, indices read with scalar loads.
 #include "attn_common.h"
 
 namespace dsa {
@@ -45,12 +45,14 @@ namespace dsa {
 namespace {
 
 // S^T for one tile (32 keys x the wave's 32 heads), unscaled, -inf at empty slots; `mx`
-// receives the lane pair's (= one head's) tile max in scaled log2 units.
-template <int H, int DQK, int DV>
+// receives the lane pair's (= one head's) tile max in scaled log2 units.  The first KQR K
+// steps of Q come from qf, the rest from the staged rows in c.qlds.
+template <int H, int DQK, int DV, int KQR = AttnCfg<H, DQK, DV>::KSR>
 __device__ __forceinline__ f32x16 tile_logits(const AttnArgs& a, const RowCtx& c,
                                               const bf16x8* qf, const uint16_t* tile,
                                               unsigned vmask, float& mx) {
   using C = AttnCfg<H, DQK, DV>;
+  static_assert(KQR == C::KSR || KQR == C::KS, "Q split");
   f32x16 s = (f32x16){};
   // row key_perm(hl), logical chunk 2*ks + g at physical chunk (2*ks + g) ^ swz(row): the
   // XOR only touches the low 3 bits, so four per-lane bases (ks mod 4) plus the immediate
@@ -63,7 +65,8 @@ __device__ __forceinline__ f32x16 tile_logits(const AttnArgs& a, const RowCtx& c
   for (int j = 0; j < 4; ++j)
     abase[j] = ltile + arow_i * C::ROWE + (((2 * j + c.g) ^ asw) - 2 * j) * 8;
   auto arow_at = [&](int ks) { return abase[ks & 3] + ks * 16; };
-  const uint16_t* qlrow = c.qlds + (C::DQL > 0 ? c.head % H : 0) * C::QROWE + c.g * 8;
+  const uint16_t* qlrow = KQR < C::KS ? c.qlds + (C::DQL > 0 ? c.head % H : 0) * C::QROWE + c.g * 8
+                                       : nullptr;
   // A fragments (and, past the register part of Q, the staged Q fragments) are read one
   // group of K steps ahead of their MFMAs; sched_barrier bounds the live fragments
   constexpr int QG = 3;                 // K steps per prefetch group (36 = 12 x 3)
@@ -76,7 +79,7 @@ __device__ __forceinline__ f32x16 tile_logits(const AttnArgs& a, const RowCtx& c
       const int ks = gi * QG + u;
       if (ks < C::KS) {
         af[buf][u] = *(lds_cb8_t)(arow_at(ks));
-        if (ks >= C::KSR) bt[buf][u] = *reinterpret_cast<const bf16x8*>(qlrow + (ks - C::KSR) * 16);
+        if (ks >= KQR) bt[buf][u] = *reinterpret_cast<const bf16x8*>(qlrow + (ks - KQR) * 16);
       }
     }
   };
@@ -89,7 +92,7 @@ __device__ __forceinline__ f32x16 tile_logits(const AttnArgs& a, const RowCtx& c
     for (int u = 0; u < QG; ++u) {
       const int ks = gi * QG + u;
       if (ks < C::KS) {
-        const bf16x8 bq = ks < C::KSR ? qf[ks < C::KSR ? ks : 0] : bt[cur][u];
+        const bf16x8 bq = ks < KQR ? qf[ks < KQR ? ks : 0] : bt[cur][u];
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][u], bq, s, 0, 0, 0);
       }
     }
@@ -237,12 +240,12 @@ __device__ __forceinline__ void write_row_staged(const AttnArgs& a, const RowCtx
 // Logits and probabilities of one tile for the wave's heads (pf: the lane's 16 keys as the
 // B operand of the value product).  Returns whether some head's max exceeded the scaling max
 // by more than the fast path's range.
-template <int H, int DQK, int DV>
+template <int H, int DQK, int DV, int KQR = AttnCfg<H, DQK, DV>::KSR>
 __device__ __forceinline__ bool tile_probs(const AttnArgs& a, const RowCtx& c, const bf16x8* qf,
                                            const uint16_t* tile, unsigned vmask, float& m_used,
                                            float& m_true, float& lsum, bf16x8* pf) {
   float mx;
-  f32x16 s = tile_logits<H, DQK, DV>(a, c, qf, tile, vmask, mx);
+  f32x16 s = tile_logits<H, DQK, DV, KQR>(a, c, qf, tile, vmask, mx);
   m_true = fmaxf(m_true, mx);
   if (m_used == kNegInf) m_used = mx;  // first tile with a valid key
   const bool over = mx > m_used + kOverflowLog2;
@@ -349,24 +352,22 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
   return true;
 }
 
-// ---- software-pipelined fast path ----------------------------------------------------------
-// One step of the pipelined loop.  The logits of tile kt (32 keys x the wave's 32 heads) are
-// interleaved with the output product of the previous tile vt, whose probabilities arrive in
-// pf; then the probabilities of kt are formed (returned in pf) while the second half of that
-// output product runs.  The gather of a later tile goes out piece by piece between the
-// MFMAs (so: byte offsets in kv of this wave's rows of it, wbg: LDS address of the wave's
-// first row in the destination buffer), and the bookkeeping of the step runs in their shadow:
-// this wave's validity bits of the gathered tile (gbits) go to vmw, the bits of kt (every
-// wave's) are read from vmr.  Each lane owns one head's value columns, as in tile_pv.
-// vcarry: the first two value fragments of vt on entry (read before the barrier), those of kt
-// on return.  Returns whether some head's max outgrew the scaling range.
-// MODE: kStepFull as above; kStepNoGather for the step whose later tile would lie past the
-// row's last valid slot (nothing to gather); kStepPvOnly for the row's last step: the output
-// product of vt alone (there is no later tile to form logits for).
+// ---- four-buffer ring fast path (128 heads) ------------------------------------------------
+// Q lives in VGPRs whole (36 fragments), which frees the LDS the staged Q tail took: the tile
+// ring is four buffers deep, so a gather has two steps to land instead of one.  Step t forms
+// the output product of tile t and the logits of tile t+1 while tile t+2 lands and the gather of
+// tile t+3 goes out, then meets the other waves at its only barrier.
+// The row's slot indices reach LDS in chunks of eight tiles by LDS DMA (no compiler-tracked
+// vector load in the loop: the compiler does not see the tile gathers, so its wait for such a
+// load would also drain every gather in flight); each step reads its two tiles' slots from
+// there: the validity of the tile whose logits it forms and the rows of the tile it gathers.
 constexpr int kStepFull = 0, kStepNoGather = 1, kStepPvOnly = 2;
+constexpr int kIdxChunk = 256;   // index slots per chunk (eight tiles); the LDS ring holds two
+
+typedef __attribute__((address_space(3))) const int32_t* lds_ci32_t;
 
 // Lane offsets (elements, from a tile's base) of the first two value fragments of a tile,
-// [fragment][half]: the addressing of pipe_tile's vfrag for fragments 0 and 1, computed once
+// [fragment][half]: the addressing of ring_tile's vfrag for fragments 0 and 1, computed once
 // per row; those two fragments of each tile are read ahead, across the step's barrier.
 template <int H, int DQK, int DV>
 __device__ __forceinline__ void vcarry_offsets(const RowCtx& c, unsigned (*vo)[2]) {
@@ -390,16 +391,59 @@ __device__ __forceinline__ bf16x8 vfrag_at(lds_cptr_t tile, const unsigned* vo) 
   return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 }
 
+// Index chunk ch (slots 256 ch .. 256 ch + 255 of the row, reads clamped to the row's last
+// slot) into ring half ch % 2 at LDS byte address idxr: each wave copies 64 slots with one
+// dword LDS DMA.  Completion is tracked by hand (vmcnt before a barrier).
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void idx_chunk_dma(const AttnArgs& a, const RowCtx& c, int ch,
+                                              unsigned idxr) {
+  const int slot = min(ch * kIdxChunk + c.wave_u * 64 + c.lane, a.topk - 1);
+  const unsigned voff = (unsigned)slot * 4u;
+  const unsigned m0v = idxr + (unsigned)((ch & 1) * kIdxChunk * 4) + (unsigned)c.wave_u * 256u;
+  const int32_t* base = c.idx_row;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
+}
+
+// A slot index as the gather uses it: byte offset of its latent row in kv (0 for a slot past
+// topk or an index outside [0, n_k): such rows are gathered from row 0 and masked); returns
+// the validity ballot.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ uint64_t decode_slot(const AttnArgs& a, int v, int slot, unsigned& off) {
+  using C = AttnCfg<H, DQK, DV>;
+  const bool ok = slot < a.topk && (unsigned)v < (unsigned)a.n_k;
+  off = ok ? (unsigned)v * (C::CPR * 16u) : 0u;
+  return __ballot(ok);
+}
+
+// Row offsets (scalars) of this wave's eight rows of a tile whose slots sit in lanes
+// lane0 .. lane0 + 31 of `off`.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void wave_row_offsets(const RowCtx& c, unsigned off, int lane0,
+                                                 unsigned* so) {
+#pragma unroll
+  for (int j = 0; j < AttnCfg<H, DQK, DV>::RPW; ++j)
+    so[j] = __builtin_amdgcn_readlane(off, lane0 + c.wave_u * AttnCfg<H, DQK, DV>::RPW + j);
+}
+
+// One step.  The logits of tile kt (32 keys x the wave's 32 heads, validity bits vmask) are
+// interleaved with the output product of the previous tile vt, whose probabilities arrive in
+// pf; then the probabilities of kt are formed (returned in pf) while the second half of that
+// output product runs.  The gather of a later tile goes out piece by piece between the MFMAs
+// (so: byte offsets in kv of this wave's rows of it, wbg: LDS address of the wave's first row
+// in the destination buffer).  Each lane owns one head's value columns, as in tile_pv.
+// vcarry: the first two value fragments of vt on entry (read before the barrier), those of kt
+// on return.  Returns whether some head's max outgrew the scaling range.
+// MODE: kStepFull as above; kStepNoGather when no later tile is left to gather; kStepPvOnly
+// for the row's last step: the output product of vt alone.
 template <int H, int DQK, int DV, int MODE>
-__device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, const bf16x8* qf,
-                                          lds_cptr_t ktile, const unsigned* vmr, lds_cptr_t vtile,
+__device__ __forceinline__ bool ring_tile(const AttnArgs& a, const RowCtx& c, const bf16x8* qf,
+                                          lds_cptr_t ktile, unsigned vmask, lds_cptr_t vtile,
                                           bf16x8* pf, f32x16* o, float& m_used, float& m_true,
-                                          float& lsum, const unsigned* so, unsigned gbits,
-                                          unsigned* vmw, const unsigned* loff, unsigned wbg,
-                                          bf16x8* vcarry, const unsigned (*vco)[2]) {
+                                          float& lsum, const unsigned* so, const unsigned* loff,
+                                          unsigned wbg, bf16x8* vcarry, const unsigned (*vco)[2]) {
   using C = AttnCfg<H, DQK, DV>;
   typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
-  unsigned vmw_in[C::NW];
   // logits operands: addressing as in tile_logits
   const int arow_i = key_perm(c.hl);
   const int asw = C::SWZ ? swz(arow_i) : 0;
@@ -407,17 +451,15 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     abase[j] = ktile + arow_i * C::ROWE + (((2 * j + c.g) ^ asw) - 2 * j) * 8;
-  const uint16_t* qlrow = c.qlds + c.head * C::QROWE + c.g * 8;
   constexpr int QG = 2;                    // K steps per prefetch group
   constexpr int NG = C::KS / QG;
   static_assert(C::KS % QG == 0, "logits K steps");
-  bf16x8 af[2][QG], bt[2][QG];
+  bf16x8 af[2][QG];
   auto fetch = [&](int gi, int buf) {
 #pragma unroll
     for (int u = 0; u < QG; ++u) {
       const int ks = gi * QG + u;
       af[buf][u] = *(lds_cb8_t)(abase[ks & 3] + ks * 16);
-      if (ks >= C::KSR) bt[buf][u] = *reinterpret_cast<const bf16x8*>(qlrow + (ks - C::KSR) * 16);
     }
   };
   // value operands: addressing as in tile_pv
@@ -492,25 +534,19 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
         for (int j = ks * NPA / C::KS; j < (ks + 1) * NPA / C::KS; ++j) pv(j);
         continue;
       }
-      const bf16x8 bq = ks < C::KSR ? qf[ks < C::KSR ? ks : 0] : bt[cur][u];
       // the logits accumulator is pinned to VGPRs (the AGPRs hold the output accumulator);
       // VALU reads it after the last step: wait out the MFMA write-to-read distance there
       if (ks == 0)
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(af[cur][u]), "v"(bq));
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(af[cur][u]), "v"(qf[ks]));
       else if (ks == C::KS - 1)
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                     : "+v"(s) : "v"(af[cur][u]), "v"(bq));
+                     : "+v"(s) : "v"(af[cur][u]), "v"(qf[ks]));
       else
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(af[cur][u]), "v"(bq));
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(af[cur][u]), "v"(qf[ks]));
       if (GATHER && ks >= 2 && ks < 2 + C::NI) gather_piece(ks - 2);
 #pragma unroll
       for (int j = ks * NPA / C::KS; j < (ks + 1) * NPA / C::KS; ++j)
         if (j >= NPRE) pv(j);
-    }
-    if (GATHER && gi == 4 && c.lane == 0) *vmw = gbits;
-    if (LOGITS && gi == 5) {
-#pragma unroll
-      for (int w = 0; w < C::NW; ++w) vmw_in[w] = vmr[w];
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -519,9 +555,6 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
     for (int j = NPA; j < NP; ++j) pv(j);
     return false;
   }
-  unsigned vmask = 0;
-#pragma unroll
-  for (int w = 0; w < C::NW; ++w) vmask |= vmw_in[w] << (w * C::RPW);
 
   // probabilities of kt (as in tile_logits / tile_probs), interleaved with the second half
   // of the output product of vt
@@ -577,123 +610,128 @@ __device__ __forceinline__ bool pipe_tile(const AttnArgs& a, const RowCtx& c, co
   return over;
 }
 
-// Pipelined fast path.  Same 3-deep LDS ring as the other fast paths, used one tile later:
-// step t forms the output product of tile t and the logits of tile t+1 while the gather of
-// tile t+2 is in flight, then waits for that gather and meets the other waves at the step's
-// only barrier.  The probabilities of tile 0 are formed before the loop; the last step's
-// logits run over the empty tile past the row's last valid slot (every key masked).
-template <int H, int DQK, int DV, bool AL8>
-__device__ __forceinline__ bool accumulate_pipe(const AttnArgs& a, const RowCtx& c,
-                                                const bf16x8* qf, int ib_cur, int ib_nxt) {
+// The ring fast path of one row.  bufs: the four tile buffers; idxr: the index ring (chunks 0
+// and 1 landed in the row prologue), idxr_lds its LDS byte address; flags: NW ints.
+// Tiles past the row's last valid slot are neither gathered nor computed: the last two steps
+// with logits gather nothing, and the row's last step is the output product of its last tile
+// alone.  Returns false -- outputs not written -- when some head's max outgrew the scaling
+// range (the loop still runs to the end: a second loop exit would keep the accumulator from
+// staying in registers).
+template <int H, int DQK, int DV>
+__device__ __forceinline__ bool accumulate_ring(const AttnArgs& a, const RowCtx& c,
+                                                const bf16x8* qf, uint16_t* const* bufs,
+                                                const int32_t* idxr, unsigned idxr_lds,
+                                                int* flags) {
   using C = AttnCfg<H, DQK, DV>;
   constexpr int RPW = C::RPW;
+  static_assert(RPW == 8 && C::NW == 4 && C::NK == 32, "ring slot layout");
   f32x16 o[C::MTV];
 #pragma unroll
   for (int mt = 0; mt < C::MTV; ++mt) o[mt] = (f32x16){};
   float m_used = kNegInf, m_true = kNegInf, lsum = 0.f;
-  bool overflow = false;
   unsigned loff[C::NI];
-  unsigned wb[3];
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) loff[i] = flat_lane_offset<H, DQK, DV>(c, i);
+  unsigned wb[4];
 #pragma unroll
-  for (int k = 0; k < 3; ++k)
-    wb[k] = (unsigned)(size_t)(lds_u16_ptr_t)(c.buf[k]) + c.wave_u * (RPW * C::ROWE * 2);
-  auto tile_mask = [&](int slot) {
-    unsigned vmask = 0;
-#pragma unroll
-    for (int w = 0; w < C::NW; ++w) vmask |= c.vm[slot * C::NW + w] << (w * RPW);
-    return vmask;
-  };
-  // index blocks (eight tiles each) of the tiles the loop gathers: gcur holds the block of
-  // tile t+2 at step t, converted to row offsets and validity bits; ib_nxt the raw block after it
-  GatherBlk gcur = gather_blk<H, DQK, DV>(a, c, ib_cur, 0);
+  for (int k = 0; k < 4; ++k)
+    wb[k] = (unsigned)(size_t)(lds_u16_ptr_t)(bufs[k]) + c.wave_u * (RPW * C::ROWE * 2);
+  const lds_ci32_t ir = (lds_ci32_t)idxr;
+  // slot read by this lane for step t: lanes 0..31 the tile whose logits the step forms (t+1),
+  // lanes 32..63 the tile it gathers (t+3)
+  auto step_slot = [&](int t) { return (t + 1 + 2 * (c.lane >> 5)) * C::NK + (c.lane & 31); };
+
+  // tiles 0, 1, 2 from chunk 0
+  unsigned mask0;
   {
-    unsigned so0[RPW], so1[RPW];
-    tile_offsets<H, DQK, DV>(gcur, 0, so0);
-    tile_offsets<H, DQK, DV>(gcur, 1, so1);
-    gather_tile_flat_so<H, DQK, DV>(a, c, so0, loff, wb[0]);
-    gather_tile_flat_so<H, DQK, DV>(a, c, so1, loff, wb[1]);
+    const int s0 = c.lane, s1 = 2 * C::NK + (c.lane & 31);
+    unsigned off0, off1, so[RPW];
+    mask0 = (unsigned)decode_slot<H, DQK, DV>(a, ir[s0], s0, off0);
+    (void)decode_slot<H, DQK, DV>(a, ir[s1], s1, off1);
+    wave_row_offsets<H, DQK, DV>(c, off0, 0, so);
+    gather_tile_flat_so<H, DQK, DV>(a, c, so, loff, wb[0]);
+    wave_row_offsets<H, DQK, DV>(c, off0, 32, so);
+    gather_tile_flat_so<H, DQK, DV>(a, c, so, loff, wb[1]);
+    wave_row_offsets<H, DQK, DV>(c, off1, 32, so);
+    gather_tile_flat_so<H, DQK, DV>(a, c, so, loff, wb[2]);
   }
-  if (c.lane == 0) {
-    c.vm[0 * C::NW + c.wave] = tile_vbits(gcur, 0);
-    c.vm[1 * C::NW + c.wave] = tile_vbits(gcur, 1);
-  }
-  wait_vm_barrier<C::GOPS>();          // tile 0 landed; tile 1 may be in flight
+  wait_vm_barrier<2 * C::NI>();        // tile 0 landed; tiles 1 and 2 may be in flight
   bf16x8 pf[2];
   // overflow of this wave's heads, combined over the waves once the row is done
-  bool over_any = tile_probs<H, DQK, DV>(a, c, qf, c.buf[0], tile_mask(0), m_used, m_true, lsum,
-                                         pf);
-  wait_vm_barrier<0>();                // tile 1 landed
-
-  // step t: output product of t (slot sv) with the logits of t+1 (slot sk) and the gather of
-  // t+2 (slot sg, free since the previous step's barrier).  Tiles past the row's last valid
-  // slot are neither gathered nor computed: step ntiles-2 gathers nothing, and the last step
-  // is the output product of tile ntiles-1 alone.
-  // the first two value fragments of the tile whose output product comes next
+  bool over_any = tile_probs<H, DQK, DV, C::KS>(a, c, qf, bufs[0], mask0, m_used, m_true, lsum,
+                                                 pf);
+  int iv = ir[step_slot(0)];
+  wait_vm_barrier<C::NI>();            // tile 1 landed
   unsigned vco[2][2];
   vcarry_offsets<H, DQK, DV>(c, vco);
-  bf16x8 vcarry[2] = {vfrag_at<H, DQK, DV>((lds_cptr_t)c.buf[0], vco[0]),
-                      vfrag_at<H, DQK, DV>((lds_cptr_t)c.buf[0], vco[1])};
-  auto step = [&](auto mode, int t, lds_cptr_t bv, lds_cptr_t bk, unsigned wbg, int sk, int sg) {
-    constexpr int MODE = decltype(mode)::value;
-    unsigned so[RPW] = {};
-    unsigned gbits = 0u;
-    if constexpr (MODE == kStepFull) {
-      const int u = t + 2;
-      if ((u & 7) == 0) gcur = gather_blk<H, DQK, DV>(a, c, ib_nxt, u / 8);
-      tile_offsets<H, DQK, DV>(gcur, u, so);
-      gbits = tile_vbits(gcur, u);
-      if ((u & 7) == 0) ib_nxt = load_idx_block<H, DQK, DV>(a, c, u / 8 + 1);   // 8 tiles on
-    }
-    over_any |= pipe_tile<H, DQK, DV, MODE>(a, c, qf, bk, c.vm + sk * C::NW, bv, pf, o, m_used,
-                                            m_true, lsum, so, gbits,
-                                            c.vm + sg * C::NW + c.wave, loff, wbg, vcarry,
-                                            vco);
-    if constexpr (MODE != kStepPvOnly) wait_vm_barrier<0>();   // tile t+2 landed; t free
-  };
-  // one step per loop iteration, the ring slots (LDS addresses, gather bases and slot numbers)
-  // rotating in registers: the accumulator keeps its registers across iterations, and no
-  // indexed private array (scratch memory) is involved
-  lds_cptr_t bv = (lds_cptr_t)c.buf[0], bk = (lds_cptr_t)c.buf[1], bg = (lds_cptr_t)c.buf[2];
-  unsigned wv = wb[0], wk = wb[1], wg = wb[2];
-  int sv = 0, sk = 1, sg = 2;
+  bf16x8 vcarry[2] = {vfrag_at<H, DQK, DV>((lds_cptr_t)bufs[0], vco[0]),
+                      vfrag_at<H, DQK, DV>((lds_cptr_t)bufs[0], vco[1])};
+
+  // ring slots (LDS addresses, gather bases) rotating in registers: the accumulator keeps its
+  // registers across iterations, and no indexed private array (scratch memory) is involved
+  lds_cptr_t bv = (lds_cptr_t)bufs[0], bk = (lds_cptr_t)bufs[1], bl = (lds_cptr_t)bufs[2],
+             bg = (lds_cptr_t)bufs[3];
+  unsigned wv = wb[0], wk = wb[1], wl = wb[2], wg = wb[3];
   auto rotate = [&]() {
     const lds_cptr_t b0 = bv;
     bv = bk;
-    bk = bg;
+    bk = bl;
+    bl = bg;
     bg = b0;
     const unsigned w0 = wv;
     wv = wk;
-    wk = wg;
+    wk = wl;
+    wl = wg;
     wg = w0;
-    const int s0 = sv;
-    sv = sk;
-    sk = sg;
-    sg = s0;
   };
-  for (int t = 0; t < c.ntiles - 2; ++t) {
-    step(std::integral_constant<int, kStepFull>{}, t, bv, bk, wg, sk, sg);
+  // step t: output product of t, logits of t+1, gather of t+3 into the buffer tile t-1 left;
+  // then wait for this wave's gather of t+2 and meet at the barrier
+  auto step = [&](auto mode, int t) {
+    constexpr int MODE = decltype(mode)::value;
+    unsigned vmask = 0u;
+    unsigned so[RPW] = {};
+    if constexpr (MODE != kStepPvOnly) {
+      unsigned off;
+      vmask = (unsigned)decode_slot<H, DQK, DV>(a, iv, step_slot(t), off);
+      if constexpr (MODE == kStepFull) {
+        wave_row_offsets<H, DQK, DV>(c, off, 32, so);
+        // chunk t/8 + 1 (first needed by the gather of step t + 5) into the ring half that
+        // chunk t/8 - 1 left; issued before the step's gather, so the step's final wait
+        // covers it
+        if ((t & 7) == 0 && t > 0) idx_chunk_dma<H, DQK, DV>(a, c, t / 8 + 1, idxr_lds);
+      }
+    }
+    over_any |= ring_tile<H, DQK, DV, MODE>(a, c, qf, bk, vmask, bv, pf, o, m_used, m_true, lsum,
+                                            so, loff, wg, vcarry, vco);
+    if constexpr (MODE != kStepPvOnly) {
+      iv = ir[step_slot(t + 1) & (2 * kIdxChunk - 1)];
+      if constexpr (MODE == kStepFull) wait_vm_barrier<C::NI>();   // t+2 landed, t+3 in flight
+      else wait_vm_barrier<0>();
+    }
+  };
+  const int T = c.ntiles;
+  for (int t = 0; t < T - 3; ++t) {
+    step(std::integral_constant<int, kStepFull>{}, t);
     rotate();
   }
-  if (c.ntiles >= 2) {
-    step(std::integral_constant<int, kStepNoGather>{}, c.ntiles - 2, bv, bk, wg, sk, sg);
+  for (int t = max(T - 3, 0); t < T - 1; ++t) {
+    step(std::integral_constant<int, kStepNoGather>{}, t);
     rotate();
   }
-  if (c.ntiles >= 1) step(std::integral_constant<int, kStepPvOnly>{}, c.ntiles - 1, bv, bk, wg, sk, sg);
+  if (T >= 1) step(std::integral_constant<int, kStepPvOnly>{}, T - 1);
   // no gather may outlive the block; the accumulator's last MFMA writes are read by VALU next
   asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  if (c.lane == 0) c.flags[c.wave] = __ballot(over_any) != 0ull;
+  if (c.lane == 0) flags[c.wave] = __ballot(over_any) != 0ull;
   __syncthreads();
+  bool overflow = false;
 #pragma unroll
-  for (int w = 0; w < C::NW; ++w) overflow |= c.flags[w] != 0;
+  for (int w = 0; w < C::NW; ++w) overflow |= flags[w] != 0;
   if (overflow) return false;
-  // the ring and the staged Q are free (every wave is past the loop): 32 KB per wave
-  static_assert(C::TILE >= 32 * DV && C::QLDS >= 32 * DV && C::NW == 4, "staging space");
-  const lds_cptr_t stg = c.wave_u == 0 ? (lds_cptr_t)c.buf[0]
-                       : (c.wave_u == 1 ? (lds_cptr_t)c.buf[1]
-                       : (c.wave_u == 2 ? (lds_cptr_t)c.buf[2] : (lds_cptr_t)c.qlds));
-  write_row_staged<H, DQK, DV>(a, c, o, lsum, m_used, m_true, (uint16_t*)stg);
+  // the ring is free (every wave is past the loop): one 36 KB buffer per wave for the staging
+  static_assert(C::TILE >= 32 * DV, "staging space");
+  uint16_t* const stg = c.wave_u == 0 ? bufs[0]
+                      : (c.wave_u == 1 ? bufs[1] : (c.wave_u == 2 ? bufs[2] : bufs[3]));
+  write_row_staged<H, DQK, DV>(a, c, o, lsum, m_used, m_true, stg);
   return true;
 }
 
@@ -757,15 +795,10 @@ __device__ __forceinline__ void attn_row(const AttnArgs& a, int bi, int nblk, ui
   c.vm = vmring;
 
   // Row prologue in one memory round trip: the staged part of Q goes to LDS by LDS DMA, and
-  // the pipelined path's first two index blocks, the register part of Q and the index scan
-  // (tiles past the last valid slot are never gathered or computed) are all issued before
-  // anything waits.
+  // the register part of Q and the index scan (tiles past the last valid slot are never
+  // gathered or computed) are issued before anything waits.
+  static_assert(EXACT || !C::PIPE, "the 128-head fast path is k_sparse_attn_ring");
   stage_q_tail<H, DQK, DV>(a, c, qlds);
-  int ib0 = 0, ib1 = 0;
-  if constexpr (C::PIPE && !EXACT) {
-    ib0 = load_idx_block<H, DQK, DV>(a, c, 0);
-    ib1 = load_idx_block<H, DQK, DV>(a, c, 1);
-  }
   bf16x8 qf[C::KSR];
   load_q<H, DQK, DV>(a, c, qf);
   int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
@@ -796,14 +829,101 @@ __device__ __forceinline__ void attn_row(const AttnArgs& a, int bi, int nblk, ui
     }
     accumulate_exact<H, DQK, DV>(a, c, qf, m_fix);
   } else {
-    bool done;
-    if constexpr (C::PIPE) done = accumulate_pipe<H, DQK, DV, AL8>(a, c, qf, ib0, ib1);
-    else done = accumulate_fast<H, DQK, DV, AL8>(a, c, qf);
+    const bool done = accumulate_fast<H, DQK, DV, AL8>(a, c, qf);
     if (!done && c.tid == 0) a.out[(size_t)c.row * H * DV] = kOverflowMark;
   }
 }
 
 }  // namespace
+
+// The fast path of the 128-head shape: a block per row, the four-buffer tile ring, the index
+// ring and all of Q in registers (no staged Q).
+template <int H, int DQK, int DV>
+__global__ __launch_bounds__(64 * ((H + 31) / 32)) void k_sparse_attn_ring(AttnArgs a) {
+  using C = AttnCfg<H, DQK, DV>;
+  static_assert(C::PIPE, "ring path shape");
+  __shared__ __attribute__((aligned(16))) uint16_t kv0[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv1[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv2[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv3[C::TILE];
+  __shared__ __attribute__((aligned(16))) int32_t idxr[2 * kIdxChunk];
+  __shared__ int flags[C::NW];
+  __shared__ int s_last[C::NW];
+
+  // XCD-aware row order, as in attn_row
+  int blk = (int)blockIdx.x;
+  if (a.xcd_remap) blk = (blk & 7) * ((int)gridDim.x >> 3) + (blk >> 3);
+  RowCtx c;
+  if (a.use_segs) {
+    const int g0 = seg_of_block(a.segs, blk);
+    c.row = a.segs.q_start[g0] + (blk - a.segs.blk_off[g0]);
+  } else {
+    c.row = blk;
+  }
+  c.tid = threadIdx.x;
+  c.lane = c.tid & 63;
+  c.wave = c.tid >> 6;
+  c.wave_u = __builtin_amdgcn_readfirstlane(c.wave);
+  c.hl = c.lane & 31;
+  c.g = c.lane >> 5;
+  c.head = c.wave * 32 + c.hl;
+  c.idx_row = a.idx + (size_t)c.row * a.topk;
+  c.buf[0] = c.buf[1] = c.buf[2] = nullptr;
+  c.qlds = nullptr;
+  c.flags = flags;
+  c.vm = nullptr;
+  uint16_t* const bufs[4] = {kv0, kv1, kv2, kv3};
+  const unsigned idxr_lds = (unsigned)(size_t)(__attribute__((address_space(3))) int32_t*)idxr;
+
+  // Row prologue in one memory round trip: the first two index chunks go to LDS by LDS DMA,
+  // and so do the wave's 32 Q rows (36 KB, into the ring buffer numbered like the wave), while
+  // the index scan loads.  Q travels through LDS because the register layout wants, per load
+  // instruction, 32 bytes of each of 32 head rows: fetched directly that is 32 cache lines per
+  // instruction, against 9 for the coalesced 1 KB pieces of the DMA.  The Q rows are stored
+  // like tile rows (chunks swizzled by swz), so the fragment reads below are free of bank
+  // conflicts.
+  idx_chunk_dma<H, DQK, DV>(a, c, 0, idxr_lds);
+  idx_chunk_dma<H, DQK, DV>(a, c, 1, idxr_lds);
+  static_assert(C::TILE == 32 * DQK && C::SWZ, "a wave's Q rows fill one ring buffer");
+  uint16_t* const qbuf = c.wave_u == 0 ? kv0 : (c.wave_u == 1 ? kv1 : (c.wave_u == 2 ? kv2 : kv3));
+  {
+    const uint16_t* qsrc = a.q + ((size_t)c.row * H + c.wave_u * 32) * DQK;
+    const unsigned qdst = (unsigned)(size_t)(lds_u16_ptr_t)qbuf;
+#pragma unroll 4
+    for (int i = 0; i < C::TILE * 2 / 1024; ++i) {
+      const int f = i * 64 + c.lane;            // physical chunk f % CPR of row f / CPR
+      const int r = f / C::CPR, ch = f - r * C::CPR;
+      const unsigned voff = (unsigned)(r * C::CPR + (ch ^ swz(r))) * 16u;
+      const unsigned m0v = qdst + (unsigned)i * 1024u;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(m0v), "v"(voff), "s"(qsrc) : "memory", "m0");
+    }
+  }
+  int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
+  last = (int)wave_max_u32((unsigned)(last + 1)) - 1;   // (last >= -1)
+  if (c.lane == 0) s_last[c.wave] = last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // index chunks landed (DMA is not tracked)
+  __syncthreads();
+  last = -1;
+#pragma unroll
+  for (int w = 0; w < C::NW; ++w) last = max(last, s_last[w]);
+  c.ntiles = (last + C::NK) / C::NK;
+  // compiler-visible vmcnt(0): the index scan loads are done before the gather ring starts,
+  // so the compiler adds no waits for them inside the loop
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // the wave's Q fragments: head row hl, logical chunk 2 ks + g
+  bf16x8 qf[C::KS];
+  {
+    typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
+    const int sw = swz(c.hl);
+    const lds_cptr_t qrow = (lds_cptr_t)qbuf + c.hl * C::ROWE;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = *(lds_cb8_t)(qrow + ((2 * ks + c.g) ^ sw) * 8);
+  }
+  __syncthreads();   // every wave holds its Q: the ring buffers take tiles from here on
+  const bool done = accumulate_ring<H, DQK, DV>(a, c, qf, bufs, idxr, idxr_lds, flags);
+  if (!done && c.tid == 0) a.out[(size_t)c.row * H * DV] = kOverflowMark;
+}
 
 // EXACT = false: the fast path over blocks = rows (a block per row).
 // EXACT = true: a grid-stride pass that recomputes only rows the fast path marked, with the
@@ -856,11 +976,8 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int h, int d_qk, int d_v, int n
   AttnArgs ax = a;
   ax.nrows = nblocks;
   const int exact_grid = nblocks < 1024 ? nblocks : 1024;
-  // 8-slot index blocks: topk a multiple of 8 and 32-byte aligned index rows
-  const bool al8 = a.topk >= 8 && a.topk % 8 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 31) == 0;
   if (h == 128 && d_qk == 576 && d_v == 512) {
-    if (al8) k_sparse_attn<128, 576, 512, false, true><<<nblocks, 256, 0, s>>>(ax);
-    else k_sparse_attn<128, 576, 512, false, false><<<nblocks, 256, 0, s>>>(ax);
+    k_sparse_attn_ring<128, 576, 512><<<nblocks, 256, 0, s>>>(ax);
     k_sparse_attn<128, 576, 512, true, false><<<exact_grid, 256, 0, s>>>(ax);
   } else if (h == 8 && d_qk == 80 && d_v == 64) {
     k_sparse_attn<8, 80, 64, false, false><<<nblocks, 64, 0, s>>>(ax);

@@ -64,8 +64,9 @@ struct AttnCfg {
   // vector-memory instructions one wave issues per tile gather
   static constexpr int GOPS = FLAT ? NI : RPW * ((CPR + 63) / 64);
   static_assert(GOPS < 64, "vmcnt range");
-  // Software-pipelined fast path: the logits of tile t+1 are interleaved with the output
-  // product of tile t (each wave: its own heads, all value columns), one barrier per tile.
+  // Shape of the ring fast path (four tile buffers, all of Q in VGPRs): the logits of tile
+  // t+1 are interleaved with the output product of tile t (each wave: its own heads, all value
+  // columns), one barrier per tile.
   static constexpr bool PIPE = H == 128 && DV == 512 && NW == 4 && FLAT && NI <= KS;
   static_assert(DQK % 16 == 0 && DV % 32 == 0 && DV <= DQK && DQR % 16 == 0, "head dims");
 };
@@ -159,72 +160,6 @@ __device__ __forceinline__ TileIdx<H, DQK, DV> load_tile_idx_s(const Args& a,
     }
   }
   return r;
-}
-
-// The slot indices of tiles 8 blk .. 8 blk + 7 for this wave's rows, one VGPR per wave through
-// the vector-memory path: lane l holds slot (8 blk + l/8) NK + wave RPW + l%8 (-1 past topk).
-// Scalar loads share lgkmcnt with LDS reads and may return out of order, so while one is
-// outstanding every LDS operand wait becomes a full drain that also waits out the scalar
-// load's memory latency; this load counts against vmcnt, in order with the gathers, and a
-// block is fetched eight tiles before its first use.
-// The load is unconditional (address clamped to the row): a select on the loaded value would
-// make the compiler wait for the load right here; slots past topk are masked when the block
-// is read.
-template <int H, int DQK, int DV, class Args>
-__device__ __forceinline__ int load_idx_block(const Args& a, const RowCtx& c, int blk) {
-  using C = AttnCfg<H, DQK, DV>;
-  static_assert(C::RPW == 8, "eight slots per wave and tile");
-  const int slot = (blk * 8 + (c.lane >> 3)) * C::NK + c.wave_u * C::RPW + (c.lane & 7);
-  return c.idx_row[min(slot, a.topk - 1)];
-}
-
-// The indices of tile u (block u / 8 in `ib`) as scalars, -1 past topk; the block's load must
-// have completed.
-template <int H, int DQK, int DV, class Args>
-__device__ __forceinline__ TileIdx<H, DQK, DV> tile_idx_from_block(const Args& a, const RowCtx& c,
-                                                                   int ib, int u) {
-  using C = AttnCfg<H, DQK, DV>;
-  TileIdx<H, DQK, DV> r;
-  const int s0 = u * C::NK + c.wave_u * C::RPW;
-#pragma unroll
-  for (int j = 0; j < C::RPW; ++j) {
-    const int v = __builtin_amdgcn_readlane(ib, (u & 7) * 8 + j);
-    r.v[j] = s0 + j < a.topk ? v : -1;
-  }
-  return r;
-}
-
-// An index block (see load_idx_block) turned, once per eight tiles, into what the gather needs:
-// each lane's byte offset of its slot's latent row in kv (0 for a slot past topk or an index
-// outside [0, n_k): such rows are gathered from row 0 and masked), and the validity ballot,
-// whose byte b holds the bits of tile 8 blk + b for this wave's rows.  Per tile the gather
-// then needs eight lane reads and a shift, not a compare-and-select chain per slot.
-struct GatherBlk {
-  unsigned off;
-  uint64_t bits;
-};
-
-template <int H, int DQK, int DV, class Args>
-__device__ __forceinline__ GatherBlk gather_blk(const Args& a, const RowCtx& c, int raw, int blk) {
-  using C = AttnCfg<H, DQK, DV>;
-  const int slot = (blk * 8 + (c.lane >> 3)) * C::NK + c.wave_u * C::RPW + (c.lane & 7);
-  const bool ok = slot < a.topk && (unsigned)raw < (unsigned)a.n_k;
-  GatherBlk g;
-  g.off = ok ? (unsigned)raw * (C::CPR * 16u) : 0u;
-  g.bits = __ballot(ok);
-  return g;
-}
-
-// Row byte offsets (scalars) of this wave's rows of tile u, from the block holding u.
-template <int H, int DQK, int DV>
-__device__ __forceinline__ void tile_offsets(const GatherBlk& g, int u, unsigned* so) {
-  static_assert(AttnCfg<H, DQK, DV>::RPW == 8, "eight slots per wave and tile");
-#pragma unroll
-  for (int j = 0; j < 8; ++j) so[j] = __builtin_amdgcn_readlane(g.off, (u & 7) * 8 + j);
-}
-
-__device__ __forceinline__ unsigned tile_vbits(const GatherBlk& g, int u) {
-  return (unsigned)(g.bits >> ((u & 7) * 8)) & 0xFFu;
 }
 
 // Validity bits of this wave's slots of a tile (bit j: row wave*RPW + j).
