@@ -26,4 +26,6 @@ from .dsa import (  # noqa: F401
     sparse_attn_bwd,
     indexer_kl_row,
     indexer_kl_loss_grad,
+    dense_attn_row,
+    dense_attn,
 )

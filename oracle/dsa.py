@@ -1,5 +1,5 @@
 """Plain float64 oracle for the DSA forward (with the sparse-attention backward and the indexer
-KL loss) on one CP rank.
+KL loss) on one CP rank, and for the dense causal attention of an Ulysses head shard.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the bench's CPU-baseline
 leg, never by the product path.  Nothing here is blocked, fused or reordered beyond what the
@@ -25,7 +25,10 @@ Sources (four web pages on DeepSeek Sparse Attention and its context parallelism
   query_rope, key_rope) with query-side tensors sharded along the sequence and key-side tensors
   replicated, the indexer-loss boundary that consumes softmax_max / softmax_sum, and the BSND /
   TND layouts; section "基础用法" / load_balance: with head-tail balance the mask is built from
-  K's (global) length; section "适用边界": position ids and masks align with the global window.
+  K's (global) length; section "适用边界": position ids and masks align with the global window;
+  section "ContextParallel 模式": the Pure Ulysses / Hybrid placements of the dense attention.
+* Page "自定义Context Parallel特性", section "SDPA Ulysses CP": the dense model's attention runs
+  as an ordinary SDPA on a head shard that holds the whole sequence.
 
 Readings where the pages are silent (each also listed in the design notes):
 
@@ -445,3 +448,54 @@ def indexer_kl_loss_grad(q_idx, k_idx, w_idx, q, kv, idx, scale: float, loss_gra
                                                             idx[i], scale, loss_grad)
         np.add.at(dk, sel, rows)
     return losses, dq, dw, dk
+
+
+# ----------------------------------------------------------------------------------------
+# dense causal attention on an Ulysses head shard
+# ----------------------------------------------------------------------------------------
+
+
+def dense_attn_row(q_i, k_win, v_win, scale: float):
+    """Causal softmax attention of one query token over the keys of its window, head by head.
+
+    Page "自定义Context Parallel特性", section "SDPA Ulysses CP": an all-to-all turns the
+    sequence-sharded Q/K/V into head-sharded ones, so one device holds the whole context of
+    its heads and runs the ordinary SDPA on them; per head h,
+    z = scale * q[h] . K[:, h]^T over the window, p = softmax(z), out[h] = p . V[:, h].  Also
+    returns lse = log sum exp z (natural log, scaled logits), the statistic a backward uses.
+    q_i [H, D], k_win [L, H, D], v_win [L, H, D_v]; L >= 1."""
+    q_i = np.asarray(q_i, dtype=np.float64)
+    k_win = np.asarray(k_win, dtype=np.float64)
+    v_win = np.asarray(v_win, dtype=np.float64)
+    z = scale * np.einsum("hd,lhd->hl", q_i, k_win)     # [H, L]
+    m = z.max(axis=1)
+    e = np.exp(z - m[:, None])
+    l = e.sum(axis=1)
+    out = np.einsum("hl,lhd->hd", e, v_win) / l[:, None]
+    return out, m + np.log(l)
+
+
+def dense_attn(q, k, v, segments, scale: float, rows=None):
+    """``dense_attn_row`` over the local rows: q [n_q, H, D], k [n_k, H, D], v [n_k, H, D_v].
+
+    Row i of a segment attends keys k_start .. k_start + pos0 + r of k and v (``row_windows``):
+    one segment with pos0 = 0 is plain causal attention over a sequence (pure Ulysses: page
+    "context_parallel.md", section "ContextParallel 模式", Q/K/V moved from a sequence shard to a
+    head shard); a segment with pos0 > 0 is a sequence shard of the queries against the whole
+    gathered K/V (the Hybrid mode, which also gathers K/V over the Colossal group); packed
+    documents are one segment each.  Returns (out [n, H, D_v], lse [n, H]) for the computed
+    rows; rows covered by no segment give out 0 and lse -inf."""
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    n_q, H = q.shape[0], q.shape[1]
+    k_lo, L = row_windows(segments, n_q, k.shape[0])
+    rows_arr = np.arange(n_q) if rows is None else np.asarray(rows)
+    out = np.zeros((len(rows_arr), H, v.shape[2]))
+    lse = np.full((len(rows_arr), H), -np.inf)
+    for o, i in enumerate(rows_arr):
+        if L[i] < 0:
+            continue
+        lo, hi = k_lo[i], k_lo[i] + L[i]
+        out[o], lse[o] = dense_attn_row(q[i], k[lo:hi], v[lo:hi], scale)
+    return out, lse

@@ -663,3 +663,73 @@ def test_generator_is_deterministic_and_shaped():
     assert a["kv"].shape == (256, 80) and a["w_idx"].dtype == torch.float32
     assert torch.equal(a["w_idx"], a["w_idx"].to(torch.bfloat16).float())
     assert float(a["w_idx"].min()) >= 0 and float(a["w_idx"].max()) <= 0.5
+
+
+# ---- dense causal attention (Ulysses head shard) -------------------------------------------
+
+
+def _dense_inputs(n, H, D, Dv, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(n, H, D, generator=g, dtype=torch.float64)
+    k = torch.randn(n, H, D, generator=g, dtype=torch.float64)
+    v = torch.randn(n, H, Dv, generator=g, dtype=torch.float64)
+    return q, k, v
+
+
+def test_dense_attn_matches_library_sdpa_causal():
+    # plain causal SDPA of torch (float64, CPU) over [H, S, D] is the definition written out
+    n, H, D, Dv = 37, 3, 192, 128
+    q, k, v = _dense_inputs(n, H, D, Dv, 11)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = O.dense_attn(q.numpy(), k.numpy(), v.numpy(), [(0, n, 0, n, 0)], scale)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1), is_causal=True, scale=scale)
+    np.testing.assert_allclose(out, ref.transpose(0, 1).numpy(), rtol=0, atol=1e-12)
+    z = scale * torch.einsum("qhd,khd->hqk", q, k)
+    z = z.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), -math.inf)
+    np.testing.assert_allclose(lse, torch.logsumexp(z, dim=-1).T.numpy(), rtol=0, atol=1e-12)
+
+
+def test_dense_attn_hybrid_shard_and_documents():
+    # a query shard at positions 40.. of a 64-key sequence (Hybrid: Q sharded, K/V gathered)
+    # is a masked SDPA with the mask from the global positions, and equals those rows of the
+    # unsharded call; packed documents equal each document alone
+    n, H, D, Dv = 64, 2, 192, 128
+    q, k, v = _dense_inputs(n, H, D, Dv, 12)
+    scale = 0.07
+    full, lse_full = O.dense_attn(q.numpy(), k.numpy(), v.numpy(), [(0, n, 0, n, 0)], scale)
+    sh, lse_sh = O.dense_attn(q[40:].numpy(), k.numpy(), v.numpy(), [(0, 24, 0, n, 40)], scale)
+    np.testing.assert_array_equal(sh, full[40:])
+    np.testing.assert_array_equal(lse_sh, lse_full[40:])
+    pos = torch.arange(40, 64)[:, None]
+    mask = torch.arange(n)[None, :] <= pos
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q[40:].transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1), attn_mask=mask, scale=scale)
+    np.testing.assert_allclose(sh, ref.transpose(0, 1).numpy(), rtol=0, atol=1e-12)
+    segs = [(0, 20, 0, 20, 0), (20, 44, 20, 44, 0)]
+    packed, lse_p = O.dense_attn(q.numpy(), k.numpy(), v.numpy(), segs, scale)
+    a, la = O.dense_attn(q[:20].numpy(), k[:20].numpy(), v[:20].numpy(), [(0, 20, 0, 20, 0)], scale)
+    b, lb = O.dense_attn(q[20:].numpy(), k[20:].numpy(), v[20:].numpy(), [(0, 44, 0, 44, 0)], scale)
+    np.testing.assert_array_equal(packed, np.concatenate([a, b]))
+    np.testing.assert_array_equal(lse_p, np.concatenate([la, lb]))
+    sub, lsub = O.dense_attn(q.numpy(), k.numpy(), v.numpy(), segs, scale, rows=[43, 2, 20])
+    np.testing.assert_array_equal(sub, packed[[43, 2, 20]])
+    np.testing.assert_array_equal(lsub, lse_p[[43, 2, 20]])
+
+
+def test_dense_attn_closed_forms():
+    n, H, D, Dv = 9, 2, 192, 128
+    q, k, v = _dense_inputs(n, H, D, Dv, 13)
+    segs = [(0, n, 0, n, 0)]
+    out, lse = O.dense_attn(q.numpy(), k.numpy(), v.numpy(), segs, 0.1)
+    # the first row sees one key: out is that key's value row, lse its logit
+    np.testing.assert_array_equal(out[0], v[0].numpy())
+    np.testing.assert_allclose(lse[0], 0.1 * (q[0] * k[0]).sum(-1).numpy(), rtol=1e-13)
+    # zero queries: every logit is 0, so out is the mean of the window's values and lse = log L
+    out0, lse0 = O.dense_attn(np.zeros((n, H, D)), k.numpy(), v.numpy(), segs, 0.1)
+    for i in range(n):
+        np.testing.assert_allclose(out0[i], v[: i + 1].numpy().mean(axis=0), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse0[i], math.log(i + 1), rtol=0, atol=1e-15)
+    # uncovered rows: zero output, lse -inf
+    o2, l2 = O.dense_attn(q.numpy(), k.numpy(), v.numpy(), [(0, 4, 0, n, 0)], 0.1)
+    assert np.all(o2[4:] == 0) and np.all(l2[4:] == -np.inf)
