@@ -193,6 +193,30 @@ dsa_status dsa_forward(const dsa_shape *shape, const void *q_idx, const float *q
                        size_t workspace_bytes, void *stream);
 
 /*
+ * Dense causal attention of an Ulysses head shard (page "自定义Context Parallel特性", section
+ * "SDPA Ulysses CP": an all-to-all moves Q/K/V from a sequence shard to a head shard, so one
+ * device runs ordinary SDPA over the whole sequence of its heads; page "context_parallel.md",
+ * section "ContextParallel 模式": Pure Ulysses and Hybrid placements).  Per local row i of a
+ * segment (row r of it, window keys k_start .. k_start + pos0 + r, as for the DSA calls) and
+ * head h:
+ *   z_s = softmax_scale * q[i,h,:] . k[s,h,:];  out[i,h,:] = sum_s softmax(z)_s v[s,h,:];
+ *   lse[i,h] = log(sum_s exp(z_s)) (natural log).
+ * One segment (0, S, 0, S, 0) is plain causal attention over a sequence; a query shard of
+ * the sequence against gathered K/V (Hybrid) sets pos0 to the shard's offset; packed
+ * documents are one segment each.  Used fields of `shape`: n_q, n_k, h (the shard's heads,
+ * >= 1), d_qk = 192, d_v = 128 (the only dims built: DSA_ERR_UNSUPPORTED otherwise),
+ * softmax_scale (finite, > 0), segs / n_segs; the rest is ignored.
+ *   q [n_q, h, 192], k [n_k, h, 192], v [n_k, h, 128], out [n_q, h, 128]: bf16 (BSHD with the
+ *   batch folded into rows), 16-byte aligned; lse [n_q, h] fp32, may be NULL.
+ * n_k * h * 192 * 2 bytes must stay below 4 GiB.  Rows covered by no segment are left
+ * untouched.  bf16 MFMA with fp32 accumulation; the softmax max is rebased only when it grows
+ * by more than 2^8, so probabilities stay below 2^8 before normalisation.  Device memory owned
+ * by the caller; nothing is allocated.
+ */
+dsa_status dsa_dense_attn(const dsa_shape *shape, const void *q, const void *k, const void *v,
+                          void *out, float *lse, void *stream);
+
+/*
  * Sparse-attention backward (page "CANNTorchTitan: ...", section "SparseFlashAttentionGrad"):
  * for each row i, head h and selected slot s (valid index k = topk_idx[i][s]):
  *   z = softmax_scale * q[i,h,:] . kv[k,:];  P = exp(z - softmax_max[i,h]) / softmax_sum[i,h];

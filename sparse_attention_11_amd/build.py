@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 
 SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "attention.hip", "attention_bwd.hip", "indexer_kl.hip",
-           "quant.hip"]
+           "quant.hip", "dense_attn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -26,6 +26,8 @@ hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v
 hipError_t launch_quant_fp8_rows(const QuantArgs& a, hipStream_t s);
 hipError_t launch_indexer_kl(const IdxKlArgs& a, const KeyListArgs& kl, hipStream_t s);
 hipError_t launch_loss_total(const float* loss, int n, float* out, hipStream_t s);
+hipError_t launch_dense_attn(const DenseArgs& a, int nqblk, hipStream_t s);
+int dense_rows_per_block();
 }  // namespace dsa
 
 namespace {
@@ -516,6 +518,43 @@ dsa_status dsa_sparse_attn(const dsa_shape* shape, const void* q, const void* kv
   st = run_attn(shape, nullptr, q, kv, topk_idx, out, softmax_max, softmax_sum,
                 static_cast<hipStream_t>(stream));
   return st == DSA_OK ? ok() : st;
+}
+
+dsa_status dsa_dense_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
+                          void* out, float* lse, void* stream) {
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedSegs, p);
+  if (st != DSA_OK) return st;
+  if (shape->h < 1) return fail(DSA_ERR_INVALID_ARG, "h must be >= 1 (got %d)", shape->h);
+  if (shape->d_qk != 192 || shape->d_v != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "dense attention dims (d_qk=%d, d_v=%d) not built",
+                shape->d_qk, shape->d_v);
+  if (!std::isfinite(shape->softmax_scale) || !(shape->softmax_scale > 0.f))
+    return fail(DSA_ERR_INVALID_ARG, "softmax_scale must be finite and positive");
+  // the tile DMA addresses key rows with 32-bit byte offsets
+  if ((int64_t)shape->n_k * shape->h * shape->d_qk * 2 > (int64_t)UINT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "K of %d rows x %d heads exceeds 4 GiB", shape->n_k,
+                shape->h);
+  if (p.covered_rows == 0) return ok();
+  if (!q || !k || !v || !out) return fail(DSA_ERR_INVALID_ARG, "dense attention tensor is NULL");
+  if ((st = check_align({{q, 16, "q"}, {k, 16, "k"}, {v, 16, "v"}, {out, 16, "out"},
+                         {lse, 4, "lse"}})) != DSA_OK)
+    return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (const dsa::SegTable& t : make_tables(p, dsa::dense_rows_per_block())) {
+    dsa::DenseArgs a = {};
+    a.segs = t;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.h = shape->h;
+    a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
+    hipError_t e = dsa::launch_dense_attn(a, t.blk_off[t.n], hs);
+    if (e != hipSuccess) return hip_fail(e, "dense attention launch");
+  }
+  return ok();
 }
 
 dsa_status dsa_forward(const dsa_shape* shape, const void* q_idx, const float* q_scale,

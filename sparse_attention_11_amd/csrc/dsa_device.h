@@ -95,6 +95,18 @@ struct AttnArgs {
   float scale_log2;       // softmax_scale * log2(e)
 };
 
+// Dense causal attention of a head shard: per-head K and V (not a shared latent row).
+struct DenseArgs {
+  SegTable segs;          // query blocks of 256 rows per segment (blk_off), times the heads
+  const uint16_t* q;      // [n_q, H, 192] bf16
+  const uint16_t* k;      // [n_k, H, 192] bf16
+  const uint16_t* v;      // [n_k, H, 128] bf16
+  uint16_t* out;          // [n_q, H, 128] bf16
+  float* lse;             // [n_q, H] natural-log logsumexp of the scaled logits, or null
+  int h;
+  float scale_log2;       // softmax_scale * log2(e)
+};
+
 // Sparse-attention backward over one chunk of query rows (pointers offset to the chunk).
 struct AttnBwdArgs {
   const uint16_t* q;      // [rows, H, DQK] bf16

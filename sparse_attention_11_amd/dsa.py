@@ -58,6 +58,7 @@ _SIGS = {
     "dsa_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P, _P,
                                            _P, _P, _P, _P]),
     "dsa_quantize_fp8_rows": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
+    "dsa_dense_attn": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P]),
     "dsa_sparse_attn_bwd": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P, _P, _P,
                                            _P, _P, _P, ctypes.c_size_t, _P]),
     "dsa_sparse_attn_bwd_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(Shape),
@@ -259,6 +260,28 @@ def dsa_sparse_attn(q, kv, topk_idx, softmax_scale: float, d_v: int, out=None, s
                                           _ptr(out), _ptr(smax), _ptr(ssum),
                                           _stream(q.device, stream)))
     return out, smax, ssum
+
+
+def dsa_dense_attn(q, k, v, segments, softmax_scale: float, out=None, lse=True, stream=None):
+    """Dense causal attention of a head shard: q [n_q,h,192], k [n_k,h,192], v [n_k,h,128]
+    (bf16), rows windowed by ``segments`` as in the DSA calls.  Returns (out [n_q,h,128] bf16,
+    lse [n_q,h] fp32 or None when ``lse`` is False)."""
+    _dev(q, "q", (torch.bfloat16,), 3)
+    _dev(k, "k", (torch.bfloat16,), 3)
+    _dev(v, "v", (torch.bfloat16,), 3)
+    n_q, h, d_qk = q.shape
+    n_k, d_v = k.shape[0], v.shape[2]
+    if k.shape[1:] != (h, d_qk) or v.shape[:2] != (n_k, h):
+        raise ValueError("q [n_q,h,d_qk], k [n_k,h,d_qk], v [n_k,h,d_v] mismatch")
+    if out is None:
+        out = torch.empty(n_q, h, d_v, dtype=torch.bfloat16, device=q.device)
+    _dev(out, "out", (torch.bfloat16,), 3)
+    lse_t = torch.empty(n_q, h, dtype=torch.float32, device=q.device) if lse else None
+    sh = _shape(n_q=n_q, n_k=n_k, h=h, d_qk=d_qk, d_v=d_v, softmax_scale=softmax_scale,
+                segments=segments)
+    _check(load_library().dsa_dense_attn(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                         _ptr(lse_t), _stream(q.device, stream)))
+    return out, lse_t
 
 
 def dsa_sparse_attn_bwd_workspace_bytes(n_q: int, n_k: int, topk: int, h: int = 128,

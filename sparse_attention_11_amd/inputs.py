@@ -157,3 +157,54 @@ def generate(wl: Workload, seed: int | None = None, device="cpu", gen_device="cp
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 copy of a bf16 / fp32 tensor, for the oracle."""
     return t.detach().to("cpu").double().numpy()
+
+
+# ---- dense causal attention of an Ulysses head shard ---------------------------------------
+# DeepSeek-V3's attention (the dense model the CP pages run under Ulysses) in its training
+# form: 128 heads, q/k heads 192 wide (128 + 64 rope), v heads 128 wide.  One rank of an
+# 8-way Ulysses group holds all 32K positions of 16 heads.  Q, K and V are N(0, 1) in bf16,
+# drawn in that order on a CPU generator seeded with 2000 + workload number.
+
+
+@dataclass(frozen=True)
+class DenseWorkload:
+    name: str
+    n: int                   # query rows = key rows (the packed sequence)
+    h: int                   # heads of the shard
+    segments: tuple
+    d_qk: int = 192
+    d_v: int = 128
+    seed: int = 2000
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_qk)
+
+
+DENSE_WORKLOADS = {
+    0: DenseWorkload("ulysses-tiny-S300-h3", 300, 3, ((0, 300, 0, 300, 0),), seed=2000),
+    1: DenseWorkload("ulysses-cp8-rank-32K-h16", 32768, 16, ((0, 32768, 0, 32768, 0),),
+                     seed=2001),
+}
+
+
+def dense_workload(n: int) -> DenseWorkload:
+    return DENSE_WORKLOADS[n]
+
+
+def generate_dense(wl: DenseWorkload, seed: int | None = None, device="cpu", gen_device="cpu"):
+    """q [n, h, d_qk], k [n, h, d_qk], v [n, h, d_v], bf16 N(0, 1), on ``device``."""
+    g = torch.Generator(device=gen_device)
+    g.manual_seed(wl.seed if seed is None else seed)
+    kw = dict(generator=g, device=gen_device, dtype=torch.float32)
+    out = {}
+    for name, width in (("q", wl.d_qk), ("k", wl.d_qk), ("v", wl.d_v)):
+        t = torch.empty(wl.n, wl.h, width, dtype=torch.bfloat16, device=gen_device)
+        step = max(1, (1 << 26) // (wl.h * width))
+        for r in range(0, wl.n, step):
+            m = min(step, wl.n - r)
+            t[r:r + m] = _bf16(torch.randn(m, wl.h, width, **kw))
+        out[name] = t
+    if str(device) != str(gen_device):
+        out = {k: v.to(device) for k, v in out.items()}
+    return out

@@ -334,3 +334,27 @@ def test_package_exposes_every_binding():
         if name.endswith(("_workspace_bytes",)) or name.startswith("dsa_"):
             if hasattr(dsa, name):
                 assert getattr(pkg, name) is getattr(dsa, name), name
+
+
+def test_dense_attention_argument_checks(lib):
+    def call(h=2, d_qk=192, d_v=128, scale=0.1, segs=((0, 4, 0, 4, 0),), n_k=4, q=FAKE, k=FAKE,
+             v=FAKE, out=FAKE, lse=None):
+        sh = dsa._shape(n_q=4, n_k=n_k, h=h, d_qk=d_qk, d_v=d_v, softmax_scale=scale,
+                        segments=segs)
+        return lib.dsa_dense_attn(ctypes.byref(sh), q, k, v, out, lse, None)
+    assert call(d_qk=576, d_v=512) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(d_v=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(h=0) == dsa.DSA_ERR_INVALID_ARG
+    for bad in (0.0, -0.1, float("nan"), float("inf")):
+        assert call(scale=bad) == dsa.DSA_ERR_INVALID_ARG, bad
+    assert call(segs=((0, 4, 0, 4, 1),)) == dsa.DSA_ERR_INVALID_ARG      # position past k_len
+    assert call(segs=((0, 4, 0, 8, 0),)) == dsa.DSA_ERR_INVALID_ARG      # keys past n_k
+    for name in ("q", "k", "v", "out"):
+        assert call(**{name: None}) == dsa.DSA_ERR_INVALID_ARG, name
+        assert call(**{name: ctypes.c_void_p(0x1008)}) == dsa.DSA_ERR_INVALID_ARG, name
+    assert call(lse=ctypes.c_void_p(0x1002)) == dsa.DSA_ERR_INVALID_ARG
+    # K over 4 GiB of 32-bit DMA offsets
+    big = ((0, 4, 0, 4, 0),)
+    assert call(h=128, n_k=90000, segs=big) == dsa.DSA_ERR_UNSUPPORTED
+    # no covered row: nothing is read or launched, even with NULL tensors
+    assert call(segs=(), q=None, k=None, v=None, out=None) == dsa.DSA_OK
