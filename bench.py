@@ -186,6 +186,26 @@ def backward_stage(args, n=5):
     return rec
 
 
+def dense_stage(args):
+    """Dense causal attention of one 8-way Ulysses rank (32768 positions, 16 of DeepSeek-V3's
+    128 heads, q/k 192 and v 128 wide): time per call and useful TFLOP/s (every causal
+    (query, key) pair once, 2 (192 + 128) flop per pair and head)."""
+    wl = I.dense_workload(1)
+    stream = torch.cuda.current_stream()
+    g = I.generate_dense(wl, device=torch.device("cuda:0"), gen_device="cuda")
+    out = torch.empty(wl.n, wl.h, wl.d_v, dtype=torch.bfloat16, device="cuda:0")
+    reps = max(3, min(args.steps, 10))
+    ms = time_launches(lambda: dsa.dsa_dense_attn(g["q"], g["k"], g["v"], wl.segments,
+                                                  wl.softmax_scale, out=out), reps, stream)
+    pairs = sum(L * (L + 1) // 2 for (_, L, _, _, _) in wl.segments)
+    flop = 2.0 * pairs * wl.h * (wl.d_qk + wl.d_v)
+    tf = flop / (ms * 1e-3) / 1e12
+    print(f"bench: dense attention {wl.name} {ms:.3f} ms {tf:.1f} TFLOP/s", file=sys.stderr,
+          flush=True)
+    return {"workload": wl.name, "ms": ms, "flop": flop, "tflops": tf,
+            "mfma_frac": tf / PEAK_BF16_TFLOPS}
+
+
 def head_tail_stage(args):
     """The CP-degree-8 head-tail share (two 2048-query chunks against 32768 keys): the fused
     indexer + top-k with bf16 index inputs and with e4m3 codes and per-token scales (quantized
@@ -484,6 +504,7 @@ def main():
                             "per_launch_flop": W["f_attn"]}
     if stages:
         line["head_tail"] = head_tail_stage(args)
+        line["dense_attn"] = dense_stage(args)
     if not args.no_backward:
         line["backward"] = backward_stage(args)
     if not args.no_cpu_baseline:
