@@ -590,7 +590,7 @@ __global__ __launch_bounds__(256) void k_keys_scatter(KeyListArgs a) {
 
 // dkv[k] += sum of the key's contributions; one wave per key, so the row is owned and the
 // update is a plain read-modify-write.  Lane l sums dims 8 l .. 8 l + 7 (and, for l < 8,
-// the 64 dims past 512), four entries in flight.
+// the 64 dims past 512), eight entries in flight.
 template <int DQK>
 __global__ __launch_bounds__(256) void k_bwd_reduce(AttnBwdArgs a) {
   static_assert(DQK == 576, "lane split of the latent row");
@@ -616,6 +616,13 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(AttnBwdArgs a) {
     }
   };
   int p = beg;
+  for (; p + 8 <= end; p += 8) {
+    int e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = a.list[p + j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) add(e[j]);
+  }
   for (; p + 4 <= end; p += 4) {
     const int e0 = a.list[p], e1 = a.list[p + 1], e2 = a.list[p + 2], e3 = a.list[p + 3];
     add(e0);
