@@ -357,14 +357,10 @@ __device__ __forceinline__ bool accumulate_fast(const AttnArgs& a, const RowCtx&
 // ring is four buffers deep, so a gather has two steps to land instead of one.  Step t forms
 // the output product of tile t and the logits of tile t+1 while tile t+2 lands and the gather of
 // tile t+3 goes out, then meets the other waves at its only barrier.
-// The row's slot indices reach LDS in chunks of eight tiles by LDS DMA (no compiler-tracked
-// vector load in the loop: the compiler does not see the tile gathers, so its wait for such a
-// load would also drain every gather in flight); each step reads its two tiles' slots from
-// there: the validity of the tile whose logits it forms and the rows of the tile it gathers.
+// The row's slot indices reach LDS in chunks of eight tiles by LDS DMA (idx_chunk_dma); each
+// step reads its two tiles' slots from there: the validity of the tile whose logits it forms
+// and the rows of the tile it gathers.
 constexpr int kStepFull = 0, kStepNoGather = 1, kStepPvOnly = 2;
-constexpr int kIdxChunk = 256;   // index slots per chunk (eight tiles); the LDS ring holds two
-
-typedef __attribute__((address_space(3))) const int32_t* lds_ci32_t;
 
 // Lane offsets (elements, from a tile's base) of the first two value fragments of a tile,
 // [fragment][half]: the addressing of ring_tile's vfrag for fragments 0 and 1, computed once
@@ -389,41 +385,6 @@ __device__ __forceinline__ bf16x8 vfrag_at(lds_cptr_t tile, const unsigned* vo) 
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(tile + vo[0]));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(tile + vo[1]));
   return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-}
-
-// Index chunk ch (slots 256 ch .. 256 ch + 255 of the row, reads clamped to the row's last
-// slot) into ring half ch % 2 at LDS byte address idxr: each wave copies 64 slots with one
-// dword LDS DMA.  Completion is tracked by hand (vmcnt before a barrier).
-template <int H, int DQK, int DV>
-__device__ __forceinline__ void idx_chunk_dma(const AttnArgs& a, const RowCtx& c, int ch,
-                                              unsigned idxr) {
-  const int slot = min(ch * kIdxChunk + c.wave_u * 64 + c.lane, a.topk - 1);
-  const unsigned voff = (unsigned)slot * 4u;
-  const unsigned m0v = idxr + (unsigned)((ch & 1) * kIdxChunk * 4) + (unsigned)c.wave_u * 256u;
-  const int32_t* base = c.idx_row;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
-}
-
-// A slot index as the gather uses it: byte offset of its latent row in kv (0 for a slot past
-// topk or an index outside [0, n_k): such rows are gathered from row 0 and masked); returns
-// the validity ballot.
-template <int H, int DQK, int DV>
-__device__ __forceinline__ uint64_t decode_slot(const AttnArgs& a, int v, int slot, unsigned& off) {
-  using C = AttnCfg<H, DQK, DV>;
-  const bool ok = slot < a.topk && (unsigned)v < (unsigned)a.n_k;
-  off = ok ? (unsigned)v * (C::CPR * 16u) : 0u;
-  return __ballot(ok);
-}
-
-// Row offsets (scalars) of this wave's eight rows of a tile whose slots sit in lanes
-// lane0 .. lane0 + 31 of `off`.
-template <int H, int DQK, int DV>
-__device__ __forceinline__ void wave_row_offsets(const RowCtx& c, unsigned off, int lane0,
-                                                 unsigned* so) {
-#pragma unroll
-  for (int j = 0; j < AttnCfg<H, DQK, DV>::RPW; ++j)
-    so[j] = __builtin_amdgcn_readlane(off, lane0 + c.wave_u * AttnCfg<H, DQK, DV>::RPW + j);
 }
 
 // One step.  The logits of tile kt (32 keys x the wave's 32 heads, validity bits vmask) are

@@ -9,10 +9,11 @@
 // latent row, so both land in one fp32 dKV row (the value part in its first d_v columns).
 //
 // Three kernels over a chunk of query rows, one workgroup per row and four waves:
-//   * k_attn_bwd_p: the forward's gather ring and logits product; every 16-dim A fragment
-//     of the key tile feeds both S^T = K Q^T and (first d_v dims) dP^T = V dY^T, so the
-//     tile is read from LDS once for both.  Each wave owns 32 heads.  It writes P and
-//     softmax_scale * dS as bf16 to a [row][slot][head] workspace (zero at empty slots).
+//   * k_attn_bwd_p_ring: the forward's ring design (index ring, four tile buffers); every
+//     16-dim A fragment of the key tile feeds both S^T = K Q^T and (first d_v dims)
+//     dP^T = V dY^T, so the tile is read from LDS once for both.  Each wave owns 32 heads.
+//     It writes P and softmax_scale * dS as bf16 to a [row][slot][head] workspace (zero at
+//     empty slots), the element work of one tile interleaved with the products of the next.
 //   * k_attn_bwd_dq: gathers the key tiles again together with the wave's dS tile (both by
 //     LDS DMA) and accumulates dQ^T[dim, head] += K^T dS^T over the 18 dim tiles of the row
 //     (K^T read with the transposing LDS read), one wave per 32 heads.
@@ -40,193 +41,337 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------------
-// k_attn_bwd_p: P and softmax_scale * dS per (row, slot, head)
+// k_attn_bwd_p_ring: the same outputs for the 128-head shape, on the forward's ring design
 // ---------------------------------------------------------------------------------------
+//
+// Step t of a row forms P and softmax_scale * dS of tile t from its S^T / dP^T accumulators
+// (computed in step t-1) and stores them, interleaved with the S^T / dP^T products of tile
+// t+1, while the gather of tile t+4 goes out between the first MFMAs; then tile t+2 is waited
+// for and the block meets at one barrier.  Four tile buffers (the wave's Q rows pass through
+// them first; in step t they hold tiles t+1 .. t+3 and take t+4 into tile t's), the slot
+// indices in the LDS index ring, all of Q in AGPRs (read by the MFMAs from there) and dY in
+// VGPRs, the two tiles' accumulators alternating between two AGPR sets (about 200 registers
+// in each file).  Every step has the
+// same memory instructions: near the row's end the gathers fetch row 0 for slots past the
+// list, and the last step's products run on whatever the buffer holds (their accumulators
+// are never read).
+//
+// The wait for a tile counts only the loads issued after its gather (the next two gathers and
+// any index chunk), so the P / dS stores issued in between are waited for too; they go out
+// spread over the step, and by its end they are done.
 
-// S^T (all DQK dims) and dP^T (first DV dims) of one tile; A fragments shared.
-template <int H, int DQK, int DV>
-__device__ __forceinline__ void tile_s_dp(const RowCtx& c, const bf16x8* qf, const bf16x8* dof,
-                                          const uint16_t* tile, f32x16& s, f32x16& dp) {
+constexpr int kBwdGatherKs0 = 1;       // K step of the first gather piece (one per K step)
+constexpr int kBwdParts = 16;          // element parts per tile: one accumulator register each
+constexpr int kBwdPartKs0 = 2, kBwdPartKsStride = 2;   // K step after which part r runs
+
+// Per-row constants of the element step.
+struct BwdRowK {
+  float msub, invl, D;
+  unsigned vo0, vo4;   // store byte offsets (from the tile's row base) of parts 0-3 and 4-7
+  unsigned sel;        // byte selector assembling a head pair's dword (differs for odd heads)
+};
+
+// One ring step (PARTS) or the row prologue's products of tile 0 alone (no parts, no gather).
+template <int H, int DQK, int DV, bool PARTS>
+__device__ __forceinline__ void bwd_ring_tile(const AttnBwdArgs& a, const RowCtx& c,
+                                              const bf16x8* qf, const bf16x8* dof,
+                                              lds_cptr_t ktile, f32x16& s_nx, f32x16& d_nx,
+                                              const f32x16& s_cu, const f32x16& d_cu,
+                                              unsigned vmask, bool store,
+                                              const uint16_t* pt, const uint16_t* dt,
+                                              const BwdRowK& k,
+                                              const unsigned* so, const unsigned* loff,
+                                              unsigned wbg) {
   using C = AttnCfg<H, DQK, DV>;
   constexpr int KSV = DV / 16;
-  s = (f32x16){};
-  dp = (f32x16){};
+  typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
+  static_assert(kBwdPartKs0 + kBwdPartKsStride * (kBwdParts - 1) < C::KS, "parts placement");
+  static_assert(kBwdGatherKs0 + C::NI <= C::KS, "gather placement");
   const int arow_i = key_perm(c.hl);
   const int asw = C::SWZ ? swz(arow_i) : 0;
-  const lds_cptr_t ltile = (lds_cptr_t)tile;
   lds_cptr_t abase[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    abase[j] = ltile + arow_i * C::ROWE + (((2 * j + c.g) ^ asw) - 2 * j) * 8;
-  auto arow_at = [&](int ks) { return abase[ks & 3] + ks * 16; };
-  const uint16_t* qlrow = c.qlds + (C::DQL > 0 ? c.head % H : 0) * C::QROWE + c.g * 8;
-  constexpr int QG = 3;
-  constexpr int NG = (C::KS + QG - 1) / QG;
-  bf16x8 af[2][QG];
-#pragma unroll
-  for (int u = 0; u < QG; ++u)
-    if (u < C::KS) af[0][u] = *(__attribute__((address_space(3))) const bf16x8*)(arow_at(u));
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const int cur = gi & 1;
-    if (gi + 1 < NG) {
-#pragma unroll
-      for (int u = 0; u < QG; ++u) {
-        const int ks = (gi + 1) * QG + u;
-        if (ks < C::KS) af[cur ^ 1][u] = *(__attribute__((address_space(3))) const bf16x8*)(arow_at(ks));
-      }
-    }
+    abase[j] = ktile + arow_i * C::ROWE + (((2 * j + c.g) ^ asw) - 2 * j) * 8;
+  constexpr int QG = 2;                    // K steps per group (one sched region)
+  constexpr int NG = C::KS / QG;
+  constexpr int PF = 2;                    // groups of key fragments read ahead
+  static_assert(C::KS % QG == 0, "K steps");
+  bf16x8 af[PF + 1][QG];
+  auto fetch = [&](int gi, int buf) {
 #pragma unroll
     for (int u = 0; u < QG; ++u) {
       const int ks = gi * QG + u;
-      if (ks < C::KS) {
-        bf16x8 bq;
-        if (ks < C::KSR) bq = qf[ks < C::KSR ? ks : 0];
-        else bq = *reinterpret_cast<const bf16x8*>(qlrow + (ks - C::KSR) * 16);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][u], bq, s, 0, 0, 0);
-        if (ks < KSV) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][u], dof[ks < KSV ? ks : 0], dp, 0, 0, 0);
+      af[buf][u] = *(lds_cb8_t)(abase[ks & 3] + ks * 16);
+    }
+  };
+  auto gather_piece = [&](int gi) {
+    const int j0 = gi * 64 / C::CPR;
+    const int b = (j0 + 1) * C::CPR - 64 * gi;
+    unsigned ro = so[j0];
+    if (b < 64) {
+      // (opaque to the optimiser: a select between two loads of so[] would otherwise become
+      // one load at a lane-dependent index, a chain of compares over all of so[])
+      unsigned r1 = so[j0 + 1];
+      asm("" : "+s"(r1));
+      ro = c.lane >= b ? r1 : ro;
+    }
+    const unsigned voff = loff[gi] + ro;
+    const unsigned m0v = wbg + (unsigned)gi * 1024u;
+    const uint16_t* base = a.kv;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
+  };
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  // part r: accumulator register r of tile t (key acc_key(r, g)): P and dS of the lane's
+  // head; after an odd r the pair (r-1, r) is stored: the head pair's dword assembled across
+  // the lane pair, one store per tensor
+  float p0 = 0.f, g0 = 0.f;
+  auto part = [&](int r) {
+    // validity of the key per lane half, as a lane mask (the list's validity bits are
+    // wave-uniform): lanes 0-31 hold key acc_key(r, 0), lanes 32-63 acc_key(r, 1)
+    const uint64_t m = ((vmask >> acc_key(r, 0)) & 1u ? 0xFFFFFFFFull : 0ull) |
+                       ((vmask >> acc_key(r, 1)) & 1u ? 0xFFFFFFFF00000000ull : 0ull);
+    // the accumulators are read here, not all at the step's start (32 more live VGPRs)
+    float x, y;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(s_cu[r]));
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(d_cu[r]));
+    float p = __builtin_amdgcn_exp2f(fmaf(x, a.scale_log2, -k.msub)) * k.invl;
+    p = __builtin_amdgcn_inverse_ballot_w64(m) ? p : 0.f;
+    const float g = a.scale * p * (y - k.D);
+    if ((r & 1) == 0) {
+      p0 = p;
+      g0 = g;
+      return;
+    }
+    const int j = r >> 1;
+    const float p1 = p, g1 = g;
+    const bf16x2v pk = {(__bf16)p0, (__bf16)p1};
+    const bf16x2v gk = {(__bf16)g0, (__bf16)g1};
+    const unsigned pu = __builtin_bit_cast(unsigned, pk), gu = __builtin_bit_cast(unsigned, gk);
+    const unsigned py = (unsigned)__builtin_amdgcn_mov_dpp((int)pu, 0xB1, 0xF, 0xF, false);
+    const unsigned gy = (unsigned)__builtin_amdgcn_mov_dpp((int)gu, 0xB1, 0xF, 0xF, false);
+    const unsigned vp = __builtin_amdgcn_perm(py, pu, k.sel);
+    const unsigned vd = __builtin_amdgcn_perm(gy, gu, k.sel);
+    const unsigned vo = j < 4 ? k.vo0 : k.vo4;
+    const uint16_t* b0 = pt;
+    const uint16_t* b1 = dt;
+    // non-temporal: P and dS (34 GB at the 32K varlen shape) stream past the caches that
+    // hold the gathered latent rows and the next rows' Q / dY
+    if (store) {
+      asm volatile("global_store_dword %0, %1, %2 offset:%3 nt"
+                   :: "v"(vo), "v"(vp), "s"(b0), "n"((j & 3) * 4 * H) : "memory");
+      asm volatile("global_store_dword %0, %1, %2 offset:%3 nt"
+                   :: "v"(vo), "v"(vd), "s"(b1), "n"((j & 3) * 4 * H) : "memory");
+    }
+  };
+
+#pragma unroll
+  for (int gi = 0; gi < PF; ++gi) fetch(gi, gi);
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int cur = gi % (PF + 1);
+    if (gi + PF < NG) fetch(gi + PF, (gi + PF) % (PF + 1));
+#pragma unroll
+    for (int u = 0; u < QG; ++u) {
+      const int ks = gi * QG + u;
+      if (ks == 0)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                     : "=&a"(s_nx) : "v"(af[cur][u]), "a"(qf[ks]));
+      else if (ks == C::KS - 1)   // VALU reads the accumulators next step: wait out the MFMA
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(s_nx) : "v"(af[cur][u]), "a"(qf[ks]));
+      else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                     : "+a"(s_nx) : "v"(af[cur][u]), "a"(qf[ks]));
+      if (ks == 0)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                     : "=&a"(d_nx) : "v"(af[cur][u]), "v"(dof[0]));
+      else if (ks < KSV)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                     : "+a"(d_nx) : "v"(af[cur][u]), "v"(dof[ks < KSV ? ks : 0]));
+      if constexpr (PARTS) {
+        if (ks >= kBwdGatherKs0 && ks < kBwdGatherKs0 + C::NI) gather_piece(ks - kBwdGatherKs0);
+        if (ks >= kBwdPartKs0 && (ks - kBwdPartKs0) % kBwdPartKsStride == 0 &&
+            (ks - kBwdPartKs0) / kBwdPartKsStride < kBwdParts)
+          part((ks - kBwdPartKs0) / kBwdPartKsStride);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int H, int DQK, int DV, bool AL8>
-__global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p(AttnBwdArgs a) {
+template <int H, int DQK, int DV>
+__global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p_ring(AttnBwdArgs a) {
   using C = AttnCfg<H, DQK, DV>;
-  static_assert(H % 32 == 0, "32 heads per wave");
+  static_assert(C::PIPE && C::RPW == 8 && C::NK == 32, "ring shape");
+  static_assert(C::TILE == 32 * DQK && C::SWZ, "a wave's Q rows fill one ring buffer");
   constexpr int RPW = C::RPW;
   constexpr int KSV = DV / 16;
   __shared__ __attribute__((aligned(16))) uint16_t kv0[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t kv1[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t kv2[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t qlds[C::QLDS];
-  __shared__ unsigned vmring[3 * C::NW];
+  __shared__ __attribute__((aligned(16))) uint16_t kv3[C::TILE];
+  __shared__ __attribute__((aligned(16))) int32_t idxr[2 * kIdxChunk];
   __shared__ int s_last[C::NW];
 
   RowCtx c = make_ctx(a, block_row(a));
-  c.buf[0] = kv0;
-  c.buf[1] = kv1;
-  c.buf[2] = kv2;
-  c.qlds = qlds;
-  c.vm = vmring;
-  c.ntiles = row_tiles<H, DQK, DV>(a, c, s_last);
-  if (c.ntiles == 0) return;   // nothing selected: the row has no P / dS and no dKV share
+  uint16_t* const bufs[4] = {kv0, kv1, kv2, kv3};
+  const unsigned idxr_lds = (unsigned)(size_t)(__attribute__((address_space(3))) int32_t*)idxr;
 
-  stage_q_tail<H, DQK, DV>(a, c, qlds);
-  bf16x8 qf[C::KSR];
-  load_q<H, DQK, DV>(a, c, qf);
-  // dY fragments (B operand of dP^T, same lane layout as Q) and D = rowsum(dY * out)
+  // Row prologue in one memory round trip: index chunks 0 and 1 and the wave's 32 Q rows go
+  // to LDS by LDS DMA (Q rows stored like tile rows, chunks swizzled), dY and the forward
+  // output load into registers, the index scan finds the row's tile count.
+  idx_chunk_dma<H, DQK, DV>(a, c, 0, idxr_lds);
+  idx_chunk_dma<H, DQK, DV>(a, c, 1, idxr_lds);
+  uint16_t* const qbuf = c.wave_u == 0 ? kv0 : (c.wave_u == 1 ? kv1 : (c.wave_u == 2 ? kv2 : kv3));
+  {
+    const uint16_t* qsrc = a.q + ((size_t)c.row * H + c.wave_u * 32) * DQK;
+    const unsigned qdst = (unsigned)(size_t)(lds_u16_ptr_t)qbuf;
+#pragma unroll 4
+    for (int i = 0; i < C::TILE * 2 / 1024; ++i) {
+      const int f = i * 64 + c.lane;            // physical chunk f % CPR of row f / CPR
+      const int r = f / C::CPR, ch = f - r * C::CPR;
+      const unsigned voff = (unsigned)(r * C::CPR + (ch ^ swz(r))) * 16u;
+      const unsigned m0v = qdst + (unsigned)i * 1024u;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(m0v), "v"(voff), "s"(qsrc) : "memory", "m0");
+    }
+  }
+  // dY fragments (B operand of dP^T, the lane layout of Q) and D = rowsum(dY * out)
   bf16x8 dof[KSV];
   const size_t hrow = (size_t)c.row * H + c.head;
-  const uint16_t* dop = a.dout + hrow * DV + c.g * 8;
-  const uint16_t* op = a.out + hrow * DV + c.g * 8;
   float dpart = 0.f;
+  {
+    const uint16_t* dop = a.dout + hrow * DV + c.g * 8;
+    const uint16_t* op = a.out + hrow * DV + c.g * 8;
 #pragma unroll
-  for (int ks = 0; ks < KSV; ++ks) {
-    dof[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dop + ks * 16));
-    const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(op + ks * 16));
+    for (int ks = 0; ks < KSV; ++ks) {
+      dof[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dop + ks * 16));
+      const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(op + ks * 16));
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const bf16x2 x = {dof[ks][e], dof[ks][e + 1]};
-      const bf16x2 y = {ov[e], ov[e + 1]};
-      dpart = __builtin_amdgcn_fdot2_f32_bf16(x, y, dpart, false);
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 x = {dof[ks][e], dof[ks][e + 1]};
+        const bf16x2 y = {ov[e], ov[e + 1]};
+        dpart = __builtin_amdgcn_fdot2_f32_bf16(x, y, dpart, false);
+      }
     }
   }
-  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(dpart), __float_as_int(dpart), false, false);
-  const float D = __int_as_float(pr[0]) + __int_as_float(pr[1]);
   const float mrow = a.smax[hrow];
-  const float msub = mrow == kNegInf ? 0.f : mrow * kLog2e;   // scaled log2 units
   const float lrow = a.ssum[hrow];
-  const float invl = lrow > 0.f ? 1.f / lrow : 0.f;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // staged Q landed (DMA is not tracked)
-  __syncthreads();                        // staged Q visible
-  __builtin_amdgcn_s_waitcnt(0x0F70);     // row loads done before the gather ring starts
+  int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
+  last = (int)wave_max_u32((unsigned)(last + 1)) - 1;   // (last >= -1)
+  if (c.lane == 0) s_last[c.wave] = last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // index chunks and Q landed (DMA untracked)
+  __syncthreads();
+  last = -1;
+#pragma unroll
+  for (int w = 0; w < C::NW; ++w) last = max(last, s_last[w]);
+  const int T = (last + C::NK) / C::NK;
+  // compiler-visible vmcnt(0): the row loads are done before the ring starts, so the compiler
+  // adds no waits for them inside the loop
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (T == 0) return;   // nothing selected: the row has no P / dS and no dKV share
 
-  using TI = TileIdx<H, DQK, DV>;
+  BwdRowK k;
+  {
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(dpart), __float_as_int(dpart),
+                                                     false, false);
+    k.D = __int_as_float(pr[0]) + __int_as_float(pr[1]);
+    k.msub = mrow == kNegInf ? 0.f : mrow * kLog2e;   // scaled log2 units
+    k.invl = lrow > 0.f ? 1.f / lrow : 0.f;
+    const bool odd = c.hl & 1;
+    const int hpair = c.wave * 32 + (c.hl & ~1);
+    k.vo0 = (unsigned)(((c.g * 8 + (odd ? 1 : 0)) * H + hpair) * 2);
+    k.vo4 = k.vo0 + 16u * H * 2u;
+    k.sel = odd ? 0x03020706u : 0x05040100u;
+  }
+  bf16x8 qf[C::KS];
+  {
+    typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
+    const int sw = swz(c.hl);
+    const lds_cptr_t qrow = (lds_cptr_t)qbuf + c.hl * C::ROWE;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = *(lds_cb8_t)(qrow + ((2 * ks + c.g) ^ sw) * 8);
+  }
+  __syncthreads();   // every wave holds its Q: the ring buffers take tiles from here on
+
   unsigned loff[C::NI];
-  unsigned wb[3];
-  if constexpr (C::FLAT) {
 #pragma unroll
-    for (int i = 0; i < C::NI; ++i) loff[i] = flat_lane_offset<H, DQK, DV>(c, i);
+  for (int i = 0; i < C::NI; ++i) loff[i] = flat_lane_offset<H, DQK, DV>(c, i);
+  unsigned wb[4];
 #pragma unroll
-    for (int k = 0; k < 3; ++k)
-      wb[k] = (unsigned)(size_t)(lds_u16_ptr_t)(c.buf[k]) + c.wave_u * (RPW * C::ROWE * 2);
-  }
-  auto gather = [&](const TI& ti, int k) {
-    if constexpr (C::FLAT) gather_tile_flat<H, DQK, DV>(a, c, ti, loff, wb[k]);
-    else gather_tile_s<H, DQK, DV>(a, c, ti, c.buf[k]);
-  };
-  // P / dS stores: lanes of a head pair (hl, hl ^ 1) swap one value per register pair, so
-  // each lane writes both heads of one slot as one dword (8 dword stores per tensor and
-  // tile, issued from asm so the count before each barrier is exact)
-  const uint16_t* pbase = a.ws_p + (size_t)c.row * a.topkp * H;    // scalar row bases
-  const uint16_t* dbase = a.ws_ds + (size_t)c.row * a.topkp * H;
-  const bool odd = c.hl & 1;
-  const int hpair = c.wave * 32 + (c.hl & ~1);
-  constexpr int NST = 16;
-  static_assert(C::GOPS + 2 * NST < 64, "vmcnt range");
+  for (int q = 0; q < 4; ++q)
+    wb[q] = (unsigned)(size_t)(lds_u16_ptr_t)(bufs[q]) + c.wave_u * (RPW * C::ROWE * 2);
+  const lds_ci32_t ir = (lds_ci32_t)idxr;
+  // slot read by this lane for step t: lanes 0..31 the tile whose P / dS the step forms (t),
+  // lanes 32..63 the tile it gathers (t+4)
+  auto step_slot = [&](int t) { return (t + 4 * (c.lane >> 5)) * C::NK + (c.lane & 31); };
 
-  const int ntiles = (c.ntiles + 2) / 3 * 3;
-  const TI i0 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 0);
-  const TI i1 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 1);
-  TI i2 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 2);
-  gather(i0, 0);
-  gather(i1, 1);
-  if (c.lane == 0) {
-    c.vm[0 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i0);
-    c.vm[1 * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, i1);
+  // tiles 0 .. 3 from chunk 0
+  {
+    const int s0 = c.lane, s1 = 2 * C::NK + c.lane;
+    unsigned off0, off1, so[RPW];
+    (void)decode_slot<H, DQK, DV>(a, ir[s0], s0, off0);
+    (void)decode_slot<H, DQK, DV>(a, ir[s1], s1, off1);
+    wave_row_offsets<H, DQK, DV>(c, off0, 0, so);
+    gather_tile_flat_so<H, DQK, DV>(a, c, so, loff, wb[0]);
+    wave_row_offsets<H, DQK, DV>(c, off0, 32, so);
+    gather_tile_flat_so<H, DQK, DV>(a, c, so, loff, wb[1]);
+    wave_row_offsets<H, DQK, DV>(c, off1, 0, so);
+    gather_tile_flat_so<H, DQK, DV>(a, c, so, loff, wb[2]);
+    wave_row_offsets<H, DQK, DV>(c, off1, 32, so);
+    gather_tile_flat_so<H, DQK, DV>(a, c, so, loff, wb[3]);
   }
-  wait_vm_barrier<0>();   // both first tiles, so the steady-state count holds from step 0
+  wait_vm_barrier<3 * C::NI>();   // tile 0 landed; tiles 1 .. 3 may be in flight
+  f32x16 sa, da, sb, db;
+  {
+    const unsigned so0[RPW] = {};
+    bwd_ring_tile<H, DQK, DV, false>(a, c, qf, dof, (lds_cptr_t)bufs[0], sa, da, sb, db, 0u,
+                                     false, nullptr, nullptr, k, so0, loff, 0u);
+  }
+  int iv = ir[step_slot(0)];
+  wait_vm_barrier<2 * C::NI>();   // tile 1 landed
 
-  auto step = [&](int t, int slot, const uint16_t* cur, int ahead2, TI& nxt2) {
-    const TI i3 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, t + 3);
-    gather(nxt2, ahead2);
-    if (c.lane == 0) c.vm[((slot + 2) % 3) * C::NW + c.wave] = tile_bits<H, DQK, DV>(a, nxt2);
-    unsigned vmask = 0;
-#pragma unroll
-    for (int w = 0; w < C::NW; ++w) vmask |= c.vm[slot * C::NW + w] << (w * RPW);
-    f32x16 s, dp;
-    tile_s_dp<H, DQK, DV>(c, qf, dof, cur, s, dp);
-    if (vmask != 0xFFFFFFFFu) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (!((vmask >> acc_key(r, c.g)) & 1u)) s[r] = kNegInf;
-    }
-    uint32_t pb[16], db[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -msub)) * invl;
-      pb[r] = f32_to_bf16(p);
-      db[r] = f32_to_bf16(a.scale * p * (dp[r] - D));
-    }
-    // (every slot of the tile is stored, padding tiles too: they lie inside the row's padded
-    // area and are never read)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r0 = 2 * j, r1 = 2 * j + 1;
-      const uint32_t xp = odd ? pb[r0] : pb[r1];
-      const uint32_t xd = odd ? db[r0] : db[r1];
-      const uint32_t yp = (uint32_t)__builtin_amdgcn_mov_dpp((int)xp, 0xB1, 0xF, 0xF, false);
-      const uint32_t yd = (uint32_t)__builtin_amdgcn_mov_dpp((int)xd, 0xB1, 0xF, 0xF, false);
-      const uint32_t vp = odd ? (yp | (pb[r1] << 16)) : (pb[r0] | (yp << 16));
-      const uint32_t vd = odd ? (yd | (db[r1] << 16)) : (db[r0] | (yd << 16));
-      const int key = acc_key(odd ? r1 : r0, c.g);
-      const unsigned off = (unsigned)(((t * C::NK + key) * H + hpair) * 2);
-      const uint16_t* b0 = pbase;
-      const uint16_t* b1 = dbase;
-      asm volatile("global_store_dword %0, %1, %2" :: "v"(off), "v"(vp), "s"(b0) : "memory");
-      asm volatile("global_store_dword %0, %1, %2" :: "v"(off), "v"(vd), "s"(b1) : "memory");
-    }
-    // tile t+1 landed for every wave: after its gather come the previous and this step's
-    // stores and the gather of tile t+2
-    wait_vm_barrier<C::GOPS + 2 * NST>();
-    nxt2 = i3;
+  // ring slots rotating in registers: tile t+1 (read by step t), t+2, t+3 (landing), t (its
+  // buffer takes the gather of t+4): LDS pointers of the read side, the wave's LDS DMA
+  // address of the gather side
+  lds_cptr_t b1 = (lds_cptr_t)bufs[1], b2 = (lds_cptr_t)bufs[2], b3 = (lds_cptr_t)bufs[3],
+             b0 = (lds_cptr_t)bufs[0];
+  unsigned w0 = wb[0], w1 = wb[1], w2 = wb[2], w3 = wb[3];
+  const uint16_t* const prow = a.ws_p + (size_t)c.row * a.topkp * H;
+  const uint16_t* const drow = a.ws_ds + (size_t)c.row * a.topkp * H;
+  auto step = [&](int t, f32x16& s_nx, f32x16& d_nx, const f32x16& s_cu, const f32x16& d_cu) {
+    unsigned off, so[RPW];
+    const unsigned vmask = (unsigned)decode_slot<H, DQK, DV>(a, iv, step_slot(t), off);
+    wave_row_offsets<H, DQK, DV>(c, off, 32, so);
+    // chunk t/8 + 1 (first read at the end of step t + 3, for the gather of tile t + 8) into
+    // the ring half chunk t/8 - 1 left; a load ahead of this step's gather, so complete once
+    // the wait of step t + 2 has seen that gather land
+    if ((t & 7) == 0 && t > 0) idx_chunk_dma<H, DQK, DV>(a, c, t / 8 + 1, idxr_lds);
+    const size_t toff = (size_t)t * C::NK * H;
+    bwd_ring_tile<H, DQK, DV, true>(a, c, qf, dof, b1, s_nx, d_nx, s_cu, d_cu, vmask, t < T,
+                                    prow + toff, drow + toff, k, so, loff, w0);
+    iv = ir[step_slot(t + 1) & (2 * kIdxChunk - 1)];
+    // tile t+2 landed: its gather is followed by at least the gathers of t+3 and t+4
+    wait_vm_barrier<2 * C::NI>();
+    const lds_cptr_t bt = b0;
+    b0 = b1;
+    b1 = b2;
+    b2 = b3;
+    b3 = bt;
+    const unsigned wt = w0;
+    w0 = w1;
+    w1 = w2;
+    w2 = w3;
+    w3 = wt;
   };
-  for (int t = 0; t < ntiles; t += 3) {
-    step(t, 0, c.buf[0], 2, i2);
-    step(t + 1, 1, c.buf[1], 0, i2);
-    step(t + 2, 2, c.buf[2], 1, i2);
+  // steps in pairs (the accumulator sets alternate); for odd T the pair's second step is
+  // past the row's last tile and stores nothing (the waits count loads only, so skipped
+  // stores change no count)
+  for (int t = 0; t < T; t += 2) {
+    step(t, sb, db, sa, da);
+    step(t + 1, sa, da, sb, db);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no gather or store may outlive the block
 }
@@ -668,13 +813,9 @@ hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v
   KeyListArgs kl = {a.idx, a.list, a.cnt, a.off, a.cur, a.rows, a.n_k, a.topk, a.topkp};
   hipError_t e = launch_key_lists(kl, s);
   if (e != hipSuccess) return e;
-  if (al8) {
-    k_attn_bwd_p<128, 576, 512, true><<<a.rows, 256, 0, s>>>(a);
-    k_attn_bwd_dq<128, 576, 512, true><<<a.rows, 256, 0, s>>>(a);
-  } else {
-    k_attn_bwd_p<128, 576, 512, false><<<a.rows, 256, 0, s>>>(a);
-    k_attn_bwd_dq<128, 576, 512, false><<<a.rows, 256, 0, s>>>(a);
-  }
+  k_attn_bwd_p_ring<128, 576, 512><<<a.rows, 256, 0, s>>>(a);
+  if (al8) k_attn_bwd_dq<128, 576, 512, true><<<a.rows, 256, 0, s>>>(a);
+  else k_attn_bwd_dq<128, 576, 512, false><<<a.rows, 256, 0, s>>>(a);
   k_attn_bwd_dkv_part<128, 576, 512><<<a.rows, 256, 0, s>>>(a);
   k_bwd_reduce<576><<<(a.n_k + 3) / 4, 256, 0, s>>>(a);
   return hipGetLastError();

@@ -372,6 +372,49 @@ __device__ __forceinline__ void stage_q_tail(const Args& a, const RowCtx& c, uin
   }
 }
 
+// Index ring: a row's slot indices reach LDS in chunks of eight tiles by LDS DMA, so a tile
+// loop needs no compiler-tracked vector load (the compiler does not see the tile gathers, and
+// its wait for such a load would also drain every gather in flight) and no scalar load (whose
+// wait, shared with LDS reads, would stall the first LDS read after it).
+constexpr int kIdxChunk = 256;   // index slots per chunk (eight tiles); the LDS ring holds two
+
+typedef __attribute__((address_space(3))) const int32_t* lds_ci32_t;
+
+// Index chunk ch (slots 256 ch .. 256 ch + 255 of the row, reads clamped to the row's last
+// slot) into ring half ch % 2 at LDS byte address idxr: each wave copies 64 slots with one
+// dword LDS DMA.  Completion is tracked by hand (vmcnt before a barrier).
+template <int H, int DQK, int DV, class Args>
+__device__ __forceinline__ void idx_chunk_dma(const Args& a, const RowCtx& c, int ch,
+                                              unsigned idxr) {
+  const int slot = min(ch * kIdxChunk + c.wave_u * 64 + c.lane, a.topk - 1);
+  const unsigned voff = (unsigned)slot * 4u;
+  const unsigned m0v = idxr + (unsigned)((ch & 1) * kIdxChunk * 4) + (unsigned)c.wave_u * 256u;
+  const int32_t* base = c.idx_row;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
+}
+
+// A slot index as the gather uses it: byte offset of its latent row in kv (0 for a slot past
+// topk or an index outside [0, n_k): such rows are gathered from row 0 and masked); returns
+// the validity ballot.
+template <int H, int DQK, int DV, class Args>
+__device__ __forceinline__ uint64_t decode_slot(const Args& a, int v, int slot, unsigned& off) {
+  using C = AttnCfg<H, DQK, DV>;
+  const bool ok = slot < a.topk && (unsigned)v < (unsigned)a.n_k;
+  off = ok ? (unsigned)v * (C::CPR * 16u) : 0u;
+  return __ballot(ok);
+}
+
+// Row offsets (scalars) of this wave's eight rows of a tile whose slots sit in lanes
+// lane0 .. lane0 + 31 of `off`.
+template <int H, int DQK, int DV>
+__device__ __forceinline__ void wave_row_offsets(const RowCtx& c, unsigned off, int lane0,
+                                                 unsigned* so) {
+#pragma unroll
+  for (int j = 0; j < AttnCfg<H, DQK, DV>::RPW; ++j)
+    so[j] = __builtin_amdgcn_readlane(off, lane0 + c.wave_u * AttnCfg<H, DQK, DV>::RPW + j);
+}
+
 }  // namespace
 
 }  // namespace dsa

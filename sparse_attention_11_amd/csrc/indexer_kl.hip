@@ -47,7 +47,6 @@ constexpr int kMaxSlots = 2112;        // 66 tiles: topk <= 2048, rounded up to 
 constexpr int KT = NK * kDI;           // elements of an index-key tile (8 KB)
 constexpr int DSR = NK + 4;            // LDS row stride (elements) of the shared dS tile
 constexpr int GK = 2;                  // index-key gather instructions per wave and tile
-constexpr int NST = 4;                 // key-gradient stores per wave and tile
 constexpr int kDiLds = 2304;           // dI floats in LDS: 66 tiles x 32 rounded up to 1 KB pieces
 constexpr float kLog2e = 1.44269504088896340736f;
 static_assert(AC::RPW == 8 && AC::FLAT, "tile split of the gathers");
@@ -534,9 +533,10 @@ __global__ __launch_bounds__(256, 3) void k_idx_kl_p2(IdxKlArgs a) {
         const bf16x8 ka = __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         dqa[mb] = mfma16(ka, bds, dqa[mb]);
       }
-      // tile t+1 landed; the dS tile is complete for every wave.  In flight: tile t+2's
-      // gathers and the previous tile's key-gradient stores.
-      wait_vm_barrier<GK + NST>();
+      // tile t+1 landed; the dS tile is complete for every wave.  Counted: tile t+2's gathers
+      // only, so the key-gradient stores issued at the step's start are waited for too (they
+      // are done by then).
+      wait_vm_barrier<GK>();
       nxt2 = j3;
     };
     for (int t = 0; t < ntiles; t += 3) {
