@@ -14,9 +14,10 @@
 //     dP^T = V dY^T, so the tile is read from LDS once for both.  Each wave owns 32 heads.
 //     It writes P and softmax_scale * dS as bf16 to a [row][slot][head] workspace (zero at
 //     empty slots), the element work of one tile interleaved with the products of the next.
-//   * k_attn_bwd_dq: gathers the key tiles again together with the wave's dS tile (both by
-//     LDS DMA) and accumulates dQ^T[dim, head] += K^T dS^T over the 18 dim tiles of the row
-//     (K^T read with the transposing LDS read), one wave per 32 heads.
+//   * k_attn_bwd_dq_ring: gathers the key tiles again (index ring) together with the
+//     tile's dS block (both by LDS DMA) and accumulates dQ^T[dim, head] += K^T dS^T, each
+//     wave over 144 latent dims and all 128 heads (K^T and dS^T read with the transposing
+//     LDS read).
 //   * k_attn_bwd_dkv_part: no gather.  Each wave owns 144 of the 576 latent dims and holds
 //     Q[:, dims] and dY[:, dims] for all 128 heads as MFMA fragments (staged through LDS once
 //     per row); per tile it forms C[slot, dims] = dS^T Q + P^T dY on 16x16x32 MFMA with the
@@ -377,151 +378,194 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p_ring(AttnBwdArgs a
 }
 
 // ---------------------------------------------------------------------------------------
-// k_attn_bwd_dq: dQ = (softmax_scale * dS) K_sel
+// k_attn_bwd_dq_ring: dQ = (softmax_scale * dS) K_sel, split by latent dims
 // ---------------------------------------------------------------------------------------
+//
+// Each wave owns 144 of the 576 latent dims for all 128 heads: dQ^T[dim, head] += K^T dS^T
+// on 16x16x32 MFMA, one K step (the tile's 32 keys) per tile, 9 dim tiles x 8 head tiles of
+// accumulators.  A wave reads only its quarter of the gathered key tile (transposing LDS
+// reads) and the tile's whole dS block, half the LDS traffic of a split by heads, where every
+// wave reads the whole key tile.  Slot indices come from the LDS index ring; three tile
+// buffers, the gather of tile t+2 during step t.  Empty slots carry dS = 0, so their key
+// rows (gathered from row 0) add nothing and no validity mask is needed; the row runs its
+// tiles exactly (no padding tiles).
 
-template <int H, int DQK, int DV, bool AL8>
-__global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_dq(AttnBwdArgs a) {
+template <int H, int DQK, int DV>
+__global__ __launch_bounds__(256) void k_attn_bwd_dq_ring(AttnBwdArgs a) {
   using C = AttnCfg<H, DQK, DV>;
-  static_assert(H % 32 == 0, "32 heads per wave");
-  constexpr int RPW = C::RPW;
-  constexpr int MTQ = DQK / 32;          // 32-dim M tiles of dQ^T
-  constexpr int DSW = C::NK * 32;        // dS elements per wave and tile: [32 slots][32 heads]
-  constexpr int GOPS2 = C::GOPS + 2;     // + two 1 KB DMA pieces of the wave's dS tile
+  static_assert(H == 128 && C::NW == 4 && C::FLAT && C::RPW == 8 && C::NK == 32 && C::SWZ,
+                "ring shape");
+  constexpr int NW = C::NW;
+  constexpr int DW = DQK / NW;           // latent dims per wave (144)
+  constexpr int MT = DW / 16;            // 16-dim tiles per wave (9)
+  constexpr int NB = H / 16;             // 16-head tiles (8)
+  constexpr int DST = C::NK * H;         // dS tile elements: [32 slots][128 heads]
+  constexpr int GOPS2 = C::NI + 2;       // loads per wave and tile: the key rows and two dS pieces
+  static_assert(DQK % (16 * NW) == 0 && DST * 2 == NW * 2 * 1024, "tiling");
   __shared__ __attribute__((aligned(16))) uint16_t kv0[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t kv1[C::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t kv2[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t ds0[C::NW * DSW];
-  __shared__ __attribute__((aligned(16))) uint16_t ds1[C::NW * DSW];
-  __shared__ __attribute__((aligned(16))) uint16_t ds2[C::NW * DSW];
-  __shared__ unsigned vmring[3 * C::NW];
-  __shared__ int s_last[C::NW];
+  __shared__ __attribute__((aligned(16))) uint16_t ds0[DST];
+  __shared__ __attribute__((aligned(16))) uint16_t ds1[DST];
+  __shared__ __attribute__((aligned(16))) uint16_t ds2[DST];
+  __shared__ __attribute__((aligned(16))) int32_t idxr[2 * kIdxChunk];
+  __shared__ int s_last[NW];
 
   RowCtx c = make_ctx(a, block_row(a));
-  c.buf[0] = kv0;
-  c.buf[1] = kv1;
-  c.buf[2] = kv2;
-  c.vm = vmring;
-  c.ntiles = row_tiles<H, DQK, DV>(a, c, s_last);
-
-  f32x16 acc[MTQ];
+  const unsigned idxr_lds = (unsigned)(size_t)(__attribute__((address_space(3))) int32_t*)idxr;
+  idx_chunk_dma<H, DQK, DV>(a, c, 0, idxr_lds);
+  idx_chunk_dma<H, DQK, DV>(a, c, 1, idxr_lds);
+  int last = thread_last_valid<C::NT>(c.idx_row, a.topk, a.n_k, c.tid);
+  last = (int)wave_max_u32((unsigned)(last + 1)) - 1;   // (last >= -1)
+  if (c.lane == 0) s_last[c.wave] = last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // index chunks landed (DMA is not tracked)
+  __syncthreads();
+  last = -1;
 #pragma unroll
-  for (int mt = 0; mt < MTQ; ++mt) acc[mt] = (f32x16){};
+  for (int w = 0; w < NW; ++w) last = max(last, s_last[w]);
+  const int T = (last + C::NK) / C::NK;
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // compiler-visible: the scan loads are done
 
-  if (c.ntiles > 0) {
-    using TI = TileIdx<H, DQK, DV>;
+  const int i16 = c.lane & 15, G = c.lane >> 4;
+  const int d0 = c.wave_u * DW;
+  f32x4 acc[MT][NB];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[m][nb] = (f32x4){};
+
+  if (T > 0) {
     unsigned loff[C::NI];
-    unsigned wb[3], wd[3];
-    const uint16_t* dsb[3] = {ds0, ds1, ds2};
 #pragma unroll
     for (int i = 0; i < C::NI; ++i) loff[i] = flat_lane_offset<H, DQK, DV>(c, i);
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      wb[k] = (unsigned)(size_t)(lds_u16_ptr_t)(c.buf[k]) + c.wave_u * (RPW * C::ROWE * 2);
-      wd[k] = (unsigned)(size_t)(lds_cptr_t)(dsb[k]) + c.wave_u * (DSW * 2);
-    }
-    // dS DMA piece i: lane L copies 16 bytes (8 heads) of slot 16 i + L/4: heads
-    // 32 wave + 8 (L % 4) .. +7
+    // ring slots rotating in registers (tile t's buffers, t+1's, t+2's): LDS pointers for the
+    // reads, the wave's LDS DMA addresses for the gathers
+    lds_cptr_t k0 = (lds_cptr_t)kv0, k1 = (lds_cptr_t)kv1, k2 = (lds_cptr_t)kv2;
+    lds_cptr_t e0 = (lds_cptr_t)ds0, e1 = (lds_cptr_t)ds1, e2 = (lds_cptr_t)ds2;
+    const unsigned kwo = c.wave_u * (C::RPW * C::ROWE * 2), dwo = c.wave_u * 2048u;
+    auto lds_addr = [](lds_cptr_t p) { return (unsigned)(size_t)p; };
+    // dS tile in LDS: slot rows of 256 bytes, 16-byte chunk c of slot s at physical chunk
+    // c ^ 2 (s % 4), which makes the transposing reads (4 slots x 2 chunks per 16 lanes)
+    // conflict-free.  The wave copies slots 8 wave .. +7 with two 1 KB DMA pieces; lane L of
+    // piece i fills physical chunk L % 16 of slot 8 wave + 4 i + L / 16.
     unsigned dsoff[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dsoff[i] = (unsigned)(((16 * i + (c.lane >> 2)) * H + 32 * c.wave + 8 * (c.lane & 3)) * 2);
-    const int tiles_row = a.topkp / C::NK;
+    for (int i = 0; i < 2; ++i) {
+      const int s = 8 * c.wave + 4 * i + (c.lane >> 4), p = c.lane & 15;
+      dsoff[i] = (unsigned)((s * H + 8 * (p ^ (2 * (s & 3)))) * 2);
+    }
     const uint16_t* dsrow = a.ws_ds + (size_t)c.row * a.topkp * H;
-    auto gather = [&](const TI& ti, int t, int k) {
-      static_assert(C::FLAT, "flat gather");
-      gather_tile_flat<H, DQK, DV>(a, c, ti, loff, wb[k]);
-      const uint16_t* src = dsrow + (size_t)min(t, tiles_row - 1) * C::NK * H;
-      const unsigned m0v = wd[k];
+    auto gather = [&](int u, const unsigned* so, lds_cptr_t kd, lds_cptr_t dd) {
+      gather_tile_flat_so<H, DQK, DV>(a, c, so, loff, lds_addr(kd) + kwo);
+      const uint16_t* src = dsrow + (size_t)min(u, T - 1) * DST;
+      const unsigned dm0 = lds_addr(dd) + dwo;
       static_for<2>([&](auto I) {
         constexpr int i = decltype(I)::value;
         const unsigned voff = dsoff[i];
-        const unsigned m0 = m0v;
+        const unsigned m0 = dm0;
         const uint16_t* base = src;
         asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3"
                      :: "s"(m0), "n"(i * 1024), "v"(voff), "s"(base) : "memory", "m0", "scc");
       });
     };
-
-    // K^T fragment addressing (as the forward's value reads, over all DQK dims)
-    const int G = c.lane >> 4, i16 = c.lane & 15;
-    const int low = 2 * (G & 1) + ((i16 & 3) >> 1);
-    lds_cptr_t vb[3][2][2];
+    // transposing-read addresses (elements from the buffer base): lane i16 of group G
+    // supplies row 8 G + i16 / 4 (and + 4), columns c0 + 4 (i16 % 4) .. +3
+    const int tr_row = 8 * G + (i16 >> 2);
+    const int cq = i16 & 3;
+    // key tile: columns d0 + 16 m + 4 cq, chunk (2 (d0 / 16 + m) + cq / 2) ^ swz(row)
+    int ka[2];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int r = (G >> 1) * 8 + (i16 >> 2) + hf * 4;
-        const int sw = C::SWZ ? swz(r) : 0;
-        const lds_cptr_t b = (lds_cptr_t)c.buf[k] + r * C::ROWE + ((low ^ (sw & 3)) * 8) + (i16 & 1) * 4;
-        vb[k][hf][0] = b + (sw >> 2) * 32;
-        vb[k][hf][1] = b - (sw >> 2) * 32;
-      }
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r = tr_row + 4 * hf;
+      ka[hf] = r * C::ROWE + (cq & 1) * 4;
     }
-
-    const int ntiles = (c.ntiles + 2) / 3 * 3;
-    const TI i0 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 0);
-    const TI i1 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 1);
-    TI i2 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, 2);
-    gather(i0, 0, 0);
-    gather(i1, 1, 1);
-    wait_vm_barrier<GOPS2>();
-
-    auto step = [&](int t, int k, int ahead2, TI& nxt2) {
-      const TI i3 = load_tile_idx_s<H, DQK, DV, AL8>(a, c, t + 3);
-      gather(nxt2, t + 2, ahead2);
-      // B = (scale dS)^T[slot, head]: lane (head hl, g) takes slots 16 kk + 8 g .. +7
-      const uint16_t* dsw = dsb[k] + c.wave * DSW;
-      bf16x8 bq[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) bq[kk] = tr_frag(dsw, 32, 16 * kk + 8 * (G >> 1), 16 * (G & 1), i16);
-      if (t >= c.ntiles) {   // padding tile: no contribution
-        bq[0] = (bf16x8){};
-        bq[1] = (bf16x8){};
-      }
-      auto kfrag = [&](int kk, int mt) {
-        const int off = kk * 16 * C::ROWE + mt * 32;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[k][0][mt & 1] + off));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(vb[k][1][mt & 1] + off));
-        return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-      };
-      bf16x8 kf[2][2];
-      kf[0][0] = kfrag(0, 0);
-      kf[0][1] = kfrag(1, 0);
-#pragma unroll
-      for (int mt = 0; mt < MTQ; ++mt) {
-        const int cur = mt & 1;
-        if (mt + 1 < MTQ) {
-          kf[cur ^ 1][0] = kfrag(0, mt + 1);
-          kf[cur ^ 1][1] = kfrag(1, mt + 1);
-        }
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][0], bq[0], acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][1], bq[1], acc[mt], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      wait_vm_barrier<GOPS2>();
-      nxt2 = i3;
+    const int ksw0 = swz(tr_row), ksw1 = swz(tr_row + 4);
+    auto kfrag = [&](lds_cptr_t tb, int m) {
+      const int ch = d0 / 8 + 2 * m + (cq >> 1);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_ptr_t)(tb + ka[0] + (ch ^ ksw0) * 8));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_ptr_t)(tb + ka[1] + (ch ^ ksw1) * 8));
+      return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     };
-    for (int t = 0; t < ntiles; t += 3) {
-      step(t, 0, 2, i2);
-      step(t + 1, 1, 0, i2);
-      step(t + 2, 2, 1, i2);
+    // dS tile: columns (heads) 16 nb + 4 cq, chunk (2 nb + cq / 2) ^ 2 (row % 4)
+    const int da0 = tr_row * H + (cq & 1) * 4, da1 = (tr_row + 4) * H + (cq & 1) * 4;
+    const int dsw0 = 2 * (tr_row & 3), dsw1 = 2 * ((tr_row + 4) & 3);
+    auto dfrag = [&](lds_cptr_t db, int nb) {
+      const int ch = 2 * nb + (cq >> 1);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(db + da0 + (ch ^ dsw0) * 8));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(db + da1 + (ch ^ dsw1) * 8));
+      return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
+
+    const lds_ci32_t ir = (lds_ci32_t)idxr;
+    // slot read by this lane for step t: the tile it gathers (t+2); both lane halves read it
+    auto step_slot = [&](int t) { return (t + 2) * C::NK + (c.lane & 31); };
+    {
+      unsigned off, so[C::RPW];
+      (void)decode_slot<H, DQK, DV>(a, ir[c.lane], c.lane, off);   // tiles 0 and 1
+      wave_row_offsets<H, DQK, DV>(c, off, 0, so);
+      gather(0, so, k0, e0);
+      wave_row_offsets<H, DQK, DV>(c, off, 32, so);
+      gather(1, so, k1, e1);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int iv = ir[step_slot(0)];
+    wait_vm_barrier<GOPS2>();   // tile 0 landed; tile 1 may be in flight
+    for (int t = 0; t < T; ++t) {
+      unsigned off, so[C::RPW];
+      (void)decode_slot<H, DQK, DV>(a, iv, step_slot(t), off);
+      wave_row_offsets<H, DQK, DV>(c, off, 0, so);
+      // chunk t/8 + 1 (first read at the end of step t + 5) into the ring half chunk t/8 - 1
+      // left; a load ahead of this step's gather, so complete once tile t+2 has landed
+      if ((t & 7) == 0 && t > 0) idx_chunk_dma<H, DQK, DV>(a, c, t / 8 + 1, idxr_lds);
+      gather(t + 2, so, k2, e2);   // (past the row's last tile: row 0 and a clamped dS)
+      const lds_cptr_t tb = k0;
+      const lds_cptr_t db = e0;
+      bf16x8 bq[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) bq[nb] = dfrag(db, nb);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const bf16x8 af = kfrag(tb, m);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          // 288 accumulator registers: the first 256 fill the AGPRs; the last dim tile's are
+          // pinned to VGPRs (an asm MFMA with VGPR C / D), else the compiler cycles them
+          // through the AGPRs with copies every step
+          if (m < MT - 1)
+            acc[m][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[nb], acc[m][nb], 0, 0, 0);
+          else
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                         : "+v"(acc[m][nb]) : "v"(af), "v"(bq[nb]));
+        }
+      }
+      iv = ir[step_slot(t + 1) & (2 * kIdxChunk - 1)];
+      // tile t+1 landed: its loads are followed by tile t+2's (and maybe an index chunk)
+      wait_vm_barrier<GOPS2>();
+      const lds_cptr_t kt = k0, et = e0;
+      k0 = k1;
+      k1 = k2;
+      k2 = kt;
+      e0 = e1;
+      e1 = e2;
+      e2 = et;
+    }
+    // no gather may outlive the block; VALU reads the asm MFMAs' VGPR results next
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   }
 
-  // dQ^T C layout: lane (head hl, half g) holds dims mt*32 + q4*8 + g*4 + e
-  uint16_t* qp = a.dq + ((size_t)c.row * H + c.head) * DQK;
+  // dQ^T C layout: lane (head 16 nb + i16, group G) holds dims d0 + 16 m + 4 G .. +3
+  uint16_t* qrow = a.dq + (size_t)c.row * H * DQK;
 #pragma unroll
-  for (int mt = 0; mt < MTQ; ++mt) {
+  for (int m = 0; m < MT; ++m) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int col = mt * 32 + q4 * 8 + c.g * 4;
-      const uint32_t lo = (uint32_t)f32_to_bf16(acc[mt][q4 * 4 + 0]) |
-                          ((uint32_t)f32_to_bf16(acc[mt][q4 * 4 + 1]) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16(acc[mt][q4 * 4 + 2]) |
-                          ((uint32_t)f32_to_bf16(acc[mt][q4 * 4 + 3]) << 16);
-      *reinterpret_cast<uint2*>(qp + col) = make_uint2(lo, hi);
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint32_t lo = (uint32_t)f32_to_bf16(acc[m][nb][0]) |
+                          ((uint32_t)f32_to_bf16(acc[m][nb][1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(acc[m][nb][2]) |
+                          ((uint32_t)f32_to_bf16(acc[m][nb][3]) << 16);
+      *reinterpret_cast<uint2*>(qrow + (size_t)(16 * nb + i16) * DQK + d0 + 16 * m + 4 * G) =
+          make_uint2(lo, hi);
     }
   }
 }
@@ -814,8 +858,7 @@ hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v
   hipError_t e = launch_key_lists(kl, s);
   if (e != hipSuccess) return e;
   k_attn_bwd_p_ring<128, 576, 512><<<a.rows, 256, 0, s>>>(a);
-  if (al8) k_attn_bwd_dq<128, 576, 512, true><<<a.rows, 256, 0, s>>>(a);
-  else k_attn_bwd_dq<128, 576, 512, false><<<a.rows, 256, 0, s>>>(a);
+  k_attn_bwd_dq_ring<128, 576, 512><<<a.rows, 256, 0, s>>>(a);
   k_attn_bwd_dkv_part<128, 576, 512><<<a.rows, 256, 0, s>>>(a);
   k_bwd_reduce<576><<<(a.n_k + 3) / 4, 256, 0, s>>>(a);
   return hipGetLastError();
