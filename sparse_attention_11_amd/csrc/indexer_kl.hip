@@ -40,7 +40,6 @@ namespace {
 constexpr int kH = 128, kDQK = 576, kDV = 512;   // attention heads, latent row, value width
 constexpr int kG = 64, kDI = 128;                 // index heads, index head width
 using AC = AttnCfg<kH, kDQK, kDV>;
-using TI = TileIdx<kH, kDQK, kDV>;
 constexpr int NK = AC::NK;             // keys per tile (32)
 constexpr int kKs = kDQK / 16;         // K steps of the logits product
 constexpr int kMaxSlots = 2112;        // 66 tiles: topk <= 2048, rounded up to rings of 3 tiles
@@ -99,20 +98,23 @@ __device__ __forceinline__ float block_max(float x, float* sb) {
 // rows by LDS DMA.  Instruction i copies rows 8 w + 4 i .. +3: lane L fills physical chunk
 // L % 16 of row 8 w + 4 i + L / 16, which holds logical chunk (L % 16) ^ (row % 16).  The XOR
 // makes 16 rows x one logical chunk (the MFMA operand reads) hit 16 different bank groups.
-// Empty slots copy row 0 (masked later).
-__device__ __forceinline__ void gather_ktile(const IdxKlArgs& a, const RowCtx& c, const TI& ti,
-                                             unsigned lds_tile) {
+// Empty slots copy row 0 (masked later).  sk: byte offsets in k_idx of the wave's 8 rows,
+// scalars (0 for empty slots).
+__device__ __forceinline__ void gather_ktile_so(const IdxKlArgs& a, const RowCtx& c,
+                                                const unsigned* sk, unsigned lds_tile) {
   const int sub = c.lane >> 4, ch = c.lane & 15;
   const bool b0 = c.lane & 16, b1 = c.lane & 32;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    // two selects on lane bits (an index expression would send the indices through scratch)
-    const int lo = b0 ? ti.v[4 * i + 1] : ti.v[4 * i];
-    const int hi = b0 ? ti.v[4 * i + 3] : ti.v[4 * i + 2];
-    int id = b1 ? hi : lo;
-    id = (unsigned)id < (unsigned)a.n_k ? id : 0;
+    // (opaque to the optimiser: selects between loads of sk[] would otherwise become one load
+    // at a lane-dependent index, through scratch memory)
+    unsigned s0 = sk[4 * i], s1 = sk[4 * i + 1], s2 = sk[4 * i + 2], s3 = sk[4 * i + 3];
+    asm("" : "+s"(s0), "+s"(s1), "+s"(s2), "+s"(s3));
+    const unsigned lo = b0 ? s1 : s0;
+    const unsigned hi = b0 ? s3 : s2;
+    const unsigned ro = b1 ? hi : lo;
     const int r = c.wave * 8 + 4 * i + sub;
-    const unsigned voff = (unsigned)id * (kDI * 2u) + (unsigned)((ch ^ (r & 15)) * 16);
+    const unsigned voff = ro + (unsigned)((ch ^ (r & 15)) * 16);
     const unsigned m0v = lds_tile + (unsigned)((c.wave_u * 8 + 4 * i) * kDI * 2);
     const uint16_t* base = a.k_idx;
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
   __shared__ __attribute__((aligned(16))) float s_p[kMaxSlots];   // target mass, then dI
   __shared__ __attribute__((aligned(16))) float s_i[kMaxSlots];   // indexer values I
   __shared__ float s_red[2][2][4][NK];   // [tile parity][mass, I][wave][key]
-  __shared__ unsigned vmring[3 * 4];
+  __shared__ __attribute__((aligned(16))) int32_t idxr[2 * kIdxChunk];   // index ring
   __shared__ int s_last[4];
   __shared__ float s_blk[4];
 
@@ -143,13 +145,18 @@ __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
   c.buf[0] = kv0;
   c.buf[1] = kv1;
   c.buf[2] = kv2;
-  c.vm = vmring;
   c.ntiles = row_tiles<kH, kDQK, kDV>(a, c, s_last);
   const int row = c.row;
   if (c.ntiles == 0) {   // nothing selected: loss 0 (the pass-2 kernel zeroes the gradients)
     if (c.tid == 0) a.loss[row] = 0.f;
     return;
   }
+  // the row's slot indices reach LDS in chunks of eight tiles (no per-tile index loads,
+  // whose wait would also stall the first LDS read of every step); issued after the early
+  // exit, so no LDS DMA can outlive the block
+  const unsigned idxr_lds = lds_addr(idxr);
+  idx_chunk_dma<kH, kDQK, kDV>(a, c, 0, idxr_lds);
+  idx_chunk_dma<kH, kDQK, kDV>(a, c, 1, idxr_lds);
   const uint16_t* kts[3] = {kt0, kt1, kt2};
   const int i16 = c.lane & 15, G = c.lane >> 4;
 
@@ -200,14 +207,34 @@ __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
     wb[k] = lds_addr(c.buf[k]) + c.wave_u * (AC::RPW * AC::ROWE * 2);
     kb[k] = lds_addr(kts[k]);
   }
-  auto gather = [&](const TI& ti, int k) {
-    gather_tile_flat<kH, kDQK, kDV>(a, c, ti, loff, wb[k]);
-    gather_ktile(a, c, ti, kb[k]);
+  // gather of the tile whose slots sit in lanes lane0 .. lane0 + 31 of the decoded offsets
+  // (kvo: byte offset in kv, kio: in k_idx; 0 for empty slots)
+  auto gather = [&](unsigned kvo, unsigned kio, int lane0, int k) {
+    unsigned so[AC::RPW], sk[AC::RPW];
+#pragma unroll
+    for (int j = 0; j < AC::RPW; ++j) {
+      so[j] = __builtin_amdgcn_readlane(kvo, lane0 + c.wave_u * AC::RPW + j);
+      sk[j] = __builtin_amdgcn_readlane(kio, lane0 + c.wave_u * AC::RPW + j);
+    }
+    gather_tile_flat_so<kH, kDQK, kDV>(a, c, so, loff, wb[k]);
+    gather_ktile_so(a, c, sk, kb[k]);
   };
-  // row loads done (a wait the compiler sees, so it adds none inside the ring, where the
-  // counter also holds the in-flight gathers)
+  // a slot as the gathers use it: validity ballot, byte offsets of its rows
+  auto decode = [&](int v, int slot, unsigned& kvo, unsigned& kio) {
+    const bool ok = slot < a.topk && (unsigned)v < (unsigned)a.n_k;
+    kvo = ok ? (unsigned)v * (AC::CPR * 16u) : 0u;
+    kio = ok ? (unsigned)v * (kDI * 2u) : 0u;
+    return (unsigned)__ballot(ok);
+  };
+  const lds_ci32_t ir = (lds_ci32_t)idxr;
+  // slot read by this lane for step t: lanes 0..31 the tile the step computes (t), lanes
+  // 32..63 the tile it gathers (t+2)
+  auto step_slot = [&](int t) { return (t + 2 * (c.lane >> 5)) * NK + (c.lane & 31); };
+  // row loads and index chunks done (a wait the compiler sees, so it adds none inside the
+  // ring, where the counter also holds the in-flight gathers); the chunks are every wave's
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
 
   // ---- pass 1: target mass and indexer values per slot
   // Pipelined by one tile: while the matrix cores run tile t's logits, the wave issues the
@@ -219,15 +246,13 @@ __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
 #pragma unroll
   for (int ks = 0; ks < kKs; ++ks) asm volatile("" : "+a"(qf[ks]));
   {
-    const TI i0 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 0);
-    const TI i1 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 1);
-    TI i2 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 2);
-    gather(i0, 0);
-    gather(i1, 1);
-    if (c.lane == 0) {
-      c.vm[0 * 4 + c.wave] = tile_bits<kH, kDQK, kDV>(a, i0);
-      c.vm[1 * 4 + c.wave] = tile_bits<kH, kDQK, kDV>(a, i1);
+    {   // tiles 0 and 1 from chunk 0
+      unsigned kvo, kio;
+      (void)decode(ir[c.lane], c.lane, kvo, kio);
+      gather(kvo, kio, 0, 0);
+      gather(kvo, kio, 32, 1);
     }
+    int iv = ir[step_slot(0)];
     wait_vm_barrier<0>();
 
     f32x16 sp0 = (f32x16){}, sp1 = (f32x16){};   // previous tile: logits (two chains)
@@ -271,14 +296,16 @@ __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
                               (s_red[pb][1][2][c.lane] + s_red[pb][1][3][c.lane]);
     };
 
-    auto step = [&](int t, int slot, int ahead2, TI& nxt2) {
-      const TI i3 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, t + 3);
-      gather(nxt2, ahead2);
-      if (c.lane == 0) c.vm[ahead2 * 4 + c.wave] = tile_bits<kH, kDQK, kDV>(a, nxt2);
+    auto step = [&](int t, int slot, int ahead2) {
+      unsigned kvo, kio;
+      // validity of tile t (lanes 0..31: bit k = key k), rows of tile t+2 (lanes 32..63)
+      const unsigned vmask = decode(iv, step_slot(t), kvo, kio);
+      // chunk t/8 + 1 (first read at the end of step t + 5, for the gather of tile t + 8)
+      // into the ring half chunk t/8 - 1 left; a load ahead of this step's gather, so
+      // complete once tile t+2 has landed
+      if ((t & 7) == 0 && t > 0) idx_chunk_dma<kH, kDQK, kDV>(a, c, t / 8 + 1, idxr_lds);
+      gather(kvo, kio, 32, ahead2);
       if (t >= 2 && c.wave_u == (t & 3) && c.lane < NK) lazy_sum(t - 2);
-      unsigned vmask = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) vmask |= c.vm[slot * 4 + w] << (w * 8);
 
       // logits C[head, key]: A = Q (AGPRs), B = latent row hl of the tile, chunk 2 ks + g
       // (physical chunk (2 ks + g) ^ swz(hl)); even / odd K steps in two chains, PD
@@ -332,14 +359,15 @@ __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
       xp0 = x0;
       xp1 = x1;
       vmp = vmask;
-      // tile t+1 landed for every wave (only tile t+2's gathers may still be in flight)
+      iv = ir[step_slot(t + 1) & (2 * kIdxChunk - 1)];
+      // tile t+1 landed for every wave (only tile t+2's gathers, and maybe an index chunk
+      // ahead of them, may still be in flight)
       wait_vm_barrier<AC::GOPS + GK>();
-      nxt2 = i3;
     };
     for (int t = 0; t < ntiles; t += 3) {
-      step(t, 0, 2, i2);
-      step(t + 1, 1, 0, i2);
-      step(t + 2, 2, 1, i2);
+      step(t, 0, 2);
+      step(t + 1, 1, 0);
+      step(t + 2, 2, 1);
     }
 #pragma unroll
     for (int u = 0; u < 24; ++u) epi(u, ntiles);   // the last tile's epilogue
@@ -398,6 +426,7 @@ __global__ __launch_bounds__(256, 3) void k_idx_kl_p2(IdxKlArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t kt2[KT];
   __shared__ __attribute__((aligned(16))) uint16_t stage[kG * kDI];   // q_idx, then dS tiles
   __shared__ __attribute__((aligned(16))) float s_di[kDiLds];        // dI of the row's slots
+  __shared__ __attribute__((aligned(16))) int32_t idxr[2 * kIdxChunk];   // index ring
   __shared__ int s_last[4];
   static_assert(2 * kG * DSR <= kG * kDI, "two dS tiles fit in the staging area");
 
@@ -411,6 +440,10 @@ __global__ __launch_bounds__(256, 3) void k_idx_kl_p2(IdxKlArgs a) {
     return;
   }
   const int ntiles = (c.ntiles + 2) / 3 * 3;
+  // the row's slot indices by LDS DMA (after the early exit: no DMA outlives the block)
+  const unsigned idxr_lds = lds_addr(idxr);
+  idx_chunk_dma<kH, kDQK, kDV>(a, c, 0, idxr_lds);
+  idx_chunk_dma<kH, kDQK, kDV>(a, c, 1, idxr_lds);
   const uint16_t* kts[3] = {kt0, kt1, kt2};
   unsigned kb[3];
 #pragma unroll
@@ -485,16 +518,35 @@ __global__ __launch_bounds__(256, 3) void k_idx_kl_p2(IdxKlArgs a) {
   };
 
   {
-    const TI j0 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 0);
-    const TI j1 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 1);
-    TI j2 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, 2);
-    gather_ktile(a, c, j0, kb[0]);
-    gather_ktile(a, c, j1, kb[1]);
+    const lds_ci32_t ir = (lds_ci32_t)idxr;
+    // byte offset in k_idx of a slot's row (0 for an empty slot), and the gather of the tile
+    // whose slots sit in lanes lane0 .. lane0 + 31
+    auto kio_of = [&](int v, int slot) {
+      return (slot < a.topk && (unsigned)v < (unsigned)a.n_k) ? (unsigned)v * (kDI * 2u) : 0u;
+    };
+    auto gather = [&](unsigned kio, int lane0, int k) {
+      unsigned sk[AC::RPW];
+#pragma unroll
+      for (int j = 0; j < AC::RPW; ++j)
+        sk[j] = __builtin_amdgcn_readlane(kio, lane0 + c.wave_u * AC::RPW + j);
+      gather_ktile_so(a, c, sk, kb[k]);
+    };
+    // slot read by every lane for step t: the tile it gathers (t+2)
+    auto step_slot = [&](int t) { return (t + 2) * NK + (c.lane & 31); };
+    {   // tiles 0 and 1 from chunk 0
+      const unsigned kio = kio_of(ir[c.lane], c.lane);
+      gather(kio, 0, 0);
+      gather(kio, 32, 1);
+    }
+    int iv = ir[step_slot(0)];
     wait_vm_barrier<0>();
 
-    auto step = [&](int t, int slot, int ahead2, TI& nxt2) {
-      const TI j3 = load_tile_idx_s<kH, kDQK, kDV, AL8>(a, c, t + 3);
-      gather_ktile(a, c, nxt2, kb[ahead2]);
+    auto step = [&](int t, int slot, int ahead2) {
+      // chunk t/8 + 1 (first read at the end of step t + 5, for the gather of tile t + 8)
+      // into the ring half chunk t/8 - 1 left; a load ahead of this step's gather, so
+      // complete once tile t+2 has landed
+      if ((t & 7) == 0 && t > 0) idx_chunk_dma<kH, kDQK, kDV>(a, c, t / 8 + 1, idxr_lds);
+      gather(kio_of(iv, step_slot(t)), 0, ahead2);
       if (t > 0) key_grad(t - 1);
       const lds_cptr_t kt = (lds_cptr_t)kts[slot];
       // S^T[key, index head]: A = index-key rows i16 / 16 + i16, B = index-query rows
@@ -536,13 +588,13 @@ __global__ __launch_bounds__(256, 3) void k_idx_kl_p2(IdxKlArgs a) {
       // tile t+1 landed; the dS tile is complete for every wave.  Counted: tile t+2's gathers
       // only, so the key-gradient stores issued at the step's start are waited for too (they
       // are done by then).
+      iv = ir[step_slot(t + 1) & (2 * kIdxChunk - 1)];
       wait_vm_barrier<GK>();
-      nxt2 = j3;
     };
     for (int t = 0; t < ntiles; t += 3) {
-      step(t, 0, 2, j2);
-      step(t + 1, 1, 0, j2);
-      step(t + 2, 2, 1, j2);
+      step(t, 0, 2);
+      step(t + 1, 1, 0);
+      step(t + 2, 2, 1);
     }
     key_grad(ntiles - 1);
   }
