@@ -668,6 +668,21 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
   const unsigned coff = (unsigned)((n * DQK + d0 + 4 * G) * 2);
   constexpr int NST = 2 * NT;   // 8-byte stores per lane and tile (exact: issued from asm)
   static_assert(2 * NST + 4 < 64, "vmcnt range");
+  constexpr int NMF = KH * 4 * NT;   // MFMAs per tile
+  constexpr int SGAP = 8;            // MFMAs between two stores of the previous tile
+  static_assert(SGAP / 2 + SGAP * (NST - 1) < NMF, "store placement");
+  // The stores are software-pipelined: tile t's contributions (bf16, packed after its
+  // products) go out during step t+1, one after every SGAP of that step's MFMAs, so the write
+  // path drains while the matrix cores run (issued as a burst after the products, the stores
+  // and the products took turns and each left the other's unit idle).
+  u32x2 cst[2][NT];
+  auto store_prev = [&](int tp, int j) {
+    const int mt = j / NT, nt = j % NT;
+    const unsigned off = coff + (unsigned)(((tp * NK + 16 * mt) * DQK + 16 * nt) * 2);
+    const u32x2 d = cst[mt][nt];
+    const uint16_t* base = cbase;
+    asm volatile("global_store_dwordx2 %0, %1, %2" :: "v"(off), "v"(d), "s"(base) : "memory");
+  };
   auto step = [&](int t, int k) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -675,6 +690,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
       for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (f32x4){};
     dma_tile(t + 2, (k + 2) % 3);
     const lds_cptr_t tb = (lds_cptr_t)stage + k * TILE_E;
+    const bool sp = t > 0;   // the previous tile's stores (none before the first tile)
 #pragma unroll
     for (int kk = 0; kk < KH; ++kk) {
       // B fragments: slot 16 mt + n, heads 32 kk + 8 G .. +7 (logical chunk 4 kk + G)
@@ -688,15 +704,18 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
       // (dims past DV have zero dY fragments: the product is issued anyway -- the wave
       // owning them would otherwise only finish early, which buys nothing)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+      for (int i = 0; i < 4 * NT; ++i) {
+        const int mt = (i / NT) & 1, nt = i % NT;
+        if (i < 2 * NT)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[nt][kk], bd[mt], acc[mt][nt], 0, 0, 0);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        else
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[nt][kk], bp[mt], acc[mt][nt], 0, 0, 0);
+        const int g = kk * 4 * NT + i;   // MFMA index within the tile
+        if (g >= SGAP / 2 && (g - SGAP / 2) % SGAP == 0 && (g - SGAP / 2) / SGAP < NST) {
+          if (sp) store_prev(t - 1, (g - SGAP / 2) / SGAP);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
     // every slot of the tile is stored (empty and padding slots too: they lie inside the
     // row's padded area and are never listed), so the store count per step is fixed
@@ -704,29 +723,32 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_part(AttnBwdArgs a) {
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const unsigned off = coff + (unsigned)(((t * NK + 16 * mt) * DQK + 16 * nt) * 2);
         const uint32_t lo = (uint32_t)f32_to_bf16(acc[mt][nt][0]) |
                             ((uint32_t)f32_to_bf16(acc[mt][nt][1]) << 16);
         const uint32_t hi = (uint32_t)f32_to_bf16(acc[mt][nt][2]) |
                             ((uint32_t)f32_to_bf16(acc[mt][nt][3]) << 16);
-        const u32x2 d = {lo, hi};
-        const uint16_t* base = cbase;
-        asm volatile("global_store_dwordx2 %0, %1, %2" :: "v"(off), "v"(d), "s"(base) : "memory");
+        cst[mt][nt] = (u32x2){lo, hi};
       }
     }
-    // tile t+1 landed for every wave: after its DMA come this and the previous step's
-    // stores and the DMA of tile t+2
-    wait_vm_barrier<2 * NST + 4>();
+    // tile t+1 landed for every wave.  After its DMA (step t-1's start) come the previous
+    // tile's stores of step t-1, tile t+2's DMA and this step's stores: 2 NST + 4 memory
+    // instructions from step 2 on; at step 1, NST + 4 (step 0 stores nothing); at step 0 tile
+    // 1 landed in the prologue.  (Vector memory instructions of a wave complete in issue order,
+    // loads and stores alike.)
+    if (t >= 2) wait_vm_barrier<2 * NST + 4>();
+    else wait_vm_barrier<NST + 4>();
   };
   dma_tile(0, 0);
   dma_tile(1, 1);
-  wait_vm_barrier<0>();    // both first tiles, so the steady-state count holds from step 0
+  wait_vm_barrier<0>();    // both first tiles
   const int npad = (ntiles + 2) / 3 * 3;
   for (int t = 0; t < npad; t += 3) {
     step(t, 0);
     step(t + 1, 1);
     step(t + 2, 2);
   }
+#pragma unroll
+  for (int j = 0; j < NST; ++j) store_prev(npad - 1, j);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA or store may outlive the block
 }
 
