@@ -875,7 +875,6 @@ hipError_t launch_key_lists(const KeyListArgs& a, hipStream_t s) {
 hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (!(h == 128 && d_qk == 576 && d_v == 512)) return hipErrorInvalidValue;
-  const bool al8 = a.topk >= 8 && a.topk % 8 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 31) == 0;
   KeyListArgs kl = {a.idx, a.list, a.cnt, a.off, a.cur, a.rows, a.n_k, a.topk, a.topkp};
   hipError_t e = launch_key_lists(kl, s);
   if (e != hipSuccess) return e;

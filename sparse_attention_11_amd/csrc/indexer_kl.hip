@@ -126,7 +126,6 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
 }
 
-template <bool AL8>
 __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t kv0[AC::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t kv1[AC::TILE];
@@ -419,7 +418,6 @@ __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
 // is the accumulator's key order, so dS is the B operand as it stands); dS is shared through
 // LDS and each wave forms the key gradient dS^T q_idx of its 32 of the 128 dims for every
 // slot, written as bf16 per (row, slot).
-template <bool AL8>
 __global__ __launch_bounds__(256, 3) void k_idx_kl_p2(IdxKlArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t kt0[KT];
   __shared__ __attribute__((aligned(16))) uint16_t kt1[KT];
@@ -673,14 +671,8 @@ hipError_t launch_indexer_kl(const IdxKlArgs& a, const KeyListArgs& kl, hipStrea
   if (a.rows == 0) return hipSuccess;
   hipError_t e = launch_key_lists(kl, s);
   if (e != hipSuccess) return e;
-  const bool al8 = a.topk >= 8 && a.topk % 8 == 0 && (reinterpret_cast<uintptr_t>(a.idx) & 31) == 0;
-  if (al8) {
-    k_idx_kl_p1<true><<<a.rows, 256, 0, s>>>(a);
-    k_idx_kl_p2<true><<<a.rows, 256, 0, s>>>(a);
-  } else {
-    k_idx_kl_p1<false><<<a.rows, 256, 0, s>>>(a);
-    k_idx_kl_p2<false><<<a.rows, 256, 0, s>>>(a);
-  }
+  k_idx_kl_p1<<<a.rows, 256, 0, s>>>(a);
+  k_idx_kl_p2<<<a.rows, 256, 0, s>>>(a);
   k_idx_kl_reduce<<<(a.n_k + 15) / 16, 256, 0, s>>>(a);
   return hipGetLastError();
 }
