@@ -89,6 +89,21 @@ def test_bwd_long_windows_topk2048():
     _check_full(wl, x, idx, dq, dkv)
 
 
+@pytest.mark.parametrize("docs,topk,seed", [([100, 330], 320, 2105), ([620], 600, 2106)])
+def test_bwd_every_tile_count(docs, topk, seed):
+    """Rows with every tile count from 1 to topk / 32 (odd and even counts, the last step of a
+    pair past the row's end, rows that cross the 256-slot index chunks of the slot-index ring
+    and, at topk 600, a third chunk)."""
+    _need_gpu()
+    wl, x, g = _varlen_case(docs, topk, seed=seed)
+    print(f"bwd tile counts n_q={wl.n_q} topk={wl.topk}", flush=True)
+    out, idx, smax, ssum = _forward(wl, g)
+    dq, dkv = dsa.dsa_sparse_attn_bwd(g["q"], g["kv"], idx, out, g["dout"], smax, ssum,
+                                      wl.softmax_scale)
+    torch.cuda.synchronize()
+    _check_full(wl, x, idx, dq, dkv)
+
+
 def test_bwd_edge_cases_and_chunking():
     """topk not a multiple of 8, -1 holes anywhere, an empty row, an out-of-range index, a
     repeated key; a workspace of 3 rows (many passes) gives the same dq bit for bit."""

@@ -107,6 +107,19 @@ def test_indexer_kl_long_windows_topk2048():
     _check_full(wl, x, idx, res, loss_grad=0.37)
 
 
+@pytest.mark.parametrize("docs,topk,seed", [([100, 330], 320, 2205), ([620], 600, 2206)])
+def test_indexer_kl_every_tile_count(docs, topk, seed):
+    """Rows with every tile count from 1 to topk / 32, across the 256-slot index chunks of the
+    slot-index ring."""
+    _need_gpu()
+    wl, x, g = _case(docs, topk, seed=seed)
+    print(f"indexer KL tile counts n_q={wl.n_q} topk={wl.topk}", flush=True)
+    idx, smax, ssum = _forward(wl, g)
+    res = _kl(wl, g, idx, smax, ssum)
+    torch.cuda.synchronize()
+    _check_full(wl, x, idx, res)
+
+
 def test_indexer_kl_edge_cases_and_chunking():
     """topk not a multiple of 8, -1 holes anywhere, an empty row, an out-of-range index, a
     repeated key, a row with a single key; a workspace of 3 rows (many passes) gives the same
