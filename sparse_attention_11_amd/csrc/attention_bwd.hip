@@ -801,7 +801,7 @@ __global__ __launch_bounds__(256) void k_keys_scatter(KeyListArgs a) {
 
 // dkv[k] += sum of the key's contributions; one wave per key, so the row is owned and the
 // update is a plain read-modify-write.  Lane l sums dims 8 l .. 8 l + 7 (and, for l < 8,
-// the 64 dims past 512), eight entries in flight.
+// the 64 dims past 512), sixteen entries in flight.
 template <int DQK>
 __global__ __launch_bounds__(256) void k_bwd_reduce(AttnBwdArgs a) {
   static_assert(DQK == 576, "lane split of the latent row");
@@ -827,6 +827,13 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(AttnBwdArgs a) {
     }
   };
   int p = beg;
+  for (; p + 16 <= end; p += 16) {
+    int e[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) e[j] = a.list[p + j];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) add(e[j]);
+  }
   for (; p + 8 <= end; p += 8) {
     int e[8];
 #pragma unroll

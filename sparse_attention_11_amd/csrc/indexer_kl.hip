@@ -631,7 +631,9 @@ __global__ __launch_bounds__(256) void k_idx_kl_reduce(IdxKlArgs a) {
       s[2 * j + 1] += __uint_as_float(vv[j] & 0xFFFF0000u);
     }
   };
-  constexpr int F = 8;
+  // 16 entries in flight per lane group: a chunk's lists belong to few keys (one document's),
+  // so about one workgroup per CU has work and the sum is bound by loads in flight
+  constexpr int F = 16;
   int p = beg;
   for (; p + F <= end; p += F) {
     u32x4 v[F];
@@ -639,6 +641,13 @@ __global__ __launch_bounds__(256) void k_idx_kl_reduce(IdxKlArgs a) {
     for (int j = 0; j < F; ++j) v[j] = __builtin_nontemporal_load(src(a.list[p + j]));
 #pragma unroll
     for (int j = 0; j < F; ++j) add(v[j]);
+  }
+  for (; p + 4 <= end; p += 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(src(a.list[p + j]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) add(v[j]);
   }
   for (; p < end; ++p) add(__builtin_nontemporal_load(src(a.list[p])));
   float4* d = reinterpret_cast<float4*>(a.dk + (size_t)k * kDI + 8 * l);
