@@ -564,8 +564,10 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dq_ring(AttnBwdArgs a) {
                           ((uint32_t)f32_to_bf16(acc[m][nb][1]) << 16);
       const uint32_t hi = (uint32_t)f32_to_bf16(acc[m][nb][2]) |
                           ((uint32_t)f32_to_bf16(acc[m][nb][3]) << 16);
-      *reinterpret_cast<uint2*>(qrow + (size_t)(16 * nb + i16) * DQK + d0 + 16 * m + 4 * G) =
-          make_uint2(lo, hi);
+      // (non-temporal: dQ is not read again by the backward)
+      __builtin_nontemporal_store(
+          (u32x2){lo, hi},
+          reinterpret_cast<u32x2*>(qrow + (size_t)(16 * nb + i16) * DQK + d0 + 16 * m + 4 * G));
     }
   }
 }
