@@ -411,7 +411,7 @@ __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
   }
 }
 
-// Pass 2 (a kernel of its own: it needs 49 KB of LDS, so three workgroups share a CU and
+// Pass 2 (a kernel of its own: it needs 51 KB of LDS, so three workgroups share a CU and
 // one workgroup's waits overlap another's work).  One workgroup per row, four waves.  The
 // index-key tiles are gathered again and S^T[key, index head] recomputed; dS, dW and
 // dq_idx^T += K^T dS^T stay in registers (K^T from the transposing LDS read; the MFMA's K order
