@@ -258,42 +258,21 @@ __device__ __forceinline__ void cand_compact(CandRow& c, int k, int margin) {
   c.tau = exact ? (lo32 == 0xFFFFFFFFu ? lo32 : lo32 + 1u) : max(c.tau, lo32);
 }
 
-// One 64-lane group: lane (window offset key, valid v) offers score s.
-__device__ __forceinline__ void cand_offer(CandRow& c, float s, int key, bool v, int k) {
-  const uint32_t ok = order_key(s);
-  if (!c.init) {   // bin range from the row's first group: its span over 64 of the 256 bins
-    const uint32_t mn = wave_min_u32(v ? ok : 0xFFFFFFFFu), mx = wave_max_u32(v ? ok : 0u);
-    const uint32_t span = mx - mn;
-    c.base = mn;
-    c.shift = span == 0u ? 0 : max(0, 32 - __clz((int)span) - 6);
-    c.init = true;
-  }
-  const bool keep = v && ok >= c.tau;
-  const unsigned long long m = __ballot(keep);
-  if (keep) {
-    const int p = c.n + (int)lanes_below(m);
-    c.cs[p] = s;
-    c.ck[p] = (uint16_t)key;
-    const uint32_t d = ok < c.base ? 0u : min(255u, (ok - c.base) >> c.shift);
-    atomicAdd(&c.hist[d], 1u);
-  }
-  c.n += __popcll(m);
-}
-
 // A 64-lane group marked as candidates (bookkeeping and histogram done) whose list writes are
 // still to be issued: writing them at the end of the stage, after the key stage's loads have
 // landed, keeps the stage loop's waits on those loads from also waiting on fresh stores.
+// Only the score is per lane: lane l of the group holds key kb + l, and its list slot is the
+// row's count before the group plus the kept lanes below it.
 struct CandPend {
   float s;
-  uint32_t key;
-  int p;                    // the lane's list slot (kept lanes)
+  int kb;                   // the group's first key
+  int nb;                   // the row's candidates before the group
   unsigned long long m;     // kept lanes
   bool valid;
 };
 
-__device__ __forceinline__ void cand_mark(CandRow& c, float s, int key, bool v, int k,
-                                          CandPend& pd) {
-  (void)k;
+// Lane l offers score s of key kb + l (valid v).
+__device__ __forceinline__ void cand_mark(CandRow& c, float s, int kb, bool v, CandPend& pd) {
   const uint32_t ok = order_key(s);
   if (!c.init) {   // bin range from the row's first group: its span over 64 of the 256 bins
     const uint32_t mn = wave_min_u32(v ? ok : 0xFFFFFFFFu), mx = wave_max_u32(v ? ok : 0u);
@@ -306,10 +285,10 @@ __device__ __forceinline__ void cand_mark(CandRow& c, float s, int key, bool v, 
   const unsigned long long m = __ballot(keep);
   // the previous group's registers stay reserved until now, so no asynchronous load ever
   // lands in a register a pending store still reads
-  asm volatile("" :: "v"(pd.s), "v"(pd.key), "v"(pd.p));
+  asm volatile("" :: "v"(pd.s));
   pd.s = s;
-  pd.key = (uint32_t)key;
-  pd.p = c.n + (int)lanes_below(m);
+  pd.kb = kb;
+  pd.nb = c.n;
   pd.m = m;
   pd.valid = true;
   if (keep) {
@@ -321,9 +300,11 @@ __device__ __forceinline__ void cand_mark(CandRow& c, float s, int key, bool v, 
 
 __device__ __forceinline__ void cand_flush(const CandRow& c, CandPend& pd) {
   if (pd.valid) {
-    if ((pd.m >> (threadIdx.x & 63)) & 1ull) {
-      c.cs[pd.p] = pd.s;
-      c.ck[pd.p] = (uint16_t)pd.key;
+    const int lane = threadIdx.x & 63;
+    if ((pd.m >> lane) & 1ull) {
+      const int p = pd.nb + (int)lanes_below(pd.m);
+      c.cs[p] = pd.s;
+      c.ck[p] = (uint16_t)(pd.kb + lane);
     }
     pd.valid = false;
   }
@@ -427,21 +408,23 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   // windows copy the union's last key: finite values whose scores the epilogue masks.
   typedef __attribute__((address_space(3))) uint16_t* lds_u16_t;
   const unsigned sk_lds = (unsigned)(size_t)(lds_u16_t)&sk[0][0];
+  auto fetch_piece = [&](int t, int buf, int j) {
+    const int i = wave_u + kIdxWaves * j;
+    const int r = i * RPP + lane / CPR;
+    const int c = (lane % CPR) ^ (r & SWM);
+    const int kr = min(t * KST + r, ri.L_blk - 1);
+    const unsigned voff = (unsigned)(ri.k_lo + kr) * (unsigned)(DI * 2) + (unsigned)c * 16u;
+    // (wave-uniform; readfirstlane makes it a scalar, as M0 requires)
+    const unsigned m0v = (unsigned)__builtin_amdgcn_readfirstlane(
+        (int)(sk_lds + (unsigned)(buf * TILE * 2 + i * 1024)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(m0v), "v"(voff), "s"(ksrc) : "memory", "m0");
+  };
   auto fetch = [&](int t, int buf) {
 #pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-      const int i = wave_u + kIdxWaves * j;
-      const int r = i * RPP + lane / CPR;
-      const int c = (lane % CPR) ^ (r & SWM);
-      const int kr = min(t * KST + r, ri.L_blk - 1);
-      const unsigned voff = (unsigned)(ri.k_lo + kr) * (unsigned)(DI * 2) + (unsigned)c * 16u;
-      // (wave-uniform; readfirstlane makes it a scalar, as M0 requires)
-      const unsigned m0v = (unsigned)__builtin_amdgcn_readfirstlane(
-          (int)(sk_lds + (unsigned)(buf * TILE * 2 + i * 1024)));
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :: "s"(m0v), "v"(voff), "s"(ksrc) : "memory", "m0");
-    }
+    for (int j = 0; j < PPW; ++j) fetch_piece(t, buf, j);
   };
+  static_assert(PPW <= KS, "one DMA piece per K step at most");
 
   // Per 64-key half: the contraction (32 MFMAs into acc), then the epilogue.  The two waves of
   // a SIMD (w and w + 4) would otherwise reach their epilogues together and leave the matrix
@@ -462,7 +445,9 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   // b0: the first PF K steps' key fragments, read by the caller ahead of an epilogue so
   // their LDS latency is hidden behind it
   constexpr int PF = CAND ? 1 : 2;
-  auto mma = [&](int buf, int hh, const bf16x8 (*b0)[NTK]) {
+  // ft >= 0: this wave's DMA pieces of stage ft go out between the K steps (into the other
+  // buffer), so that the stage's DMA instructions do not all queue at the stage start
+  auto mma = [&](int buf, int hh, const bf16x8 (*b0)[NTK], int ft) {
     // both 32-key sub-tiles are computed unconditionally (keys past the row's window are
     // only masked at the store); K steps outer, so the MT x 2 accumulators form independent
     // chains and consecutive MFMAs never wait for each other
@@ -480,13 +465,14 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[mt][ks], b[nt], acc[nt][mt], 0, 0, 0);
+      if (ft >= 0 && ks % (KS / PPW) == 0) fetch_piece(ft, buf ^ 1, ks / (KS / PPW));
     }
   };
   // The epilogue's output (candidate marks, or the dense scores) is written at the end of the
   // stage, after the stage's DMA has landed: no wait of the stage loop then covers a fresh store
   CandPend pend[KST / kIdxKeys];   // per half of a stage
 #pragma unroll
-  for (int i = 0; i < KST / kIdxKeys; ++i) pend[i] = CandPend{0.f, 0u, 0, 0ull, false};
+  for (int i = 0; i < KST / kIdxKeys; ++i) pend[i] = CandPend{0.f, 0, 0, 0ull, false};
   auto epi = [&](int kb, int slot) {   // kb: first key of the half
     float sv[NTK];
 #pragma unroll
@@ -500,15 +486,15 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
     }
     // lane (hl, g) takes key kb + 32 g + hl: 64 keys over the 64 lanes, in key order
     static_assert(kIdxKeys == 64, "two 32-key groups per half-stage");
-    const int key = kb + 32 * g + hl;
+    const int key = kb + 32 * g + hl;   // = kb + lane
     const float sk_ = g ? sv[1] : sv[0];
     if constexpr (CAND) {
-      cand_mark(cr, sk_, key, key <= ri.pos, a.topk, pend[slot]);
+      cand_mark(cr, sk_, kb, key <= ri.pos, pend[slot]);
     } else {
       CandPend& pd = pend[slot];
-      asm volatile("" :: "v"(pd.s), "v"(pd.key));   // (see cand_mark)
+      asm volatile("" :: "v"(pd.s));   // (see cand_mark)
       pd.s = sk_;
-      pd.key = (uint32_t)key;
+      pd.kb = kb;
       pd.valid = true;
     }
   };
@@ -518,7 +504,8 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
       if constexpr (CAND) {
         cand_flush(cr, pend[i]);
       } else if (pend[i].valid) {
-        if ((int)pend[i].key <= ri.pos) out[pend[i].key] = pend[i].s;
+        const int key = pend[i].kb + lane;
+        if (key <= ri.pos) out[key] = pend[i].s;
         pend[i].valid = false;
       }
     }
@@ -531,7 +518,15 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1, buf ^ 1);
+    // The next stage's DMA.  In candidate mode the non-lag waves issue their pieces inside
+    // their first contraction of the stage: issued by all eight waves at the stage start, the
+    // DMA instructions queue for hundreds of cycles while the matrix pipe idles.  The lag
+    // waves start with their pending epilogue and issue theirs first (from inside their
+    // epilogue or contraction, or all by the non-lag waves, the kernel ran slower); so does
+    // the plain scores kernel, which ran slower with the spread.
+    const int ft = t + 1 < ntiles ? t + 1 : -1;
+    const bool fin = CAND && !lag && ri.ok && t * KST <= ri.pos;   // first contraction runs
+    if (ft >= 0 && !fin) fetch(ft, buf ^ 1);
     bf16x8 bn[PF][NTK];   // non-lag waves: the second half's first fragments
 #pragma unroll
     for (int hh = 0; hh < KST / kIdxKeys; ++hh) {
@@ -547,7 +542,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
         if (pkb >= 0) epi(pkb, hh);
         pkb = -1;
         if (act) {
-          mma(buf, hh, b0);
+          mma(buf, hh, b0, -1);
           pkb = kb;
         }
       } else if (act) {
@@ -556,7 +551,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_bf16(IndexerArgs a) 
         for (int k = 0; k < PF; ++k)
 #pragma unroll
           for (int nt = 0; nt < NTK; ++nt) b0[k][nt] = hh == 0 ? bfrag(buf, hh, k, nt) : bn[k][nt];
-        mma(buf, hh, b0);
+        mma(buf, hh, b0, CAND && hh == 0 ? ft : -1);
         if (hh + 1 < KST / kIdxKeys && kb + kIdxKeys <= ri.pos)
 #pragma unroll
           for (int k = 0; k < PF; ++k)
@@ -689,12 +684,13 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
   auto stash_scale = [&](int sbuf) {
     if (tid < kIdxKeys) sks[sbuf][tid] = pres;
   };
-  CandPend pend = CandPend{0.f, 0u, 0, 0ull, false};
+  CandPend pend = CandPend{0.f, 0, 0, 0ull, false};
   auto flush = [&]() {
     if constexpr (CAND) {
       cand_flush(cr, pend);
     } else if (pend.valid) {
-      if ((int)pend.key <= ri.pos) out[pend.key] = pend.s;
+      const int key = pend.kb + lane;
+      if (key <= ri.pos) out[key] = pend.s;
       pend.valid = false;
     }
   };
@@ -742,14 +738,14 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_indexer_fp8(IndexerArgs a) {
       sv[nt] = pair_sum(s);   // (both lanes of the pair hold the sum)
     }
     static_assert(kIdxKeys == 64, "two 32-key sub-tiles per stage");
-    const int key = kb + 32 * g + hl;
+    const int key = kb + 32 * g + hl;   // = kb + lane
     const float sc = (g ? sv[1] : sv[0]) * sks[sbuf][32 * g + hl];
     if constexpr (CAND) {
-      cand_mark(cr, sc, key, key <= ri.pos, a.topk, pend);
+      cand_mark(cr, sc, kb, key <= ri.pos, pend);
     } else {
-      asm volatile("" :: "v"(pend.s), "v"(pend.key));   // (see cand_mark)
+      asm volatile("" :: "v"(pend.s));   // (see cand_mark)
       pend.s = sc;
-      pend.key = (uint32_t)key;
+      pend.kb = kb;
       pend.valid = true;
     }
   };
