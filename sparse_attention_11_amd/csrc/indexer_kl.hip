@@ -100,26 +100,29 @@ __device__ __forceinline__ float block_max(float x, float* sb) {
 // makes 16 rows x one logical chunk (the MFMA operand reads) hit 16 different bank groups.
 // Empty slots copy row 0 (masked later).  sk: byte offsets in k_idx of the wave's 8 rows,
 // scalars (0 for empty slots).
-__device__ __forceinline__ void gather_ktile_so(const IdxKlArgs& a, const RowCtx& c,
-                                                const unsigned* sk, unsigned lds_tile) {
+__device__ __forceinline__ void gather_ktile_piece(const IdxKlArgs& a, const RowCtx& c,
+                                                   const unsigned* sk, unsigned lds_tile, int i) {
   const int sub = c.lane >> 4, ch = c.lane & 15;
   const bool b0 = c.lane & 16, b1 = c.lane & 32;
+  // (opaque to the optimiser: selects between loads of sk[] would otherwise become one load
+  // at a lane-dependent index, through scratch memory)
+  unsigned s0 = sk[4 * i], s1 = sk[4 * i + 1], s2 = sk[4 * i + 2], s3 = sk[4 * i + 3];
+  asm("" : "+s"(s0), "+s"(s1), "+s"(s2), "+s"(s3));
+  const unsigned lo = b0 ? s1 : s0;
+  const unsigned hi = b0 ? s3 : s2;
+  const unsigned ro = b1 ? hi : lo;
+  const int r = c.wave * 8 + 4 * i + sub;
+  const unsigned voff = ro + (unsigned)((ch ^ (r & 15)) * 16);
+  const unsigned m0v = lds_tile + (unsigned)((c.wave_u * 8 + 4 * i) * kDI * 2);
+  const uint16_t* base = a.k_idx;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
+}
+
+__device__ __forceinline__ void gather_ktile_so(const IdxKlArgs& a, const RowCtx& c,
+                                                const unsigned* sk, unsigned lds_tile) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    // (opaque to the optimiser: selects between loads of sk[] would otherwise become one load
-    // at a lane-dependent index, through scratch memory)
-    unsigned s0 = sk[4 * i], s1 = sk[4 * i + 1], s2 = sk[4 * i + 2], s3 = sk[4 * i + 3];
-    asm("" : "+s"(s0), "+s"(s1), "+s"(s2), "+s"(s3));
-    const unsigned lo = b0 ? s1 : s0;
-    const unsigned hi = b0 ? s3 : s2;
-    const unsigned ro = b1 ? hi : lo;
-    const int r = c.wave * 8 + 4 * i + sub;
-    const unsigned voff = ro + (unsigned)((ch ^ (r & 15)) * 16);
-    const unsigned m0v = lds_tile + (unsigned)((c.wave_u * 8 + 4 * i) * kDI * 2);
-    const uint16_t* base = a.k_idx;
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
-  }
+  for (int i = 0; i < GK; ++i) gather_ktile_piece(a, c, sk, lds_tile, i);
 }
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
@@ -303,7 +306,35 @@ __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
       // into the ring half chunk t/8 - 1 left; a load ahead of this step's gather, so
       // complete once tile t+2 has landed
       if ((t & 7) == 0 && t > 0) idx_chunk_dma<kH, kDQK, kDV>(a, c, t / 8 + 1, idxr_lds);
-      gather(kvo, kio, 32, ahead2);
+      // tile t+2's gather, one LDS DMA piece every third K step of the logits (issued together
+      // at the step start, the four waves' 44 DMA instructions queued for about a thousand
+      // cycles ahead of the first MFMA); each piece reads its rows' offsets from the decoded
+      // slots (lanes 32 + 8 wave ..) as it goes out
+      const int l0 = 32 + c.wave_u * AC::RPW;
+      auto piece = [&](int p) {
+        if (p < AC::NI) {   // latent rows: 1 KB of the wave's eight rows
+          const int j0 = p * 64 / AC::CPR;
+          const int b = (j0 + 1) * AC::CPR - 64 * p;
+          unsigned ro = __builtin_amdgcn_readlane(kvo, l0 + j0);
+          if (b < 64) {
+            const unsigned r1 = __builtin_amdgcn_readlane(kvo, l0 + j0 + 1);
+            ro = c.lane >= b ? r1 : ro;
+          }
+          const unsigned voff = loff[p] + ro;
+          const unsigned m0v = wb[ahead2] + (unsigned)p * 1024u;
+          const uint16_t* base = a.kv;
+          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                       :: "s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
+        } else {            // index-key rows
+          const int i = p - AC::NI;   // (< GK)
+          unsigned sk[AC::RPW];
+#pragma unroll
+          for (int j = 0; j < AC::RPW; ++j)
+            sk[j] = j / 4 == i ? __builtin_amdgcn_readlane(kio, l0 + j) : 0u;
+          gather_ktile_piece(a, c, sk, kb[ahead2], i);
+        }
+      };
+      static_assert(3 * (AC::NI + GK) <= kKs, "gather pieces placement");
       if (t >= 2 && c.wave_u == (t & 3) && c.lane < NK) lazy_sum(t - 2);
 
       // logits C[head, key]: A = Q (AGPRs), B = latent row hl of the tile, chunk 2 ks + g
@@ -344,6 +375,7 @@ __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
           asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(s1) : "a"(qa), "v"(cur));
         }
         if (ks < 24) epi(ks, t);
+        if (ks % 3 == 1 && ks / 3 < AC::NI + GK) piece(ks / 3);
         __builtin_amdgcn_sched_barrier(0);
       }
       // indexer S[index head, key]: A = index-query rows, B = index-key rows i16, 16 + i16
