@@ -292,6 +292,35 @@ dsa_status dsa_indexer_kl_loss_grad(const dsa_shape *shape, const void *q_idx, c
  * 4 * (3 * n_k + 1) bytes rounded up to 256, 1 KiB, and 2 KiB of alignment slack. */
 dsa_status dsa_indexer_kl_workspace_bytes(const dsa_shape *shape, size_t *bytes);
 
+/*
+ * The attention backward and the indexer KL loss of one training step in one call (page
+ * "CANNTorchTitan: ...", sections "SparseFlashAttentionGrad" and
+ * "SparseLightningIndexerGradKLLoss": both consume the same recomputed probabilities
+ * P[h, s] and the same top-k indices).  Results as dsa_sparse_attn_bwd followed by
+ * dsa_indexer_kl_loss_grad with the same arguments (dq bit for bit; dkv and dk_idx up to the
+ * order of their per-key sums; the losses, dq_idx and dw_idx up to fp32 rounding of the target:
+ * its per-slot head sums come from the backward's probabilities instead of a second
+ * recomputation).  Over each chunk of rows the per-key entry lists are built once for both,
+ * and the indexer loss neither gathers latent rows nor recomputes logits.
+ *   Arguments: those of dsa_sparse_attn_bwd (q .. dkv), then those of dsa_indexer_kl_loss_grad
+ *   that it does not share (q_idx .. dk_idx); the same layouts, alignment, accumulation
+ *   (dkv and dk_idx are ADDED to) and supported dimensions as those two calls (the union of
+ *   their DSA_ERR_UNSUPPORTED cases).  The workspace holds both calls' per-chunk arrays, the
+ *   indexer loss's reusing the backward's once consumed, plus 4 * topk_p bytes per row of
+ *   head sums; rows are processed in chunks of as many rows as it fits (DSA_ERR_WORKSPACE
+ *   if not even one).  Calls that update the same dkv or dk_idx must not overlap.
+ */
+dsa_status dsa_sparse_attn_bwd_indexer_kl(
+    const dsa_shape *shape, const void *q, const void *kv, const int32_t *topk_idx,
+    const void *out, const void *dout, const float *softmax_max, const float *softmax_sum,
+    void *dq, float *dkv, const void *q_idx, const void *k_idx, const float *w_idx,
+    float loss_grad, float *loss_rows, float *loss, void *dq_idx, float *dw_idx, float *dk_idx,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace size for dsa_sparse_attn_bwd_indexer_kl that processes up to 2048 rows per pass:
+ * dsa_sparse_attn_bwd's bytes per row plus 4 * topk_p, plus its fixed part. */
+dsa_status dsa_sparse_attn_bwd_indexer_kl_workspace_bytes(const dsa_shape *shape, size_t *bytes);
+
 /* Bytes of the fixed device array dsa_forward_noalloc works in (one per GPU). */
 #define DSA_NOALLOC_SCRATCH_BYTES (256u << 20)
 

@@ -10,7 +10,9 @@ _BINDING = (
     "dsa_abi_version", "dsa_last_error", "dsa_workspace_bytes", "dsa_indexer_scores",
     "dsa_topk_select", "dsa_indexer_topk", "dsa_sparse_attn", "dsa_forward", "dsa_forward_noalloc",
     "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_workspace_bytes", "dsa_indexer_kl_loss_grad",
-    "dsa_indexer_kl_workspace_bytes", "dsa_quantize_fp8_rows", "dsa_dense_attn", "Segment",
+    "dsa_indexer_kl_workspace_bytes", "dsa_sparse_attn_bwd_indexer_kl",
+    "dsa_sparse_attn_bwd_indexer_kl_workspace_bytes", "dsa_quantize_fp8_rows", "dsa_dense_attn",
+    "Segment",
     "DsaError",
     "load_library",
 )

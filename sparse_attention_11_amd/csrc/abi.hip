@@ -24,7 +24,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int h, int d_qk, int d_v, int n
                               hipStream_t s);
 hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v, hipStream_t s);
 hipError_t launch_quant_fp8_rows(const QuantArgs& a, hipStream_t s);
-hipError_t launch_indexer_kl(const IdxKlArgs& a, const KeyListArgs& kl, hipStream_t s);
+hipError_t launch_indexer_kl(const IdxKlArgs& a, const KeyListArgs& kl, hipStream_t s, bool lists);
 hipError_t launch_loss_total(const float* loss, int n, float* out, hipStream_t s);
 hipError_t launch_dense_attn(const DenseArgs& a, int nqblk, hipStream_t s);
 int dense_rows_per_block();
@@ -636,6 +636,136 @@ dsa_status dsa_sparse_attn_bwd_workspace_bytes(const dsa_shape* shape, size_t* b
   return ok();
 }
 
+// ---- attention backward and indexer loss: validation, argument set-up and the chunk loops
+
+namespace {
+
+dsa_status bwd_validate(const dsa_shape* shape, const void* q, const void* kv,
+                        const int32_t* topk_idx, const void* out, const void* dout,
+                        const float* softmax_max, const float* softmax_sum, const void* dq,
+                        const float* dkv, const void* workspace) {
+  if (!q || !kv || !topk_idx || !out || !dout || !softmax_max || !softmax_sum || !dq || !dkv)
+    return fail(DSA_ERR_INVALID_ARG, "attention backward tensor is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(dkv) % 16 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "workspace and dkv must be 16-byte aligned");
+  dsa_status st = check_attn_align(q, kv, topk_idx, out, softmax_max, softmax_sum);
+  if (st != DSA_OK) return st;
+  (void)shape;
+  return check_align({{dout, 16, "dout"}, {dq, 16, "dq"}});
+}
+
+dsa_status kl_validate(const void* q_idx, const void* k_idx, const float* w_idx, const void* q,
+                       const void* kv, const int32_t* topk_idx, const float* softmax_max,
+                       const float* softmax_sum, const float* loss_rows, const void* dq_idx,
+                       const float* dw_idx, const float* dk_idx, const void* workspace) {
+  if (!q_idx || !k_idx || !w_idx || !q || !kv || !topk_idx || !softmax_max || !softmax_sum ||
+      !loss_rows || !dq_idx || !dw_idx || !dk_idx)
+    return fail(DSA_ERR_INVALID_ARG, "indexer loss tensor is NULL");
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(w_idx, 16) || !aligned(q, 16) ||
+      !aligned(kv, 16) || !aligned(softmax_max, 16) || !aligned(softmax_sum, 16) ||
+      !aligned(dk_idx, 16) || !aligned(workspace, 16) || !aligned(dq_idx, 8) ||
+      !aligned(topk_idx, 4) || !aligned(loss_rows, 4) || !aligned(dw_idx, 4))
+    return fail(DSA_ERR_INVALID_ARG, "indexer loss tensors, dk_idx and workspace must be "
+                "16-byte aligned (dq_idx 8-byte)");
+  return DSA_OK;
+}
+
+// Rows per chunk that `workspace_bytes` holds at `per_row` bytes a row over `fixed`; 0 (with
+// the error set) if not even one.  List entries are row * topkp + slot within a chunk: the
+// chunk keeps them below 2^31.
+int chunk_rows(const dsa_shape* shape, const void* workspace, size_t workspace_bytes,
+               size_t fixed, size_t per_row, size_t topkp) {
+  const size_t fit = workspace && workspace_bytes > fixed ? (workspace_bytes - fixed) / per_row : 0;
+  if (fit == 0) {
+    fail(DSA_ERR_WORKSPACE, "workspace of at least %zu bytes (one row) needed, %zu given",
+         fixed + per_row, workspace ? workspace_bytes : (size_t)0);
+    return 0;
+  }
+  const size_t max_rows = (size_t)INT32_MAX / topkp;
+  return (int)std::min({fit, (size_t)shape->n_q, max_rows});
+}
+
+// Bump allocator over the workspace (regions 256-byte aligned).
+struct WsTake {
+  char* w;
+  size_t at = 0;
+  char* operator()(size_t bytes) {
+    char* p = w + at;
+    at = align_up(at + bytes);
+    return p;
+  }
+};
+
+// The call-wide fields of the attention backward's arguments.
+dsa::AttnBwdArgs bwd_args(const dsa_shape* shape, const void* kv, float* dkv, size_t topkp) {
+  dsa::AttnBwdArgs a = {};
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.dkv = dkv;
+  a.n_k = shape->n_k;
+  a.topk = shape->topk;
+  a.topkp = (int)topkp;
+  a.scale = shape->softmax_scale;
+  a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
+  return a;
+}
+
+// The chunk [r0, r0 + rows) of the attention backward.
+void bwd_chunk(dsa::AttnBwdArgs& a, const dsa_shape* shape, int r0, int rows, const void* q,
+               const int32_t* topk_idx, const void* out, const void* dout,
+               const float* softmax_max, const float* softmax_sum, void* dq) {
+  const int h = shape->h, dqk = shape->d_qk, dv = shape->d_v, topk = shape->topk;
+  a.rows = rows;
+  a.q = static_cast<const uint16_t*>(q) + (size_t)r0 * h * dqk;
+  a.idx = topk_idx + (size_t)r0 * topk;
+  a.out = static_cast<const uint16_t*>(out) + (size_t)r0 * h * dv;
+  a.dout = static_cast<const uint16_t*>(dout) + (size_t)r0 * h * dv;
+  a.smax = softmax_max + (size_t)r0 * h;
+  a.ssum = softmax_sum + (size_t)r0 * h;
+  a.dq = static_cast<uint16_t*>(dq) + (size_t)r0 * h * dqk;
+  a.xcd_remap = rows % 8 == 0;
+}
+
+// The call-wide fields of the indexer loss's arguments.
+dsa::IdxKlArgs kl_args(const dsa_shape* shape, const void* k_idx, const void* kv, float* dk_idx,
+                       float loss_grad, size_t topkp) {
+  dsa::IdxKlArgs a = {};
+  a.k_idx = static_cast<const uint16_t*>(k_idx);
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.dk = dk_idx;
+  a.n_k = shape->n_k;
+  a.topk = shape->topk;
+  a.topkp = (int)topkp;
+  a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
+  a.loss_grad = loss_grad;
+  return a;
+}
+
+// The chunk [r0, r0 + rows) of the indexer loss.
+void kl_chunk(dsa::IdxKlArgs& a, const dsa_shape* shape, int r0, int rows, const void* q_idx,
+              const float* w_idx, const void* q, const int32_t* topk_idx,
+              const float* softmax_max, const float* softmax_sum, float* loss_rows, void* dq_idx,
+              float* dw_idx) {
+  const int topk = shape->topk;
+  a.rows = rows;
+  a.q_idx = static_cast<const uint16_t*>(q_idx) + (size_t)r0 * 64 * 128;
+  a.w = w_idx + (size_t)r0 * 64;
+  a.q = static_cast<const uint16_t*>(q) + (size_t)r0 * 128 * 576;
+  a.idx = topk_idx + (size_t)r0 * topk;
+  a.smax = softmax_max + (size_t)r0 * 128;
+  a.ssum = softmax_sum + (size_t)r0 * 128;
+  a.loss = loss_rows + r0;
+  a.dq_idx = static_cast<uint16_t*>(dq_idx) + (size_t)r0 * 64 * 128;
+  a.dw = dw_idx + (size_t)r0 * 64;
+  a.xcd_remap = rows % 8 == 0;
+}
+
+// Combined backward workspace per row: the attention backward's, plus the fp32 per-slot head
+// sums of P handed to the indexer loss (whose per-slot arrays reuse the attention backward's
+// regions once they are consumed, and whose key lists are the attention backward's).
+size_t bwdkl_row_bytes(const dsa_shape* s) { return bwd_row_bytes(s) + bwd_topkp(s) * 4; }
+
+}  // namespace
+
 dsa_status dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void* kv,
                                const int32_t* topk_idx, const void* out, const void* dout,
                                const float* softmax_max, const float* softmax_sum, void* dq,
@@ -646,31 +776,16 @@ dsa_status dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void
   if (st != DSA_OK) return st;
   if ((st = check_bwd_dims(shape)) != DSA_OK) return st;
   if (shape->n_q == 0) return ok();
-  if (!q || !kv || !topk_idx || !out || !dout || !softmax_max || !softmax_sum || !dq || !dkv)
-    return fail(DSA_ERR_INVALID_ARG, "attention backward tensor is NULL");
-  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0 || reinterpret_cast<uintptr_t>(dkv) % 16 != 0)
-    return fail(DSA_ERR_INVALID_ARG, "workspace and dkv must be 16-byte aligned");
-  if ((st = check_attn_align(q, kv, topk_idx, out, softmax_max, softmax_sum)) != DSA_OK) return st;
-  if ((st = check_align({{dout, 16, "dout"}, {dq, 16, "dq"}})) != DSA_OK) return st;
-  const size_t per_row = bwd_row_bytes(shape);
-  const size_t fixed = bwd_fixed_bytes(shape);
-  const size_t fit = workspace && workspace_bytes > fixed ? (workspace_bytes - fixed) / per_row : 0;
-  if (fit == 0)
-    return fail(DSA_ERR_WORKSPACE, "workspace of at least %zu bytes (one row) needed, %zu given",
-                fixed + per_row, workspace ? workspace_bytes : (size_t)0);
-  // list entries are row * topkp + slot within a chunk: keep them below 2^31
+  if ((st = bwd_validate(shape, q, kv, topk_idx, out, dout, softmax_max, softmax_sum, dq, dkv,
+                         workspace)) != DSA_OK)
+    return st;
   const size_t topkp = bwd_topkp(shape);
-  const size_t max_rows = (size_t)INT32_MAX / topkp;
-  const int chunk = (int)std::min({fit, (size_t)shape->n_q, max_rows});
+  const int chunk = chunk_rows(shape, workspace, workspace_bytes, bwd_fixed_bytes(shape),
+                               bwd_row_bytes(shape), topkp);
+  if (chunk == 0) return DSA_ERR_WORKSPACE;
   const int h = shape->h, dqk = shape->d_qk, dv = shape->d_v, topk = shape->topk;
-  char* w = static_cast<char*>(workspace);
-  size_t at = 0;
-  auto take = [&](size_t bytes) {
-    char* p = w + at;
-    at = align_up(at + bytes);
-    return p;
-  };
-  dsa::AttnBwdArgs a = {};
+  WsTake take{static_cast<char*>(workspace)};
+  dsa::AttnBwdArgs a = bwd_args(shape, kv, dkv, topkp);
   a.cnt = reinterpret_cast<int*>(take((size_t)shape->n_k * 4));
   a.off = reinterpret_cast<int*>(take(((size_t)shape->n_k + 1) * 4));
   a.cur = reinterpret_cast<int*>(take((size_t)shape->n_k * 4));
@@ -678,26 +793,11 @@ dsa_status dsa_sparse_attn_bwd(const dsa_shape* shape, const void* q, const void
   a.ws_ds = reinterpret_cast<uint16_t*>(take((size_t)chunk * topkp * h * 2));
   a.ws_c = reinterpret_cast<uint16_t*>(take((size_t)chunk * topkp * dqk * 2));
   a.list = reinterpret_cast<int*>(take((size_t)chunk * topk * 4));
-  if (at > workspace_bytes)
+  if (take.at > workspace_bytes)
     return fail(DSA_ERR_WORKSPACE, "internal workspace layout exceeds %zu bytes", workspace_bytes);
-  a.kv = static_cast<const uint16_t*>(kv);
-  a.dkv = dkv;
-  a.n_k = shape->n_k;
-  a.topk = topk;
-  a.topkp = (int)topkp;
-  a.scale = shape->softmax_scale;
-  a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
   for (int r0 = 0; r0 < shape->n_q; r0 += chunk) {
-    const int rows = std::min(chunk, shape->n_q - r0);
-    a.rows = rows;
-    a.q = static_cast<const uint16_t*>(q) + (size_t)r0 * h * dqk;
-    a.idx = topk_idx + (size_t)r0 * topk;
-    a.out = static_cast<const uint16_t*>(out) + (size_t)r0 * h * dv;
-    a.dout = static_cast<const uint16_t*>(dout) + (size_t)r0 * h * dv;
-    a.smax = softmax_max + (size_t)r0 * h;
-    a.ssum = softmax_sum + (size_t)r0 * h;
-    a.dq = static_cast<uint16_t*>(dq) + (size_t)r0 * h * dqk;
-    a.xcd_remap = rows % 8 == 0;
+    bwd_chunk(a, shape, r0, std::min(chunk, shape->n_q - r0), q, topk_idx, out, dout,
+              softmax_max, softmax_sum, dq);
     hipError_t e = dsa::launch_sparse_attn_bwd(a, h, dqk, dv, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "attention backward launch");
   }
@@ -733,33 +833,15 @@ dsa_status dsa_indexer_kl_loss_grad(const dsa_shape* shape, const void* q_idx, c
     }
     return ok();
   }
-  if (!q_idx || !k_idx || !w_idx || !q || !kv || !topk_idx || !softmax_max || !softmax_sum ||
-      !loss_rows || !dq_idx || !dw_idx || !dk_idx)
-    return fail(DSA_ERR_INVALID_ARG, "indexer loss tensor is NULL");
-  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(w_idx, 16) || !aligned(q, 16) ||
-      !aligned(kv, 16) || !aligned(softmax_max, 16) || !aligned(softmax_sum, 16) ||
-      !aligned(dk_idx, 16) || !aligned(workspace, 16) || !aligned(dq_idx, 8) ||
-      !aligned(topk_idx, 4) || !aligned(loss_rows, 4) || !aligned(dw_idx, 4))
-    return fail(DSA_ERR_INVALID_ARG, "indexer loss tensors, dk_idx and workspace must be "
-                "16-byte aligned (dq_idx 8-byte)");
-  const size_t per_row = kl_row_bytes(shape);
-  const size_t fixed = kl_fixed_bytes(shape);
-  const size_t fit = workspace && workspace_bytes > fixed ? (workspace_bytes - fixed) / per_row : 0;
-  if (fit == 0)
-    return fail(DSA_ERR_WORKSPACE, "workspace of at least %zu bytes (one row) needed, %zu given",
-                fixed + per_row, workspace ? workspace_bytes : (size_t)0);
-  // list entries are row * topkp + slot within a chunk: keep them below 2^31
+  if ((st = kl_validate(q_idx, k_idx, w_idx, q, kv, topk_idx, softmax_max, softmax_sum,
+                        loss_rows, dq_idx, dw_idx, dk_idx, workspace)) != DSA_OK)
+    return st;
   const size_t topkp = kl_topkp(shape);
-  const size_t max_rows = (size_t)INT32_MAX / topkp;
-  const int chunk = (int)std::min({fit, (size_t)shape->n_q, max_rows});
+  const int chunk = chunk_rows(shape, workspace, workspace_bytes, kl_fixed_bytes(shape),
+                               kl_row_bytes(shape), topkp);
+  if (chunk == 0) return DSA_ERR_WORKSPACE;
   const int topk = shape->topk;
-  char* w = static_cast<char*>(workspace);
-  size_t at = 0;
-  auto take = [&](size_t bytes) {
-    char* p = w + at;
-    at = align_up(at + bytes);
-    return p;
-  };
+  WsTake take{static_cast<char*>(workspace)};
   dsa::KeyListArgs kl = {};
   kl.cnt = reinterpret_cast<int*>(take((size_t)shape->n_k * 4));
   kl.off = reinterpret_cast<int*>(take(((size_t)shape->n_k + 1) * 4));
@@ -767,38 +849,104 @@ dsa_status dsa_indexer_kl_loss_grad(const dsa_shape* shape, const void* q_idx, c
   uint16_t* ws_c = reinterpret_cast<uint16_t*>(take((size_t)chunk * topkp * 128 * 2));
   float* ws_di = reinterpret_cast<float*>(take((size_t)chunk * topkp * 4 + 1024));
   kl.list = reinterpret_cast<int*>(take((size_t)chunk * topk * 4));
-  if (at > workspace_bytes)
+  if (take.at > workspace_bytes)
     return fail(DSA_ERR_WORKSPACE, "internal workspace layout exceeds %zu bytes", workspace_bytes);
   kl.n_k = shape->n_k;
   kl.topk = topk;
   kl.topkp = (int)topkp;
-  dsa::IdxKlArgs a = {};
-  a.k_idx = static_cast<const uint16_t*>(k_idx);
-  a.kv = static_cast<const uint16_t*>(kv);
+  dsa::IdxKlArgs a = kl_args(shape, k_idx, kv, dk_idx, loss_grad, topkp);
   a.ws_c = ws_c;
   a.ws_di = ws_di;
-  a.dk = dk_idx;
   a.list = kl.list;
   a.off = kl.off;
-  a.n_k = shape->n_k;
-  a.topk = topk;
-  a.topkp = (int)topkp;
-  a.scale_log2 = shape->softmax_scale * 1.4426950408889634f;
-  a.loss_grad = loss_grad;
   for (int r0 = 0; r0 < shape->n_q; r0 += chunk) {
     const int rows = std::min(chunk, shape->n_q - r0);
-    a.rows = kl.rows = rows;
-    a.q_idx = static_cast<const uint16_t*>(q_idx) + (size_t)r0 * 64 * 128;
-    a.w = w_idx + (size_t)r0 * 64;
-    a.q = static_cast<const uint16_t*>(q) + (size_t)r0 * 128 * 576;
-    a.idx = kl.idx = topk_idx + (size_t)r0 * topk;
-    a.smax = softmax_max + (size_t)r0 * 128;
-    a.ssum = softmax_sum + (size_t)r0 * 128;
-    a.loss = loss_rows + r0;
-    a.dq_idx = static_cast<uint16_t*>(dq_idx) + (size_t)r0 * 64 * 128;
-    a.dw = dw_idx + (size_t)r0 * 64;
-    a.xcd_remap = rows % 8 == 0;
-    hipError_t e = dsa::launch_indexer_kl(a, kl, hs);
+    kl_chunk(a, shape, r0, rows, q_idx, w_idx, q, topk_idx, softmax_max, softmax_sum, loss_rows,
+             dq_idx, dw_idx);
+    kl.rows = rows;
+    kl.idx = a.idx;
+    hipError_t e = dsa::launch_indexer_kl(a, kl, hs, true);
+    if (e != hipSuccess) return hip_fail(e, "indexer loss launch");
+  }
+  if (loss) {
+    hipError_t e = dsa::launch_loss_total(loss_rows, shape->n_q, loss, hs);
+    if (e != hipSuccess) return hip_fail(e, "loss sum launch");
+  }
+  return ok();
+}
+
+dsa_status dsa_sparse_attn_bwd_indexer_kl_workspace_bytes(const dsa_shape* shape, size_t* bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes is NULL");
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedAttn, p);
+  if (st != DSA_OK) return st;
+  if ((st = check_bwd_dims(shape)) != DSA_OK) return st;
+  if ((st = check_kl_dims(shape)) != DSA_OK) return st;
+  *bytes = bwd_fixed_bytes(shape) + bwdkl_row_bytes(shape) * (size_t)std::min(shape->n_q, kBwdChunkRows);
+  return ok();
+}
+
+dsa_status dsa_sparse_attn_bwd_indexer_kl(
+    const dsa_shape* shape, const void* q, const void* kv, const int32_t* topk_idx,
+    const void* out, const void* dout, const float* softmax_max, const float* softmax_sum,
+    void* dq, float* dkv, const void* q_idx, const void* k_idx, const float* w_idx,
+    float loss_grad, float* loss_rows, float* loss, void* dq_idx, float* dw_idx, float* dk_idx,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  dsa_status st = check_shape(shape, kNeedAttn, p);
+  if (st != DSA_OK) return st;
+  if ((st = check_bwd_dims(shape)) != DSA_OK) return st;
+  if ((st = check_kl_dims(shape)) != DSA_OK) return st;
+  if (!std::isfinite(loss_grad)) return fail(DSA_ERR_INVALID_ARG, "loss_grad is not finite");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (shape->n_q == 0) {
+    if (loss) {
+      hipError_t e = dsa::launch_loss_total(loss_rows, 0, loss, hs);
+      if (e != hipSuccess) return hip_fail(e, "loss sum launch");
+    }
+    return ok();
+  }
+  if ((st = bwd_validate(shape, q, kv, topk_idx, out, dout, softmax_max, softmax_sum, dq, dkv,
+                         workspace)) != DSA_OK)
+    return st;
+  if ((st = kl_validate(q_idx, k_idx, w_idx, q, kv, topk_idx, softmax_max, softmax_sum,
+                        loss_rows, dq_idx, dw_idx, dk_idx, workspace)) != DSA_OK)
+    return st;
+  const size_t topkp = bwd_topkp(shape);
+  const int chunk = chunk_rows(shape, workspace, workspace_bytes, bwd_fixed_bytes(shape),
+                               bwdkl_row_bytes(shape), topkp);
+  if (chunk == 0) return DSA_ERR_WORKSPACE;
+  const int h = shape->h, dqk = shape->d_qk, dv = shape->d_v, topk = shape->topk;
+  WsTake take{static_cast<char*>(workspace)};
+  dsa::AttnBwdArgs a = bwd_args(shape, kv, dkv, topkp);
+  a.cnt = reinterpret_cast<int*>(take((size_t)shape->n_k * 4));
+  a.off = reinterpret_cast<int*>(take(((size_t)shape->n_k + 1) * 4));
+  a.cur = reinterpret_cast<int*>(take((size_t)shape->n_k * 4));
+  a.ws_p = reinterpret_cast<uint16_t*>(take((size_t)chunk * topkp * h * 2));
+  a.ws_ds = reinterpret_cast<uint16_t*>(take((size_t)chunk * topkp * h * 2));
+  a.ws_c = reinterpret_cast<uint16_t*>(take((size_t)chunk * topkp * dqk * 2));
+  a.list = reinterpret_cast<int*>(take((size_t)chunk * topk * 4));
+  a.psum = reinterpret_cast<float*>(take((size_t)chunk * topkp * 4));
+  if (take.at > workspace_bytes)
+    return fail(DSA_ERR_WORKSPACE, "internal workspace layout exceeds %zu bytes", workspace_bytes);
+  dsa::IdxKlArgs b = kl_args(shape, k_idx, kv, dk_idx, loss_grad, topkp);
+  // per slot of the chunk: the key gradient over the attention backward's contributions and
+  // dI over its probabilities, both read by then (stream order)
+  b.ws_c = a.ws_c;
+  b.ws_di = reinterpret_cast<float*>(a.ws_p);
+  static_assert(128 * 2 <= 576 * 2, "key gradients fit the contribution region");
+  b.list = a.list;
+  b.off = a.off;
+  b.psum = a.psum;
+  const dsa::KeyListArgs none = {};
+  for (int r0 = 0; r0 < shape->n_q; r0 += chunk) {
+    const int rows = std::min(chunk, shape->n_q - r0);
+    bwd_chunk(a, shape, r0, rows, q, topk_idx, out, dout, softmax_max, softmax_sum, dq);
+    hipError_t e = dsa::launch_sparse_attn_bwd(a, h, dqk, dv, hs);
+    if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+    kl_chunk(b, shape, r0, rows, q_idx, w_idx, q, topk_idx, softmax_max, softmax_sum, loss_rows,
+             dq_idx, dw_idx);
+    e = dsa::launch_indexer_kl(b, none, hs, false);
     if (e != hipSuccess) return hip_fail(e, "indexer loss launch");
   }
   if (loss) {

@@ -72,8 +72,19 @@ struct BwdRowK {
   unsigned sel;        // byte selector assembling a head pair's dword (differs for odd heads)
 };
 
+// DPP source modes of the 16-lane sums: lane l reads lane l ^ 1, l ^ 2, (l & ~7) | (7 - l % 8)
+// and l ^ 8 of its 16-lane row.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppRor8 = 0x128;
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 // One ring step (PARTS) or the row prologue's products of tile 0 alone (no parts, no gather).
-template <int H, int DQK, int DV, bool PARTS>
+// PSUM: also the sum over the 16 heads of each 16-lane row of P for every part; the lane at
+// row position r keeps part r's (hsum), so after the tile each lane holds one key's sum over
+// its row's heads.
+template <int H, int DQK, int DV, bool PARTS, bool PSUM = false>
 __device__ __forceinline__ void bwd_ring_tile(const AttnBwdArgs& a, const RowCtx& c,
                                               const bf16x8* qf, const bf16x8* dof,
                                               lds_cptr_t ktile, f32x16& s_nx, f32x16& d_nx,
@@ -82,7 +93,7 @@ __device__ __forceinline__ void bwd_ring_tile(const AttnBwdArgs& a, const RowCtx
                                               const uint16_t* pt, const uint16_t* dt,
                                               const BwdRowK& k,
                                               const unsigned* so, const unsigned* loff,
-                                              unsigned wbg) {
+                                              unsigned wbg, float& hsum) {
   using C = AttnCfg<H, DQK, DV>;
   constexpr int KSV = DV / 16;
   typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
@@ -140,6 +151,13 @@ __device__ __forceinline__ void bwd_ring_tile(const AttnBwdArgs& a, const RowCtx
     float p = __builtin_amdgcn_exp2f(fmaf(x, a.scale_log2, -k.msub)) * k.invl;
     p = __builtin_amdgcn_inverse_ballot_w64(m) ? p : 0.f;
     const float g = a.scale * p * (y - k.D);
+    if constexpr (PSUM) {
+      float hs = dpp_add<kDppXor1>(p);
+      hs = dpp_add<kDppXor2>(hs);
+      hs = dpp_add<kDppHalfMirror>(hs);
+      hs = dpp_add<kDppRor8>(hs);
+      hsum = (c.lane & 15) == r ? hs : hsum;
+    }
     if ((r & 1) == 0) {
       p0 = p;
       g0 = g;
@@ -202,7 +220,11 @@ __device__ __forceinline__ void bwd_ring_tile(const AttnBwdArgs& a, const RowCtx
   }
 }
 
-template <int H, int DQK, int DV>
+// PSUM: also each slot's sum over all heads of P (a.psum), for the indexer loss's target.  A
+// wave's 16-lane rows sum their heads inside the element parts; after the tile one lane
+// swap adds the two rows of each half, the waves' sums meet in LDS, and in the next step one
+// wave adds the four and stores the tile's 32 sums.
+template <int H, int DQK, int DV, bool PSUM>
 __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p_ring(AttnBwdArgs a) {
   using C = AttnCfg<H, DQK, DV>;
   static_assert(C::PIPE && C::RPW == 8 && C::NK == 32, "ring shape");
@@ -215,6 +237,7 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p_ring(AttnBwdArgs a
   __shared__ __attribute__((aligned(16))) uint16_t kv3[C::TILE];
   __shared__ __attribute__((aligned(16))) int32_t idxr[2 * kIdxChunk];
   __shared__ int s_last[C::NW];
+  __shared__ float s_hs[PSUM ? 2 : 1][C::NW][C::NK];   // per tile parity, wave and key
 
   RowCtx c = make_ctx(a, block_row(a));
   uint16_t* const bufs[4] = {kv0, kv1, kv2, kv3};
@@ -326,10 +349,11 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p_ring(AttnBwdArgs a
   }
   wait_vm_barrier<3 * C::NI>();   // tile 0 landed; tiles 1 .. 3 may be in flight
   f32x16 sa, da, sb, db;
+  float hsum = 0.f;
   {
     const unsigned so0[RPW] = {};
     bwd_ring_tile<H, DQK, DV, false>(a, c, qf, dof, (lds_cptr_t)bufs[0], sa, da, sb, db, 0u,
-                                     false, nullptr, nullptr, k, so0, loff, 0u);
+                                     false, nullptr, nullptr, k, so0, loff, 0u, hsum);
   }
   int iv = ir[step_slot(0)];
   wait_vm_barrier<2 * C::NI>();   // tile 1 landed
@@ -342,7 +366,22 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p_ring(AttnBwdArgs a
   unsigned w0 = wb[0], w1 = wb[1], w2 = wb[2], w3 = wb[3];
   const uint16_t* const prow = a.ws_p + (size_t)c.row * a.topkp * H;
   const uint16_t* const drow = a.ws_ds + (size_t)c.row * a.topkp * H;
+  // tile tt's head sums: the four waves' parts added (lanes 0..31 = keys), stored by the wave
+  // whose turn it is (its LDS reads follow the barrier that ended tile tt's step)
+  auto psum_flush = [&](int tt) {
+    if (c.wave_u == (tt & 3) && c.lane < C::NK) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::NW; ++w) v += s_hs[PSUM ? tt & 1 : 0][w][c.lane];
+      const float* base = a.psum + (size_t)c.row * a.topkp + (size_t)tt * C::NK;
+      const unsigned voff = (unsigned)c.lane * 4u;
+      asm volatile("global_store_dword %0, %1, %2 nt" :: "v"(voff), "v"(v), "s"(base) : "memory");
+    }
+  };
   auto step = [&](int t, f32x16& s_nx, f32x16& d_nx, const f32x16& s_cu, const f32x16& d_cu) {
+    if constexpr (PSUM) {
+      if (t > 0 && t - 1 < T) psum_flush(t - 1);
+    }
     unsigned off, so[RPW];
     const unsigned vmask = (unsigned)decode_slot<H, DQK, DV>(a, iv, step_slot(t), off);
     wave_row_offsets<H, DQK, DV>(c, off, 32, so);
@@ -351,8 +390,15 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p_ring(AttnBwdArgs a
     // the wait of step t + 2 has seen that gather land
     if ((t & 7) == 0 && t > 0) idx_chunk_dma<H, DQK, DV>(a, c, t / 8 + 1, idxr_lds);
     const size_t toff = (size_t)t * C::NK * H;
-    bwd_ring_tile<H, DQK, DV, true>(a, c, qf, dof, b1, s_nx, d_nx, s_cu, d_cu, vmask, t < T,
-                                    prow + toff, drow + toff, k, so, loff, w0);
+    bwd_ring_tile<H, DQK, DV, true, PSUM>(a, c, qf, dof, b1, s_nx, d_nx, s_cu, d_cu, vmask,
+                                          t < T, prow + toff, drow + toff, k, so, loff, w0, hsum);
+    if constexpr (PSUM) {
+      // rows 0 + 1 and 2 + 3: the sum over the wave's 32 heads of key acc_key(lane & 15, g)
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(hsum), __float_as_uint(hsum),
+                                                       false, false);
+      const float hw = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      if ((c.lane & 16) == 0) s_hs[t & 1][c.wave_u][acc_key(c.lane & 15, c.g)] = hw;
+    }
     iv = ir[step_slot(t + 1) & (2 * kIdxChunk - 1)];
     // tile t+2 landed: its gather is followed by at least the gathers of t+3 and t+4
     wait_vm_barrier<2 * C::NI>();
@@ -373,6 +419,9 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p_ring(AttnBwdArgs a
   for (int t = 0; t < T; t += 2) {
     step(t, sb, db, sa, da);
     step(t + 1, sa, da, sb, db);
+  }
+  if constexpr (PSUM) {
+    if ((T & 1) == 0) psum_flush(T - 1);   // (odd T: step T flushed it)
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no gather or store may outlive the block
 }
@@ -881,13 +930,18 @@ hipError_t launch_key_lists(const KeyListArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The chunk's key lists first, then the four kernels (the lists stay in a.list / a.off for a
+// caller that runs the indexer loss over the same chunk next).
 hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, int h, int d_qk, int d_v, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (!(h == 128 && d_qk == 576 && d_v == 512)) return hipErrorInvalidValue;
   KeyListArgs kl = {a.idx, a.list, a.cnt, a.off, a.cur, a.rows, a.n_k, a.topk, a.topkp};
   hipError_t e = launch_key_lists(kl, s);
   if (e != hipSuccess) return e;
-  k_attn_bwd_p_ring<128, 576, 512><<<a.rows, 256, 0, s>>>(a);
+  if (a.psum)
+    k_attn_bwd_p_ring<128, 576, 512, true><<<a.rows, 256, 0, s>>>(a);
+  else
+    k_attn_bwd_p_ring<128, 576, 512, false><<<a.rows, 256, 0, s>>>(a);
   k_attn_bwd_dq_ring<128, 576, 512><<<a.rows, 256, 0, s>>>(a);
   k_attn_bwd_dkv_part<128, 576, 512><<<a.rows, 256, 0, s>>>(a);
   k_bwd_reduce<576><<<(a.n_k + 3) / 4, 256, 0, s>>>(a);

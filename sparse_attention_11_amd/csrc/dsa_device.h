@@ -125,6 +125,7 @@ struct AttnBwdArgs {
   int* cnt;               // [n_k] entries per key
   int* off;               // [n_k + 1] first entry of each key in `list`
   int* cur;               // [n_k] fill cursor
+  float* psum;            // [rows, topkp] fp32 sum over heads of P per slot, or null
   int rows, n_k, topk;
   int topkp;              // workspace slots per row: topk rounded up to 96
   int xcd_remap;
@@ -149,6 +150,8 @@ struct IdxKlArgs {
   float* dk;              // [n_k, 128] fp32, accumulated
   const int* list;        // key lists of the chunk (see KeyListArgs)
   const int* off;
+  const float* psum;      // [rows, topkp] sum over heads of P per slot (from the attention
+                          // backward), or null: the target is recomputed from q and kv
   int rows, n_k, topk;
   int topkp;              // workspace slots per row: topk rounded up to 96
   int xcd_remap;

@@ -129,6 +129,44 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
 }
 
+// The row's distributions, KL term and dI (block-wide), from the target mass s_p and the
+// indexer values s_i of its ntiles * 32 slots; dI replaces the target in s_p and goes to the
+// workspace for pass 2.
+__device__ __forceinline__ void kl_row_tail(const IdxKlArgs& a, const RowCtx& c, int ntiles,
+                                            float* s_p, const float* s_i, float* s_blk) {
+  const int row = c.row;
+  {
+    const int nsl = ntiles * NK;
+    float m = kNegInf;
+    for (int s = c.tid; s < nsl; s += 256) m = fmaxf(m, s_i[s]);
+    m = block_max(m, s_blk);
+    float se = 0.f, pt = 0.f;
+    for (int s = c.tid; s < nsl; s += 256) {
+      se += expf(s_i[s] - m);
+      pt += s_p[s];
+    }
+    se = block_sum(se, s_blk);
+    pt = block_sum(pt, s_blk);
+    const float lse = m + logf(se);
+    const float ipt = pt > 0.f ? 1.f / pt : 0.f;
+    float kl = 0.f;
+    for (int s = c.tid; s < nsl; s += 256) {
+      const float p = s_p[s] * ipt;
+      const float lr = s_i[s] - lse;       // log softmax(I); -inf at empty slots
+      if (p > 0.f) kl += p * (logf(p) - lr);
+      s_p[s] = a.loss_grad * (expf(lr) - p);
+    }
+    kl = block_sum(kl, s_blk);             // (its barriers also publish dI)
+    if (c.tid == 0) a.loss[row] = kl;
+  }
+  // dI of the row's slots -> workspace, for the pass-2 kernel
+  {
+    float* dst = a.ws_di + (size_t)row * a.topkp;
+    for (int sl = c.tid * 4; sl < ntiles * NK; sl += 256 * 4)
+      *reinterpret_cast<float4*>(dst + sl) = *reinterpret_cast<const float4*>(s_p + sl);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t kv0[AC::TILE];
   __shared__ __attribute__((aligned(16))) uint16_t kv1[AC::TILE];
@@ -409,38 +447,123 @@ __global__ __launch_bounds__(256) void k_idx_kl_p1(IdxKlArgs a) {
   }
   __syncthreads();
 
-  // ---- the row's distributions, KL term and dI
-  {
-    const int nsl = ntiles * NK;
-    float m = kNegInf;
-    for (int s = c.tid; s < nsl; s += 256) m = fmaxf(m, s_i[s]);
-    m = block_max(m, s_blk);
-    float se = 0.f, pt = 0.f;
-    for (int s = c.tid; s < nsl; s += 256) {
-      se += expf(s_i[s] - m);
-      pt += s_p[s];
-    }
-    se = block_sum(se, s_blk);
-    pt = block_sum(pt, s_blk);
-    const float lse = m + logf(se);
-    const float ipt = pt > 0.f ? 1.f / pt : 0.f;
-    float kl = 0.f;
-    for (int s = c.tid; s < nsl; s += 256) {
-      const float p = s_p[s] * ipt;
-      const float lr = s_i[s] - lse;       // log softmax(I); -inf at empty slots
-      if (p > 0.f) kl += p * (logf(p) - lr);
-      s_p[s] = a.loss_grad * (expf(lr) - p);
-    }
-    kl = block_sum(kl, s_blk);             // (its barriers also publish dI)
-    if (c.tid == 0) a.loss[row] = kl;
-  }
+  kl_row_tail(a, c, ntiles, s_p, s_i, s_blk);
+}
 
-  // dI of the row's slots -> workspace, for the pass-2 kernel
-  {
-    float* dst = a.ws_di + (size_t)row * a.topkp;
-    for (int sl = c.tid * 4; sl < ntiles * NK; sl += 256 * 4)
-      *reinterpret_cast<float4*>(dst + sl) = *reinterpret_cast<const float4*>(s_p + sl);
+// Pass 1 with the target given: each slot's sum over heads of the attention probabilities
+// comes from the attention backward (its probability kernel forms them anyway), so the tiles
+// need neither the latent rows nor the logits; only the index keys are gathered (a three-tile
+// ring, tile t+2 during step t) and I formed.  44 KB of LDS: three workgroups per CU.
+__global__ __launch_bounds__(256, 3) void k_idx_kl_p1t(IdxKlArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t kt0[KT];
+  __shared__ __attribute__((aligned(16))) uint16_t kt1[KT];
+  __shared__ __attribute__((aligned(16))) uint16_t kt2[KT];
+  __shared__ __attribute__((aligned(16))) float s_p[kMaxSlots];   // target mass, then dI
+  __shared__ __attribute__((aligned(16))) float s_i[kMaxSlots];   // indexer values I
+  __shared__ float s_red[2][4][NK];   // [tile parity][wave][key] partial I
+  __shared__ __attribute__((aligned(16))) int32_t idxr[2 * kIdxChunk];   // index ring
+  __shared__ int s_last[4];
+  __shared__ float s_blk[4];
+
+  RowCtx c = make_ctx(a, block_row(a));
+  c.ntiles = row_tiles<kH, kDQK, kDV>(a, c, s_last);
+  const int row = c.row;
+  if (c.ntiles == 0) {
+    if (c.tid == 0) a.loss[row] = 0.f;
+    return;
   }
+  const unsigned idxr_lds = lds_addr(idxr);
+  idx_chunk_dma<kH, kDQK, kDV>(a, c, 0, idxr_lds);
+  idx_chunk_dma<kH, kDQK, kDV>(a, c, 1, idxr_lds);
+  const int ntiles = (c.ntiles + 2) / 3 * 3;
+  // the target mass of the row's slots (zero past its last tile)
+  for (int sl = c.tid; sl < ntiles * NK; sl += 256)
+    s_p[sl] = sl < c.ntiles * NK ? a.psum[(size_t)row * a.topkp + sl] : 0.f;
+  const uint16_t* kts[3] = {kt0, kt1, kt2};
+  const int i16 = c.lane & 15, G = c.lane >> 4;
+  bf16x8 qi[4];   // index query of head 16 wave + i16, dims 32 s + 8 G .. +7
+  {
+    const uint16_t* p = a.q_idx + ((size_t)row * kG + 16 * c.wave + i16) * kDI + 8 * G;
+#pragma unroll
+    for (int sx = 0; sx < 4; ++sx)
+      qi[sx] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p + 32 * sx));
+  }
+  const float4 wq = *reinterpret_cast<const float4*>(a.w + (size_t)row * kG + 16 * c.wave + 4 * G);
+  int koff[4];
+#pragma unroll
+  for (int sx = 0; sx < 4; ++sx) koff[sx] = i16 * kDI + (((4 * sx + G) ^ i16) * 8);
+  unsigned kb[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) kb[k] = lds_addr(kts[k]);
+  auto decode = [&](int v, int slot, unsigned& kio) {
+    const bool ok = slot < a.topk && (unsigned)v < (unsigned)a.n_k;
+    kio = ok ? (unsigned)v * (kDI * 2u) : 0u;
+    return (unsigned)__ballot(ok);
+  };
+  auto gather = [&](unsigned kio, int lane0, int k) {
+    unsigned sk[AC::RPW];
+#pragma unroll
+    for (int j = 0; j < AC::RPW; ++j)
+      sk[j] = __builtin_amdgcn_readlane(kio, lane0 + c.wave_u * AC::RPW + j);
+    gather_ktile_so(a, c, sk, kb[k]);
+  };
+  const lds_ci32_t ir = (lds_ci32_t)idxr;
+  auto step_slot = [&](int t) { return (t + 2 * (c.lane >> 5)) * NK + (c.lane & 31); };
+  auto lazy_sum = [&](int tt) {   // tile tt's per-wave partials -> I
+    const int pb = tt & 1;
+    s_i[tt * NK + c.lane] = (s_red[pb][0][c.lane] + s_red[pb][1][c.lane]) +
+                            (s_red[pb][2][c.lane] + s_red[pb][3][c.lane]);
+  };
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  {
+    unsigned kio;
+    (void)decode(ir[c.lane], c.lane, kio);
+    gather(kio, 0, 0);
+    gather(kio, 32, 1);
+  }
+  int iv = ir[step_slot(0)];
+  wait_vm_barrier<0>();
+  auto step = [&](int t, int slot, int ahead2) {
+    unsigned kio;
+    // validity of tile t (lanes 0..31), rows of tile t+2 (lanes 32..63)
+    const unsigned vmask = decode(iv, step_slot(t), kio);
+    if ((t & 7) == 0 && t > 0) idx_chunk_dma<kH, kDQK, kDV>(a, c, t / 8 + 1, idxr_lds);
+    gather(kio, 32, ahead2);
+    if (t >= 1 && c.wave_u == (t & 3) && c.lane < NK) lazy_sum(t - 1);
+    const lds_cptr_t kt = (lds_cptr_t)kts[slot];
+    bf16x8 kf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kf[j] = *(lds_cb8_t)(kt + koff[j >> 1] + (j & 1) * 16 * kDI);
+    f32x4 x0 = (f32x4){}, x1 = (f32x4){};
+#pragma unroll
+    for (int sx = 0; sx < 4; ++sx) {
+      x0 = mfma16(qi[sx], kf[2 * sx], x0);
+      x1 = mfma16(qi[sx], kf[2 * sx + 1], x1);
+    }
+    float v0 = wq.x * fmaxf(x0[0], 0.f) + wq.y * fmaxf(x0[1], 0.f) +
+               wq.z * fmaxf(x0[2], 0.f) + wq.w * fmaxf(x0[3], 0.f);
+    float v1 = wq.x * fmaxf(x1[0], 0.f) + wq.y * fmaxf(x1[1], 0.f) +
+               wq.z * fmaxf(x1[2], 0.f) + wq.w * fmaxf(x1[3], 0.f);
+    v0 = pair32_sum(pair16_sum(v0));
+    v1 = pair32_sum(pair16_sum(v1));
+    if (c.lane < NK) {   // lane = key
+      const int key = c.lane;
+      s_red[t & 1][c.wave][key] = ((vmask >> key) & 1u) ? ((c.lane & 16) ? v1 : v0) : kNegInf;
+    }
+    iv = ir[step_slot(t + 1) & (2 * kIdxChunk - 1)];
+    wait_vm_barrier<GK>();   // tile t+1 landed (only tile t+2's gathers may be in flight)
+  };
+  for (int t = 0; t < ntiles; t += 3) {
+    step(t, 0, 2);
+    step(t + 1, 1, 0);
+    step(t + 2, 2, 1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // gathers past the last tile
+  if (c.wave_u == 0 && c.lane < NK) lazy_sum(ntiles - 1);
+  __syncthreads();
+  kl_row_tail(a, c, ntiles, s_p, s_i, s_blk);
 }
 
 // Pass 2 (a kernel of its own: it needs 51 KB of LDS, so three workgroups share a CU and
@@ -708,11 +831,18 @@ __global__ __launch_bounds__(1024) void k_loss_total(const float* loss, int n, f
 
 }  // namespace
 
-hipError_t launch_indexer_kl(const IdxKlArgs& a, const KeyListArgs& kl, hipStream_t s) {
+// lists: build the chunk's key lists first (false: the caller's are already in a.list / a.off).
+// a.psum set: pass 1 takes the target from it (k_idx_kl_p1t).
+hipError_t launch_indexer_kl(const IdxKlArgs& a, const KeyListArgs& kl, hipStream_t s, bool lists) {
   if (a.rows == 0) return hipSuccess;
-  hipError_t e = launch_key_lists(kl, s);
-  if (e != hipSuccess) return e;
-  k_idx_kl_p1<<<a.rows, 256, 0, s>>>(a);
+  if (lists) {
+    hipError_t e = launch_key_lists(kl, s);
+    if (e != hipSuccess) return e;
+  }
+  if (a.psum)
+    k_idx_kl_p1t<<<a.rows, 256, 0, s>>>(a);
+  else
+    k_idx_kl_p1<<<a.rows, 256, 0, s>>>(a);
   k_idx_kl_p2<<<a.rows, 256, 0, s>>>(a);
   k_idx_kl_reduce<<<(a.n_k + 15) / 16, 256, 0, s>>>(a);
   return hipGetLastError();

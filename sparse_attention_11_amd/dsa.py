@@ -68,6 +68,13 @@ _SIGS = {
                                                 ctypes.c_size_t, _P]),
     "dsa_indexer_kl_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(Shape),
                                                       ctypes.POINTER(ctypes.c_size_t)]),
+    "dsa_sparse_attn_bwd_indexer_kl": (ctypes.c_int, [ctypes.POINTER(Shape), _P, _P, _P, _P, _P,
+                                                      _P, _P, _P, _P, _P, _P, _P,
+                                                      ctypes.c_float, _P, _P, _P, _P, _P, _P,
+                                                      ctypes.c_size_t, _P]),
+    "dsa_sparse_attn_bwd_indexer_kl_workspace_bytes": (ctypes.c_int,
+                                                       [ctypes.POINTER(Shape),
+                                                        ctypes.POINTER(ctypes.c_size_t)]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -382,6 +389,73 @@ def dsa_indexer_kl_loss_grad(q_idx, k_idx, w_idx, q, kv, topk_idx, softmax_max, 
         _ptr(loss_rows), _ptr(loss), _ptr(dq_idx), _ptr(dw_idx), _ptr(dk_idx), _ptr(workspace),
         ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev, stream)))
     return loss, loss_rows, dq_idx, dw_idx, dk_idx
+
+
+def dsa_sparse_attn_bwd_indexer_kl_workspace_bytes(n_q: int, n_k: int, topk: int) -> int:
+    sh = _shape(n_q=n_q, n_k=n_k, h_idx=64, d_idx=128, h=128, d_qk=576, d_v=512, topk=topk,
+                softmax_scale=1.0)
+    n = ctypes.c_size_t(0)
+    _check(load_library().dsa_sparse_attn_bwd_indexer_kl_workspace_bytes(ctypes.byref(sh),
+                                                                         ctypes.byref(n)))
+    return int(n.value)
+
+
+def dsa_sparse_attn_bwd_indexer_kl(q, kv, topk_idx, out, dout, softmax_max, softmax_sum,
+                                   softmax_scale: float, q_idx, k_idx, w_idx,
+                                   loss_grad: float = 1.0, dq=None, dkv=None, dk_idx=None,
+                                   workspace=None, stream=None):
+    """The attention backward and the indexer KL loss of one step in one call.
+
+    Returns (dq, dkv, loss, loss_rows, dq_idx, dw_idx, dk_idx) as dsa_sparse_attn_bwd and
+    dsa_indexer_kl_loss_grad; a given ``dkv`` / ``dk_idx`` is accumulated into, a new one
+    starts at zero."""
+    _dev(q, "q", (torch.bfloat16,), 3)
+    _dev(kv, "kv", (torch.bfloat16,), 2)
+    _dev(topk_idx, "topk_idx", (torch.int32,), 2)
+    _dev(out, "out", (torch.bfloat16,), 3)
+    _dev(dout, "dout", (torch.bfloat16,), 3)
+    _dev(softmax_max, "softmax_max", (torch.float32,), 2)
+    _dev(softmax_sum, "softmax_sum", (torch.float32,), 2)
+    _dev(q_idx, "q_idx", (torch.bfloat16,), 3)
+    _dev(k_idx, "k_idx", (torch.bfloat16,), 2)
+    _dev(w_idx, "w_idx", (torch.float32,), 2)
+    n_q, h, d_qk = q.shape
+    n_k = kv.shape[0]
+    d_v = out.shape[2]
+    topk = topk_idx.shape[1]
+    _, h_idx, d_idx = q_idx.shape
+    if (kv.shape[1] != d_qk or topk_idx.shape[0] != n_q or out.shape[:2] != (n_q, h)
+            or dout.shape != out.shape or softmax_max.shape != (n_q, h)
+            or softmax_sum.shape != (n_q, h) or q_idx.shape[0] != n_q
+            or k_idx.shape != (n_k, d_idx) or w_idx.shape != (n_q, h_idx)):
+        raise ValueError("backward / indexer loss tensor shapes do not match q [n_q,h,d_qk], "
+                         "kv [n_k,d_qk], q_idx [n_q,h_idx,d_idx], k_idx [n_k,d_idx]")
+    dev = q.device
+    if dq is None:
+        dq = torch.empty(n_q, h, d_qk, dtype=torch.bfloat16, device=dev)
+    if dkv is None:
+        dkv = torch.zeros(n_k, d_qk, dtype=torch.float32, device=dev)
+    if dk_idx is None:
+        dk_idx = torch.zeros(n_k, d_idx, dtype=torch.float32, device=dev)
+    _dev(dq, "dq", (torch.bfloat16,), 3)
+    _dev(dkv, "dkv", (torch.float32,), 2)
+    _dev(dk_idx, "dk_idx", (torch.float32,), 2)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    loss_rows = torch.empty(n_q, dtype=torch.float32, device=dev)
+    dq_idx = torch.empty(n_q, h_idx, d_idx, dtype=torch.bfloat16, device=dev)
+    dw_idx = torch.empty(n_q, h_idx, dtype=torch.float32, device=dev)
+    sh = _shape(n_q=n_q, n_k=n_k, h_idx=h_idx, d_idx=d_idx, h=h, d_qk=d_qk, d_v=d_v, topk=topk,
+                softmax_scale=softmax_scale)
+    if workspace is None:
+        nb = dsa_sparse_attn_bwd_indexer_kl_workspace_bytes(n_q, n_k, topk)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    _check(load_library().dsa_sparse_attn_bwd_indexer_kl(
+        ctypes.byref(sh), _ptr(q), _ptr(kv), _ptr(topk_idx), _ptr(out), _ptr(dout),
+        _ptr(softmax_max), _ptr(softmax_sum), _ptr(dq), _ptr(dkv), _ptr(q_idx), _ptr(k_idx),
+        _ptr(w_idx), ctypes.c_float(loss_grad), _ptr(loss_rows), _ptr(loss), _ptr(dq_idx),
+        _ptr(dw_idx), _ptr(dk_idx), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev, stream)))
+    return dq, dkv, loss, loss_rows, dq_idx, dw_idx, dk_idx
 
 
 def dsa_forward(q_idx, k_idx, w_idx, q, kv, segments, topk: int, softmax_scale: float,

@@ -260,6 +260,65 @@ def test_indexer_kl_argument_checks(lib):
     assert _kl(lib, shape(n_q=0), 0, workspace=None) == dsa.DSA_OK
 
 
+def _bwdkl(lib, sh, ws_bytes, workspace=FAKE, null=None, misalign=None, loss_grad=1.0):
+    names = ("q", "kv", "idx", "out", "dout", "smax", "ssum", "dq", "dkv", "q_idx", "k_idx",
+             "w_idx", "loss_rows", "dq_idx", "dw_idx", "dk_idx")
+    ptrs = {k: FAKE for k in names}
+    if null:
+        ptrs[null] = None
+    if misalign:
+        ptrs[misalign] = ctypes.c_void_p(0x1008)
+    return lib.dsa_sparse_attn_bwd_indexer_kl(
+        ctypes.byref(sh), ptrs["q"], ptrs["kv"], ptrs["idx"], ptrs["out"], ptrs["dout"],
+        ptrs["smax"], ptrs["ssum"], ptrs["dq"], ptrs["dkv"], ptrs["q_idx"], ptrs["k_idx"],
+        ptrs["w_idx"], ctypes.c_float(loss_grad), ptrs["loss_rows"], None, ptrs["dq_idx"],
+        ptrs["dw_idx"], ptrs["dk_idx"], workspace, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_backward_with_indexer_loss_argument_checks(lib):
+    # workspace: the attention backward's (per row two bf16 [topk_p, h] arrays, the bf16
+    # [topk_p, d_qk] contributions, topk list entries) plus fp32 [topk_p] head sums per row;
+    # per call 3 n_k + 1 ints and alignment slack
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    def row(topk, topkp):
+        return 2 * topkp * 128 * 2 + topkp * 576 * 2 + topk * 4 + topkp * 4
+
+    def shape(**kw):
+        base = dict(n_q=5000, n_k=8192, h_idx=64, d_idx=128, h=128, d_qk=576, d_v=512, topk=2048,
+                    softmax_scale=0.1)
+        base.update(kw)
+        return dsa._shape(**base)
+
+    sh = shape()
+    n = ctypes.c_size_t(0)
+    assert lib.dsa_sparse_attn_bwd_indexer_kl_workspace_bytes(ctypes.byref(sh),
+                                                              ctypes.byref(n)) == dsa.DSA_OK
+    fixed = al((3 * 8192 + 1) * 4) + 8 * 256
+    assert n.value == fixed + 2048 * row(2048, 2112)
+    assert dsa.dsa_sparse_attn_bwd_indexer_kl_workspace_bytes(10, 100, 100) == \
+        al((3 * 100 + 1) * 4) + 8 * 256 + 10 * row(100, 192)
+    per_row = fixed + row(2048, 2112)
+    assert _bwdkl(lib, sh, per_row - 1) == dsa.DSA_ERR_WORKSPACE
+    assert _bwdkl(lib, sh, per_row, workspace=None) == dsa.DSA_ERR_WORKSPACE
+    for name in ("q", "dout", "dkv", "q_idx", "w_idx", "loss_rows", "dk_idx"):
+        assert _bwdkl(lib, sh, per_row, null=name) == dsa.DSA_ERR_INVALID_ARG, name
+    for name in ("dkv", "q_idx", "w_idx", "dk_idx", "dout"):
+        assert _bwdkl(lib, sh, per_row, misalign=name) == dsa.DSA_ERR_INVALID_ARG, name
+    assert _bwdkl(lib, sh, per_row, workspace=ctypes.c_void_p(0x1008)) == dsa.DSA_ERR_INVALID_ARG
+    assert _bwdkl(lib, sh, per_row, loss_grad=float("inf")) == dsa.DSA_ERR_INVALID_ARG
+    # the union of the two calls' unsupported cases
+    assert _bwdkl(lib, shape(h_idx=4, d_idx=32), 1 << 30) == dsa.DSA_ERR_UNSUPPORTED
+    assert _bwdkl(lib, shape(h=8, d_qk=80, d_v=64), 1 << 30) == dsa.DSA_ERR_UNSUPPORTED
+    assert _bwdkl(lib, shape(topk=2049), 1 << 30) == dsa.DSA_ERR_UNSUPPORTED
+    fp8 = shape()
+    fp8.idx_dtype = dsa.DSA_IDX_FP8_E4M3
+    assert _bwdkl(lib, fp8, 1 << 30) == dsa.DSA_ERR_UNSUPPORTED
+    # nothing to do for zero rows (and no total requested)
+    assert _bwdkl(lib, shape(n_q=0), 0, workspace=None) == dsa.DSA_OK
+
+
 def test_quantize_argument_checks(lib):
     assert lib.dsa_quantize_fp8_rows(FAKE, -1, 8, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
     assert lib.dsa_quantize_fp8_rows(FAKE, 0, 8, FAKE, FAKE, None) == dsa.DSA_OK
