@@ -143,7 +143,7 @@ def backward_stage(args, n=5):
     """Training-side kernels on the packed varlen workload (8 documents, 32768 tokens): the
     GPU forward supplies indices, output and softmax statistics; the sparse-attention backward
     (P / dS, dQ, dKV kernels) and the indexer KL loss with its gradients are each timed on
-    their own with HIP events."""
+    their own with HIP events, then both in the one combined call."""
     wl = I.workload(n)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
@@ -183,6 +183,25 @@ def backward_stage(args, n=5):
           flush=True)
     rec["indexer_kl"] = {"ms": kms, "flop": kflop, "tflops": kflop / (kms * 1e-3) / 1e12,
                          "mfma_frac": kflop / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    del kws
+    # both in one call (dsa_sparse_attn_bwd_indexer_kl): the indexer loss takes its target
+    # from the backward's probabilities and shares its key lists; the useful work is the
+    # backward's plus the indexer part of the loss (3 x 2 h_idx d_idx per slot)
+    dq = torch.empty_like(g["q"])
+    cws = torch.empty(dsa.dsa_sparse_attn_bwd_indexer_kl_workspace_bytes(wl.n_q, wl.n_k, wl.topk),
+                      dtype=torch.uint8, device=dev)
+
+    def both():
+        dsa.dsa_sparse_attn_bwd_indexer_kl(g["q"], g["kv"], idx, out, g["dout"], smax, ssum,
+                                           wl.softmax_scale, g["q_idx"], g["k_idx"], g["w_idx"],
+                                           dq=dq, dkv=dkv, dk_idx=dk, workspace=cws)
+    cms = time_launches(both, reps, stream)
+    cflop = flop + 2.0 * n_sel * 3 * wl.h_idx * wl.d_idx
+    print(f"bench: backward + indexer loss in one call {wl.name} {cms:.3f} ms (separate "
+          f"{ms + kms:.3f} ms)", file=sys.stderr, flush=True)
+    rec["with_indexer_kl"] = {"ms": cms, "separate_ms": ms + kms, "flop": cflop,
+                              "tflops": cflop / (cms * 1e-3) / 1e12,
+                              "mfma_frac": cflop / (cms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     return rec
 
 
