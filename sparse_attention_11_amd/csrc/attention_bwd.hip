@@ -73,17 +73,18 @@ struct BwdRowK {
 };
 
 // DPP source modes of the 16-lane sums: lane l reads lane l ^ 1, l ^ 2, (l & ~7) | (7 - l % 8)
-// and l ^ 8 of its 16-lane row.
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppRor8 = 0x128;
+// and l ^ 8 of its 16-lane row; row_shr:1 moves every lane's value one lane up the row.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppRor8 = 0x128,
+              kDppShr1 = 0x111;
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float x) {
   return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
 // One ring step (PARTS) or the row prologue's products of tile 0 alone (no parts, no gather).
-// PSUM: also the sum over the 16 heads of each 16-lane row of P for every part; the lane at
-// row position r keeps part r's (hsum), so after the tile each lane holds one key's sum over
-// its row's heads.
+// PSUM: also the sum over the 16 heads of each 16-lane row of P for every part, shifted into
+// hsum at row position 0 while the earlier parts' sums move one lane up (no per-lane select),
+// so after the tile row position i holds part 15 - i's sum over its row's heads.
 template <int H, int DQK, int DV, bool PARTS, bool PSUM = false>
 __device__ __forceinline__ void bwd_ring_tile(const AttnBwdArgs& a, const RowCtx& c,
                                               const bf16x8* qf, const bf16x8* dof,
@@ -156,7 +157,9 @@ __device__ __forceinline__ void bwd_ring_tile(const AttnBwdArgs& a, const RowCtx
       hs = dpp_add<kDppXor2>(hs);
       hs = dpp_add<kDppHalfMirror>(hs);
       hs = dpp_add<kDppRor8>(hs);
-      hsum = (c.lane & 15) == r ? hs : hsum;
+      // (row position 0 has no source lane: it keeps `old`, the new sum)
+      hsum = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(hs), __float_as_int(hsum),
+                                                        kDppShr1, 0xF, 0xF, false));
     }
     if ((r & 1) == 0) {
       p0 = p;
@@ -393,11 +396,12 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p_ring(AttnBwdArgs a
     bwd_ring_tile<H, DQK, DV, true, PSUM>(a, c, qf, dof, b1, s_nx, d_nx, s_cu, d_cu, vmask,
                                           t < T, prow + toff, drow + toff, k, so, loff, w0, hsum);
     if constexpr (PSUM) {
-      // rows 0 + 1 and 2 + 3: the sum over the wave's 32 heads of key acc_key(lane & 15, g)
+      // rows 0 + 1 and 2 + 3: the sum over the wave's 32 heads of key
+      // acc_key(15 - lane % 16, g)
       const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(hsum), __float_as_uint(hsum),
                                                        false, false);
       const float hw = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      if ((c.lane & 16) == 0) s_hs[t & 1][c.wave_u][acc_key(c.lane & 15, c.g)] = hw;
+      if ((c.lane & 16) == 0) s_hs[t & 1][c.wave_u][acc_key(15 - (c.lane & 15), c.g)] = hw;
     }
     iv = ir[step_slot(t + 1) & (2 * kIdxChunk - 1)];
     // tile t+2 landed: its gather is followed by at least the gathers of t+3 and t+4
