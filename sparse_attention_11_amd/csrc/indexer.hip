@@ -301,10 +301,11 @@ __device__ __forceinline__ void cand_mark(CandRow& c, float s, int kb, bool v, C
 __device__ __forceinline__ void cand_flush(const CandRow& c, CandPend& pd) {
   if (pd.valid) {
     const int lane = threadIdx.x & 63;
-    if ((pd.m >> lane) & 1ull) {
-      const int p = pd.nb + (int)lanes_below(pd.m);
-      c.cs[p] = pd.s;
-      c.ck[p] = (uint16_t)(pd.kb + lane);
+    if (__builtin_amdgcn_inverse_ballot_w64(pd.m)) {
+      // 32-bit byte offsets from the row's (scalar) list bases
+      const unsigned p = (unsigned)pd.nb + (unsigned)lanes_below(pd.m);
+      *reinterpret_cast<float*>(reinterpret_cast<char*>(c.cs) + p * 4u) = pd.s;
+      *reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(c.ck) + p * 2u) = (uint16_t)(pd.kb + lane);
     }
     pd.valid = false;
   }
@@ -336,7 +337,8 @@ __device__ __forceinline__ RowInfo indexer_row(const SegTable& segs) {
   const int g = seg_of_block(segs, blk);
   const int nb = segs.blk_off[g + 1] - segs.blk_off[g];
   const int lb = nb - 1 - (blk - segs.blk_off[g]);  // later rows (longer windows) first
-  const int wave = threadIdx.x >> 6;
+  // (wave-uniform, and known so: the row's pointers and window bounds stay scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   ri.q_len = segs.q_len[g];
   const int r0 = lb * kIdxWaves;
   ri.r = r0 + wave;
