@@ -14,6 +14,9 @@
 //     dP^T = V dY^T, so the tile is read from LDS once for both.  Each wave owns 32 heads.
 //     It writes P and softmax_scale * dS as bf16 to a [row][slot][head] workspace (zero at
 //     empty slots), the element work of one tile interleaved with the products of the next.
+//     For the combined backward + indexer-loss call it also writes each slot's fp32 sum of P
+//     over the heads (the indexer loss's target, page section
+//     "SparseLightningIndexerGradKLLoss"), from the fp32 probabilities before rounding.
 //   * k_attn_bwd_dq_ring: gathers the key tiles again (index ring) together with the
 //     tile's dS block (both by LDS DMA) and accumulates dQ^T[dim, head] += K^T dS^T, each
 //     wave over 144 latent dims and all 128 heads (K^T and dS^T read with the transposing

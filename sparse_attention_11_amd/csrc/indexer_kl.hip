@@ -29,6 +29,9 @@
 //     that owns 32 of its 128 dims and written as bf16 per (row, slot).
 //   * The per-slot key gradients are then summed per key (the chunk's entries grouped by key,
 //     16 lanes per key) and added to dk_idx: no float atomics.
+// When the attention backward runs in the same call it hands over each slot's sum over heads
+// of P, and pass 1 (k_idx_kl_p1t) gathers only the index keys and forms I; the target mass is
+// read, not recomputed.
 #include <algorithm>
 
 #include "attn_common.h"
