@@ -89,6 +89,27 @@ def test_bwd_kl_matches_separate_calls_and_oracle(docs, topk, seed, pos0, n_k):
     K._check_full(wl, x, idx, (loss, loss_rows, dq_idx, dw, dk))
 
 
+def test_bwd_kl_rows_without_selections_and_holes():
+    """Rows whose indices are all empty (-1) get no gradient and loss 0, and holes (-1 or out of
+    range) inside other rows' lists are skipped, in the combined call as in the separate ones."""
+    _need_gpu()
+    wl, x, g = B._varlen_case([70, 130], 96, seed=2306)
+    out, idx, smax, ssum = _forward(wl, g)
+    idx = idx.clone()
+    idx[[0, 5, 77, 150]] = -1                      # no selection at all
+    idx[10, 3] = -1                                # holes
+    idx[120, [0, 7, 40]] = -1
+    idx[121, 2] = wl.n_k + 5                       # out of range: empty
+    got = _combined(wl, g, out, idx, smax, ssum)
+    ref = _separate(wl, g, out, idx, smax, ssum)
+    torch.cuda.synchronize()
+    _check_same(got, ref)
+    dq, dkv, loss, loss_rows, dq_idx, dw, dk = got
+    for r in (0, 5, 77, 150):
+        assert torch.all(dq[r] == 0) and float(loss_rows[r]) == 0.0
+        assert torch.all(dq_idx[r] == 0) and torch.all(dw[r] == 0)
+
+
 def test_bwd_kl_chunked_and_accumulating():
     """A workspace of 3 rows (many chunks) reproduces the per-row outputs of one chunk bit for
     bit; given dkv / dk_idx are added to; a loss gradient other than 1."""
