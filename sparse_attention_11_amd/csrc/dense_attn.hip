@@ -94,11 +94,10 @@ __global__ __launch_bounds__(kNWd * 64) void k_dense_attn(DenseArgs a) {
   // DMA of tile t into ring slot s: wave w copies pieces w kPcW .. + kPcW - 1 of the 40 (K
   // pieces first); key rows past the block's last position are clamped to it (in bounds,
   // masked by causality)
-  auto issue_tile = [&](int t, int s) {
+  auto issue_piece = [&](int t, int s, int i) {
     const int kbase = kst + t * kKeysT;
     const int klast = kst + plast;
-#pragma unroll
-    for (int i = 0; i < kPcW; ++i) {
+    {
       const int pc = wave_u * kPcW + i;
       if (pc < kKPc) {
         const int f = pc * 64 + lane;
@@ -116,6 +115,11 @@ __global__ __launch_bounds__(kNWd * 64) void k_dense_attn(DenseArgs a) {
       }
     }
   };
+  auto issue_tile = [&](int t, int s) {
+#pragma unroll
+    for (int i = 0; i < kPcW; ++i) issue_piece(t, s, i);
+  };
+  static_assert(2 * kPcW <= kKsD, "one DMA piece every second K step of the logits");
 
   // prologue: tiles 0 and 1 in flight with the wave's Q rows (B operand: lane (hl, g) holds
   // dims 16 ks + 8 g .. + 7 of row hl)
@@ -148,8 +152,12 @@ __global__ __launch_bounds__(kNWd * 64) void k_dense_attn(DenseArgs a) {
   typedef __attribute__((address_space(3))) const bf16x8* lds_cb8_t;
   for (int t = 0, s = 0; t < T; ++t, s = (s == kRing - 1 ? 0 : s + 1)) {
     const int s2 = s == 0 ? 2 : s - 1;             // slot of tile t + 2 (= slot of t - 1)
-    if (t + 2 < T) issue_tile(t + 2, s2);
-    if (wactive && t <= t_last) {
+    // tile t + 2's DMA: between the logits' K steps when the wave computes this tile (issued
+    // by all eight waves together at the step start, the 40 DMA instructions queue while the
+    // matrix pipe idles), else here
+    const bool busy = wactive && t <= t_last;
+    if (t + 2 < T && !busy) issue_tile(t + 2, s2);
+    if (busy) {
       const lds_cptr_t kt = (lds_cptr_t)ring + s * kKTileE;
       const lds_cptr_t vt = (lds_cptr_t)ring + kRing * kKTileE + s * kVTileE;
       f32x16 sc[2] = {(f32x16){}, (f32x16){}};
@@ -160,6 +168,7 @@ __global__ __launch_bounds__(kNWd * 64) void k_dense_attn(DenseArgs a) {
         const bf16x8 a1 = *(lds_cb8_t)(kt + (arow + 32) * kDq + ch);
         sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], sc[0], 0, 0, 0);
         sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], sc[1], 0, 0, 0);
+        if (t + 2 < T && ks % 2 == 0 && ks / 2 < kPcW) issue_piece(t + 2, s2, ks / 2);
       }
       const int kt0 = t * kKeysT;
       if (kt0 + kKeysT - 1 > wpos_lo) {            // the tile crosses this wave's diagonal
