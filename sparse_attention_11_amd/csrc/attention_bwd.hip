@@ -77,17 +77,24 @@ struct BwdRowK {
 
 // DPP source modes of the 16-lane sums: lane l reads lane l ^ 1, l ^ 2, (l & ~7) | (7 - l % 8)
 // and l ^ 8 of its 16-lane row; row_shr:1 moves every lane's value one lane up the row.
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppRor8 = 0x128,
-              kDppShr1 = 0x111;
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor8 = 0x128, kDppShl4 = 0x104,
+              kDppShr4 = 0x114;
 template <int CTRL>
-__device__ __forceinline__ float dpp_add(float x) {
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// x of lane L ^ 4 within each row of 16: banks 1 and 3 (lanes 4-7, 12-15) take lane L - 4,
+// banks 0 and 2 lane L + 4
+__device__ __forceinline__ float dpp_xor4(float x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppShr4, 0xF, 0xA, false);
+  return __int_as_float(__builtin_amdgcn_update_dpp(lo, __float_as_int(x), kDppShl4, 0xF, 0x5, false));
 }
 
 // One ring step (PARTS) or the row prologue's products of tile 0 alone (no parts, no gather).
-// PSUM: also the sum over the 16 heads of each 16-lane row of P for every part, shifted into
-// hsum at row position 0 while the earlier parts' sums move one lane up (no per-lane select),
-// so after the tile row position i holds part 15 - i's sum over its row's heads.
+// PSUM: also the sum over the 16 heads of each 16-lane row of P for every part, by a
+// transposing butterfly over the parts as they come (partners lane ^ 1, ^ 2, ^ 4, ^ 8: at
+// each level a lane keeps the half of the pending sums its lane bit names and adds the
+// partner's copy of it), so after the tile row position i holds part i's sum in hsum.
 template <int H, int DQK, int DV, bool PARTS, bool PSUM = false>
 __device__ __forceinline__ void bwd_ring_tile(const AttnBwdArgs& a, const RowCtx& c,
                                               const bf16x8* qf, const bf16x8* dof,
@@ -143,6 +150,7 @@ __device__ __forceinline__ void bwd_ring_tile(const AttnBwdArgs& a, const RowCtx
   // head; after an odd r the pair (r-1, r) is stored: the head pair's dword assembled across
   // the lane pair, one store per tensor
   float p0 = 0.f, g0 = 0.f;
+  float hx1 = 0.f, hx2 = 0.f, hx3 = 0.f;   // pending butterfly sums (PSUM)
   auto part = [&](int r) {
     // validity of the key per lane half, as a lane mask (the list's validity bits are
     // wave-uniform): lanes 0-31 hold key acc_key(r, 0), lanes 32-63 acc_key(r, 1)
@@ -156,13 +164,27 @@ __device__ __forceinline__ void bwd_ring_tile(const AttnBwdArgs& a, const RowCtx
     p = __builtin_amdgcn_inverse_ballot_w64(m) ? p : 0.f;
     const float g = a.scale * p * (y - k.D);
     if constexpr (PSUM) {
-      float hs = dpp_add<kDppXor1>(p);
-      hs = dpp_add<kDppXor2>(hs);
-      hs = dpp_add<kDppHalfMirror>(hs);
-      hs = dpp_add<kDppRor8>(hs);
-      // (row position 0 has no source lane: it keeps `old`, the new sum)
-      hsum = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(hs), __float_as_int(hsum),
-                                                        kDppShr1, 0xF, 0xF, false));
+      static_assert(kBwdParts == 16, "one butterfly level per bit of the part index");
+      // lane-bit masks as SGPR pairs: lanes with bit 0 / 1 / 2 / 3 set
+      const bool b0 = __builtin_amdgcn_inverse_ballot_w64(0xAAAAAAAAAAAAAAAAull);
+      const bool b1 = __builtin_amdgcn_inverse_ballot_w64(0xCCCCCCCCCCCCCCCCull);
+      const bool b2 = __builtin_amdgcn_inverse_ballot_w64(0xF0F0F0F0F0F0F0F0ull);
+      const bool b3 = __builtin_amdgcn_inverse_ballot_w64(0xFF00FF00FF00FF00ull);
+      if (r & 1) {   // parts r-1 (p0) and r over lane pairs
+        const float x1 = (b0 ? p : p0) + dpp_mov<kDppXor1>(b0 ? p0 : p);
+        if ((r & 2) == 0) {
+          hx1 = x1;
+        } else {     // parts r-3 .. r over lane quads
+          const float x2 = (b1 ? x1 : hx1) + dpp_mov<kDppXor2>(b1 ? hx1 : x1);
+          if ((r & 4) == 0) {
+            hx2 = x2;
+          } else {   // parts r-7 .. r over lane octets
+            const float x3 = (b2 ? x2 : hx2) + dpp_xor4(b2 ? hx2 : x2);
+            if ((r & 8) == 0) hx3 = x3;
+            else hsum = (b3 ? x3 : hx3) + dpp_mov<kDppRor8>(b3 ? hx3 : x3);
+          }
+        }
+      }
     }
     if ((r & 1) == 0) {
       p0 = p;
@@ -399,12 +421,11 @@ __global__ __launch_bounds__(64 * (H / 32)) void k_attn_bwd_p_ring(AttnBwdArgs a
     bwd_ring_tile<H, DQK, DV, true, PSUM>(a, c, qf, dof, b1, s_nx, d_nx, s_cu, d_cu, vmask,
                                           t < T, prow + toff, drow + toff, k, so, loff, w0, hsum);
     if constexpr (PSUM) {
-      // rows 0 + 1 and 2 + 3: the sum over the wave's 32 heads of key
-      // acc_key(15 - lane % 16, g)
+      // rows 0 + 1 and 2 + 3: the sum over the wave's 32 heads of key acc_key(lane % 16, g)
       const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(hsum), __float_as_uint(hsum),
                                                        false, false);
       const float hw = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      if ((c.lane & 16) == 0) s_hs[t & 1][c.wave_u][acc_key(15 - (c.lane & 15), c.g)] = hw;
+      if ((c.lane & 16) == 0) s_hs[t & 1][c.wave_u][acc_key(c.lane & 15, c.g)] = hw;
     }
     iv = ir[step_slot(t + 1) & (2 * kIdxChunk - 1)];
     // tile t+2 landed: its gather is followed by at least the gathers of t+3 and t+4
